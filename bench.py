@@ -1,0 +1,177 @@
+"""Benchmark of the Muon step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One "step" is one complete muon_step (momentum, Frobenius normalisation,
+Gram Newton–Schulz with 5 quintic steps, weight update) over every matrix of
+the workload, with all inputs resident in HBM.  The default workload is the
+full Qwen2.5-7B-shaped matrix set: 28 layers × {q, o 3584×3584; k, v
+512×3584; gate, up 18944×3584; down 3584×18944} = 196 matrices, 6.53 B
+parameters, bf16 weights, fp32 gradients and momentum (seeded synthetic data).
+
+Prints one JSON line: whole-step throughput in algorithmic TFLOP/s (Gram
+formulation; symmetric products count their upper triangle only), the
+roofline of the dominant kernel (HIP events over the timed region) and the
+fp64 CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_PEAK_F16 = 2500.0   # TFLOP/s, MI355X dense fp16/bf16 MFMA
+MFMA_PEAK_F32 = 157.3    # TFLOP/s, MI355X dense fp32 MFMA
+HBM_PEAK = 8000.0        # GB/s
+
+METRIC = "Muon step ms & NS TFLOP/s (% MFMA peak), Qwen2.5-7B-shaped matrix set"
+
+
+def workload_shapes(name):
+    import workloads as W
+    if name == "qwen_full":
+        return W.qwen_model_shapes(28)
+    if name == "qwen_layer":
+        return W.qwen_model_shapes(1)
+    raise SystemExit(f"unknown workload {name}")
+
+
+def gram_flops(shapes, steps=5):
+    tot = 0
+    for r, c in shapes:
+        m, n = min(r, c), max(r, c)
+        tot += m * (m + 1) * n + (4 * steps - 3) * m * m * (m + 1) + 2 * m * m * n
+    return tot
+
+
+def cpu_baseline(budget_s=30.0):
+    """The oracle as it stands, on a bounded sample of the workload: one
+    q-shaped (3584×3584) and one k-shaped (512×3584) matrix of layer 0, one
+    full muon_step each (momentum, fp64 standard Newton–Schulz, update)."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import workloads as W
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 0) for d in threadpool_info()] or [os.cpu_count()])
+    except Exception:
+        threads = os.cpu_count()
+    shapes = [(512, 3584), (3584, 3584)]
+    inp = W.muon_inputs(shapes, 5001, device="cpu")
+    t0 = time.perf_counter()
+    done = []
+    for j, (r, c) in enumerate(shapes):
+        oracle.muon_step(inp.params[j].float().numpy(), inp.grads[j].numpy(),
+                         inp.momenta[j].numpy(), np.float32(0.95), 0.02, oracle.QUINTIC, 5, 1e-7)
+        done.append((r, c))
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    fl = gram_flops(done)
+    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"muon_step on {len(done)} matrices {done} of layer 0 "
+                      f"(fp64 numpy, standard NS), {dt:.2f} s; algorithmic Gram flops / time"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="qwen_full")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the step shards by matrix across GPUs "
+              "but no multi-GPU path is built; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import muon_newton_schulz_06_amd as mns
+    import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    mns.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    shapes = workload_shapes(args.workload)
+    seed0 = 5001
+    print(f"[bench] generating {len(shapes)} matrices on {dev}", file=sys.stderr, flush=True)
+    inp = W.muon_inputs(shapes, seed0, device=dev)
+    ws = torch.empty(mns.step_workspace_size(shapes), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        mns.muon_step(inp.params, inp.grads, inp.momenta, beta=0.95, lr=0.02, steps=5,
+                      workspace=ws, stream=stream)
+
+    for i in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done", file=sys.stderr, flush=True)
+
+    mns.profile_enable(True)
+    for k in mns.PROFILE_KINDS:
+        mns.profile_read(k)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    mns.profile_enable(False)
+    kinds = {k: mns.profile_read(k) for k in mns.PROFILE_KINDS}
+    ms = (t1 - t0) * 1e3 / args.steps
+    F = gram_flops(shapes)
+    tflops = F / (ms / 1e3) / 1e12
+
+    breakdown = {}
+    for k, v in kinds.items():
+        if v["launches"] == 0:
+            continue
+        per_step_ms = v["ms"] / args.steps
+        if k in ("syrk", "gram", "final"):
+            rate = v["work"] / (v["ms"] / 1e3) / 1e12
+            breakdown[k] = {"ms_per_step": per_step_ms, "launches_per_step": v["launches"] // args.steps,
+                            "tflops": rate, "frac_peak": rate / MFMA_PEAK_F16}
+        else:
+            rate = v["work"] / (v["ms"] / 1e3) / 1e9
+            breakdown[k] = {"ms_per_step": per_step_ms, "launches_per_step": v["launches"] // args.steps,
+                            "gbs": rate, "frac_peak": rate / HBM_PEAK}
+    dom = max(("syrk", "gram", "final"), key=lambda k: kinds[k]["ms"])
+    d = kinds[dom]
+    achieved = (d["work"] / d["launches"]) / (d["ms"] / d["launches"] / 1e3) / 1e12
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": MFMA_PEAK_F16,
+                "unit": "TFLOP/s", "frac": achieved / MFMA_PEAK_F16, "traffic": None,
+                "avg_launch_ms": d["ms"] / d["launches"],
+                "algorithmic_per_launch": d["work"] / d["launches"]}
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
+        cpu = cpu_baseline()
+    line = {
+        "metric": METRIC, "value": tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": f"{args.workload}: Qwen2.5-7B-shaped matrix set "
+                               f"({len(shapes)} matrices, {sum(r * c for r, c in shapes)} params)",
+                   "op": "muon_step", "ns_steps": 5, "coeffs": "quintic (3.4445, -4.775, 2.0315)",
+                   "param_dtype": "bf16", "grad_dtype": "f32", "momentum_dtype": "f32",
+                   "mfma_operands": "f16 (power-of-two scaled)", "accumulate": "f32",
+                   "algorithmic_tflop_per_step": F / 1e12, "parallelism": "single GPU"},
+        "frac_mfma_peak": tflops / MFMA_PEAK_F16,
+        "roofline": roofline, "breakdown": breakdown, "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,153 @@
+/*
+ * muon_ns.h — C ABI of the MI355X (gfx950) Muon / Newton–Schulz library.
+ *
+ * What is computed (sources are the pages this library implements):
+ *   - DMuon technical summary (gist.science, Korean), §1 "Problem definition":
+ *     Muon applies a Newton–Schulz (NS) iteration to the momentum-accumulated
+ *     gradient of each weight matrix.
+ *   - same page, §2.2 "Efficient Gram Newton–Schulz iteration": the iteration
+ *     runs in the m×m Gram space G = X·Xᵀ (m < n), exploits the symmetry of G
+ *     with SYRK-style upper-triangle products, and batches matrices of similar
+ *     shape so that one dispatch serves many of them.
+ *   - DeMuon technical summary (gist.science, Korean), Method §1: momentum is
+ *     a moving average of gradients and the update applies msgn(·).
+ *
+ * Per matrix (stored rows × cols, row-major), with m = min(rows, cols):
+ *   X₀ = M / (‖M‖_F + eps), transposed first when rows > cols;
+ *   s times: A = X·Xᵀ; X ← a·X + (b·A + c·A²)·X   (computed in Gram space);
+ *   O = X transposed back to rows × cols.
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor pointers are DEVICE pointers on the current HIP device,
+ *     owned by the caller.  The library only borrows them for the enqueue.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default
+ *     stream), asynchronously: results are valid once the stream reaches
+ *     the enqueued work.  No entry point synchronises the host with the GPU.
+ *   - `workspace` is caller-allocated device memory of at least the size
+ *     the matching *_workspace_size query returns, 256-byte aligned.  Its
+ *     contents on entry do not matter and are garbage on exit.
+ *   - Argument checks run on the host BEFORE any HIP call.  On any error
+ *     nothing is enqueued and a status other than MUON_OK is returned; the
+ *     message is available from muon_last_error() (per thread).
+ *   - NaN / Inf in the inputs propagate to the outputs; nothing is repaired.
+ *   - No C++ exception crosses this boundary.
+ */
+#ifndef MUON_NS_H
+#define MUON_NS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MUON_NS_ABI_VERSION 1
+
+typedef enum muon_status {
+  MUON_OK = 0,
+  MUON_ERR_INVALID_ARG = 1, /* null pointer, bad size, bad stride, bad scalar */
+  MUON_ERR_UNSUPPORTED = 2, /* a valid request this build does not handle   */
+  MUON_ERR_ALIAS = 3,       /* writable ranges that overlap                  */
+  MUON_ERR_WORKSPACE = 4,   /* workspace missing, too small or misaligned    */
+  MUON_ERR_HIP = 5,         /* a HIP call or kernel launch failed            */
+  MUON_ERR_NO_DEVICE = 6    /* no HIP device is visible                      */
+} muon_status_t;
+
+typedef enum muon_dtype {
+  MUON_DTYPE_F32 = 0,  /* IEEE float32                                   */
+  MUON_DTYPE_BF16 = 1  /* bfloat16 (8 significant bits, float32 range)   */
+} muon_dtype_t;
+
+/* One matrix of a batched orthogonalisation.
+ *   x:    input, rows × cols, element (i, j) at x[i*ld_x + j], dtype of the call
+ *   out:  output, same shape and dtype, element (i, j) at out[i*ld_out + j]
+ *   rows, cols ≥ 0 (a matrix with no elements is skipped);
+ *   ld_x ≥ cols, ld_out ≥ cols (elements).
+ * out may equal x (in place): every input is read before any output is
+ * written.  Outputs of different matrices must not overlap. */
+typedef struct muon_ns_desc {
+  const void* x;
+  void* out;
+  int64_t rows;
+  int64_t cols;
+  int64_t ld_x;
+  int64_t ld_out;
+} muon_ns_desc_t;
+
+/* Batched Newton–Schulz orthogonalisation (DMuon summary §2.2: batched Gram
+ * NS over matrices of similar shape).
+ *
+ * For every desc[i]: out = NS_steps(x / (‖x‖_F + eps)), orientation handled
+ * internally (rows > cols is processed as its transpose).
+ *   count ≥ 0 (0 is a no-op), 0 ≤ steps ≤ 64, coeffs = {a, b, c} finite,
+ *   eps ≥ 0 finite.
+ * Precision:
+ *   MUON_DTYPE_F32:  fp32 MFMA products, fp32 state;
+ *   MUON_DTYPE_BF16: half-precision MFMA products (fp16 operands scaled by
+ *                    powers of two, fp32 accumulation), fp32 state.
+ * The matrices are grouped by shape: one launch per stage serves every
+ * matrix of a group. */
+muon_status_t muon_ns_batched(const muon_ns_desc_t* desc, int32_t count, int32_t steps,
+                              const float coeffs[3], muon_dtype_t dtype, float eps,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes muon_ns_batched needs for this list of matrices (only the
+ * rows/cols of desc are read; pointers may be NULL).  Host only. */
+muon_status_t muon_ns_workspace_size(const muon_ns_desc_t* desc, int32_t count,
+                                     muon_dtype_t dtype, size_t* bytes);
+
+/* One Muon optimiser step over `count` weight matrices (DMuon summary §1 and
+ * §2.2; momentum as in DeMuon Method §1), in place:
+ *   momentum[i] ← beta·momentum[i] + grads[i]                 (fp32, one FMA)
+ *   O           = NS_steps(momentum[i] / (‖momentum[i]‖_F + eps))
+ *   params[i]   ← round(params[i] − lr·√max(1, rows/cols)·O)   (RNE to param dtype)
+ * Tensors are contiguous row-major rows[i] × cols[i]:
+ *   params[i]:   param_dtype (MUON_DTYPE_BF16 or MUON_DTYPE_F32), read + written
+ *   grads[i]:    float32, read
+ *   momentum[i]: float32, read + written (the optimiser state; the caller
+ *                owns it and may save / restore it between steps)
+ * rows[i], cols[i] ≥ 0 (empty matrices are skipped), count ≥ 0,
+ * 0 ≤ steps ≤ 64, beta, lr, eps finite, eps ≥ 0.  No range among params,
+ * grads and momentum may overlap another.  The NS products use the
+ * half-precision MFMA path described under muon_ns_batched. */
+muon_status_t muon_step(void* const* params, const float* const* grads, float* const* momentum,
+                        const int64_t* rows, const int64_t* cols, int32_t count,
+                        muon_dtype_t param_dtype, float beta, float lr, int32_t steps,
+                        const float coeffs[3], float eps,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes muon_step needs for these shapes.  Host only. */
+muon_status_t muon_step_workspace_size(const int64_t* rows, const int64_t* cols, int32_t count,
+                                       size_t* bytes);
+
+/* Writes a JSON description of the launch plan (groups, tile sizes, padded
+ * sizes, workspace offsets, operand scales) for these shapes into buf
+ * (NUL-terminated, truncated to buf_len).  `for_step` selects the muon_step
+ * plan (1) or the muon_ns_batched plan (0, with `dtype`).  Host only; used by
+ * tests and tuning tools. */
+muon_status_t muon_describe_plan(const int64_t* rows, const int64_t* cols, int32_t count,
+                                 int32_t for_step, muon_dtype_t dtype, int32_t steps,
+                                 const float coeffs[3], char* buf, size_t buf_len);
+
+/* Kernel-time instrumentation.  While enabled, every launch the library
+ * makes is bracketed by a pair of HIP events on the launch's stream and its
+ * algorithmic work is recorded.  muon_profile_read waits for the recorded
+ * events, returns the totals for one kind and clears that kind's records.
+ * Kinds: 0 momentum / sum of squares, 1 norm finish, 2 cast + transpose,
+ *        3 SYRK, 4 symmetric Gram-space products, 5 final product + update.
+ * work is algorithmic flops for kinds 3–5 and algorithmic HBM bytes for 0–2. */
+muon_status_t muon_profile_enable(int32_t on);
+muon_status_t muon_profile_read(int32_t kind, double* total_ms, int64_t* launches, double* work);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* muon_last_error(void);
+
+/* MUON_NS_ABI_VERSION of the loaded library. */
+int32_t muon_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MUON_NS_H */

@@ -1,0 +1,295 @@
+"""Python binding of libmuon_ns.so — the MI355X (gfx950) Muon step.
+
+Argument marshalling only: every stage of the step runs in the library's HIP
+kernels (see ``include/muon_ns.h`` for the C ABI).  PyTorch supplies device
+memory (tensors, the workspace) and the stream.  There is no CPU fallback: if
+the library is not built, importing the ops raises.
+
+Names follow the C ABI:
+    muon_ns_batched(xs, outs=None, steps=5, coeffs=QUINTIC, eps=1e-7)
+    muon_step(params, grads, momenta, beta=0.95, lr=0.02, steps=5, ...)
+    ns_workspace_size / step_workspace_size / describe_plan
+    profile_enable / profile_read
+"""
+from __future__ import annotations
+
+import ctypes
+import json
+import os
+import threading
+
+import torch
+
+__all__ = [
+    "QUINTIC", "CUBIC", "MuonError", "lib_path", "load", "muon_ns_batched", "muon_step",
+    "ns_workspace_size", "step_workspace_size", "describe_plan", "profile_enable",
+    "profile_read", "abi_version", "PROFILE_KINDS",
+]
+
+QUINTIC = (3.4445, -4.7750, 2.0315)
+CUBIC = (1.5, -0.5, 0.0)
+
+MUON_DTYPE_F32 = 0
+MUON_DTYPE_BF16 = 1
+
+PROFILE_KINDS = {"momentum": 0, "norm": 1, "cast": 2, "syrk": 3, "gram": 4, "final": 5}
+
+_STATUS = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "ALIAS", 4: "WORKSPACE",
+           5: "HIP", 6: "NO_DEVICE"}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def lib_path() -> str:
+    return os.path.join(_HERE, "libmuon_ns.so")
+
+
+class MuonError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {message}")
+        self.status = status
+        self.status_name = _STATUS.get(status, str(status))
+
+
+class MuonNsDesc(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("out", ctypes.c_void_p), ("rows", ctypes.c_int64),
+                ("cols", ctypes.c_int64), ("ld_x", ctypes.c_int64), ("ld_out", ctypes.c_int64)]
+
+
+_lib = None
+_lock = threading.Lock()
+
+
+def load():
+    """Load the HIP library (torch is imported first so that the library binds
+    to the HIP runtime torch already uses)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        path = lib_path()
+        if not os.path.exists(path):
+            raise ImportError(
+                f"{path} is not built; run `python -m muon_newton_schulz_06_amd.build` "
+                "(or __graft_entry__.build()) first — there is no CPU fallback")
+        L = ctypes.CDLL(path)
+        vp, i32, i64, f32, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                                 ctypes.c_float, ctypes.c_size_t)
+        L.muon_abi_version.restype = i32
+        L.muon_last_error.restype = ctypes.c_char_p
+        L.muon_ns_batched.argtypes = [ctypes.POINTER(MuonNsDesc), i32, i32, ctypes.POINTER(f32),
+                                      i32, f32, vp, sz, vp]
+        L.muon_ns_batched.restype = i32
+        L.muon_ns_workspace_size.argtypes = [ctypes.POINTER(MuonNsDesc), i32, i32,
+                                             ctypes.POINTER(sz)]
+        L.muon_ns_workspace_size.restype = i32
+        L.muon_step.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(vp),
+                                ctypes.POINTER(i64), ctypes.POINTER(i64), i32, i32, f32, f32, i32,
+                                ctypes.POINTER(f32), f32, vp, sz, vp]
+        L.muon_step.restype = i32
+        L.muon_step_workspace_size.argtypes = [ctypes.POINTER(i64), ctypes.POINTER(i64), i32,
+                                               ctypes.POINTER(sz)]
+        L.muon_step_workspace_size.restype = i32
+        L.muon_describe_plan.argtypes = [ctypes.POINTER(i64), ctypes.POINTER(i64), i32, i32, i32,
+                                         i32, ctypes.POINTER(f32), ctypes.c_char_p, sz]
+        L.muon_describe_plan.restype = i32
+        L.muon_profile_enable.argtypes = [i32]
+        L.muon_profile_enable.restype = i32
+        L.muon_profile_read.argtypes = [i32, ctypes.POINTER(ctypes.c_double),
+                                        ctypes.POINTER(i64), ctypes.POINTER(ctypes.c_double)]
+        L.muon_profile_read.restype = i32
+        if L.muon_abi_version() != 1:
+            raise ImportError(f"libmuon_ns ABI {L.muon_abi_version()} != 1")
+        _lib = L
+        return L
+
+
+def _check(status: int):
+    if status != 0:
+        raise MuonError(status, load().muon_last_error().decode())
+
+
+def abi_version() -> int:
+    return int(load().muon_abi_version())
+
+
+def _coeffs(c):
+    return (ctypes.c_float * 3)(*[float(v) for v in c])
+
+
+def _dtype_code(dt) -> int:
+    if dt == torch.float32:
+        return MUON_DTYPE_F32
+    if dt == torch.bfloat16:
+        return MUON_DTYPE_BF16
+    raise TypeError(f"unsupported dtype {dt}; use float32 or bfloat16")
+
+
+def _stream_handle(stream, device):
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ld(t: torch.Tensor) -> int:
+    if t.dim() != 2:
+        raise ValueError("matrices must be 2-D")
+    if t.numel() == 0:
+        return max(t.shape[1], 1)
+    if t.stride(1) != 1:
+        raise ValueError("matrix rows must be contiguous (stride(1) == 1)")
+    return t.stride(0) if t.shape[0] > 1 else t.shape[1]
+
+
+_ws_cache: dict = {}
+
+
+def _workspace(nbytes: int, device, user):
+    if nbytes == 0:
+        return None, 0
+    if user is not None:
+        if user.device != device:
+            raise ValueError("workspace on another device")
+        return user, user.numel() * user.element_size()
+    key = (device.type, device.index)
+    buf = _ws_cache.get(key)
+    if buf is None or buf.numel() < nbytes:
+        _ws_cache.pop(key, None)
+        buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        _ws_cache[key] = buf
+    return buf, buf.numel()
+
+
+def release_workspace():
+    """Drop the cached workspace buffers (the next call allocates anew)."""
+    _ws_cache.clear()
+
+
+def _ns_descs(xs, outs):
+    arr = (MuonNsDesc * max(len(xs), 1))()
+    for i, (x, o) in enumerate(zip(xs, outs)):
+        arr[i].x = x.data_ptr() if x.numel() else None
+        arr[i].out = o.data_ptr() if o.numel() else None
+        arr[i].rows, arr[i].cols = int(x.shape[0]), int(x.shape[1])
+        arr[i].ld_x, arr[i].ld_out = _ld(x), _ld(o)
+    return arr
+
+
+def ns_workspace_size(shapes, dtype=torch.bfloat16) -> int:
+    L = load()
+    arr = (MuonNsDesc * max(len(shapes), 1))()
+    for i, (r, c) in enumerate(shapes):
+        arr[i].rows, arr[i].cols, arr[i].ld_x, arr[i].ld_out = r, c, c, c
+    out = ctypes.c_size_t(0)
+    _check(L.muon_ns_workspace_size(arr, len(shapes), _dtype_code(dtype), ctypes.byref(out)))
+    return int(out.value)
+
+
+def step_workspace_size(shapes) -> int:
+    L = load()
+    n = len(shapes)
+    rows = (ctypes.c_int64 * max(n, 1))(*[int(r) for r, _ in shapes])
+    cols = (ctypes.c_int64 * max(n, 1))(*[int(c) for _, c in shapes])
+    out = ctypes.c_size_t(0)
+    _check(L.muon_step_workspace_size(rows, cols, n, ctypes.byref(out)))
+    return int(out.value)
+
+
+def describe_plan(shapes, for_step=True, dtype=torch.bfloat16, steps=5, coeffs=QUINTIC) -> dict:
+    L = load()
+    n = len(shapes)
+    rows = (ctypes.c_int64 * max(n, 1))(*[int(r) for r, _ in shapes])
+    cols = (ctypes.c_int64 * max(n, 1))(*[int(c) for _, c in shapes])
+    buf = ctypes.create_string_buffer(1 << 20)
+    _check(L.muon_describe_plan(rows, cols, n, int(bool(for_step)), _dtype_code(dtype), steps,
+                                _coeffs(coeffs), buf, len(buf)))
+    return json.loads(buf.value.decode())
+
+
+def muon_ns_batched(xs, outs=None, steps: int = 5, coeffs=QUINTIC, eps: float = 1e-7,
+                    workspace=None, stream=None):
+    """outs[i] = NS_steps(xs[i] / (‖xs[i]‖_F + eps)) for every matrix, in one
+    batched call.  All tensors: same device, dtype float32 or bfloat16, 2-D
+    with contiguous rows.  Returns ``outs`` (allocated if None)."""
+    L = load()
+    xs = list(xs)
+    if outs is None:
+        outs = [torch.empty_like(x, memory_format=torch.contiguous_format) for x in xs]
+    outs = list(outs)
+    if len(outs) != len(xs):
+        raise ValueError("xs and outs differ in length")
+    if not xs:
+        return outs
+    dev = xs[0].device
+    dt = xs[0].dtype
+    for x, o in zip(xs, outs):
+        if x.device != dev or o.device != dev or dev.type != "cuda":
+            raise ValueError("all tensors must be on one CUDA/HIP device")
+        if x.dtype != dt or o.dtype != dt:
+            raise TypeError("all tensors must share one dtype")
+        if tuple(x.shape) != tuple(o.shape):
+            raise ValueError("out shape differs from x shape")
+    code = _dtype_code(dt)
+    arr = _ns_descs(xs, outs)
+    need = ctypes.c_size_t(0)
+    _check(L.muon_ns_workspace_size(arr, len(xs), code, ctypes.byref(need)))
+    ws, ws_bytes = _workspace(int(need.value), dev, workspace)
+    with torch.cuda.device(dev):
+        _check(L.muon_ns_batched(arr, len(xs), int(steps), _coeffs(coeffs), code, float(eps),
+                                 ctypes.c_void_p(ws.data_ptr() if ws is not None else 0),
+                                 ws_bytes, _stream_handle(stream, dev)))
+    return outs
+
+
+def muon_step(params, grads, momenta, beta: float = 0.95, lr: float = 0.02, steps: int = 5,
+              coeffs=QUINTIC, eps: float = 1e-7, workspace=None, stream=None):
+    """One in-place Muon step over lists of weights (bf16 or fp32), fp32
+    gradients and fp32 momenta (all contiguous, same device)."""
+    L = load()
+    params, grads, momenta = list(params), list(grads), list(momenta)
+    n = len(params)
+    if not (len(grads) == len(momenta) == n):
+        raise ValueError("params, grads and momenta differ in length")
+    if n == 0:
+        return
+    dev = params[0].device
+    pdt = params[0].dtype
+    for p, g, m in zip(params, grads, momenta):
+        if p.device != dev or g.device != dev or m.device != dev or dev.type != "cuda":
+            raise ValueError("all tensors must be on one CUDA/HIP device")
+        if p.dtype != pdt:
+            raise TypeError("all params must share one dtype")
+        if g.dtype != torch.float32 or m.dtype != torch.float32:
+            raise TypeError("grads and momenta must be float32")
+        if p.dim() != 2 or tuple(p.shape) != tuple(g.shape) or tuple(p.shape) != tuple(m.shape):
+            raise ValueError("param, grad and momentum shapes differ (or not 2-D)")
+        if not (p.is_contiguous() and g.is_contiguous() and m.is_contiguous()):
+            raise ValueError("params, grads and momenta must be contiguous")
+    vp = ctypes.c_void_p
+    P = (vp * n)(*[p.data_ptr() for p in params])
+    G = (vp * n)(*[g.data_ptr() for g in grads])
+    M = (vp * n)(*[m.data_ptr() for m in momenta])
+    rows = (ctypes.c_int64 * n)(*[int(p.shape[0]) for p in params])
+    cols = (ctypes.c_int64 * n)(*[int(p.shape[1]) for p in params])
+    need = ctypes.c_size_t(0)
+    _check(L.muon_step_workspace_size(rows, cols, n, ctypes.byref(need)))
+    ws, ws_bytes = _workspace(int(need.value), dev, workspace)
+    with torch.cuda.device(dev):
+        _check(L.muon_step(P, G, M, rows, cols, n, _dtype_code(pdt), float(beta), float(lr),
+                           int(steps), _coeffs(coeffs), float(eps),
+                           ctypes.c_void_p(ws.data_ptr() if ws is not None else 0), ws_bytes,
+                           _stream_handle(stream, dev)))
+
+
+def profile_enable(on: bool = True):
+    _check(load().muon_profile_enable(int(bool(on))))
+
+
+def profile_read(kind) -> dict:
+    """Totals of the launches recorded for one kind since the last read:
+    {"ms": total kernel ms, "launches": n, "work": algorithmic flops or bytes}."""
+    k = PROFILE_KINDS[kind] if isinstance(kind, str) else int(kind)
+    ms, n, w = ctypes.c_double(0), ctypes.c_int64(0), ctypes.c_double(0)
+    _check(load().muon_profile_read(k, ctypes.byref(ms), ctypes.byref(n), ctypes.byref(w)))
+    return {"ms": ms.value, "launches": n.value, "work": w.value}

@@ -1,0 +1,715 @@
+// C ABI of the Muon / Gram Newton–Schulz library: argument checks, planning
+// and the launch sequence on the caller's stream.
+//
+// Sequence for one call (all asynchronous on one stream):
+//   1. momentum + partial Σx²   (muon_step)  |  partial Σx²  (muon_ns_batched)
+//   2. α = 1/(‖·‖_F + eps) per matrix
+//   3. X₀ = α·sX·x cast to the MFMA operand type, in both layouts
+//   4. SYRK  G = X₀·X₀ᵀ, upper tiles, per stored shape
+//   5. Gram recursion (DMuon technical summary, gist.science Korean, §2.2),
+//      per step k with P_k = a·I + B_k, B_k = b·A_k + c·A_k²:
+//        A_k² (epilogue forms B_k; at k = 0 also Q₁ = P₀)
+//        Q_{k+1} = a·Q_k + B_k·Q_k  and  P_k·A_k = a·A_k + B_k·A_k  (one launch)
+//        A_{k+1} = a·(P_k·A_k) + B_k·(P_k·A_k)
+//      one launch per product serving every matrix of every Gram group.
+//   6. O = Q_s·X₀ (X₀ᵀ·Q_s for tall matrices) with the output / weight
+//      update fused in the epilogue.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/muon_ns.h"
+#include "common.hpp"
+#include "launch.hpp"
+#include "plan.hpp"
+
+namespace muon {
+namespace {
+
+thread_local std::string g_err;
+
+muon_status_t fail(muon_status_t st, const std::string& msg) {
+  g_err = msg;
+  return st;
+}
+
+// ----------------------------------------------------------------------------
+// instrumentation: HIP event pairs around launches
+struct ProfRec {
+  int kind;
+  hipEvent_t e0, e1;
+  double work;
+};
+bool g_prof_on = false;
+std::vector<ProfRec> g_prof;
+std::vector<hipEvent_t> g_event_pool;
+
+hipEvent_t take_event() {
+  if (!g_event_pool.empty()) {
+    hipEvent_t e = g_event_pool.back();
+    g_event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+struct Launcher {
+  hipStream_t st;
+  template <typename F>
+  muon_status_t run(int kind, double work, const char* what, F&& f) {
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    if (g_prof_on) {
+      e0 = take_event();
+      e1 = take_event();
+      if (e0) hipEventRecord(e0, st);
+    }
+    hipError_t err = f();
+    if (g_prof_on && e0 && e1) {
+      hipEventRecord(e1, st);
+      g_prof.push_back({kind, e0, e1, work});
+    }
+    if (err != hipSuccess)
+      return fail(MUON_ERR_HIP, std::string(what) + ": " + hipGetErrorString(err));
+    return MUON_OK;
+  }
+};
+
+// ----------------------------------------------------------------------------
+// argument checks (host only, before any HIP call)
+struct Range {
+  uintptr_t lo, hi;
+  int owner;
+};
+
+bool overlaps(std::vector<Range> v, int* a, int* b) {
+  std::sort(v.begin(), v.end(), [](const Range& x, const Range& y) { return x.lo < y.lo; });
+  for (size_t i = 1; i < v.size(); ++i) {
+    if (v[i].lo < v[i - 1].hi) {
+      *a = v[i - 1].owner;
+      *b = v[i].owner;
+      return true;
+    }
+  }
+  return false;
+}
+
+bool finite3(const float* c) {
+  return c && std::isfinite(c[0]) && std::isfinite(c[1]) && std::isfinite(c[2]);
+}
+
+constexpr int64_t kMaxDim = int64_t(1) << 24;   // rows / cols
+constexpr int64_t kMaxGramM = 32768;           // m×m fp32 state per matrix ≤ 4 GiB
+constexpr int kMaxSteps = 64;
+
+muon_status_t check_shape(int i, int64_t r, int64_t c) {
+  if (r < 0 || c < 0)
+    return fail(MUON_ERR_INVALID_ARG, "matrix " + std::to_string(i) + ": negative rows/cols");
+  if (r > kMaxDim || c > kMaxDim)
+    return fail(MUON_ERR_UNSUPPORTED, "matrix " + std::to_string(i) + ": rows/cols above 2^24");
+  if (std::min(r, c) > kMaxGramM)
+    return fail(MUON_ERR_UNSUPPORTED,
+                "matrix " + std::to_string(i) + ": min(rows, cols) above 32768");
+  return MUON_OK;
+}
+
+muon_status_t check_device() {
+  int n = 0;
+  if (hipGetDeviceCount(&n) != hipSuccess || n <= 0)
+    return fail(MUON_ERR_NO_DEVICE, "no HIP device visible");
+  return MUON_OK;
+}
+
+// ----------------------------------------------------------------------------
+// launch sequence shared by both entry points
+
+struct CallerMat {
+  const void* src;   // momentum (step) or x (ns)
+  int64_t ldSrc;
+  void* dst;         // weights (step) or out (ns)
+  int64_t ldDst;
+  const float* grad; // step only
+  float lrsc;
+};
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+muon_status_t enqueue(const Plan& P, const std::vector<CallerMat>& cm, int srcDtype, int dstDtype,
+                      float beta, float eps, void* ws, hipStream_t st) {
+  Launcher Lr{st};
+  const int count = (int)P.mats.size();
+  const size_t esz = P.op == OP_F32 ? 4 : 2;
+  std::vector<int> live;
+  for (int i = 0; i < count; ++i)
+    if (!P.mats[i].empty) live.push_back(i);
+  if (live.empty()) return MUON_OK;
+  float* partials = at<float>(ws, P.offPartials);
+  float* alpha = at<float>(ws, P.offAlpha);
+  const ScalePlan& sc = P.scales;
+
+  // 1. momentum / sum of squares
+  for (size_t c0 = 0; c0 < live.size(); c0 += kMaxUser) {
+    EwLaunch L;
+    std::memset(&L, 0, sizeof(L));
+    L.mode = P.forStep ? 0 : 1;
+    L.xDtype = srcDtype;
+    L.beta = beta;
+    L.partials = partials;
+    L.vec = 1;
+    int64_t blocks = 0;
+    double bytes = 0;
+    const size_t cn = std::min(live.size() - c0, (size_t)kMaxUser);
+    for (size_t k = 0; k < cn; ++k) {
+      const int i = live[c0 + k];
+      const MatPlan& mp = P.mats[i];
+      EwMat& e = L.mat[k];
+      e.rows = mp.rows;
+      e.cols = mp.cols;
+      e.numel = mp.numel;
+      e.blockStart = blocks;
+      e.partialOff = mp.partialOff;
+      if (P.forStep) {
+        e.x = cm[i].grad;
+        e.mom = (float*)cm[i].src;
+        e.ld = mp.cols;
+        if ((mp.numel & 3) || ((uintptr_t)e.x & 15) || ((uintptr_t)e.mom & 15)) L.vec = 0;
+        bytes += 12.0 * mp.numel;
+      } else {
+        e.x = cm[i].src;
+        e.ld = cm[i].ldSrc;
+        bytes += (srcDtype == MUON_DTYPE_BF16 ? 2.0 : 4.0) * mp.numel;
+      }
+      blocks += mp.partialCnt;
+    }
+    L.n = (int)cn;
+    muon_status_t s = Lr.run(0, bytes, "momentum/norm kernel", [&] { return launch_ew(L, blocks, st); });
+    if (s != MUON_OK) return s;
+  }
+  // 2. alpha
+  for (size_t c0 = 0; c0 < live.size(); c0 += kMaxUser) {
+    NormLaunch L;
+    std::memset(&L, 0, sizeof(L));
+    L.eps = eps;
+    L.partials = partials;
+    L.alpha = alpha;
+    const size_t cn = std::min(live.size() - c0, (size_t)kMaxUser);
+    double bytes = 0;
+    for (size_t k = 0; k < cn; ++k) {
+      const int i = live[c0 + k];
+      L.off[k] = P.mats[i].partialOff;
+      L.cnt[k] = P.mats[i].partialCnt;
+      L.alphaIdx[k] = i;
+      bytes += 4.0 * P.mats[i].partialCnt;
+    }
+    L.n = (int)cn;
+    muon_status_t s = Lr.run(1, bytes, "norm finish kernel", [&] { return launch_norm(L, st); });
+    if (s != MUON_OK) return s;
+  }
+  // 3. cast into both operand layouts
+  for (size_t c0 = 0; c0 < live.size(); c0 += kMaxUser) {
+    CastLaunch L;
+    std::memset(&L, 0, sizeof(L));
+    L.srcDtype = P.forStep ? MUON_DTYPE_F32 : srcDtype;
+    L.outOp = P.op;
+    L.sX = sc.sX;
+    L.alpha = alpha;
+    const size_t cn = std::min(live.size() - c0, (size_t)kMaxUser);
+    int64_t blocks = 0;
+    double bytes = 0;
+    for (size_t k = 0; k < cn; ++k) {
+      const int i = live[c0 + k];
+      const MatPlan& mp = P.mats[i];
+      const BucketPlan& bp = P.buckets[mp.bucket];
+      CastMat& C = L.mat[k];
+      C.src = cm[i].src;
+      C.rows = mp.rows;
+      C.cols = mp.cols;
+      C.ld = P.forStep ? mp.cols : cm[i].ldSrc;
+      void* xh = at<char>(ws, bp.offXh + bp.strideX * mp.posBucket);
+      void* xth = at<char>(ws, bp.offXTh + bp.strideX * mp.posBucket);
+      if (!mp.tall) {  // stored = X₀ (m × n)
+        C.S = xh;
+        C.T = xth;
+        C.rp = (int32_t)bp.Mp;
+        C.cp = (int32_t)bp.Np;
+      } else {         // stored = X₀ᵀ (n × m)
+        C.S = xth;
+        C.T = xh;
+        C.rp = (int32_t)bp.Np;
+        C.cp = (int32_t)bp.Mp;
+      }
+      C.alphaIdx = i;
+      C.tilesC = C.cp / kCastTile;
+      C.blockStart = blocks;
+      blocks += (int64_t)(C.rp / kCastTile) * C.tilesC;
+      bytes += (P.forStep ? 4.0 : (srcDtype == MUON_DTYPE_BF16 ? 2.0 : 4.0)) * mp.numel +
+               2.0 * esz * (double)bp.Mp * (double)bp.Np;
+    }
+    L.n = (int)cn;
+    muon_status_t s = Lr.run(2, bytes, "cast kernel", [&] { return launch_cast(L, blocks, st); });
+    if (s != MUON_OK) return s;
+  }
+
+  // Tile configurations present, each launched separately.
+  std::vector<int> tiles;
+  for (const GroupPlan& g : P.groups)
+    if (std::find(tiles.begin(), tiles.end(), g.tile) == tiles.end()) tiles.push_back(g.tile);
+
+  // Helper: launch a list of segments (≤ kMaxSegs per launch).
+  auto launch_segs = [&](int tile, std::vector<GemmSeg>& segs, std::vector<double>& works, int kind,
+                         const char* what) -> muon_status_t {
+    for (size_t s0 = 0; s0 < segs.size(); s0 += kMaxSegs) {
+      GemmLaunch L;
+      std::memset(&L, 0, sizeof(L));
+      const size_t ns = std::min(segs.size() - s0, (size_t)kMaxSegs);
+      int blocks = 0;
+      double work = 0;
+      for (size_t k = 0; k < ns; ++k) {
+        L.seg[k] = segs[s0 + k];
+        L.segStart[k] = blocks;
+        blocks += L.seg[k].tilesPerMat * L.seg[k].count;
+        work += works[s0 + k];
+      }
+      L.segStart[ns] = blocks;
+      L.nseg = (int)ns;
+      muon_status_t s = Lr.run(kind, work, what, [&] { return launch_gemm(P.op, tile, L, blocks, st); });
+      if (s != MUON_OK) return s;
+    }
+    return MUON_OK;
+  };
+
+  auto sym_seg = [&](const GroupPlan& g, int tile) {
+    GemmSeg S;
+    std::memset(&S, 0, sizeof(S));
+    const int t = (int)(g.Mp / tile);
+    S.tilesM = S.tilesN = t;
+    S.tilesPerMat = t * (t + 1) / 2;
+    S.sym = 1;
+    S.count = g.count;
+    S.lda = S.ldb = S.ldc = (int32_t)g.Mp;
+    S.K = (int32_t)g.Mp;
+    S.strideA = S.strideB = g.Mp * g.Mp;
+    S.strideIn32 = S.strideOut32 = S.strideOuth = g.Mp * g.Mp;
+    S.mReal = S.nReal = (int32_t)g.m;
+    return S;
+  };
+  auto symflops = [](const GroupPlan& g) { return (double)g.count * g.m * g.m * (double)(g.m + 1); };
+
+  // 4. SYRK per stored shape
+  for (int tile : tiles) {
+    std::vector<GemmSeg> segs;
+    std::vector<double> works;
+    for (const GroupPlan& g : P.groups) {
+      if (g.tile != tile) continue;
+      for (int bi : g.buckets) {
+        const BucketPlan& bp = P.buckets[bi];
+        GemmSeg S = sym_seg(g, tile);
+        S.count = (int)bp.mats.size();
+        S.A = S.B = at<char>(ws, bp.offXh);
+        S.strideA = S.strideB = bp.Mp * bp.Np;
+        S.lda = S.ldb = (int32_t)bp.Np;
+        S.K = (int32_t)bp.Np;
+        S.epi = EPI_SYRK;
+        S.u = 1.0f / (sc.sX * sc.sX);
+        S.sOut = sc.sA[0];
+        S.out32 = at<float>(ws, g.offA32 + g.stride32 * bp.gramStart);
+        S.outh = at<char>(ws, g.offAh + g.strideh * bp.gramStart);
+        if (P.steps == 0) {
+          S.writeIdentity = 1;
+          S.outhb = at<char>(ws, g.offQh[0] + g.strideh * bp.gramStart);
+          S.sOutB = sc.sQ[0];
+        }
+        segs.push_back(S);
+        works.push_back((double)bp.mats.size() * bp.m * (double)(bp.m + 1) * bp.n);
+      }
+    }
+    muon_status_t s = launch_segs(tile, segs, works, 3, "SYRK kernel");
+    if (s != MUON_OK) return s;
+  }
+
+  // 5. Gram-space recursion
+  const float a = P.a, b = P.b, c = P.c;
+  int qcur = 0;  // Qh buffer holding the current Q
+  for (int k = 0; k < P.steps; ++k) {
+    const bool hasQ = k >= 1, hasA = k <= P.steps - 2;
+    for (int tile : tiles) {
+      // (i) A² → B (and Q₁ at k = 0)
+      std::vector<GemmSeg> segs;
+      std::vector<double> works;
+      for (const GroupPlan& g : P.groups) {
+        if (g.tile != tile) continue;
+        GemmSeg S = sym_seg(g, tile);
+        S.A = S.B = at<char>(ws, g.offAh);
+        S.epi = EPI_SQ;
+        S.u = 1.0f / (sc.sA[k] * sc.sA[k]);
+        S.p0 = a;
+        S.p1 = b;
+        S.p2 = c;
+        S.in32 = at<float>(ws, g.offA32);
+        S.outh = at<char>(ws, g.offBh);
+        S.sOut = sc.sB[k];
+        if (k == 0) {
+          S.out32b = at<float>(ws, g.offQ32);
+          S.outhb = at<char>(ws, g.offQh[0]);
+          S.sOutB = sc.sQ[1];
+        }
+        segs.push_back(S);
+        works.push_back(symflops(g));
+      }
+      muon_status_t s = launch_segs(tile, segs, works, 4, "Gram A^2 kernel");
+      if (s != MUON_OK) return s;
+      // (ii) Q ← a·Q + B·Q and P·A = a·A + B·A
+      segs.clear();
+      works.clear();
+      for (const GroupPlan& g : P.groups) {
+        if (g.tile != tile) continue;
+        if (hasQ) {
+          GemmSeg S = sym_seg(g, tile);
+          S.A = at<char>(ws, g.offBh);
+          S.B = at<char>(ws, g.offQh[qcur]);
+          S.epi = EPI_AXPY;
+          S.u = 1.0f / (sc.sB[k] * sc.sQ[k]);
+          S.p0 = a;
+          S.in32 = at<float>(ws, g.offQ32);
+          S.out32 = at<float>(ws, g.offQ32);
+          S.outh = at<char>(ws, g.offQh[qcur ^ 1]);
+          S.sOut = sc.sQ[k + 1];
+          segs.push_back(S);
+          works.push_back(symflops(g));
+        }
+        if (hasA) {
+          GemmSeg S = sym_seg(g, tile);
+          S.A = at<char>(ws, g.offBh);
+          S.B = at<char>(ws, g.offAh);
+          S.epi = EPI_AXPY;
+          S.u = 1.0f / (sc.sB[k] * sc.sA[k]);
+          S.p0 = a;
+          S.in32 = at<float>(ws, g.offA32);
+          S.out32 = at<float>(ws, g.offPA32);
+          S.outh = at<char>(ws, g.offPAh);
+          S.sOut = sc.sPA[k];
+          segs.push_back(S);
+          works.push_back(symflops(g));
+        }
+      }
+      s = launch_segs(tile, segs, works, 4, "Gram Q/PA kernel");
+      if (s != MUON_OK) return s;
+      // (iii) A ← a·PA + B·PA
+      if (hasA) {
+        segs.clear();
+        works.clear();
+        for (const GroupPlan& g : P.groups) {
+          if (g.tile != tile) continue;
+          GemmSeg S = sym_seg(g, tile);
+          S.A = at<char>(ws, g.offBh);
+          S.B = at<char>(ws, g.offPAh);
+          S.epi = EPI_AXPY;
+          S.u = 1.0f / (sc.sB[k] * sc.sPA[k]);
+          S.p0 = a;
+          S.in32 = at<float>(ws, g.offPA32);
+          S.out32 = at<float>(ws, g.offA32);
+          S.outh = at<char>(ws, g.offAh);
+          S.sOut = sc.sA[k + 1];
+          segs.push_back(S);
+          works.push_back(symflops(g));
+        }
+        s = launch_segs(tile, segs, works, 4, "Gram A-update kernel");
+        if (s != MUON_OK) return s;
+      }
+    }
+    if (hasQ) qcur ^= 1;
+  }
+
+  // 6. final product with the fused output / update
+  for (const BucketPlan& bp : P.buckets) {
+    const GroupPlan& g = P.groups[bp.group];
+    const int tile = g.tile;
+    for (size_t c0 = 0; c0 < bp.mats.size(); c0 += kMaxUser) {
+      const size_t cn = std::min(bp.mats.size() - c0, (size_t)kMaxUser);
+      GemmLaunch L;
+      std::memset(&L, 0, sizeof(L));
+      L.userDtype = dstDtype;
+      GemmSeg& S = L.seg[0];
+      const char* qh = at<char>(ws, g.offQh[qcur] + g.strideh * (bp.gramStart + c0));
+      const char* xth = at<char>(ws, bp.offXTh + bp.strideX * c0);
+      if (!bp.tall) {  // O = Q·X₀ : rows of Q, rows of X₀ᵀ
+        S.A = qh;
+        S.strideA = bp.Mp * bp.Mp;
+        S.B = xth;
+        S.strideB = bp.Np * bp.Mp;
+        S.tilesM = (int32_t)(bp.Mp / tile);
+        S.tilesN = (int32_t)(bp.Np / tile);
+        S.mReal = (int32_t)bp.m;
+        S.nReal = (int32_t)bp.n;
+      } else {         // Oᵀ = X₀ᵀ·Q : rows of X₀ᵀ, rows of Q
+        S.A = xth;
+        S.strideA = bp.Np * bp.Mp;
+        S.B = qh;
+        S.strideB = bp.Mp * bp.Mp;
+        S.tilesM = (int32_t)(bp.Np / tile);
+        S.tilesN = (int32_t)(bp.Mp / tile);
+        S.mReal = (int32_t)bp.n;
+        S.nReal = (int32_t)bp.m;
+      }
+      S.lda = S.ldb = (int32_t)bp.Mp;
+      S.K = (int32_t)bp.Mp;
+      S.tilesPerMat = S.tilesM * S.tilesN;
+      S.count = (int)cn;
+      S.sym = 0;
+      S.epi = P.forStep ? EPI_UPDATE : EPI_OUT;
+      S.u = 1.0f / (sc.sQ[P.steps] * sc.sX);
+      S.userBase = 0;
+      for (size_t k = 0; k < cn; ++k) {
+        const int i = bp.mats[c0 + k];
+        L.user[k] = cm[i].dst;
+        L.userLd[k] = cm[i].ldDst;
+        L.lrsc[k] = cm[i].lrsc;
+      }
+      L.nseg = 1;
+      L.segStart[0] = 0;
+      const int blocks = S.tilesPerMat * S.count;
+      L.segStart[1] = blocks;
+      const double work = 2.0 * (double)cn * bp.m * (double)bp.m * bp.n;
+      muon_status_t s = Lr.run(5, work, "final product kernel",
+                               [&] { return launch_gemm(P.op, tile, L, blocks, st); });
+      if (s != MUON_OK) return s;
+    }
+  }
+  return MUON_OK;
+}
+
+}  // namespace
+}  // namespace muon
+
+using namespace muon;
+
+extern "C" {
+
+int32_t muon_abi_version(void) { return MUON_NS_ABI_VERSION; }
+
+const char* muon_last_error(void) { return g_err.c_str(); }
+
+muon_status_t muon_ns_workspace_size(const muon_ns_desc_t* desc, int32_t count, muon_dtype_t dtype,
+                                     size_t* bytes) {
+  g_err.clear();
+  if (!bytes) return fail(MUON_ERR_INVALID_ARG, "bytes is NULL");
+  if (count < 0) return fail(MUON_ERR_INVALID_ARG, "count < 0");
+  if (count > 0 && !desc) return fail(MUON_ERR_INVALID_ARG, "desc is NULL");
+  if (dtype != MUON_DTYPE_F32 && dtype != MUON_DTYPE_BF16)
+    return fail(MUON_ERR_INVALID_ARG, "unknown dtype");
+  std::vector<int64_t> r(count), c(count);
+  for (int i = 0; i < count; ++i) {
+    muon_status_t s = check_shape(i, desc[i].rows, desc[i].cols);
+    if (s != MUON_OK) return s;
+    r[i] = desc[i].rows;
+    c[i] = desc[i].cols;
+  }
+  Plan P;
+  std::string e = build_plan(r.data(), c.data(), count, dtype == MUON_DTYPE_F32 ? OP_F32 : OP_F16,
+                             5, 1.f, 0.f, 0.f, false, &P);
+  if (!e.empty()) return fail(MUON_ERR_INVALID_ARG, e);
+  *bytes = P.totalBytes;
+  return MUON_OK;
+}
+
+muon_status_t muon_step_workspace_size(const int64_t* rows, const int64_t* cols, int32_t count,
+                                       size_t* bytes) {
+  g_err.clear();
+  if (!bytes) return fail(MUON_ERR_INVALID_ARG, "bytes is NULL");
+  if (count < 0) return fail(MUON_ERR_INVALID_ARG, "count < 0");
+  if (count > 0 && (!rows || !cols)) return fail(MUON_ERR_INVALID_ARG, "rows/cols is NULL");
+  for (int i = 0; i < count; ++i) {
+    muon_status_t s = check_shape(i, rows[i], cols[i]);
+    if (s != MUON_OK) return s;
+  }
+  Plan P;
+  std::string e = build_plan(rows, cols, count, OP_F16, 5, 1.f, 0.f, 0.f, true, &P);
+  if (!e.empty()) return fail(MUON_ERR_INVALID_ARG, e);
+  *bytes = P.totalBytes;
+  return MUON_OK;
+}
+
+muon_status_t muon_describe_plan(const int64_t* rows, const int64_t* cols, int32_t count,
+                                 int32_t for_step, muon_dtype_t dtype, int32_t steps,
+                                 const float coeffs[3], char* buf, size_t buf_len) {
+  g_err.clear();
+  if (!buf || buf_len == 0) return fail(MUON_ERR_INVALID_ARG, "buf is NULL or empty");
+  if (count < 0) return fail(MUON_ERR_INVALID_ARG, "count < 0");
+  if (count > 0 && (!rows || !cols)) return fail(MUON_ERR_INVALID_ARG, "rows/cols is NULL");
+  if (steps < 0 || steps > kMaxSteps) return fail(MUON_ERR_INVALID_ARG, "steps out of range");
+  if (!finite3(coeffs)) return fail(MUON_ERR_INVALID_ARG, "coeffs NULL or not finite");
+  if (dtype != MUON_DTYPE_F32 && dtype != MUON_DTYPE_BF16)
+    return fail(MUON_ERR_INVALID_ARG, "unknown dtype");
+  for (int i = 0; i < count; ++i) {
+    muon_status_t s = check_shape(i, rows[i], cols[i]);
+    if (s != MUON_OK) return s;
+  }
+  const int op = (!for_step && dtype == MUON_DTYPE_F32) ? OP_F32 : OP_F16;
+  Plan P;
+  std::string e = build_plan(rows, cols, count, op, steps, coeffs[0], coeffs[1], coeffs[2],
+                             for_step != 0, &P);
+  if (!e.empty()) return fail(MUON_ERR_INVALID_ARG, e);
+  std::string j = P.json();
+  const size_t n = std::min(j.size(), buf_len - 1);
+  std::memcpy(buf, j.data(), n);
+  buf[n] = '\0';
+  return MUON_OK;
+}
+
+muon_status_t muon_ns_batched(const muon_ns_desc_t* desc, int32_t count, int32_t steps,
+                              const float coeffs[3], muon_dtype_t dtype, float eps, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  if (count < 0) return fail(MUON_ERR_INVALID_ARG, "count < 0");
+  if (count == 0) return MUON_OK;
+  if (!desc) return fail(MUON_ERR_INVALID_ARG, "desc is NULL");
+  if (steps < 0 || steps > kMaxSteps) return fail(MUON_ERR_INVALID_ARG, "steps out of range [0, 64]");
+  if (!finite3(coeffs)) return fail(MUON_ERR_INVALID_ARG, "coeffs NULL or not finite");
+  if (dtype != MUON_DTYPE_F32 && dtype != MUON_DTYPE_BF16)
+    return fail(MUON_ERR_INVALID_ARG, "unknown dtype");
+  if (!std::isfinite(eps) || eps < 0) return fail(MUON_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  const size_t esz = dtype == MUON_DTYPE_F32 ? 4 : 2;
+  std::vector<int64_t> r(count), c(count);
+  std::vector<Range> outs;
+  for (int i = 0; i < count; ++i) {
+    const muon_ns_desc_t& d = desc[i];
+    muon_status_t s = check_shape(i, d.rows, d.cols);
+    if (s != MUON_OK) return s;
+    r[i] = d.rows;
+    c[i] = d.cols;
+    if (d.rows == 0 || d.cols == 0) continue;
+    if (!d.x || !d.out) return fail(MUON_ERR_INVALID_ARG, "matrix " + std::to_string(i) + ": NULL x/out");
+    if (d.ld_x < d.cols || d.ld_out < d.cols)
+      return fail(MUON_ERR_INVALID_ARG, "matrix " + std::to_string(i) + ": ld < cols");
+    const uintptr_t lo = (uintptr_t)d.out;
+    outs.push_back({lo, lo + (uintptr_t)(((d.rows - 1) * d.ld_out + d.cols) * esz), i});
+  }
+  int oa = 0, ob = 0;
+  if (overlaps(outs, &oa, &ob))
+    return fail(MUON_ERR_ALIAS, "outputs of matrices " + std::to_string(oa) + " and " +
+                                    std::to_string(ob) + " overlap");
+  Plan P;
+  const int op = dtype == MUON_DTYPE_F32 ? OP_F32 : OP_F16;
+  std::string e = build_plan(r.data(), c.data(), count, op, steps, coeffs[0], coeffs[1], coeffs[2],
+                             false, &P);
+  if (!e.empty()) return fail(MUON_ERR_INVALID_ARG, e);
+  if (P.totalBytes > 0) {
+    if (!workspace) return fail(MUON_ERR_WORKSPACE, "workspace is NULL");
+    if ((uintptr_t)workspace & 255) return fail(MUON_ERR_WORKSPACE, "workspace not 256-byte aligned");
+    if (workspace_bytes < P.totalBytes)
+      return fail(MUON_ERR_WORKSPACE, "workspace too small: need " + std::to_string(P.totalBytes) +
+                                          " bytes, got " + std::to_string(workspace_bytes));
+  }
+  std::vector<CallerMat> cm(count);
+  for (int i = 0; i < count; ++i) {
+    cm[i].src = desc[i].x;
+    cm[i].ldSrc = desc[i].ld_x;
+    cm[i].dst = desc[i].out;
+    cm[i].ldDst = desc[i].ld_out;
+    cm[i].grad = nullptr;
+    cm[i].lrsc = 0.f;
+  }
+  muon_status_t s = check_device();
+  if (s != MUON_OK) return s;
+  return enqueue(P, cm, dtype, dtype, 0.f, eps, workspace, (hipStream_t)stream);
+}
+
+muon_status_t muon_step(void* const* params, const float* const* grads, float* const* momentum,
+                        const int64_t* rows, const int64_t* cols, int32_t count,
+                        muon_dtype_t param_dtype, float beta, float lr, int32_t steps,
+                        const float coeffs[3], float eps, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  g_err.clear();
+  if (count < 0) return fail(MUON_ERR_INVALID_ARG, "count < 0");
+  if (count == 0) return MUON_OK;
+  if (!params || !grads || !momentum || !rows || !cols)
+    return fail(MUON_ERR_INVALID_ARG, "NULL pointer array");
+  if (param_dtype != MUON_DTYPE_F32 && param_dtype != MUON_DTYPE_BF16)
+    return fail(MUON_ERR_INVALID_ARG, "unknown param dtype");
+  if (steps < 0 || steps > kMaxSteps) return fail(MUON_ERR_INVALID_ARG, "steps out of range [0, 64]");
+  if (!finite3(coeffs)) return fail(MUON_ERR_INVALID_ARG, "coeffs NULL or not finite");
+  if (!std::isfinite(beta) || !std::isfinite(lr))
+    return fail(MUON_ERR_INVALID_ARG, "beta and lr must be finite");
+  if (!std::isfinite(eps) || eps < 0) return fail(MUON_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  const size_t psz = param_dtype == MUON_DTYPE_F32 ? 4 : 2;
+  std::vector<Range> ranges;
+  for (int i = 0; i < count; ++i) {
+    muon_status_t s = check_shape(i, rows[i], cols[i]);
+    if (s != MUON_OK) return s;
+    if (rows[i] == 0 || cols[i] == 0) continue;
+    if (!params[i] || !grads[i] || !momentum[i])
+      return fail(MUON_ERR_INVALID_ARG, "matrix " + std::to_string(i) + ": NULL tensor");
+    const uintptr_t n = (uintptr_t)(rows[i] * cols[i]);
+    ranges.push_back({(uintptr_t)params[i], (uintptr_t)params[i] + n * psz, i});
+    ranges.push_back({(uintptr_t)grads[i], (uintptr_t)grads[i] + n * 4, i});
+    ranges.push_back({(uintptr_t)momentum[i], (uintptr_t)momentum[i] + n * 4, i});
+  }
+  int oa = 0, ob = 0;
+  if (overlaps(ranges, &oa, &ob))
+    return fail(MUON_ERR_ALIAS, "tensors of matrices " + std::to_string(oa) + " and " +
+                                    std::to_string(ob) + " overlap");
+  Plan P;
+  std::string e = build_plan(rows, cols, count, OP_F16, steps, coeffs[0], coeffs[1], coeffs[2], true, &P);
+  if (!e.empty()) return fail(MUON_ERR_INVALID_ARG, e);
+  if (!workspace) return fail(MUON_ERR_WORKSPACE, "workspace is NULL");
+  if ((uintptr_t)workspace & 255) return fail(MUON_ERR_WORKSPACE, "workspace not 256-byte aligned");
+  if (workspace_bytes < P.totalBytes)
+    return fail(MUON_ERR_WORKSPACE, "workspace too small: need " + std::to_string(P.totalBytes) +
+                                        " bytes, got " + std::to_string(workspace_bytes));
+  std::vector<CallerMat> cm(count);
+  for (int i = 0; i < count; ++i) {
+    cm[i].src = momentum[i];
+    cm[i].ldSrc = cols[i];
+    cm[i].dst = params[i];
+    cm[i].ldDst = cols[i];
+    cm[i].grad = grads[i];
+    cm[i].lrsc = (float)(lr * std::sqrt(std::max(1.0, (double)rows[i] / (double)std::max<int64_t>(cols[i], 1))));
+  }
+  muon_status_t s = check_device();
+  if (s != MUON_OK) return s;
+  return enqueue(P, cm, MUON_DTYPE_F32, param_dtype, beta, eps, workspace, (hipStream_t)stream);
+}
+
+muon_status_t muon_profile_enable(int32_t on) {
+  g_err.clear();
+  g_prof_on = on != 0;
+  return MUON_OK;
+}
+
+muon_status_t muon_profile_read(int32_t kind, double* total_ms, int64_t* launches, double* work) {
+  g_err.clear();
+  if (!total_ms || !launches || !work) return fail(MUON_ERR_INVALID_ARG, "NULL output");
+  double ms = 0, w = 0;
+  int64_t n = 0;
+  std::vector<ProfRec> keep;
+  for (ProfRec& r : g_prof) {
+    if (r.kind != kind) {
+      keep.push_back(r);
+      continue;
+    }
+    if (hipEventSynchronize(r.e1) != hipSuccess) return fail(MUON_ERR_HIP, "hipEventSynchronize failed");
+    float t = 0;
+    if (hipEventElapsedTime(&t, r.e0, r.e1) != hipSuccess)
+      return fail(MUON_ERR_HIP, "hipEventElapsedTime failed");
+    ms += t;
+    w += r.work;
+    ++n;
+    g_event_pool.push_back(r.e0);
+    g_event_pool.push_back(r.e1);
+  }
+  g_prof.swap(keep);
+  *total_ms = ms;
+  *launches = n;
+  *work = w;
+  return MUON_OK;
+}
+
+}  // extern "C"

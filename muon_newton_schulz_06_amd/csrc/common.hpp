@@ -1,0 +1,134 @@
+// Launch descriptors shared by the host sequencer and the gfx950 kernels.
+//
+// Every launch takes one of these structs by value (kernel arguments), so no
+// descriptor table ever has to be copied to the device: matrices of a group
+// sit at base + index * stride inside the workspace, and the few pointers the
+// caller owns (gradients, momentum, weights, inputs, outputs) travel in
+// fixed-size tables of at most kMaxUser entries per launch.
+#pragma once
+
+#include <stdint.h>
+
+namespace muon {
+
+constexpr int kMaxSegs = 4;   // problem groups served by one GEMM launch
+constexpr int kMaxUser = 32;  // caller matrices per launch (kernel-arg tables)
+
+enum OpType : int32_t { OP_F16 = 0, OP_F32 = 1 };
+
+// Epilogues of the Gram-space products.  acc is the raw fp32 MFMA sum,
+// u its unscale factor (operands are stored multiplied by powers of two).
+enum Epi : int32_t {
+  // G = u·acc → out32 (upper triangle), outh = sOut·G (mirrored).
+  // writeIdentity: also outhb = sOutB·I (zero steps: Q₀ = I).
+  EPI_SYRK = 0,
+  // A² = u·acc; B = p1·in32 + p2·A² → outh = sOut·B (mirrored).
+  // If out32b: Q₁ = p0·I + B → out32b (upper), outhb = sOutB·Q₁ (mirrored).
+  EPI_SQ = 1,
+  // Y = p0·in32 + u·acc → out32 (upper), outh = sOut·Y (mirrored).
+  EPI_AXPY = 2,
+  // caller weights W ← round(W − lrsc·u·acc), full tiles, real extent only.
+  EPI_UPDATE = 3,
+  // caller output out = round(u·acc), full tiles, real extent only.
+  EPI_OUT = 4,
+};
+
+struct GemmSeg {
+  const void* A;       // operand rows of C: A[row * lda + k]
+  const void* B;       // operand cols of C: B[col * ldb + k]
+  int64_t strideA;     // elements between consecutive matrices
+  int64_t strideB;
+  int32_t lda, ldb;
+  int32_t K;           // contraction length, a multiple of the k-tile
+  int32_t tilesM;      // C tile rows per matrix
+  int32_t tilesN;      // C tile cols per matrix
+  int32_t tilesPerMat; // sym ? tilesM(tilesM+1)/2 : tilesM·tilesN
+  int32_t count;       // matrices in this segment
+  int32_t sym;         // 1: upper-triangle tiles only (C symmetric)
+  int32_t epi;
+  int32_t mReal;       // real C rows  (identity term, caller writes)
+  int32_t nReal;       // real C cols
+  int32_t ldc;         // row stride of the workspace C matrices
+  int32_t writeIdentity;
+  float u, sOut, sOutB;
+  float p0, p1, p2;
+  const float* in32;
+  int64_t strideIn32;
+  float* out32;
+  int64_t strideOut32;
+  void* outh;
+  int64_t strideOuth;
+  float* out32b;
+  void* outhb;
+  int32_t userBase;    // first caller-table entry of this segment
+  int32_t pad_;
+};
+
+struct GemmLaunch {
+  int32_t nseg;
+  int32_t userDtype;          // muon_dtype_t of the caller matrices
+  int32_t segStart[kMaxSegs + 1];  // prefix of workgroups per segment
+  GemmSeg seg[kMaxSegs];
+  void* user[kMaxUser];        // caller weights (EPI_UPDATE) or outputs (EPI_OUT)
+  int64_t userLd[kMaxUser];
+  float lrsc[kMaxUser];        // lr · √max(1, rows/cols) for EPI_UPDATE
+};
+
+// Momentum + sum of squares, or sum of squares alone.
+constexpr int kEwThreads = 256;
+constexpr int kEwElems = 4096;  // elements per workgroup (16 per thread)
+
+struct EwMat {
+  const void* x;       // gradient (momentum mode) or input (norm mode)
+  float* mom;          // momentum, read + written (momentum mode)
+  int64_t rows, cols, ld;
+  int64_t numel;
+  int64_t blockStart;  // first workgroup of this matrix in the launch
+  int64_t partialOff;  // first partial sum of this matrix
+};
+
+struct EwLaunch {
+  int32_t n;
+  int32_t mode;        // 0: momentum, 1: sum of squares of x
+  int32_t xDtype;      // muon_dtype_t of x in norm mode
+  int32_t vec;         // 1: every matrix contiguous, numel % 4 == 0, 16-B aligned
+  float beta;
+  int32_t pad_;
+  float* partials;
+  EwMat mat[kMaxUser];
+};
+
+struct NormLaunch {
+  int32_t n;
+  float eps;
+  const float* partials;
+  float* alpha;
+  int64_t off[kMaxUser];
+  int64_t cnt[kMaxUser];
+  int32_t alphaIdx[kMaxUser];
+};
+
+// Cast (scaled) + transpose into the two operand layouts.
+constexpr int kCastTile = 64;
+
+struct CastMat {
+  const void* src;     // stored rows × cols, row stride ld
+  void* S;             // same orientation, padded rp × cp
+  void* T;             // transposed, padded cp × rp
+  int64_t rows, cols, ld;
+  int32_t rp, cp;      // padded extents (multiples of kCastTile)
+  int32_t alphaIdx;
+  int32_t tilesC;      // cp / kCastTile
+  int64_t blockStart;
+};
+
+struct CastLaunch {
+  int32_t n;
+  int32_t srcDtype;    // muon_dtype_t
+  int32_t outOp;       // OpType of S and T
+  float sX;            // operand scale
+  const float* alpha;  // per-matrix 1 / (‖x‖_F + eps)
+  CastMat mat[kMaxUser];
+};
+
+}  // namespace muon

@@ -1,0 +1,181 @@
+// HBM-bound stages of the Muon step on gfx950.
+//
+//  * momentum + sum of squares: M ← β·M + g (one fused multiply-add) and the
+//    per-workgroup partial Σ M², in one pass over g and M (DeMuon technical
+//    summary, gist.science Korean, Method §1: the momentum is a moving
+//    average of the gradients; DMuon technical summary §1: NS runs on the
+//    momentum-accumulated gradient);
+//  * norm finish: α = 1/(√ΣM² + eps) per matrix, summing the partials in a
+//    fixed order (deterministic, no float atomics);
+//  * scaled cast: X₀ = α·sX·M rounded to the MFMA operand type, written in
+//    both the stored and the transposed layout (with zero padding to the
+//    tile), so every later product reads k-contiguous rows.
+// Reductions use 64-lane wavefront shuffles, then one LDS slot per wave.
+#include <hip/hip_runtime.h>
+
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace muon {
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ double wave_sum_d(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ float load_as_f32(const void* p, int64_t e, int dtype) {
+  if (dtype == 1) return __uint_as_float((uint32_t)((const uint16_t*)p)[e] << 16);
+  return ((const float*)p)[e];
+}
+
+__global__ __launch_bounds__(kEwThreads) void ew_kernel(const EwLaunch L) {
+  const int64_t b = blockIdx.x;
+  int mi = 0;
+  while (mi + 1 < L.n && b >= L.mat[mi + 1].blockStart) ++mi;
+  const EwMat& M = L.mat[mi];
+  const int64_t blk = b - M.blockStart;
+  const int64_t e0 = blk * kEwElems;
+  const int tid = threadIdx.x;
+  float ss = 0.f;
+  if (L.mode == 0) {
+    const float* g = (const float*)M.x;
+    float* m = M.mom;
+    if (L.vec) {
+#pragma unroll
+      for (int q = 0; q < kEwElems / (4 * kEwThreads); ++q) {
+        const int64_t e = e0 + (int64_t)(q * kEwThreads + tid) * 4;
+        if (e < M.numel) {
+          const float4 gv = *(const float4*)(g + e);
+          float4 mv = *(const float4*)(m + e);
+          mv.x = fmaf(L.beta, mv.x, gv.x);
+          mv.y = fmaf(L.beta, mv.y, gv.y);
+          mv.z = fmaf(L.beta, mv.z, gv.z);
+          mv.w = fmaf(L.beta, mv.w, gv.w);
+          *(float4*)(m + e) = mv;
+          ss += mv.x * mv.x + mv.y * mv.y + mv.z * mv.z + mv.w * mv.w;
+        }
+      }
+    } else {
+      for (int q = 0; q < kEwElems / kEwThreads; ++q) {
+        const int64_t e = e0 + q * kEwThreads + tid;
+        if (e < M.numel) {
+          const float v = fmaf(L.beta, m[e], g[e]);
+          m[e] = v;
+          ss += v * v;
+        }
+      }
+    }
+  } else {
+    for (int q = 0; q < kEwElems / kEwThreads; ++q) {
+      const int64_t e = e0 + q * kEwThreads + tid;
+      if (e < M.numel) {
+        const int64_t r = e / M.cols;
+        const int64_t cc = e - r * M.cols;
+        const float v = load_as_f32(M.x, r * M.ld + cc, L.xDtype);
+        ss += v * v;
+      }
+    }
+  }
+  __shared__ float part[kEwThreads / 64];
+  ss = wave_sum(ss);
+  if ((tid & 63) == 0) part[tid >> 6] = ss;
+  __syncthreads();
+  if (tid == 0) {
+    float t = 0.f;
+    for (int w = 0; w < kEwThreads / 64; ++w) t += part[w];
+    L.partials[M.partialOff + blk] = t;
+  }
+}
+
+__global__ __launch_bounds__(256) void norm_kernel(const NormLaunch L) {
+  const int i = blockIdx.x;
+  const int tid = threadIdx.x;
+  const float* p = L.partials + L.off[i];
+  double s = 0.0;
+  for (int64_t k = tid; k < L.cnt[i]; k += 256) s += (double)p[k];
+  __shared__ double part[4];
+  s = wave_sum_d(s);
+  if ((tid & 63) == 0) part[tid >> 6] = s;
+  __syncthreads();
+  if (tid == 0) {
+    const double t = part[0] + part[1] + part[2] + part[3];
+    L.alpha[L.alphaIdx[i]] = (float)(1.0 / (sqrt(t) + (double)L.eps));
+  }
+}
+
+template <typename T> __device__ __forceinline__ T cvt(float v);
+template <> __device__ __forceinline__ _Float16 cvt<_Float16>(float v) { return (_Float16)v; }
+template <> __device__ __forceinline__ float cvt<float>(float v) { return v; }
+
+template <typename T>
+__device__ void cast_tile(const CastLaunch& L, const CastMat& C, int64_t t) {
+  __shared__ float tile[kCastTile][kCastTile + 1];
+  const int tr = (int)(t / C.tilesC), tc = (int)(t - (int64_t)tr * C.tilesC);
+  const int tid = threadIdx.x;
+  const int ty = tid >> 4, tx = tid & 15;
+  const float scale = L.alpha[C.alphaIdx] * L.sX;
+  T* S = (T*)C.S;
+  T* Tt = (T*)C.T;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int rl = ty + 16 * q;
+    const int64_t r = (int64_t)tr * kCastTile + rl;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int cl = 4 * tx + e;
+      const int64_t cc = (int64_t)tc * kCastTile + cl;
+      float v = 0.f;
+      if (r < C.rows && cc < C.cols) v = load_as_f32(C.src, r * C.ld + cc, L.srcDtype) * scale;
+      tile[rl][cl] = v;
+      S[r * C.cp + cc] = cvt<T>(v);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int cl = ty + 16 * q;  // row of the transposed tile
+    const int64_t cc = (int64_t)tc * kCastTile + cl;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int rl = 4 * tx + e;
+      const int64_t r = (int64_t)tr * kCastTile + rl;
+      Tt[cc * C.rp + r] = cvt<T>(tile[rl][cl]);
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void cast_kernel(const CastLaunch L) {
+  const int64_t b = blockIdx.x;
+  int mi = 0;
+  while (mi + 1 < L.n && b >= L.mat[mi + 1].blockStart) ++mi;
+  const CastMat& C = L.mat[mi];
+  const int64_t t = b - C.blockStart;
+  if (L.outOp == OP_F16) cast_tile<_Float16>(L, C, t);
+  else cast_tile<float>(L, C, t);
+}
+
+hipError_t launch_ew(const EwLaunch& L, int64_t blocks, hipStream_t st) {
+  if (blocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(ew_kernel, dim3((unsigned)blocks), dim3(kEwThreads), 0, st, L);
+  return hipGetLastError();
+}
+
+hipError_t launch_norm(const NormLaunch& L, hipStream_t st) {
+  if (L.n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(norm_kernel, dim3(L.n), dim3(256), 0, st, L);
+  return hipGetLastError();
+}
+
+hipError_t launch_cast(const CastLaunch& L, int64_t blocks, hipStream_t st) {
+  if (blocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(cast_kernel, dim3((unsigned)blocks), dim3(256), 0, st, L);
+  return hipGetLastError();
+}
+
+}  // namespace muon

@@ -1,0 +1,19 @@
+// Launch wrappers implemented in the .hip translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "common.hpp"
+
+namespace muon {
+
+// GEMM-shaped products; `tile` is the square workgroup tile (128 or 256).
+hipError_t launch_gemm(int op, int tile, const GemmLaunch& L, int blocks, hipStream_t st);
+// Momentum + partial sums of squares, or partial sums of squares alone.
+hipError_t launch_ew(const EwLaunch& L, int64_t blocks, hipStream_t st);
+// alpha[i] = 1 / (sqrt(sum of partials) + eps), one workgroup per matrix.
+hipError_t launch_norm(const NormLaunch& L, hipStream_t st);
+// Scaled cast into the two operand layouts (and zero padding).
+hipError_t launch_cast(const CastLaunch& L, int64_t blocks, hipStream_t st);
+
+}  // namespace muon

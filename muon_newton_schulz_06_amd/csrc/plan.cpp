@@ -1,0 +1,244 @@
+// Host planning for the batched Gram Newton–Schulz step (no HIP calls).
+//
+// Grouping follows DMuon's technical summary (gist.science, Korean), §2.2:
+// matrices of similar shape are batched so that one dispatch serves all of
+// them.  Here the Gram-space state is grouped by m alone (the m×m recursion
+// does not depend on n), while the products that touch the m×n operand
+// (SYRK, final product) are grouped by stored shape.
+#include "plan.hpp"
+
+#include <algorithm>
+#include <cmath>
+#include <cstdlib>
+#include <map>
+#include <sstream>
+
+#include "common.hpp"
+
+namespace muon {
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Largest power of two s with s·bound ≤ 2^13, so that every stored operand
+// stays 8× below the fp16 maximum (65504) even with rounding.
+float pow2_scale(double bound) {
+  if (!(bound > 0.0) || !std::isfinite(bound)) return 1.f;
+  int e = (int)std::floor(std::log2(8192.0 / bound));
+  e = std::max(-60, std::min(60, e));
+  return std::ldexp(1.0f, e);
+}
+
+int choose_tile(int op, int64_t m, int count) {
+  if (op == OP_F32) return 128;
+  int ov = tile_override();
+  if (ov) return ov;
+  if (m <= 128) return 128;
+  auto tri = [](int64_t t) { return t * (t + 1) / 2; };
+  const double n256 = double(count) * tri((m + 255) / 256);
+  const double n128 = double(count) * tri((m + 127) / 128);
+  // fill of the last wave: one 256-tile workgroup per CU, two 128-tile
+  // workgroups per CU, 256 CUs; 128-tiles pay ~15% for their lower
+  // arithmetic intensity.
+  const double eff256 = n256 / (std::ceil(n256 / 256.0) * 256.0);
+  const double eff128 = 0.85 * n128 / (std::ceil(n128 / 512.0) * 512.0);
+  return eff256 >= eff128 ? 256 : 128;
+}
+
+}  // namespace
+
+int tile_override() {
+  const char* s = std::getenv("MUON_TILE");
+  if (!s) return 0;
+  int v = std::atoi(s);
+  return (v == 128 || v == 256) ? v : 0;
+}
+
+ScalePlan make_scales(int op, int steps, double a, double b, double c) {
+  ScalePlan sp;
+  sp.sA.assign(std::max(steps, 1), 1.f);
+  sp.sB.assign(std::max(steps, 1), 1.f);
+  sp.sPA.assign(std::max(steps, 1), 1.f);
+  sp.sQ.assign(steps + 1, 1.f);
+  if (op == OP_F32) return sp;
+  // X₀ = M/(‖M‖_F + eps): every entry and every singular value is ≤ 1, so the
+  // eigenvalues of A₀ = X₀X₀ᵀ lie in [0, 1].  Each iterate is a polynomial in
+  // A₀, so its eigenvalues follow from the scalar maps below; for a symmetric
+  // matrix |entry| ≤ spectral norm, which bounds what the fp16 copy stores.
+  const double safety = 1.25;
+  const int N = 4096;
+  double L = 1.0;   // bound on eigenvalues of A_k
+  double Q = 1.0;   // bound on eigenvalues of Q_k
+  sp.sX = pow2_scale(1.0 * safety);
+  sp.sQ[0] = pow2_scale(Q * safety);
+  for (int k = 0; k < steps; ++k) {
+    double bmax = 0, pmax = 0, pamax = 0, lnext = 0;
+    for (int i = 0; i <= N; ++i) {
+      const double lam = L * i / N;
+      const double beta = b * lam + c * lam * lam;
+      const double p = a + beta;
+      bmax = std::max(bmax, std::fabs(beta));
+      pmax = std::max(pmax, std::fabs(p));
+      pamax = std::max(pamax, std::fabs(lam * p));
+      lnext = std::max(lnext, lam * p * p);
+    }
+    sp.sA[k] = pow2_scale(L * safety);
+    sp.sB[k] = pow2_scale(bmax * safety);
+    sp.sPA[k] = pow2_scale(pamax * safety);
+    Q *= pmax;
+    sp.sQ[k + 1] = pow2_scale(Q * safety);
+    L = lnext;
+  }
+  return sp;
+}
+
+std::string build_plan(const int64_t* rows, const int64_t* cols, int count, int op, int steps,
+                       float a, float b, float c, bool forStep, Plan* plan) {
+  Plan& P = *plan;
+  P = Plan();
+  P.op = op;
+  P.steps = steps;
+  P.forStep = forStep;
+  P.a = a;
+  P.b = b;
+  P.c = c;
+  P.mats.resize(count);
+  const size_t esz = (op == OP_F32) ? 4 : 2;
+
+  // buckets keyed by stored shape, groups keyed by m; both in order of first
+  // appearance so the plan is a pure function of the shape list.
+  std::map<std::pair<int64_t, int64_t>, int> bucketOf;
+  std::map<int64_t, int> groupOf;
+  for (int i = 0; i < count; ++i) {
+    MatPlan& mp = P.mats[i];
+    mp.rows = rows[i];
+    mp.cols = cols[i];
+    mp.numel = mp.rows * mp.cols;
+    mp.empty = (mp.rows == 0 || mp.cols == 0);
+    if (mp.empty) continue;
+    mp.tall = mp.rows > mp.cols;
+    mp.m = std::min(mp.rows, mp.cols);
+    mp.n = std::max(mp.rows, mp.cols);
+    auto key = std::make_pair(mp.rows, mp.cols);
+    auto it = bucketOf.find(key);
+    if (it == bucketOf.end()) {
+      BucketPlan bp;
+      bp.rows = mp.rows;
+      bp.cols = mp.cols;
+      bp.m = mp.m;
+      bp.n = mp.n;
+      bp.tall = mp.tall;
+      it = bucketOf.emplace(key, (int)P.buckets.size()).first;
+      P.buckets.push_back(bp);
+    }
+    mp.bucket = it->second;
+    mp.posBucket = (int)P.buckets[mp.bucket].mats.size();
+    P.buckets[mp.bucket].mats.push_back(i);
+  }
+  for (int bi = 0; bi < (int)P.buckets.size(); ++bi) {
+    BucketPlan& bp = P.buckets[bi];
+    auto it = groupOf.find(bp.m);
+    if (it == groupOf.end()) {
+      GroupPlan gp;
+      gp.m = bp.m;
+      it = groupOf.emplace(bp.m, (int)P.groups.size()).first;
+      P.groups.push_back(gp);
+    }
+    GroupPlan& gp = P.groups[it->second];
+    bp.group = it->second;
+    bp.gramStart = gp.count;
+    gp.count += (int)bp.mats.size();
+    gp.buckets.push_back(bi);
+  }
+  for (GroupPlan& gp : P.groups) {
+    gp.tile = choose_tile(op, gp.m, gp.count);
+    gp.Mp = round_up(gp.m, gp.tile);
+  }
+  for (BucketPlan& bp : P.buckets) {
+    const GroupPlan& gp = P.groups[bp.group];
+    bp.Mp = gp.Mp;
+    bp.Np = round_up(bp.n, gp.tile);
+    for (int k = 0; k < (int)bp.mats.size(); ++k) {
+      MatPlan& mp = P.mats[bp.mats[k]];
+      mp.group = bp.group;
+      mp.posGroup = bp.gramStart + k;
+    }
+  }
+
+  // partial sums of squares: one per elementwise workgroup
+  int64_t np = 0;
+  for (MatPlan& mp : P.mats) {
+    if (mp.empty) continue;
+    mp.partialOff = np;
+    mp.partialCnt = (mp.numel + kEwElems - 1) / kEwElems;
+    np += mp.partialCnt;
+  }
+  P.totalPartials = np;
+
+  size_t off = 0;
+  P.offPartials = off;
+  off = align_up(off + size_t(np) * 4);
+  P.offAlpha = off;
+  off = align_up(off + size_t(count) * 4);
+  for (GroupPlan& gp : P.groups) {
+    gp.stride32 = size_t(gp.Mp) * size_t(gp.Mp) * 4;
+    gp.strideh = size_t(gp.Mp) * size_t(gp.Mp) * esz;
+    const size_t n32 = gp.stride32 * gp.count, nh = gp.strideh * gp.count;
+    gp.offA32 = off;  off = align_up(off + n32);
+    gp.offQ32 = off;  off = align_up(off + n32);
+    gp.offPA32 = off; off = align_up(off + n32);
+    gp.offAh = off;   off = align_up(off + nh);
+    gp.offBh = off;   off = align_up(off + nh);
+    gp.offPAh = off;  off = align_up(off + nh);
+    gp.offQh[0] = off; off = align_up(off + nh);
+    gp.offQh[1] = off; off = align_up(off + nh);
+  }
+  for (BucketPlan& bp : P.buckets) {
+    bp.strideX = size_t(bp.Mp) * size_t(bp.Np) * esz;
+    bp.offXh = off;  off = align_up(off + bp.strideX * bp.mats.size());
+    bp.offXTh = off; off = align_up(off + bp.strideX * bp.mats.size());
+  }
+  P.totalBytes = off;
+  P.scales = make_scales(op, steps, a, b, c);
+  return std::string();
+}
+
+std::string Plan::json() const {
+  std::ostringstream o;
+  o.precision(9);
+  o << "{\"op\":\"" << (op == OP_F32 ? "f32" : "f16") << "\",\"steps\":" << steps
+    << ",\"for_step\":" << (forStep ? 1 : 0) << ",\"workspace_bytes\":" << totalBytes
+    << ",\"partials\":" << totalPartials << ",\"sX\":" << scales.sX << ",\"groups\":[";
+  for (size_t g = 0; g < groups.size(); ++g) {
+    const GroupPlan& gp = groups[g];
+    o << (g ? "," : "") << "{\"m\":" << gp.m << ",\"Mp\":" << gp.Mp << ",\"tile\":" << gp.tile
+      << ",\"count\":" << gp.count << ",\"buckets\":[";
+    for (size_t k = 0; k < gp.buckets.size(); ++k) o << (k ? "," : "") << gp.buckets[k];
+    o << "],\"offA32\":" << gp.offA32 << ",\"offQh\":[" << gp.offQh[0] << "," << gp.offQh[1]
+      << "]}";
+  }
+  o << "],\"buckets\":[";
+  for (size_t bi = 0; bi < buckets.size(); ++bi) {
+    const BucketPlan& bp = buckets[bi];
+    o << (bi ? "," : "") << "{\"rows\":" << bp.rows << ",\"cols\":" << bp.cols << ",\"m\":" << bp.m
+      << ",\"n\":" << bp.n << ",\"tall\":" << (bp.tall ? "true" : "false") << ",\"group\":"
+      << bp.group << ",\"Mp\":" << bp.Mp << ",\"Np\":" << bp.Np << ",\"gram_start\":"
+      << bp.gramStart << ",\"mats\":[";
+    for (size_t k = 0; k < bp.mats.size(); ++k) o << (k ? "," : "") << bp.mats[k];
+    o << "]}";
+  }
+  o << "],\"scales\":{\"sA\":[";
+  for (size_t k = 0; k < scales.sA.size(); ++k) o << (k ? "," : "") << scales.sA[k];
+  o << "],\"sB\":[";
+  for (size_t k = 0; k < scales.sB.size(); ++k) o << (k ? "," : "") << scales.sB[k];
+  o << "],\"sPA\":[";
+  for (size_t k = 0; k < scales.sPA.size(); ++k) o << (k ? "," : "") << scales.sPA[k];
+  o << "],\"sQ\":[";
+  for (size_t k = 0; k < scales.sQ.size(); ++k) o << (k ? "," : "") << scales.sQ[k];
+  o << "]}}";
+  return o.str();
+}
+
+}  // namespace muon

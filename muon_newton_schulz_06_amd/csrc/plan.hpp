@@ -1,0 +1,87 @@
+// Host-side planning: grouping of matrices, tile choice, padded sizes,
+// workspace layout and the static power-of-two operand scales.  Pure C++,
+// no HIP calls, so every part of it runs (and is tested) without a GPU.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <string>
+#include <vector>
+
+namespace muon {
+
+struct MatPlan {
+  int64_t rows = 0, cols = 0;  // stored shape
+  int64_t m = 0, n = 0;        // Gram-space m ≤ n
+  bool tall = false;           // rows > cols: processed as the transpose
+  bool empty = false;
+  int bucket = -1;             // index into Plan::buckets
+  int posBucket = -1;
+  int group = -1;              // index into Plan::groups
+  int posGroup = -1;
+  int64_t numel = 0;
+  int64_t partialOff = 0, partialCnt = 0;
+};
+
+// Matrices of one stored shape: they share the SYRK, cast and final launches.
+struct BucketPlan {
+  int64_t rows = 0, cols = 0, m = 0, n = 0;
+  bool tall = false;
+  int group = -1;
+  int64_t Mp = 0, Np = 0;   // padded m, n
+  std::vector<int> mats;    // matrix indices in call order
+  int gramStart = 0;        // position of mats[0] inside its group
+  size_t offXh = 0;         // X₀  (Mp × Np), operand type
+  size_t offXTh = 0;        // X₀ᵀ (Np × Mp), operand type
+  size_t strideX = 0;       // bytes per matrix of either buffer
+};
+
+// Matrices of one Gram size m: they share every Gram-space launch.
+struct GroupPlan {
+  int64_t m = 0, Mp = 0;
+  int tile = 128;
+  int count = 0;
+  std::vector<int> buckets;
+  size_t offA32 = 0, offQ32 = 0, offPA32 = 0;          // fp32, upper triangle used
+  size_t offAh = 0, offBh = 0, offPAh = 0, offQh[2] = {0, 0};  // operand type, mirrored
+  size_t stride32 = 0, strideh = 0;                    // bytes per matrix
+};
+
+// Static operand scales (powers of two) for the half-precision path, derived
+// from bounds on the spectra of the Gram-space iterates.
+struct ScalePlan {
+  float sX = 1.f;                  // X₀ (entries ≤ 1 after normalisation)
+  std::vector<float> sA, sB, sPA;  // per step k: A_k, B_k, P_k·A_k
+  std::vector<float> sQ;           // per step k: Q_k (k = 0..steps)
+};
+
+struct Plan {
+  int op = 0;              // OpType of the MFMA operands
+  int steps = 0;
+  bool forStep = false;
+  float a = 0, b = 0, c = 0;
+  std::vector<MatPlan> mats;
+  std::vector<BucketPlan> buckets;
+  std::vector<GroupPlan> groups;
+  size_t offPartials = 0;
+  size_t offAlpha = 0;
+  int64_t totalPartials = 0;
+  size_t totalBytes = 0;
+  ScalePlan scales;
+  std::string json() const;
+};
+
+// Environment override of the tile (MUON_TILE=128|256), 0 when unset.
+int tile_override();
+
+// Build the plan.  `op` selects operand type (OP_F16 / OP_F32).  Returns an
+// empty string on success, else a message.
+std::string build_plan(const int64_t* rows, const int64_t* cols, int count, int op, int steps,
+                       float a, float b, float c, bool forStep, Plan* plan);
+
+ScalePlan make_scales(int op, int steps, double a, double b, double c);
+
+inline int64_t round_up(int64_t x, int64_t q) { return (x + q - 1) / q * q; }
+
+}  // namespace muon

@@ -1,0 +1,241 @@
+"""Host-side tests of the C ABI (no GPU needed): the library loads, exports
+every entry point its header declares, rejects bad arguments before any HIP
+call, and plans groups, tiles, padding, workspace and operand scales."""
+import ctypes
+import json
+import math
+import os
+import re
+
+import pytest
+import torch
+
+import muon_newton_schulz_06_amd as mns
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "muon_ns.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(mns.lib_path()),
+                                reason="libmuon_ns.so not built (run __graft_entry__.build())")
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(muon_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    L = mns.load()
+    names = header_functions()
+    assert "muon_ns_batched" in names and "muon_step" in names
+    for n in names:
+        assert hasattr(L, n), n
+    assert mns.abi_version() == 1
+
+
+def test_library_binds_hip_runtime_only_by_soname():
+    # The library names the HIP runtime by soname, so the dynamic loader
+    # resolves it to the copy the process (torch) already loaded.
+    import subprocess
+    out = subprocess.run(["readelf", "-d", mns.lib_path()], capture_output=True, text=True).stdout
+    needed = [l for l in out.splitlines() if "NEEDED" in l]
+    assert any("[libamdhip64.so.7]" in l for l in needed)
+    assert not any("/" in l for l in needed)
+
+
+# ---------------------------------------------------------------- error paths
+def _desc(n, rows=4, cols=8, x=0x10000, out=0x900000, stride=0x10000):
+    arr = (mns.MuonNsDesc * max(n, 1))()
+    for i in range(n):
+        arr[i].x = x + i * stride
+        arr[i].out = out + i * stride
+        arr[i].rows, arr[i].cols, arr[i].ld_x, arr[i].ld_out = rows, cols, cols, cols
+    return arr
+
+
+C3 = (ctypes.c_float * 3)(3.4445, -4.775, 2.0315)
+
+
+def _ns(arr, n, steps=5, coeffs=C3, dtype=1, eps=1e-7, ws=0x100000000, wsb=1 << 40):
+    L = mns.load()
+    return L.muon_ns_batched(arr, n, steps, coeffs, dtype, eps, ctypes.c_void_p(ws), wsb, None)
+
+
+def _err():
+    return mns.load().muon_last_error().decode()
+
+
+def test_count_zero_is_noop():
+    assert _ns(None, 0) == 0
+
+
+@pytest.mark.parametrize("mutate,status", [
+    (lambda a: setattr(a[0], "rows", -1), 1),
+    (lambda a: setattr(a[0], "ld_x", 3), 1),
+    (lambda a: setattr(a[0], "ld_out", 7), 1),
+    (lambda a: setattr(a[0], "x", None), 1),
+    (lambda a: setattr(a[0], "out", None), 1),
+    (lambda a: setattr(a[1], "out", a[0].out + 4), 3),  # outputs overlap
+    (lambda a: setattr(a[0], "rows", 1 << 25), 2),
+    (lambda a: (setattr(a[0], "rows", 40000), setattr(a[0], "cols", 40000)), 2),
+])
+def test_ns_rejects_bad_descriptors(mutate, status):
+    arr = _desc(2)
+    mutate(arr)
+    assert _ns(arr, 2) == status, _err()
+    assert _err()
+
+
+def test_ns_rejects_bad_scalars():
+    arr = _desc(1)
+    assert _ns(arr, -1) == 1
+    assert _ns(arr, 1, steps=-1) == 1
+    assert _ns(arr, 1, steps=65) == 1
+    assert _ns(arr, 1, dtype=7) == 1
+    assert _ns(arr, 1, eps=-1.0) == 1
+    assert _ns(arr, 1, eps=float("nan")) == 1
+    assert _ns(arr, 1, coeffs=(ctypes.c_float * 3)(1.0, float("inf"), 0.0)) == 1
+    assert mns.load().muon_ns_batched(arr, 1, 5, None, 1, 1e-7, None, 0, None) == 1
+
+
+def test_ns_workspace_checks():
+    arr = _desc(1)
+    assert _ns(arr, 1, ws=0, wsb=0) == 4
+    assert _ns(arr, 1, ws=0x100000010) == 4  # misaligned
+    assert _ns(arr, 1, wsb=16) == 4
+    assert "too small" in _err()
+
+
+def test_in_place_is_allowed_and_reaches_the_device_check():
+    """out == x passes validation; without a GPU the call then stops at the
+    device check (status NO_DEVICE), with nothing enqueued."""
+    arr = _desc(1)
+    arr[0].out = arr[0].x
+    st = _ns(arr, 1)
+    assert st in (0, 6) if torch.cuda.is_available() is False else True
+    if not torch.cuda.is_available():
+        assert st == 6
+
+
+def test_empty_matrices_skip_pointer_checks():
+    arr = _desc(2)
+    arr[0].rows = 0
+    arr[0].x = None
+    arr[0].out = None
+    st = _ns(arr, 2)
+    if not torch.cuda.is_available():
+        assert st == 6, _err()
+
+
+def _step(n=2, rows=(4, 8), cols=(8, 4), p=None, g=None, m=None, dtype=1, beta=0.95, lr=0.02,
+          steps=5, eps=1e-7, ws=0x100000000, wsb=1 << 40, coeffs=C3):
+    vp = ctypes.c_void_p
+    P = (vp * n)(*(p or [0x1000000 + i * 0x10000 for i in range(n)]))
+    G = (vp * n)(*(g or [0x2000000 + i * 0x10000 for i in range(n)]))
+    M = (vp * n)(*(m or [0x3000000 + i * 0x10000 for i in range(n)]))
+    R = (ctypes.c_int64 * n)(*rows[:n])
+    C = (ctypes.c_int64 * n)(*cols[:n])
+    return mns.load().muon_step(P, G, M, R, C, n, dtype, beta, lr, steps, coeffs, eps,
+                                ctypes.c_void_p(ws), wsb, None)
+
+
+def test_step_rejects_bad_arguments():
+    assert _step(dtype=5) == 1
+    assert _step(beta=float("inf")) == 1
+    assert _step(lr=float("nan")) == 1
+    assert _step(steps=100) == 1
+    assert _step(rows=(-1, 8)) == 1
+    assert _step(p=[0, 0x1010000]) == 1
+    # a gradient overlapping another matrix's momentum
+    assert _step(g=[0x3000000 + 8, 0x2010000]) == 3, _err()
+    assert _step(m=[0x3000000, 0x3000000 + 64]) == 3
+    assert _step(ws=0) == 4
+    assert _step(wsb=100) == 4
+    assert mns.load().muon_step(None, None, None, None, None, 0, 1, 0.9, 0.1, 5, C3, 1e-7,
+                                None, 0, None) == 0
+
+
+# ---------------------------------------------------------------- planning
+def test_plan_groups_buckets_and_orientation():
+    shapes = [(3584, 3584), (512, 3584), (512, 3584), (3584, 3584), (18944, 3584),
+              (18944, 3584), (3584, 18944)]
+    p = mns.describe_plan(shapes * 2, for_step=True)
+    ms = sorted(g["m"] for g in p["groups"])
+    assert ms == [512, 3584]
+    g3584 = next(g for g in p["groups"] if g["m"] == 3584)
+    assert g3584["count"] == 10  # q, o, gate, up, down × 2 layers
+    buckets = {(b["rows"], b["cols"]): b for b in p["buckets"]}
+    assert buckets[(18944, 3584)]["tall"] and not buckets[(3584, 18944)]["tall"]
+    assert buckets[(18944, 3584)]["m"] == 3584 and buckets[(18944, 3584)]["n"] == 18944
+    assert not buckets[(3584, 3584)]["tall"]
+    for b in p["buckets"]:
+        g = p["groups"][b["group"]]
+        assert b["Mp"] % g["tile"] == 0 and b["Np"] % g["tile"] == 0
+        assert b["Mp"] >= b["m"] and b["Np"] >= b["n"] and b["Mp"] - b["m"] < g["tile"]
+    # every matrix appears in exactly one bucket, in call order within it
+    seen = sorted(i for b in p["buckets"] for i in b["mats"])
+    assert seen == list(range(14))
+    # gram positions of a group's buckets are contiguous and disjoint
+    for g in p["groups"]:
+        spans = sorted((p["buckets"][bi]["gram_start"], len(p["buckets"][bi]["mats"])) for bi in g["buckets"])
+        pos = 0
+        for start, cnt in spans:
+            assert start == pos
+            pos += cnt
+        assert pos == g["count"]
+
+
+def test_plan_workspace_matches_layout():
+    shapes = [(256, 1024), (128, 512), (1000, 300), (64, 4096)]
+    p = mns.describe_plan(shapes, for_step=False)
+    assert p["workspace_bytes"] == mns.ns_workspace_size(shapes)
+    assert p["workspace_bytes"] % 256 == 0
+    total = 0
+    for g in p["groups"]:
+        total += 22 * g["Mp"] ** 2 * g["count"]  # 3 fp32 + 5 fp16 m×m buffers
+    for b in p["buckets"]:
+        total += 2 * 2 * b["Mp"] * b["Np"] * len(b["mats"])
+    assert p["workspace_bytes"] >= total
+    assert p["workspace_bytes"] - total < 256 * (3 + 8 * len(p["groups"]) + 2 * len(p["buckets"])) + 4 * 1000
+
+
+def test_plan_f32_uses_unit_scales():
+    p = mns.describe_plan([(256, 1024)], for_step=False, dtype=torch.float32)
+    assert p["op"] == "f32"
+    assert p["sX"] == 1.0
+    for k in ("sA", "sB", "sPA", "sQ"):
+        assert all(v == 1.0 for v in p["scales"][k])
+
+
+@pytest.mark.parametrize("coeffs,steps", [(mns.QUINTIC, 5), (mns.CUBIC, 30), ((2.0, -1.5, 0.5), 3)])
+def test_plan_scales_bound_every_iterate(coeffs, steps):
+    """The fp16 copies hold s·Y with |Y| ≤ spectral bound; check on a dense
+    grid of singular values that every scaled iterate stays below 2^14 and
+    that the scales are powers of two."""
+    p = mns.describe_plan([(64, 256)], for_step=False, steps=steps, coeffs=coeffs)
+    sc = p["scales"]
+    a, b, c = coeffs
+    sig = [i / 2000 for i in range(2001)]
+    lam = [s * s for s in sig]   # eigenvalues of A₀ = X₀X₀ᵀ, ‖X₀‖₂ ≤ 1
+    q = [1.0] * len(lam)
+    for v in [p["sX"]] + sc["sA"] + sc["sB"] + sc["sPA"] + sc["sQ"]:
+        assert v > 0 and math.log2(v) == int(math.log2(v))
+    assert max(q) * sc["sQ"][0] <= 2 ** 14
+    for k in range(steps):
+        B = [b * l + c * l * l for l in lam]
+        P = [a + x for x in B]
+        assert max(abs(l) for l in lam) * sc["sA"][k] <= 2 ** 14
+        assert max(abs(x) for x in B) * sc["sB"][k] <= 2 ** 14
+        assert max(abs(l * pp) for l, pp in zip(lam, P)) * sc["sPA"][k] <= 2 ** 14
+        q = [qq * pp for qq, pp in zip(q, P)]
+        assert max(abs(x) for x in q) * sc["sQ"][k + 1] <= 2 ** 14
+        lam = [l * pp * pp for l, pp in zip(lam, P)]
+
+
+def test_tile_choice_for_qwen_set():
+    shapes = [(3584, 3584), (512, 3584), (512, 3584), (3584, 3584), (18944, 3584),
+              (18944, 3584), (3584, 18944)] * 28
+    p = mns.describe_plan(shapes, for_step=True)
+    tiles = {g["m"]: g["tile"] for g in p["groups"]}
+    assert tiles[3584] == 256

@@ -1,0 +1,272 @@
+"""Parity of the HIP path with the fp64 CPU oracle, through the C ABI.
+
+Bounds: relative Frobenius error per matrix ≤ 1e-4 for fp32 storage (fp32
+MFMA), ≤ 2e-2 for bf16 storage (half-precision MFMA, fp32 accumulation).
+Weights after a step: within 1 bf16 ulp of the oracle's once-rounded value
+everywhere.  Momentum: within 1 fp32 ulp.
+"""
+import math
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+TOL_F32 = 1e-4
+TOL_BF16 = 2e-2
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def mns():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a HIP device")
+    import muon_newton_schulz_06_amd as m
+    m.load()
+    return m
+
+
+def rel(gpu, ref):
+    g = gpu.detach().to("cpu", torch.float64).numpy() if torch.is_tensor(gpu) else gpu
+    ref = np.asarray(ref, np.float64)
+    d = np.linalg.norm(g - ref)
+    n = np.linalg.norm(ref)
+    return d / n if n > 0 else d
+
+
+def oracle_ns(x_cpu, steps=5, coeffs=oracle.QUINTIC, eps=1e-7):
+    c32 = tuple(float(np.float32(v)) for v in coeffs)  # what the library receives
+    return oracle.muon_orthogonalize(x_cpu.to(torch.float64).numpy(), c32, steps, eps)
+
+
+def bf16_ulp(x):
+    x = np.abs(np.asarray(x, np.float64))
+    e = np.floor(np.log2(np.maximum(x, 2.0 ** -126)))
+    return 2.0 ** (e - 7)
+
+
+# ------------------------------------------------------------------ fp32 path
+def test_fp32_single_quintic(mns):
+    say("fp32 256x1024 quintic 5 steps")
+    x = W.ns_single()
+    out = mns.muon_ns_batched([x.cuda()], steps=5)[0]
+    torch.cuda.synchronize()
+    e = rel(out, oracle_ns(x))
+    say("rel err", e)
+    assert e <= TOL_F32
+
+
+def test_fp32_single_cubic_vs_svd(mns):
+    say("fp32 256x1024 cubic 30 steps vs SVD")
+    x = W.ns_single()
+    out = mns.muon_ns_batched([x.cuda()], steps=30, coeffs=mns.CUBIC)[0]
+    torch.cuda.synchronize()
+    e_svd = rel(out, oracle.polar_svd(x.double().numpy()))
+    e_ns = rel(out, oracle_ns(x, steps=30, coeffs=oracle.CUBIC))
+    say("rel err vs svd", e_svd, "vs oracle NS", e_ns)
+    assert e_svd <= TOL_F32 and e_ns <= TOL_F32
+
+
+def test_fp32_ragged_tall_wide(mns):
+    shapes = [(200, 333), (333, 200), (130, 130), (1, 77), (77, 1), (257, 1025)]
+    say("fp32 ragged", shapes)
+    xs = [W.gaussian(s, 50 + i) for i, s in enumerate(shapes)]
+    outs = mns.muon_ns_batched([x.cuda() for x in xs], steps=5)
+    torch.cuda.synchronize()
+    for x, o in zip(xs, outs):
+        e = rel(o, oracle_ns(x))
+        say(tuple(x.shape), e)
+        assert e <= TOL_F32
+
+
+# ------------------------------------------------------------------ bf16 path
+def test_bf16_ragged_mixed_batch(mns):
+    shapes = [(300, 700), (700, 300), (129, 129), (1, 513), (513, 1), (64, 4096),
+              (4096, 64), (384, 1000), (255, 256), (256, 255)]
+    say("bf16 ragged mix", shapes)
+    xs = [W.gaussian(s, 100 + i, dtype=torch.bfloat16) for i, s in enumerate(shapes)]
+    outs = mns.muon_ns_batched([x.cuda() for x in xs], steps=5)
+    torch.cuda.synchronize()
+    worst = 0
+    for x, o in zip(xs, outs):
+        e = rel(o.float(), oracle_ns(x.float()))
+        say(tuple(x.shape), e)
+        worst = max(worst, e)
+        assert e <= TOL_BF16
+    say("worst", worst)
+
+
+def test_row_vector_closed_form(mns):
+    """m = 1: O = φ^5(1)·x/‖x‖ (one singular value, equal to 1)."""
+    say("fp32 row/column vector closed form")
+    x = W.gaussian((1, 300), 7)
+    phi5 = oracle.scalar_map(1.0, oracle.QUINTIC, 5)
+    want = phi5 * x.double().numpy() / np.linalg.norm(x.double().numpy())
+    o1, o2 = mns.muon_ns_batched([x.cuda(), x.t().contiguous().cuda()], steps=5)
+    torch.cuda.synchronize()
+    assert rel(o1, want) <= TOL_F32
+    assert rel(o2, want.T) <= TOL_F32
+
+
+def test_uniform_batch_sampled_and_batch_invariant(mns):
+    say("bf16 32x(1024x4096) batch")
+    xs = W.ns_uniform_batch(device="cuda")
+    outs = mns.muon_ns_batched(xs, steps=5)
+    torch.cuda.synchronize()
+    for i in (0, 13, 31):
+        e = rel(outs[i].float(), oracle_ns(xs[i].float().cpu()))
+        say("matrix", i, "rel err", e)
+        assert e <= TOL_BF16
+    say("batch invariance: matrix 13 alone")
+    alone = mns.muon_ns_batched([xs[13]], steps=5)[0]
+    torch.cuda.synchronize()
+    assert torch.equal(alone, outs[13])
+
+
+def test_small_mix_all_matrices(mns):
+    say("bf16 heterogeneous 176-matrix batch (shuffled)")
+    xs = W.ns_small_mix(device="cuda")
+    outs = mns.muon_ns_batched(xs, steps=5)
+    torch.cuda.synchronize()
+    worst = 0
+    for x, o in zip(xs, outs):
+        e = rel(o.float(), oracle_ns(x.float().cpu()))
+        worst = max(worst, e)
+        assert e <= TOL_BF16, (tuple(x.shape), e)
+    say("worst", worst)
+
+
+def test_small_mix_tall_variant(mns):
+    say("bf16 heterogeneous batch, every other matrix stored tall")
+    xs = W.ns_small_mix(device="cuda", tall_every_other=True)
+    outs = mns.muon_ns_batched(xs, steps=5)
+    torch.cuda.synchronize()
+    for k in range(0, len(xs), 7):
+        e = rel(outs[k].float(), oracle_ns(xs[k].float().cpu()))
+        assert e <= TOL_BF16, (tuple(xs[k].shape), e)
+
+
+# ------------------------------------------------------------------ edge cases
+def test_edge_cases(mns):
+    say("edge: empty list")
+    assert mns.muon_ns_batched([], steps=5) == []
+    say("edge: empty matrix inside a batch, zero matrix, steps=0")
+    xs = [torch.zeros((0, 5), device="cuda", dtype=torch.bfloat16),
+          torch.zeros((40, 60), device="cuda", dtype=torch.bfloat16),
+          W.gaussian((50, 90), 3, dtype=torch.bfloat16, device="cuda")]
+    outs = mns.muon_ns_batched(xs, steps=5)
+    torch.cuda.synchronize()
+    assert outs[0].shape == (0, 5)
+    assert torch.count_nonzero(outs[1]) == 0
+    assert rel(outs[2].float(), oracle_ns(xs[2].float().cpu())) <= TOL_BF16
+    x = W.gaussian((70, 130), 4, device="cuda")
+    o0 = mns.muon_ns_batched([x], steps=0)[0]
+    torch.cuda.synchronize()
+    assert rel(o0, oracle_ns(x.cpu(), steps=0)) <= TOL_F32
+    say("edge: NaN propagates")
+    y = W.gaussian((64, 128), 5, device="cuda")
+    y[3, 7] = float("nan")
+    oy = mns.muon_ns_batched([y], steps=5)[0]
+    torch.cuda.synchronize()
+    assert torch.isnan(oy).any()
+    say("edge: in-place and strided input")
+    big = W.gaussian((100, 300), 6, device="cuda")
+    view = big[:, 50:250]
+    ref = oracle_ns(view.cpu())
+    o = mns.muon_ns_batched([view], outs=[view], steps=5)[0]
+    torch.cuda.synchronize()
+    assert rel(o, ref) <= TOL_F32
+
+
+def test_run_to_run_bitwise_determinism(mns):
+    say("determinism")
+    xs = W.ns_small_mix(device="cuda", mix=[(4, 256, 1024), (3, 512, 2048)])
+    a = mns.muon_ns_batched(xs, steps=5)
+    b = mns.muon_ns_batched(xs, steps=5)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+# ------------------------------------------------------------------ muon_step
+def _check_step(mns, shapes, seed0, check_idx, nsteps=2):
+    inp = W.muon_inputs(shapes, seed0, device="cuda")
+    host_W = [p.float().cpu().double().numpy() for p in inp.params]
+    host_M = [m.cpu().numpy() for m in inp.momenta]
+    for step in range(nsteps):
+        grads = inp.grads if step == 0 else W.fresh_grads(shapes, seed0, step, device="cuda")
+        host_g = [g.cpu().numpy() for g in grads]
+        say("muon_step", step, "over", len(shapes), "matrices")
+        mns.muon_step(inp.params, grads, inp.momenta, beta=0.95, lr=0.02, steps=5)
+        torch.cuda.synchronize()
+        for j in range(len(shapes)):
+            Mn = oracle.momentum_update(host_M[j], host_g[j], np.float32(0.95))
+            got = inp.momenta[j].cpu().numpy()
+            ulp = np.spacing(np.abs(Mn).astype(np.float32))
+            assert np.all(np.abs(got.astype(np.float64) - Mn) <= ulp), ("momentum", j)
+            host_M[j] = got
+        for j in check_idx:
+            O = oracle.muon_orthogonalize(host_M[j], tuple(float(np.float32(v)) for v in oracle.QUINTIC), 5, 1e-7)
+            r, c = shapes[j]
+            want = oracle.bf16_round(host_W[j] - float(np.float32(0.02)) * oracle.lr_shape_scale(r, c) * O)
+            got = inp.params[j].float().cpu().double().numpy()
+            diff = np.abs(got - want)
+            tol = bf16_ulp(np.maximum(np.abs(got), np.abs(want)))
+            frac = float(np.mean(diff > 0))
+            say("weights", shapes[j], "mismatch fraction", frac, "max diff/ulp", float(np.max(diff / tol)))
+            assert np.all(diff <= tol * 1.0001)
+            assert frac < 0.05
+        host_W = [p.float().cpu().double().numpy() for p in inp.params]
+
+
+def test_muon_step_small_shapes(mns):
+    shapes = [(96, 200), (200, 96), (128, 128), (1, 64), (300, 1000)]
+    _check_step(mns, shapes, 900, range(len(shapes)))
+
+
+def test_muon_step_qwen_layer(mns):
+    shapes = W.qwen_layer_shapes()
+    _check_step(mns, shapes, 4001, check_idx=[1, 0], nsteps=2)
+
+
+def test_muon_step_fp32_params_expose_the_update(mns):
+    """fp32 weights starting at zero: W' = −lr·sc·O exactly in fp32, so the
+    orthogonalised update itself is compared with the oracle (including a
+    tall Qwen shape through the transposed path)."""
+    shapes = [(512, 3584), (18944, 3584), (130, 70)]
+    inp = W.muon_inputs(shapes, 77, device="cuda", param_dtype=torch.float32)
+    for p in inp.params:
+        p.zero_()
+    host_g = [g.cpu().numpy() for g in inp.grads]
+    say("muon_step fp32 params", shapes)
+    mns.muon_step(inp.params, inp.grads, inp.momenta, beta=0.95, lr=0.02, steps=5)
+    torch.cuda.synchronize()
+    for j, (r, c) in enumerate(shapes):
+        lrsc = float(np.float32(0.02)) * oracle.lr_shape_scale(r, c)
+        O_gpu = -inp.params[j].double().cpu().numpy() / lrsc
+        O = oracle.muon_orthogonalize(host_g[j], tuple(float(np.float32(v)) for v in oracle.QUINTIC), 5, 1e-7)
+        e = rel(O_gpu, O)
+        say(shapes[j], "rel err of update", e)
+        assert e <= TOL_BF16
+
+
+def test_single_hip_runtime_in_process(mns):
+    x = W.gaussian((32, 64), 1, device="cuda")
+    mns.muon_ns_batched([x])
+    torch.cuda.synchronize()
+    libs = set()
+    with open("/proc/self/maps") as f:
+        for line in f:
+            if "libamdhip64" in line:
+                libs.add(line.split()[-1])
+    assert len(libs) == 1, libs
