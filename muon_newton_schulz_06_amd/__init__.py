@@ -133,13 +133,19 @@ def _stream_handle(stream, device):
 
 
 def _ld(t: torch.Tensor) -> int:
+    """Row stride in elements of a 2-D tensor whose rows are contiguous.
+    Strides of size-1 dimensions carry no information and are ignored."""
     if t.dim() != 2:
         raise ValueError("matrices must be 2-D")
+    rows, cols = t.shape
     if t.numel() == 0:
-        return max(t.shape[1], 1)
-    if t.stride(1) != 1:
+        return max(cols, 1)
+    if cols > 1 and t.stride(1) != 1:
         raise ValueError("matrix rows must be contiguous (stride(1) == 1)")
-    return t.stride(0) if t.shape[0] > 1 else t.shape[1]
+    ld = t.stride(0) if rows > 1 else cols
+    if ld < cols:
+        raise ValueError("row stride smaller than the row length")
+    return ld
 
 
 _ws_cache: dict = {}
