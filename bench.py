@@ -87,6 +87,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="qwen_full")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run only a plain 1 GiB read + 1 GiB write kernel (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the step shards by matrix across GPUs "
@@ -99,6 +101,16 @@ def main():
     import workloads as W
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.calibrate_copy:
+        # A kernel of known traffic for scaling the FETCH_SIZE / WRITE_SIZE
+        # counters: y = 2·x over 2^28 fp32 values reads and writes 1 GiB each.
+        x = torch.ones(1 << 28, device="cuda")
+        y = torch.empty_like(x)
+        for _ in range(3):
+            torch.mul(x, 2.0, out=y)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "mul_out", "read_bytes": 1 << 30, "write_bytes": 1 << 30}))
+        return
     mns.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)

@@ -104,7 +104,7 @@ bool finite3(const float* c) {
 }
 
 constexpr int64_t kMaxDim = int64_t(1) << 24;   // rows / cols
-constexpr int64_t kMaxGramM = 32768;           // m×m fp32 state per matrix ≤ 4 GiB
+constexpr int64_t kMaxGramM = 32768;           // five m×m operand copies per matrix ≤ 10 GiB
 constexpr int kMaxSteps = 64;
 
 muon_status_t check_shape(int i, int64_t r, int64_t c) {
@@ -266,6 +266,9 @@ muon_status_t enqueue(const Plan& P, const std::vector<CallerMat>& cm, int srcDt
   // Helper: launch a list of segments (≤ kMaxSegs per launch).
   auto launch_segs = [&](int tile, std::vector<GemmSeg>& segs, std::vector<double>& works, int kind,
                          const char* what) -> muon_status_t {
+    for (const GemmSeg& S : segs)
+      if (tile == 256 && (S.in32 || S.out32))
+        return fail(MUON_ERR_UNSUPPORTED, "internal: fp32 state on a 256-tile launch");
     for (size_t s0 = 0; s0 < segs.size(); s0 += kMaxSegs) {
       GemmLaunch L;
       std::memset(&L, 0, sizeof(L));
@@ -297,9 +300,13 @@ muon_status_t enqueue(const Plan& P, const std::vector<CallerMat>& cm, int srcDt
     S.lda = S.ldb = S.ldc = (int32_t)g.Mp;
     S.K = (int32_t)g.Mp;
     S.strideA = S.strideB = g.Mp * g.Mp;
-    S.strideIn32 = S.strideOut32 = S.strideOuth = g.Mp * g.Mp;
+    S.strideInh = S.strideOuth = g.Mp * g.Mp;
+    S.strideIn32 = S.strideOut32 = g.Mp * g.Mp;
     S.mReal = S.nReal = (int32_t)g.m;
     return S;
+  };
+  auto f32 = [&](const GroupPlan& g, size_t off) -> float* {
+    return g.state32 ? at<float>(ws, off) : nullptr;
   };
   auto symflops = [](const GroupPlan& g) { return (double)g.count * g.m * g.m * (double)(g.m + 1); };
 
@@ -320,8 +327,8 @@ muon_status_t enqueue(const Plan& P, const std::vector<CallerMat>& cm, int srcDt
         S.epi = EPI_SYRK;
         S.u = 1.0f / (sc.sX * sc.sX);
         S.sOut = sc.sA[0];
-        S.out32 = at<float>(ws, g.offA32 + g.stride32 * bp.gramStart);
         S.outh = at<char>(ws, g.offAh + g.strideh * bp.gramStart);
+        if (g.state32) S.out32 = at<float>(ws, g.offA32 + g.stride32 * bp.gramStart);
         if (P.steps == 0) {
           S.writeIdentity = 1;
           S.outhb = at<char>(ws, g.offQh[0] + g.strideh * bp.gramStart);
@@ -335,7 +342,8 @@ muon_status_t enqueue(const Plan& P, const std::vector<CallerMat>& cm, int srcDt
     if (s != MUON_OK) return s;
   }
 
-  // 5. Gram-space recursion
+  // 5. Gram-space recursion.  Every product's previous iterate (the a·Y and
+  // b·A terms) is its B operand, read back from the operand copy.
   const float a = P.a, b = P.b, c = P.c;
   int qcur = 0;  // Qh buffer holding the current Q
   for (int k = 0; k < P.steps; ++k) {
@@ -347,17 +355,18 @@ muon_status_t enqueue(const Plan& P, const std::vector<CallerMat>& cm, int srcDt
       for (const GroupPlan& g : P.groups) {
         if (g.tile != tile) continue;
         GemmSeg S = sym_seg(g, tile);
-        S.A = S.B = at<char>(ws, g.offAh);
+        S.A = S.B = S.inh = at<char>(ws, g.offAh);
+        S.in32 = f32(g, g.offA32);
+        S.inIsB = 1;
+        S.sIn = 1.0f / sc.sA[k];
         S.epi = EPI_SQ;
         S.u = 1.0f / (sc.sA[k] * sc.sA[k]);
         S.p0 = a;
         S.p1 = b;
         S.p2 = c;
-        S.in32 = at<float>(ws, g.offA32);
         S.outh = at<char>(ws, g.offBh);
         S.sOut = sc.sB[k];
         if (k == 0) {
-          S.out32b = at<float>(ws, g.offQ32);
           S.outhb = at<char>(ws, g.offQh[0]);
           S.sOutB = sc.sQ[1];
         }
@@ -374,12 +383,12 @@ muon_status_t enqueue(const Plan& P, const std::vector<CallerMat>& cm, int srcDt
         if (hasQ) {
           GemmSeg S = sym_seg(g, tile);
           S.A = at<char>(ws, g.offBh);
-          S.B = at<char>(ws, g.offQh[qcur]);
+          S.B = S.inh = at<char>(ws, g.offQh[qcur]);
+          S.inIsB = 1;
+          S.sIn = 1.0f / sc.sQ[k];
           S.epi = EPI_AXPY;
           S.u = 1.0f / (sc.sB[k] * sc.sQ[k]);
           S.p0 = a;
-          S.in32 = at<float>(ws, g.offQ32);
-          S.out32 = at<float>(ws, g.offQ32);
           S.outh = at<char>(ws, g.offQh[qcur ^ 1]);
           S.sOut = sc.sQ[k + 1];
           segs.push_back(S);
@@ -388,12 +397,14 @@ muon_status_t enqueue(const Plan& P, const std::vector<CallerMat>& cm, int srcDt
         if (hasA) {
           GemmSeg S = sym_seg(g, tile);
           S.A = at<char>(ws, g.offBh);
-          S.B = at<char>(ws, g.offAh);
+          S.B = S.inh = at<char>(ws, g.offAh);
+          S.in32 = f32(g, g.offA32);
+          S.out32 = f32(g, g.offPA32);
+          S.inIsB = 1;
+          S.sIn = 1.0f / sc.sA[k];
           S.epi = EPI_AXPY;
           S.u = 1.0f / (sc.sB[k] * sc.sA[k]);
           S.p0 = a;
-          S.in32 = at<float>(ws, g.offA32);
-          S.out32 = at<float>(ws, g.offPA32);
           S.outh = at<char>(ws, g.offPAh);
           S.sOut = sc.sPA[k];
           segs.push_back(S);
@@ -410,12 +421,14 @@ muon_status_t enqueue(const Plan& P, const std::vector<CallerMat>& cm, int srcDt
           if (g.tile != tile) continue;
           GemmSeg S = sym_seg(g, tile);
           S.A = at<char>(ws, g.offBh);
-          S.B = at<char>(ws, g.offPAh);
+          S.B = S.inh = at<char>(ws, g.offPAh);
+          S.in32 = f32(g, g.offPA32);
+          S.out32 = f32(g, g.offA32);
+          S.inIsB = 1;
+          S.sIn = 1.0f / sc.sPA[k];
           S.epi = EPI_AXPY;
           S.u = 1.0f / (sc.sB[k] * sc.sPA[k]);
           S.p0 = a;
-          S.in32 = at<float>(ws, g.offPA32);
-          S.out32 = at<float>(ws, g.offA32);
           S.outh = at<char>(ws, g.offAh);
           S.sOut = sc.sA[k + 1];
           segs.push_back(S);

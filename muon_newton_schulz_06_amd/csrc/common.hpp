@@ -16,16 +16,19 @@ constexpr int kMaxUser = 32;  // caller matrices per launch (kernel-arg tables)
 
 enum OpType : int32_t { OP_F16 = 0, OP_F32 = 1 };
 
-// Epilogues of the Gram-space products.  acc is the raw fp32 MFMA sum,
-// u its unscale factor (operands are stored multiplied by powers of two).
+// Epilogues of the Gram-space products.  acc is the raw fp32 MFMA sum and u
+// its unscale factor (operands are stored multiplied by powers of two).  An
+// epilogue that needs the previous iterate Y reads it as in32[i][j] when the
+// group keeps fp32 state for the A-chain (A and P·A), else as sIn·inh[i][j]
+// from the scaled operand copy.
 enum Epi : int32_t {
-  // G = u·acc → out32 (upper triangle), outh = sOut·G (mirrored).
+  // G = u·acc → outh = sOut·G (mirrored).
   // writeIdentity: also outhb = sOutB·I (zero steps: Q₀ = I).
   EPI_SYRK = 0,
-  // A² = u·acc; B = p1·in32 + p2·A² → outh = sOut·B (mirrored).
-  // If out32b: Q₁ = p0·I + B → out32b (upper), outhb = sOutB·Q₁ (mirrored).
+  // A² = u·acc; B = p1·A + p2·A² (A from inh) → outh = sOut·B (mirrored).
+  // If outhb: Q₁ = p0·I + B → outhb = sOutB·Q₁ (mirrored).
   EPI_SQ = 1,
-  // Y = p0·in32 + u·acc → out32 (upper), outh = sOut·Y (mirrored).
+  // Y' = p0·Y + u·acc (Y from inh) → outh = sOut·Y' (mirrored).
   EPI_AXPY = 2,
   // caller weights W ← round(W − lrsc·u·acc), full tiles, real extent only.
   EPI_UPDATE = 3,
@@ -50,16 +53,18 @@ struct GemmSeg {
   int32_t nReal;       // real C cols
   int32_t ldc;         // row stride of the workspace C matrices
   int32_t writeIdentity;
-  float u, sOut, sOutB;
+  int32_t inIsB;       // inh is the B operand of this product (same matrix)
+  float u, sOut, sOutB, sIn;
   float p0, p1, p2;
-  const float* in32;
+  const void* inh;     // previous iterate (operand copy), read at (i, j)
+  int64_t strideInh;
+  const float* in32;   // previous iterate in fp32 (upper triangle) or null
   int64_t strideIn32;
-  float* out32;
+  float* out32;        // result in fp32 (upper triangle) or null
   int64_t strideOut32;
-  void* outh;
+  void* outh;          // result copy, written mirrored
   int64_t strideOuth;
-  float* out32b;
-  void* outhb;
+  void* outhb;         // second result copy (EPI_SQ first step, EPI_SYRK zero steps)
   int32_t userBase;    // first caller-table entry of this segment
   int32_t pad_;
 };

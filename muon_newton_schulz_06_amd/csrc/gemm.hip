@@ -50,15 +50,50 @@ template <typename T> struct OpInfo;
 template <> struct OpInfo<_Float16> { static constexpr int BK = 64; };
 template <> struct OpInfo<float> { static constexpr int BK = 32; };
 
-// Workgroups are dispatched round-robin over the 8 XCDs (each with its own
-// L2).  Give every XCD a contiguous range of logical tiles, so that tiles
-// sharing operand row panels run under the same L2.
-__device__ __forceinline__ int xcd_remap(int b, int G) {
-  constexpr int X = 8;
+// Workgroups are dispatched round-robin over the 8 XCDs, each with its own
+// L2.  Logical tiles are handed out in windows of 8 × 32: inside a window
+// XCD x runs a contiguous run of 32 logical tiles (which share operand row
+// panels in its L2), and all XCDs work inside the same window (which keeps
+// the working set of the shared last-level cache small).  The tail of the
+// grid that does not fill a window keeps the identity mapping.
+__device__ __forceinline__ int xcd_window_remap(int b, int G) {
+  constexpr int X = 8, C = 32, W = X * C;
+  const int full = G / W;
+  if (b >= full * W) return b;
   const int x = b % X, i = b / X;
-  const int q = G / X, r = G % X;
-  const int base = x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q;
-  return base + i;
+  return (i / C) * W + x * C + (i % C);
+}
+
+// Tile order inside one matrix: bands of kBand tile rows, column by column
+// inside a band, so consecutive tiles reuse the band's row panels of A and a
+// short run of B panels.  sym: upper triangle only (ti ≤ tj).
+constexpr int kBand = 4;
+
+__device__ __forceinline__ void decode_tile(int t, int tilesM, int tilesN, bool sym, int& ti,
+                                            int& tj) {
+  int r0 = 0;
+  for (;;) {
+    const int h = min(kBand, tilesM - r0);
+    const int cnt = sym ? h * (h + 1) / 2 + h * (tilesN - r0 - h) : h * tilesN;
+    if (t < cnt || r0 + h >= tilesM) break;
+    t -= cnt;
+    r0 += h;
+  }
+  const int h = min(kBand, tilesM - r0);
+  if (sym) {
+    int col = r0;
+    for (;;) {
+      const int cnt = min(col - r0 + 1, h);
+      if (t < cnt) break;
+      t -= cnt;
+      ++col;
+    }
+    ti = r0 + t;
+    tj = col;
+  } else {
+    tj = t / h;
+    ti = r0 + (t - tj * h);
+  }
 }
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
@@ -86,26 +121,26 @@ __device__ __forceinline__ void store_mirror(T* base, int ldc, int i, int j, T v
 // struct is only ever read, never addressed, and no private copy is made).
 template <typename T>
 struct EpiArgs {
-  float* out32;
+  const T* inh;
   const float* in32;
+  float* out32;
   T* outh;
-  float* out32b;
   T* outhb;
   void* user;
   int64_t userLd;
   int ldc, mReal, nReal, writeIdentity, userDtype;
-  float u, sOut, sOutB, p0, p1, p2, lrsc;
+  float u, sOut, sOutB, sIn, p0, p1, p2, lrsc;
 };
 
-// Epilogue for one accumulator element (i, j).  EPI is a compile-time
-// constant so each instantiation carries only its own code.
+// Epilogue for one accumulator element (i, j) (register-staged kernel).  EPI
+// is a compile-time constant so each instantiation carries only its own code.
 template <typename T, int EPI>
 __device__ __forceinline__ void epilogue(const EpiArgs<T>& E, int i, int j, float acc) {
   const int ldc = E.ldc;
   if constexpr (EPI == EPI_SYRK) {
     if (i > j) return;
     const float g = E.u * acc;
-    E.out32[(int64_t)i * ldc + j] = g;
+    if (E.out32) E.out32[(int64_t)i * ldc + j] = g;
     store_mirror<T>(E.outh, ldc, i, j, to_op<T>(E.sOut * g));
     if (E.writeIdentity) {
       const float q = (i == j && i < E.mReal) ? E.sOutB : 0.f;
@@ -114,18 +149,20 @@ __device__ __forceinline__ void epilogue(const EpiArgs<T>& E, int i, int j, floa
   } else if constexpr (EPI == EPI_SQ) {
     if (i > j) return;
     const int64_t e = (int64_t)i * ldc + j;
-    const float bb = E.p1 * E.in32[e] + E.p2 * (E.u * acc);
-    store_mirror<T>(E.outh, ldc, i, j, to_op<T>(E.sOut * bb));
-    if (E.out32b) {
-      const float q = bb + ((i == j && i < E.mReal) ? E.p0 : 0.f);
-      E.out32b[e] = q;
-      store_mirror<T>(E.outhb, ldc, i, j, to_op<T>(E.sOutB * q));
+    const float a = E.in32 ? E.in32[e] : E.sIn * (float)E.inh[e];
+    const float bb = E.p1 * a + E.p2 * (E.u * acc);
+    const T bh = to_op<T>(E.sOut * bb);
+    store_mirror<T>(E.outh, ldc, i, j, bh);
+    if (E.outhb) {  // Q₁ = a·I + B₀ from the stored B₀ (as the 256-tile kernel does)
+      const float q = (E.sOutB / E.sOut) * (float)bh + ((i == j && i < E.mReal) ? E.sOutB * E.p0 : 0.f);
+      store_mirror<T>(E.outhb, ldc, i, j, to_op<T>(q));
     }
   } else if constexpr (EPI == EPI_AXPY) {
     if (i > j) return;
     const int64_t e = (int64_t)i * ldc + j;
-    const float y = E.p0 * E.in32[e] + E.u * acc;
-    E.out32[e] = y;
+    const float prev = E.in32 ? E.in32[e] : E.sIn * (float)E.inh[e];
+    const float y = E.p0 * prev + E.u * acc;
+    if (E.out32) E.out32[e] = y;
     store_mirror<T>(E.outh, ldc, i, j, to_op<T>(E.sOut * y));
   } else if constexpr (EPI == EPI_UPDATE) {
     if (i >= E.mReal || j >= E.nReal) return;
@@ -161,6 +198,58 @@ __device__ __forceinline__ void epilogue_all(const EpiArgs<T>& E, int gi0, int g
   }
 }
 
+// Locates this workgroup's segment, matrix and tile.
+struct TilePos {
+  int seg, mat, ti, tj;
+};
+
+__device__ __forceinline__ TilePos locate(const GemmLaunch& L) {
+  const int lid = xcd_window_remap(blockIdx.x, gridDim.x);
+  TilePos p;
+  p.seg = 0;
+  while (p.seg + 1 < L.nseg && lid >= L.segStart[p.seg + 1]) ++p.seg;
+  const GemmSeg& S = L.seg[p.seg];
+  int t = lid - L.segStart[p.seg];
+  p.mat = t / S.tilesPerMat;
+  t -= p.mat * S.tilesPerMat;
+  decode_tile(t, S.tilesM, S.tilesN, S.sym != 0, p.ti, p.tj);
+  return p;
+}
+
+template <typename T, int EPI>
+__device__ __forceinline__ EpiArgs<T> make_epi(const GemmLaunch& L, const GemmSeg& S, int mat) {
+  EpiArgs<T> E;
+  E.ldc = S.ldc;
+  E.mReal = S.mReal;
+  E.nReal = S.nReal;
+  E.writeIdentity = S.writeIdentity;
+  E.u = S.u;
+  E.sOut = S.sOut;
+  E.sOutB = S.sOutB;
+  E.sIn = S.sIn;
+  E.p0 = S.p0;
+  E.p1 = S.p1;
+  E.p2 = S.p2;
+  E.inh = S.inh ? (const T*)S.inh + mat * S.strideInh : nullptr;
+  E.in32 = S.in32 ? S.in32 + mat * S.strideIn32 : nullptr;
+  E.out32 = S.out32 ? S.out32 + mat * S.strideOut32 : nullptr;
+  E.outh = S.outh ? (T*)S.outh + mat * S.strideOuth : nullptr;
+  E.outhb = S.outhb ? (T*)S.outhb + mat * S.strideOuth : nullptr;
+  E.user = nullptr;
+  E.userLd = 0;
+  E.lrsc = 0.f;
+  E.userDtype = L.userDtype;
+  if constexpr (EPI == EPI_UPDATE || EPI == EPI_OUT) {
+    const int k = S.userBase + mat;
+    E.user = L.user[k];
+    E.userLd = L.userLd[k];
+    E.lrsc = L.lrsc[k];
+  }
+  return E;
+}
+
+// ---------------------------------------------------------------------------
+// Register-staged kernel: 128×128 tiles (fp16 and fp32 operands).
 template <typename T, int BM, int BN, int WM, int WN, int EPI>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const GemmLaunch L) {
   constexpr int NT = 64 * WM * WN;
@@ -176,27 +265,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const GemmLaunch L) 
 
   __shared__ u32x4 smem[2][(BM + BN) * CH];
 
-  const int lid = xcd_remap(blockIdx.x, gridDim.x);
-  int s = 0;
-  while (s + 1 < L.nseg && lid >= L.segStart[s + 1]) ++s;
-  const GemmSeg& S = L.seg[s];
-  int t = lid - L.segStart[s];
-  const int mat = t / S.tilesPerMat;
-  t -= mat * S.tilesPerMat;
-  int ti, tj;
-  if (S.sym) {
-    int rowlen = S.tilesM;
-    ti = 0;
-    while (t >= rowlen) {
-      t -= rowlen;
-      ++ti;
-      --rowlen;
-    }
-    tj = ti + t;
-  } else {
-    ti = t / S.tilesN;
-    tj = t - ti * S.tilesN;
-  }
+  const TilePos tp = locate(L);
+  const GemmSeg& S = L.seg[tp.seg];
+  const int mat = tp.mat, ti = tp.ti, tj = tp.tj;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -283,20 +354,22 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const GemmLaunch L) 
           const int row = wm * WTM + fi * 32 + lr;
           u32x4 v0 = sa[row * CH + (c0 ^ (row & 7))];
           u32x4 v1 = sa[row * CH + ((c0 + 1) ^ (row & 7))];
-          av[fi][0] = __uint_as_float(v0[0]); av[fi][1] = __uint_as_float(v0[1]);
-          av[fi][2] = __uint_as_float(v0[2]); av[fi][3] = __uint_as_float(v0[3]);
-          av[fi][4] = __uint_as_float(v1[0]); av[fi][5] = __uint_as_float(v1[1]);
-          av[fi][6] = __uint_as_float(v1[2]); av[fi][7] = __uint_as_float(v1[3]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            av[fi][e] = __uint_as_float(v0[e]);
+            av[fi][4 + e] = __uint_as_float(v1[e]);
+          }
         }
 #pragma unroll
         for (int fj = 0; fj < FN; ++fj) {
           const int row = wn * WTN + fj * 32 + lr;
           u32x4 v0 = sb[row * CH + (c0 ^ (row & 7))];
           u32x4 v1 = sb[row * CH + ((c0 + 1) ^ (row & 7))];
-          bv[fj][0] = __uint_as_float(v0[0]); bv[fj][1] = __uint_as_float(v0[1]);
-          bv[fj][2] = __uint_as_float(v0[2]); bv[fj][3] = __uint_as_float(v0[3]);
-          bv[fj][4] = __uint_as_float(v1[0]); bv[fj][5] = __uint_as_float(v1[1]);
-          bv[fj][6] = __uint_as_float(v1[2]); bv[fj][7] = __uint_as_float(v1[3]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            bv[fj][e] = __uint_as_float(v0[e]);
+            bv[fj][4 + e] = __uint_as_float(v1[e]);
+          }
         }
 #pragma unroll
         for (int e = 0; e < 8; ++e)
@@ -313,40 +386,457 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const GemmLaunch L) 
 
   // 32×32 accumulator layout: lane l, register r holds
   // row 8·(r/4) + 4·(l/32) + r%4, column l%32 of the block.
-  EpiArgs<T> E;
-  E.ldc = S.ldc;
-  E.mReal = S.mReal;
-  E.nReal = S.nReal;
-  E.writeIdentity = S.writeIdentity;
-  E.u = S.u;
-  E.sOut = S.sOut;
-  E.sOutB = S.sOutB;
-  E.p0 = S.p0;
-  E.p1 = S.p1;
-  E.p2 = S.p2;
-  E.out32 = S.out32 ? S.out32 + mat * S.strideOut32 : nullptr;
-  E.in32 = S.in32 ? S.in32 + mat * S.strideIn32 : nullptr;
-  E.outh = S.outh ? (T*)S.outh + mat * S.strideOuth : nullptr;
-  E.out32b = S.out32b ? S.out32b + mat * S.strideOut32 : nullptr;
-  E.outhb = S.outhb ? (T*)S.outhb + mat * S.strideOuth : nullptr;
-  E.user = nullptr;
-  E.userLd = 0;
-  E.lrsc = 0.f;
-  E.userDtype = L.userDtype;
-  if constexpr (EPI == EPI_UPDATE || EPI == EPI_OUT) {
-    const int k = S.userBase + mat;
-    E.user = L.user[k];
-    E.userLd = L.userLd[k];
-    E.lrsc = L.lrsc[k];
-  }
+  const EpiArgs<T> E = make_epi<T, EPI>(L, S, mat);
   const int gi0 = ti * BM + wm * WTM, gj0 = tj * BN + wn * WTN;
   epilogue_all<T, EPI, FM, FN>(E, gi0, gj0, lh, lr, acc);
+}
+
+// ---------------------------------------------------------------------------
+// 256×256 fp16 kernel with direct global→LDS loads.
+//
+// 8 waves (2 × 4, each a 128×64 block of 32×32×16 MFMAs), k-tile 32, and a
+// 4-stage LDS ring (4 × 32 KiB): the loads of k-tile kt+3 are in flight
+// while k-tile kt is multiplied, so about three k-tiles of latency are
+// covered without registers for staging.  Each 16-byte load lands straight
+// in LDS (global_load_lds_dwordx4: a wave writes 1 KiB contiguously); the
+// bank swizzle is applied on the global side by choosing which chunk each
+// lane fetches.  One barrier per k-tile.  Each ring slot is its own LDS
+// object so that waits on outstanding loads into one slot do not serialise
+// reads of another.
+constexpr int kRowB = 64;                 // bytes per 32-element fp16 k-row
+constexpr int kStageA = 256 * kRowB;      // 16 KiB
+constexpr int kStage = 2 * kStageA;       // A + B tiles, 32 KiB
+
+// Chunk swizzle for 64-byte rows: conflict-free ds_read_b128 whether the LDS
+// serves 8 lanes × 16 B (32 banks) or 16 lanes × 16 B (64 banks) per cycle.
+__device__ __forceinline__ int swz4(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+
+typedef __attribute__((address_space(3))) char* lds_ptr_t;
+
+// One 16-byte global→LDS load per lane: lane l writes lds_base + 16·l.
+// Issued through inline asm so that the compiler, which cannot tell the ring
+// slots apart, does not add a wait for all outstanding loads before every
+// LDS read; the kernel counts these loads itself (s_waitcnt vmcnt).
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gptr), "s"(lds_base)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const char* p) {
+  return (uint32_t)(uintptr_t)(lds_ptr_t)p;
+}
+
+// ----- staged epilogues of the 256-tile kernel ------------------------------
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+
+// Symmetric results: every value is written through LDS twice, once as the
+// tile itself (rows of C) and once transposed (the mirrored tile), each time
+// with 16-byte global stores covering 512 contiguous bytes per half-wave.
+// LDS holds one 256×256 fp16 tile (128 KiB): row r = 512 bytes, 16-byte chunk
+// c at c ^ (r & 31).
+__device__ __forceinline__ int stage_off(int row, int col) {
+  return row * 512 + ((((col >> 3) ^ (row & 31))) << 4) + (col & 7) * 2;
+}
+
+// acc → LDS as rows of C (one 2-byte write per element).
+template <int FM, int FN>
+__device__ __forceinline__ void stage_rows(char* lds, int wm, int wn, int lr, int lh,
+                                           const floatx16 (&acc)[FM][FN]) {
+  static_for<0, FM>([&](auto fi) {
+    static_for<0, FN>([&](auto fj) {
+      static_for<0, 16>([&](auto rc) {
+        constexpr int r = decltype(rc)::value;
+        const int il = wm * 128 + fi * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+        const int jl = wn * 64 + fj * 32 + lr;
+        *(_Float16*)(lds + stage_off(il, jl)) = (_Float16)acc[fi][fj][r];
+      });
+    });
+  });
+}
+
+// acc → LDS as rows of Cᵀ: a lane's four consecutive rows of one column are
+// one 8-byte write.
+template <int FM, int FN>
+__device__ __forceinline__ void stage_cols(char* lds, int wm, int wn, int lr, int lh,
+                                           const floatx16 (&acc)[FM][FN]) {
+  static_for<0, FM>([&](auto fi) {
+    static_for<0, FN>([&](auto fj) {
+      static_for<0, 4>([&](auto q) {
+        const int jl = wn * 64 + fj * 32 + lr;
+        const int il = wm * 128 + fi * 32 + 8 * q + 4 * lh;
+        half4 v;
+        v[0] = (_Float16)acc[fi][fj][4 * q + 0];
+        v[1] = (_Float16)acc[fi][fj][4 * q + 1];
+        v[2] = (_Float16)acc[fi][fj][4 * q + 2];
+        v[3] = (_Float16)acc[fi][fj][4 * q + 3];
+        *(half4*)(lds + stage_off(jl, il)) = v;
+      });
+    });
+  });
+}
+
+// Second copy written from the same staged values (EPI_SQ, first step):
+// dst2 = rs·v + dv on the diagonal of the matrix (global index < mReal).
+struct SecondCopy {
+  _Float16* dst2;
+  float rs, dv;
+  int mReal;
+};
+
+__device__ __forceinline__ u32x4 second_value(u32x4 v, const SecondCopy& sc, int grow, int gcol0) {
+  half8 h = __builtin_bit_cast(half8, v);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    float f = sc.rs * (float)h[e];
+    if (gcol0 + e == grow && grow < sc.mReal) f += sc.dv;
+    h[e] = (_Float16)f;
+  }
+  return __builtin_bit_cast(u32x4, h);
+}
+
+// Staged tile → global tile (tr, tc) of dst (and of sc.dst2 when kTwo).  On a
+// diagonal tile only the upper elements (cl ≥ rl, kUpper) or the strictly
+// lower ones (cl < rl) belong to this copy.
+template <bool kUpper, bool kTwo>
+__device__ __forceinline__ void store_staged(_Float16* dst, int ldc, const char* lds, int tr,
+                                             int tc, bool diag, int tid, const SecondCopy& sc) {
+#pragma unroll 4
+  for (int it = 0; it < 16; ++it) {
+    const int idx = it * 512 + tid;
+    const int rl = idx >> 5, c = idx & 31;
+    const u32x4 v = *(const u32x4*)(lds + rl * 512 + ((c ^ (rl & 31)) << 4));
+    const int64_t off = ((int64_t)tr * 256 + rl) * ldc + (int64_t)tc * 256 + c * 8;
+    _Float16* p = dst + off;
+    u32x4 v2 = v;
+    if constexpr (kTwo) v2 = second_value(v, sc, tr * 256 + rl, tc * 256 + c * 8);
+    if (!diag) {
+      *(u32x4*)p = v;
+      if constexpr (kTwo) *(u32x4*)(sc.dst2 + off) = v2;
+      continue;
+    }
+    const int c0 = c * 8;
+    const bool all = kUpper ? (c0 >= rl) : (c0 + 7 < rl);
+    const bool none = kUpper ? (c0 + 7 < rl) : (c0 >= rl);
+    if (all) {
+      *(u32x4*)p = v;
+      if constexpr (kTwo) *(u32x4*)(sc.dst2 + off) = v2;
+    } else if (!none) {
+      const half8 hv = __builtin_bit_cast(half8, v);
+      const half8 hv2 = __builtin_bit_cast(half8, v2);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (kUpper ? (c0 + e >= rl) : (c0 + e < rl)) {
+          p[e] = hv[e];
+          if constexpr (kTwo) sc.dst2[off + e] = hv2[e];
+        }
+    }
+  }
+}
+
+// Writes the symmetric result held in acc (already scaled for storage) to
+// dst: the tile (ti, tj) from its rows, the tile (tj, ti) from its columns.
+template <int FM, int FN, bool kTwo>
+__device__ __forceinline__ void write_symmetric(_Float16* dst, int ldc, char* lds, int ti, int tj,
+                                                int wm, int wn, int lr, int lh, int tid,
+                                                const floatx16 (&acc)[FM][FN],
+                                                const SecondCopy& sc) {
+  const bool diag = ti == tj;
+  stage_rows<FM, FN>(lds, wm, wn, lr, lh, acc);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  store_staged<true, kTwo>(dst, ldc, lds, ti, tj, diag, tid, sc);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  stage_cols<FM, FN>(lds, wm, wn, lr, lh, acc);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  store_staged<false, kTwo>(dst, ldc, lds, tj, ti, diag, tid, sc);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Caller-facing outputs (weight update or plain output): the tile is staged
+// in LDS in two 128-row halves as fp32 (row pitch 1040 bytes: 16 bytes of
+// padding keep the two lane halves of a store on different banks and every
+// address an immediate offset), then every thread handles runs of 4
+// consecutive columns with 8- or 16-byte global accesses.
+constexpr int kDensePitch = 1040;
+template <int EPI, int FM, int FN>
+__device__ __forceinline__ void dense_staged(const EpiArgs<_Float16>& E, char* lds, int ti, int tj,
+                                             int wm, int wn, int lr, int lh, int tid,
+                                             const floatx16 (&acc)[FM][FN]) {
+  const bool vec_ok = (E.userLd % 4 == 0) && (((uintptr_t)E.user & 15) == 0);
+  for (int half = 0; half < 2; ++half) {
+    if (half) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (wm == half) {
+      static_for<0, FM>([&](auto fi) {
+        static_for<0, FN>([&](auto fj) {
+          static_for<0, 16>([&](auto rc) {
+            constexpr int r = decltype(rc)::value;
+            const int row = fi * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+            const int jl = wn * 64 + fj * 32 + lr;
+            *(float*)(lds + row * kDensePitch + jl * 4) = E.u * acc[fi][fj][r];
+          });
+        });
+      });
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll 1
+    for (int it = 0; it < 16; ++it) {
+      const int idx = it * 512 + tid;
+      const int row = idx >> 6, c = idx & 63;
+      const int64_t i = (int64_t)ti * 256 + half * 128 + row;
+      const int64_t j = (int64_t)tj * 256 + c * 4;
+      if (i >= E.mReal || j >= E.nReal) continue;
+      const u32x4 raw = *(const u32x4*)(lds + row * kDensePitch + c * 16);
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = __uint_as_float(raw[e]);
+      const int64_t base = i * E.userLd + j;
+      const bool full = vec_ok && (j + 3 < E.nReal);
+      if constexpr (EPI == EPI_UPDATE) {
+        if (E.userDtype == 1) {
+          uint16_t* w = (uint16_t*)E.user + base;
+          if (full) {
+            const uint2 wv = *(const uint2*)w;
+            const uint32_t in[2] = {wv.x, wv.y};
+            uint32_t o[2];
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+              const float a0 = bf16_to_f32((uint16_t)(in[p] & 0xffffu)) - E.lrsc * v[2 * p];
+              const float a1 = bf16_to_f32((uint16_t)(in[p] >> 16)) - E.lrsc * v[2 * p + 1];
+              o[p] = (uint32_t)f32_to_bf16_rne(a0) | ((uint32_t)f32_to_bf16_rne(a1) << 16);
+            }
+            *(uint2*)w = make_uint2(o[0], o[1]);
+          } else {
+            for (int e = 0; e < 4 && j + e < E.nReal; ++e)
+              w[e] = f32_to_bf16_rne(bf16_to_f32(w[e]) - E.lrsc * v[e]);
+          }
+        } else {
+          float* w = (float*)E.user + base;
+          if (full) {
+            float4 wv = *(const float4*)w;
+            wv.x -= E.lrsc * v[0];
+            wv.y -= E.lrsc * v[1];
+            wv.z -= E.lrsc * v[2];
+            wv.w -= E.lrsc * v[3];
+            *(float4*)w = wv;
+          } else {
+            for (int e = 0; e < 4 && j + e < E.nReal; ++e) w[e] = w[e] - E.lrsc * v[e];
+          }
+        }
+      } else {  // EPI_OUT
+        if (E.userDtype == 1) {
+          uint16_t* o = (uint16_t*)E.user + base;
+          if (full) {
+            const uint32_t p0 = (uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
+            const uint32_t p1 = (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
+            *(uint2*)o = make_uint2(p0, p1);
+          } else {
+            for (int e = 0; e < 4 && j + e < E.nReal; ++e) o[e] = f32_to_bf16_rne(v[e]);
+          }
+        } else {
+          float* o = (float*)E.user + base;
+          if (full) *(float4*)o = make_float4(v[0], v[1], v[2], v[3]);
+          else
+            for (int e = 0; e < 4 && j + e < E.nReal; ++e) o[e] = v[e];
+        }
+      }
+    }
+  }
+}
+
+template <int EPI>
+__global__ __launch_bounds__(512) void gemm256_kernel(const GemmLaunch L) {
+  using T = _Float16;
+  constexpr int BM = 256, BN = 256, BK = 32, WN = 4;
+  constexpr int WTM = 128, WTN = 64, FM = 4, FN = 2;
+  constexpr bool kSym = EPI == EPI_SYRK || EPI == EPI_SQ || EPI == EPI_AXPY;
+  constexpr bool kCapture = EPI == EPI_SQ || EPI == EPI_AXPY;
+  // 4-slot ring for the main loop; reused by the staged epilogue.
+  __shared__ __attribute__((aligned(1024))) char lds[128 * kDensePitch];
+  static_assert(128 * kDensePitch >= 4 * kStage, "ring must fit");
+  char* const st0 = lds;
+  char* const st1 = lds + kStage;
+  char* const st2 = lds + 2 * kStage;
+  char* const st3 = lds + 3 * kStage;
+
+  const TilePos tp = locate(L);
+  const GemmSeg& S = L.seg[tp.seg];
+  const int mat = tp.mat, ti = tp.ti, tj = tp.tj;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave - wm * WN;
+  const int lr = lane & 31, lh = lane >> 5;
+
+  const T* Ag = (const T*)S.A + mat * S.strideA + (int64_t)ti * BM * S.lda;
+  const T* Bg = (const T*)S.B + mat * S.strideB + (int64_t)tj * BN * S.ldb;
+
+  // wave w fills rows [32w, 32w + 32) of the A and of the B tile, 16 rows
+  // (1 KiB) per instruction; lane l writes row 16p + l/4, physical chunk l%4
+  // and therefore fetches logical chunk (l%4) ^ swz4(row).
+  const int lrow = lane >> 2, lpc = lane & 3;
+  const T* gA[2];
+  const T* gB[2];
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int r = wave * 32 + p * 16 + lrow;
+    const int lc = lpc ^ swz4(r);
+    gA[p] = Ag + (int64_t)r * S.lda + lc * 8;
+    gB[p] = Bg + (int64_t)r * S.ldb + lc * 8;
+  }
+  const int dstA = wave * 32 * kRowB;
+  auto issue = [&gA, &gB, dstA](char* st, int kt) {
+    const int k0 = kt * BK;
+    const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(st) + dstA);
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      dma16(gA[p] + k0, base + p * 16 * kRowB);
+      dma16(gB[p] + k0, base + kStageA + p * 16 * kRowB);
+    }
+  };
+
+  floatx16 acc[FM][FN];
+#pragma unroll
+  for (int fi = 0; fi < FM; ++fi)
+#pragma unroll
+    for (int fj = 0; fj < FN; ++fj)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[fi][fj][e] = 0.f;
+
+  // Fragment addresses: rows base + lr with base a multiple of 32, so the
+  // swizzle depends on lr only.
+  const int sw = swz4(lr);
+  auto compute = [&acc, wm, wn, lr, lh, sw](const char* st) {
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      const int pc = ((2 * kk + lh) ^ sw) * 16;
+      half8 af[FM], bf[FN];
+#pragma unroll
+      for (int fi = 0; fi < FM; ++fi)
+        af[fi] = *(const half8*)(st + (wm * WTM + fi * 32 + lr) * kRowB + pc);
+#pragma unroll
+      for (int fj = 0; fj < FN; ++fj)
+        bf[fj] = *(const half8*)(st + kStageA + (wn * WTN + fj * 32 + lr) * kRowB + pc);
+#pragma unroll
+      for (int fi = 0; fi < FM; ++fi)
+#pragma unroll
+        for (int fj = 0; fj < FN; ++fj)
+          acc[fi][fj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[fi], bf[fj], acc[fi][fj], 0, 0, 0);
+    }
+  };
+
+  // The epilogues of A², B·Q, B·A and B·(P·A) need the previous iterate Y at
+  // the output positions.  Y is the B operand (a symmetric matrix), so when
+  // the ring holds k-tile ti·8 + wm·4 + fi, its B tile contains
+  // Y[tj·256 + jl][k] = Y[i][j] for this wave's rows i of block fi: each lane
+  // copies its four consecutive i of each column (one 8-byte LDS read).
+  half4 ycap[kCapture ? FM : 1][FN][4];
+  const int capBase = ti * 8 + wm * 4;
+  auto capture_fi = [&ycap, wn, lr, lh, sw](const char* st, auto fic) {
+    constexpr int fi = decltype(fic)::value;
+    if constexpr (kCapture) {
+#pragma unroll
+      for (int fj = 0; fj < FN; ++fj)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          ycap[fi][fj][q] = *(const half4*)(st + kStageA + (wn * WTN + fj * 32 + lr) * kRowB +
+                                            ((q ^ sw) << 4) + lh * 8);
+    }
+  };
+  auto capture = [&](const char* st, int k) {
+    if constexpr (kCapture) {
+      switch (k - capBase) {
+        case 0: capture_fi(st, std::integral_constant<int, 0>{}); break;
+        case 1: capture_fi(st, std::integral_constant<int, 1>{}); break;
+        case 2: capture_fi(st, std::integral_constant<int, 2>{}); break;
+        case 3: capture_fi(st, std::integral_constant<int, 3>{}); break;
+        default: break;
+      }
+    }
+  };
+
+  const int KT = S.K / BK;
+  // Each k-tile is 4 load instructions per wave; wait until the oldest
+  // outstanding k-tile has landed, leaving the younger ones in flight.
+  // The barrier is a bare s_barrier: a __syncthreads() would also wait for
+  // every outstanding load (the loads of the younger k-tiles included).  The
+  // "memory" clobber keeps the compiler from moving LDS accesses across it;
+  // every wave's own ds_reads of the slot about to be refilled completed
+  // before its MFMAs, hence before it reached the barrier.
+  auto step = [&](const char* cur, char* nxt, int k) {
+    const int ahead = min(2, KT - 1 - k);
+    if (ahead >= 2) asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+    else if (ahead == 1) asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    if (k + 3 < KT) issue(nxt, k + 3);
+    capture(cur, k);
+    compute(cur);
+  };
+
+  issue(st0, 0);
+  if (KT > 1) issue(st1, 1);
+  if (KT > 2) issue(st2, 2);
+  for (int kt = 0; kt < KT; kt += 4) {
+    step(st0, st3, kt);
+    if (kt + 1 < KT) step(st1, st0, kt + 1);
+    if (kt + 2 < KT) step(st2, st1, kt + 2);
+    if (kt + 3 < KT) step(st3, st2, kt + 3);
+  }
+
+  // Every wave is done with the ring before it is reused for staging.
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  const EpiArgs<T> E = make_epi<T, EPI>(L, S, mat);
+  if constexpr (kSym) {
+    // acc ← storage value of the result: sOut·y(i, j).
+    static_for<0, FM>([&](auto fi) {
+      static_for<0, FN>([&](auto fj) {
+        static_for<0, 16>([&](auto rc) {
+          constexpr int r = decltype(rc)::value;
+          const float a = E.u * acc[fi][fj][r];
+          float y;
+          if constexpr (EPI == EPI_SYRK) {
+            y = a;
+          } else {
+            const float prev = E.sIn * (float)ycap[fi][fj][r >> 2][r & 3];
+            y = (EPI == EPI_SQ) ? E.p1 * prev + E.p2 * a : E.p0 * prev + a;
+          }
+          acc[fi][fj][r] = E.sOut * y;
+        });
+      });
+    });
+    SecondCopy sc{E.outhb, E.sOutB / E.sOut, E.sOutB * E.p0, E.mReal};
+    if (EPI == EPI_SQ && E.outhb) {
+      // first step: Q₁ = a·I + B₀ written from the same staged B₀ values
+      write_symmetric<FM, FN, true>(E.outh, E.ldc, lds, ti, tj, wm, wn, lr, lh, tid, acc, sc);
+    } else {
+      write_symmetric<FM, FN, false>(E.outh, E.ldc, lds, ti, tj, wm, wn, lr, lh, tid, acc, sc);
+    }
+    if constexpr (EPI == EPI_SYRK) {
+      if (E.writeIdentity) {  // zero steps: Q₀ = I (rare; element by element)
+        const int gi0 = ti * BM + wm * WTM, gj0 = tj * BN + wn * WTN;
+        static_for<0, FM>([&](auto fi) {
+          static_for<0, FN>([&](auto fj) {
+            static_for<0, 16>([&](auto rc) {
+              constexpr int r = decltype(rc)::value;
+              const int i = gi0 + fi * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+              const int j = gj0 + fj * 32 + lr;
+              if (i <= j)
+                store_mirror<T>(E.outhb, E.ldc, i, j, (T)((i == j && i < E.mReal) ? E.sOutB : 0.f));
+            });
+          });
+        });
+      }
+    }
+  } else {
+    dense_staged<EPI, FM, FN>(E, lds, ti, tj, wm, wn, lr, lh, tid, acc);
+  }
 }
 
 template <int EPI>
 hipError_t launch_epi(int op, int tile, const GemmLaunch& L, int blocks, hipStream_t st) {
   if (op == OP_F16 && tile == 256) {
-    hipLaunchKernelGGL((gemm_kernel<_Float16, 256, 256, 2, 4, EPI>), dim3(blocks), dim3(512), 0, st, L);
+    hipLaunchKernelGGL((gemm256_kernel<EPI>), dim3(blocks), dim3(512), 0, st, L);
   } else if (op == OP_F16 && tile == 128) {
     hipLaunchKernelGGL((gemm_kernel<_Float16, 128, 128, 2, 2, EPI>), dim3(blocks), dim3(256), 0, st, L);
   } else if (op == OP_F32 && tile == 128) {

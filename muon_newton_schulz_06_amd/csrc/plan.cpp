@@ -153,7 +153,11 @@ std::string build_plan(const int64_t* rows, const int64_t* cols, int count, int 
     gp.buckets.push_back(bi);
   }
   for (GroupPlan& gp : P.groups) {
-    gp.tile = choose_tile(op, gp.m, gp.count);
+    // fp16 operands lose the relative accuracy of the small eigenvalues of A
+    // unless the a·A terms of the A-chain are carried in fp32; only the
+    // 128-tile kernel carries that state.
+    gp.state32 = (op == OP_F16) && gp.m <= kState32MaxM;
+    gp.tile = gp.state32 ? 128 : choose_tile(op, gp.m, gp.count);
     gp.Mp = round_up(gp.m, gp.tile);
   }
   for (BucketPlan& bp : P.buckets) {
@@ -183,17 +187,18 @@ std::string build_plan(const int64_t* rows, const int64_t* cols, int count, int 
   P.offAlpha = off;
   off = align_up(off + size_t(count) * 4);
   for (GroupPlan& gp : P.groups) {
-    gp.stride32 = size_t(gp.Mp) * size_t(gp.Mp) * 4;
     gp.strideh = size_t(gp.Mp) * size_t(gp.Mp) * esz;
-    const size_t n32 = gp.stride32 * gp.count, nh = gp.strideh * gp.count;
-    gp.offA32 = off;  off = align_up(off + n32);
-    gp.offQ32 = off;  off = align_up(off + n32);
-    gp.offPA32 = off; off = align_up(off + n32);
+    const size_t nh = gp.strideh * gp.count;
     gp.offAh = off;   off = align_up(off + nh);
     gp.offBh = off;   off = align_up(off + nh);
     gp.offPAh = off;  off = align_up(off + nh);
     gp.offQh[0] = off; off = align_up(off + nh);
     gp.offQh[1] = off; off = align_up(off + nh);
+    if (gp.state32) {
+      gp.stride32 = size_t(gp.Mp) * size_t(gp.Mp) * 4;
+      gp.offA32 = off;  off = align_up(off + gp.stride32 * gp.count);
+      gp.offPA32 = off; off = align_up(off + gp.stride32 * gp.count);
+    }
   }
   for (BucketPlan& bp : P.buckets) {
     bp.strideX = size_t(bp.Mp) * size_t(bp.Np) * esz;
@@ -214,9 +219,10 @@ std::string Plan::json() const {
   for (size_t g = 0; g < groups.size(); ++g) {
     const GroupPlan& gp = groups[g];
     o << (g ? "," : "") << "{\"m\":" << gp.m << ",\"Mp\":" << gp.Mp << ",\"tile\":" << gp.tile
+      << ",\"state32\":" << (gp.state32 ? "true" : "false")
       << ",\"count\":" << gp.count << ",\"buckets\":[";
     for (size_t k = 0; k < gp.buckets.size(); ++k) o << (k ? "," : "") << gp.buckets[k];
-    o << "],\"offA32\":" << gp.offA32 << ",\"offQh\":[" << gp.offQh[0] << "," << gp.offQh[1]
+    o << "],\"offAh\":" << gp.offAh << ",\"offQh\":[" << gp.offQh[0] << "," << gp.offQh[1]
       << "]}";
   }
   o << "],\"buckets\":[";

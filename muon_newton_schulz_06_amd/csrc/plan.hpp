@@ -43,9 +43,13 @@ struct GroupPlan {
   int tile = 128;
   int count = 0;
   std::vector<int> buckets;
-  size_t offA32 = 0, offQ32 = 0, offPA32 = 0;          // fp32, upper triangle used
-  size_t offAh = 0, offBh = 0, offPAh = 0, offQh[2] = {0, 0};  // operand type, mirrored
-  size_t stride32 = 0, strideh = 0;                    // bytes per matrix
+  // Gram-space iterates, operand type, scaled, full (mirrored) matrices.
+  size_t offAh = 0, offBh = 0, offPAh = 0, offQh[2] = {0, 0};
+  size_t strideh = 0;  // bytes per matrix
+  // fp32 copies of A and P·A (upper triangle used) when state32.
+  bool state32 = false;
+  size_t offA32 = 0, offPA32 = 0;
+  size_t stride32 = 0;
 };
 
 // Static operand scales (powers of two) for the half-precision path, derived
@@ -74,6 +78,10 @@ struct Plan {
 
 // Environment override of the tile (MUON_TILE=128|256), 0 when unset.
 int tile_override();
+
+// Largest Gram size m that keeps fp32 state for the A-chain on the
+// half-precision path (smaller, worse-conditioned Gram matrices need it).
+constexpr int64_t kState32MaxM = 2048;
 
 // Build the plan.  `op` selects operand type (OP_F16 / OP_F32).  Returns an
 // empty string on success, else a message.

@@ -193,11 +193,16 @@ def test_plan_workspace_matches_layout():
     assert p["workspace_bytes"] % 256 == 0
     total = 0
     for g in p["groups"]:
-        total += 22 * g["Mp"] ** 2 * g["count"]  # 3 fp32 + 5 fp16 m×m buffers
+        total += 10 * g["Mp"] ** 2 * g["count"]  # 5 fp16 m×m operand copies
+        if g["state32"]:
+            total += 8 * g["Mp"] ** 2 * g["count"]  # fp32 A and P·A
     for b in p["buckets"]:
         total += 2 * 2 * b["Mp"] * b["Np"] * len(b["mats"])
     assert p["workspace_bytes"] >= total
     assert p["workspace_bytes"] - total < 256 * (3 + 8 * len(p["groups"]) + 2 * len(p["buckets"])) + 4 * 1000
+    # small Gram sizes keep fp32 A-chain state on the 128-tile kernel
+    assert all(g["state32"] == (g["m"] <= 2048) and (not g["state32"] or g["tile"] == 128)
+               for g in p["groups"])
 
 
 def test_plan_f32_uses_unit_scales():

@@ -123,6 +123,18 @@ def test_bf16_ragged_mixed_batch(mns):
     say("worst", worst)
 
 
+def test_bf16_square_without_fp32_state(mns):
+    """Gram size above the fp32-state limit (2048): the 256-tile, state-free
+    path on a square matrix, the worst-conditioned Gram case."""
+    say("bf16 2304x2304 square, state-free Gram path")
+    x = W.gaussian((2304, 2304), 77, dtype=torch.bfloat16)
+    o = mns.muon_ns_batched([x.cuda()], steps=5)[0]
+    torch.cuda.synchronize()
+    e = rel(o.float(), oracle_ns(x.float()))
+    say("rel err", e)
+    assert e <= TOL_BF16
+
+
 def test_row_vector_closed_form(mns):
     """m = 1: O = φ^5(1)·x/‖x‖ (one singular value, equal to 1)."""
     say("fp32 row/column vector closed form")
