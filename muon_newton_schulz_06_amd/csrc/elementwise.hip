@@ -113,39 +113,68 @@ template <typename T> __device__ __forceinline__ T cvt(float v);
 template <> __device__ __forceinline__ _Float16 cvt<_Float16>(float v) { return (_Float16)v; }
 template <> __device__ __forceinline__ float cvt<float>(float v) { return v; }
 
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+
+// One 64×64 tile: 16 threads per 64-element row (16-byte fp32 loads when the
+// source allows), the stored-layout copy written straight from registers
+// (8 bytes per thread for fp16), the transposed copy through an fp32 LDS
+// tile (pitch 65: conflict-free column reads) with 16-byte stores of 8
+// consecutive elements.  Out-of-range elements (padding) are written as 0.
 template <typename T>
 __device__ void cast_tile(const CastLaunch& L, const CastMat& C, int64_t t) {
   __shared__ float tile[kCastTile][kCastTile + 1];
   const int tr = (int)(t / C.tilesC), tc = (int)(t - (int64_t)tr * C.tilesC);
   const int tid = threadIdx.x;
-  const int ty = tid >> 4, tx = tid & 15;
+  const int tx = tid & 15, ty = tid >> 4;
   const float scale = L.alpha[C.alphaIdx] * L.sX;
   T* S = (T*)C.S;
   T* Tt = (T*)C.T;
+  const int64_t r0 = (int64_t)tr * kCastTile, c0 = (int64_t)tc * kCastTile;
+  const bool full = (r0 + kCastTile <= C.rows) && (c0 + kCastTile <= C.cols);
+  const bool vec = full && L.srcDtype == 0 && (C.ld % 4 == 0) && (((uintptr_t)C.src & 15) == 0);
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int rl = ty + 16 * q;
-    const int64_t r = (int64_t)tr * kCastTile + rl;
+    const int64_t r = r0 + rl;
+    const int cl = 4 * tx;
+    float v[4];
+    if (vec) {
+      const float4 x = *(const float4*)((const float*)C.src + r * C.ld + c0 + cl);
+      v[0] = x.x * scale; v[1] = x.y * scale; v[2] = x.z * scale; v[3] = x.w * scale;
+    } else {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int cl = 4 * tx + e;
-      const int64_t cc = (int64_t)tc * kCastTile + cl;
-      float v = 0.f;
-      if (r < C.rows && cc < C.cols) v = load_as_f32(C.src, r * C.ld + cc, L.srcDtype) * scale;
-      tile[rl][cl] = v;
-      S[r * C.cp + cc] = cvt<T>(v);
+      for (int e = 0; e < 4; ++e) {
+        const int64_t cc = c0 + cl + e;
+        v[e] = (r < C.rows && cc < C.cols) ? load_as_f32(C.src, r * C.ld + cc, L.srcDtype) * scale : 0.f;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) tile[rl][cl + e] = v[e];
+    T* dst = S + r * C.cp + c0 + cl;
+    if constexpr (sizeof(T) == 2) {
+      half4_t h;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) h[e] = (_Float16)v[e];
+      *(half4_t*)dst = h;
+    } else {
+      *(float4*)dst = make_float4(v[0], v[1], v[2], v[3]);
     }
   }
   __syncthreads();
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int cl = ty + 16 * q;  // row of the transposed tile
-    const int64_t cc = (int64_t)tc * kCastTile + cl;
+  for (int p = 0; p < 2; ++p) {
+    const int id = p * 256 + tid;
+    const int cl = id >> 3, rl0 = (id & 7) * 8;
+    T* dst = Tt + (c0 + cl) * C.rp + r0 + rl0;
+    if constexpr (sizeof(T) == 2) {
+      half8_t h;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int rl = 4 * tx + e;
-      const int64_t r = (int64_t)tr * kCastTile + rl;
-      Tt[cc * C.rp + r] = cvt<T>(tile[rl][cl]);
+      for (int e = 0; e < 8; ++e) h[e] = (_Float16)tile[rl0 + e][cl];
+      *(half8_t*)dst = h;
+    } else {
+      *(float4*)dst = make_float4(tile[rl0][cl], tile[rl0 + 1][cl], tile[rl0 + 2][cl], tile[rl0 + 3][cl]);
+      *(float4*)(dst + 4) = make_float4(tile[rl0 + 4][cl], tile[rl0 + 5][cl], tile[rl0 + 6][cl], tile[rl0 + 7][cl]);
     }
   }
 }
