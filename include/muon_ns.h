@@ -83,9 +83,12 @@ typedef struct muon_ns_desc {
  *   count ≥ 0 (0 is a no-op), 0 ≤ steps ≤ 64, coeffs = {a, b, c} finite,
  *   eps ≥ 0 finite.
  * Precision:
- *   MUON_DTYPE_F32:  fp32 MFMA products, fp32 state;
+ *   MUON_DTYPE_F32:  fp32 MFMA products on fp32 operand copies;
  *   MUON_DTYPE_BF16: half-precision MFMA products (fp16 operands scaled by
- *                    powers of two, fp32 accumulation), fp32 state.
+ *                    powers of two, fp32 accumulation).  The Gram-space
+ *                    iterates live as those scaled fp16 copies, plus fp32
+ *                    copies of A and P·A when m ≤ 2048 (small Gram matrices
+ *                    are the worst conditioned).
  * The matrices are grouped by shape: one launch per stage serves every
  * matrix of a group. */
 muon_status_t muon_ns_batched(const muon_ns_desc_t* desc, int32_t count, int32_t steps,
@@ -135,8 +138,10 @@ muon_status_t muon_describe_plan(const int64_t* rows, const int64_t* cols, int32
  * algorithmic work is recorded.  muon_profile_read waits for the recorded
  * events, returns the totals for one kind and clears that kind's records.
  * Kinds: 0 momentum / sum of squares, 1 norm finish, 2 cast + transpose,
- *        3 SYRK, 4 symmetric Gram-space products, 5 final product + update.
- * work is algorithmic flops for kinds 3–5 and algorithmic HBM bytes for 0–2. */
+ *        3 SYRK, 4 symmetric Gram-space products on 128×128 tiles,
+ *        5 final product + update, 6 Gram-space a·Y + B·Y products on
+ *        256×256 tiles, 7 Gram-space A² products on 256×256 tiles.
+ * work is algorithmic flops for kinds 3–7 and algorithmic HBM bytes for 0–2. */
 muon_status_t muon_profile_enable(int32_t on);
 muon_status_t muon_profile_read(int32_t kind, double* total_ms, int64_t* launches, double* work);
 

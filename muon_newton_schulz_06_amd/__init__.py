@@ -32,7 +32,8 @@ CUBIC = (1.5, -0.5, 0.0)
 MUON_DTYPE_F32 = 0
 MUON_DTYPE_BF16 = 1
 
-PROFILE_KINDS = {"momentum": 0, "norm": 1, "cast": 2, "syrk": 3, "gram": 4, "final": 5}
+PROFILE_KINDS = {"momentum": 0, "norm": 1, "cast": 2, "syrk": 3, "gram128": 4, "final": 5,
+                 "gram256_axpy": 6, "gram256_sq": 7}
 
 _STATUS = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "ALIAS", 4: "WORKSPACE",
            5: "HIP", 6: "NO_DEVICE"}

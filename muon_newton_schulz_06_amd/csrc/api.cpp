@@ -283,7 +283,9 @@ muon_status_t enqueue(const Plan& P, const std::vector<CallerMat>& cm, int srcDt
       }
       L.segStart[ns] = blocks;
       L.nseg = (int)ns;
-      muon_status_t s = Lr.run(kind, work, what, [&] { return launch_gemm(P.op, tile, L, blocks, st); });
+      int k = kind;
+      if (kind == 4 && tile == 256) k = (L.seg[0].epi == EPI_AXPY) ? 6 : 7;
+      muon_status_t s = Lr.run(k, work, what, [&] { return launch_gemm(P.op, tile, L, blocks, st); });
       if (s != MUON_OK) return s;
     }
     return MUON_OK;
