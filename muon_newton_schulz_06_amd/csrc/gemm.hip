@@ -514,7 +514,7 @@ __device__ __forceinline__ u32x4 second_value(u32x4 v, const SecondCopy& sc, int
 template <bool kUpper, bool kTwo>
 __device__ __forceinline__ void store_staged(_Float16* dst, int ldc, const char* lds, int tr,
                                              int tc, bool diag, int tid, const SecondCopy& sc) {
-#pragma unroll 4
+#pragma unroll
   for (int it = 0; it < 16; ++it) {
     const int idx = it * 512 + tid;
     const int rl = idx >> 5, c = idx & 31;
@@ -562,15 +562,98 @@ __device__ __forceinline__ void write_symmetric(_Float16* dst, int ldc, char* ld
   stage_cols<FM, FN>(lds, wm, wn, lr, lh, acc);
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   store_staged<false, kTwo>(dst, ldc, lds, tj, ti, diag, tid, sc);
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  // The kernel ends here (LDS is not used again), so no closing barrier.
 }
 
 // Caller-facing outputs (weight update or plain output): the tile is staged
 // in LDS in two 128-row halves as fp32 (row pitch 1040 bytes: 16 bytes of
 // padding keep the two lane halves of a store on different banks and every
 // address an immediate offset), then every thread handles runs of 4
-// consecutive columns with 8- or 16-byte global accesses.
+// consecutive columns with 8- or 16-byte global accesses.  Thread t covers
+// columns 4·(t % 64) + 0..3 of rows 8·it + t / 64 (it = 0..15) of each half.
 constexpr int kDensePitch = 1040;
+constexpr int kDenseIters = 16;
+
+// bf16 weights of the update, fetched into registers ahead of use: the first
+// half-tile while the last k-tiles are multiplied, the second half before the
+// first is staged.  Every thread issues exactly kDenseIters loads per half
+// (addresses clamped into the matrix, so the count is uniform and every
+// access is in bounds); values outside the matrix are never used.
+struct WeightPrefetch {
+  uint2 v[2][kDenseIters];
+};
+
+// Prefetching is used for bf16 weights with 8-byte aligned rows and tiles
+// that lie entirely inside the matrix (the fast path below has no bounds
+// checks).
+__device__ __forceinline__ bool weight_prefetch_ok(const EpiArgs<_Float16>& E, int ti, int tj) {
+  return E.userDtype == 1 && (E.userLd % 4 == 0) && (((uintptr_t)E.user & 15) == 0) &&
+         (int64_t)ti * 256 + 256 <= E.mReal && (int64_t)tj * 256 + 256 <= E.nReal;
+}
+
+template <int kHalf>
+__device__ __forceinline__ void weight_prefetch(const EpiArgs<_Float16>& E, int ti, int tj, int tid,
+                                                WeightPrefetch& W) {
+  const uint16_t* w = (const uint16_t*)E.user;
+  const int64_t j = min((int64_t)tj * 256 + (tid & 63) * 4, (int64_t)E.nReal - 4);
+#pragma unroll
+  for (int it = 0; it < kDenseIters; ++it) {
+    const int64_t i = min((int64_t)ti * 256 + kHalf * 128 + it * 8 + (tid >> 6), (int64_t)E.mReal - 1);
+    W.v[kHalf][it] = *(const uint2*)(w + i * E.userLd + j);
+  }
+}
+
+// acc of the waves of row half `half` → LDS as fp32 rows (u applied).
+template <int FM, int FN>
+__device__ __forceinline__ void stage_dense_half(char* lds, int half, float u, int wm, int wn,
+                                                 int lr, int lh, const floatx16 (&acc)[FM][FN]) {
+  if (half) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  if (wm == half) {
+    static_for<0, FM>([&](auto fi) {
+      static_for<0, FN>([&](auto fj) {
+        static_for<0, 16>([&](auto rc) {
+          constexpr int r = decltype(rc)::value;
+          const int row = fi * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+          const int jl = wn * 64 + fj * 32 + lr;
+          *(float*)(lds + row * kDensePitch + jl * 4) = u * acc[fi][fj][r];
+        });
+      });
+    });
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Weight update of a tile inside the matrix with prefetched bf16 weights.
+template <int FM, int FN>
+__device__ __forceinline__ void update_prefetched(const EpiArgs<_Float16>& E, char* lds, int ti,
+                                                  int tj, int wm, int wn, int lr, int lh, int tid,
+                                                  const floatx16 (&acc)[FM][FN],
+                                                  WeightPrefetch& W) {
+  weight_prefetch<1>(E, ti, tj, tid, W);
+  const int c = tid & 63;
+  uint16_t* const w0 = (uint16_t*)E.user + ((int64_t)ti * 256 + (tid >> 6)) * E.userLd +
+                       (int64_t)tj * 256 + c * 4;
+  static_for<0, 2>([&](auto hc) {
+    constexpr int half = decltype(hc)::value;
+    stage_dense_half<FM, FN>(lds, half, E.u, wm, wn, lr, lh, acc);
+#pragma unroll
+    for (int it = 0; it < kDenseIters; ++it) {
+      const int row = it * 8 + (tid >> 6);
+      const u32x4 raw = *(const u32x4*)(lds + row * kDensePitch + c * 16);
+      const uint2 wv = W.v[half][it];
+      const uint32_t in[2] = {wv.x, wv.y};
+      uint32_t o[2];
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const float a0 = bf16_to_f32((uint16_t)(in[p] & 0xffffu)) - E.lrsc * __uint_as_float(raw[2 * p]);
+        const float a1 = bf16_to_f32((uint16_t)(in[p] >> 16)) - E.lrsc * __uint_as_float(raw[2 * p + 1]);
+        o[p] = (uint32_t)f32_to_bf16_rne(a0) | ((uint32_t)f32_to_bf16_rne(a1) << 16);
+      }
+      *(uint2*)(w0 + (int64_t)(half * 128 + it * 8) * E.userLd) = make_uint2(o[0], o[1]);
+    }
+  });
+}
+
 template <int EPI, int FM, int FN>
 __device__ __forceinline__ void dense_staged(const EpiArgs<_Float16>& E, char* lds, int ti, int tj,
                                              int wm, int wn, int lr, int lh, int tid,
@@ -592,7 +675,7 @@ __device__ __forceinline__ void dense_staged(const EpiArgs<_Float16>& E, char* l
     }
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll 1
-    for (int it = 0; it < 16; ++it) {
+    for (int it = 0; it < kDenseIters; ++it) {
       const int idx = it * 512 + tid;
       const int row = idx >> 6, c = idx & 63;
       const int64_t i = (int64_t)ti * 256 + half * 128 + row;
@@ -769,8 +852,19 @@ __global__ __launch_bounds__(512) void gemm256_kernel(const GemmLaunch L) {
   };
 
   const int KT = S.K / BK;
+  // Weight update: the first half of the tile's bf16 weights is loaded at
+  // k-tile KT − 3, after the last k-tile's operand loads, and lands while the
+  // last three k-tiles are multiplied.
+  [[maybe_unused]] WeightPrefetch wpf;
+  [[maybe_unused]] EpiArgs<T> Ew;
+  bool pref = false;
+  if constexpr (EPI == EPI_UPDATE) {
+    Ew = make_epi<T, EPI>(L, S, mat);
+    pref = KT >= 3 && weight_prefetch_ok(Ew, ti, tj);
+  }
   // Each k-tile is 4 load instructions per wave; wait until the oldest
-  // outstanding k-tile has landed, leaving the younger ones in flight.
+  // outstanding k-tile has landed, leaving the younger ones in flight (and
+  // the 16 weight loads, when they were issued after it).
   // The barrier is a bare s_barrier: a __syncthreads() would also wait for
   // every outstanding load (the loads of the younger k-tiles included).  The
   // "memory" clobber keeps the compiler from moving LDS accesses across it;
@@ -778,10 +872,16 @@ __global__ __launch_bounds__(512) void gemm256_kernel(const GemmLaunch L) {
   // before its MFMAs, hence before it reached the barrier.
   auto step = [&](const char* cur, char* nxt, int k) {
     const int ahead = min(2, KT - 1 - k);
+    const bool wpend = pref && k >= KT - 2;  // weight loads younger than k-tile k
     if (ahead >= 2) asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+    else if (ahead == 1 && wpend) asm volatile("s_waitcnt vmcnt(20)\n\ts_barrier" ::: "memory");
     else if (ahead == 1) asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
+    else if (wpend) asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
     else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
     if (k + 3 < KT) issue(nxt, k + 3);
+    if constexpr (EPI == EPI_UPDATE) {
+      if (pref && k == KT - 3) weight_prefetch<0>(Ew, ti, tj, tid, wpf);
+    }
     capture(cur, k);
     compute(cur);
   };
@@ -841,6 +941,12 @@ __global__ __launch_bounds__(512) void gemm256_kernel(const GemmLaunch L) {
       }
     }
   } else {
+    if constexpr (EPI == EPI_UPDATE) {
+      if (pref) {
+        update_prefetched<FM, FN>(E, lds, ti, tj, wm, wn, lr, lh, tid, acc, wpf);
+        return;
+      }
+    }
     dense_staged<EPI, FM, FN>(E, lds, ti, tj, wm, wn, lr, lh, tid, acc);
   }
 }
