@@ -29,6 +29,8 @@ __device__ __forceinline__ double wave_sum_d(double v) {
   return v;
 }
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ float load_as_f32(const void* p, int64_t e, int dtype) {
   if (dtype == 1) return __uint_as_float((uint32_t)((const uint16_t*)p)[e] << 16);
   return ((const float*)p)[e];
@@ -46,9 +48,32 @@ __global__ __launch_bounds__(kEwThreads) void ew_kernel(const EwLaunch L) {
   if (L.mode == 0) {
     const float* g = (const float*)M.x;
     float* m = M.mom;
-    if (L.vec) {
+    constexpr int Q = kEwElems / (4 * kEwThreads);
+    if (L.vec && e0 + kEwElems <= M.numel) {
+      // Whole block inside the matrix: every load is issued before the
+      // first store (the compiler cannot prove that g and M do not overlap,
+      // so interleaved load/store pairs would serialise on memory latency).
+      f32x4 gv[Q], mv[Q];
 #pragma unroll
-      for (int q = 0; q < kEwElems / (4 * kEwThreads); ++q) {
+      for (int q = 0; q < Q; ++q) {
+        const int64_t e = e0 + (int64_t)(q * kEwThreads + tid) * 4;
+        gv[q] = __builtin_nontemporal_load((const f32x4*)(g + e));
+        mv[q] = *(const f32x4*)(m + e);
+      }
+#pragma unroll
+      for (int q = 0; q < Q; ++q) {
+        const int64_t e = e0 + (int64_t)(q * kEwThreads + tid) * 4;
+        f32x4 v;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          v[c] = fmaf(L.beta, mv[q][c], gv[q][c]);
+          ss += v[c] * v[c];
+        }
+        *(f32x4*)(m + e) = v;
+      }
+    } else if (L.vec) {
+#pragma unroll
+      for (int q = 0; q < Q; ++q) {
         const int64_t e = e0 + (int64_t)(q * kEwThreads + tid) * 4;
         if (e < M.numel) {
           const float4 gv = *(const float4*)(g + e);
@@ -133,32 +158,42 @@ __device__ void cast_tile(const CastLaunch& L, const CastMat& C, int64_t t) {
   const int64_t r0 = (int64_t)tr * kCastTile, c0 = (int64_t)tc * kCastTile;
   const bool full = (r0 + kCastTile <= C.rows) && (c0 + kCastTile <= C.cols);
   const bool vec = full && L.srcDtype == 0 && (C.ld % 4 == 0) && (((uintptr_t)C.src & 15) == 0);
+  // All four source rows are loaded before anything is stored (the
+  // compiler cannot prove that the source and the copies do not overlap).
+  const int cl = 4 * tx;
+  float v[4][4];
+  if (vec) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f32x4 x = *(const f32x4*)((const float*)C.src + (r0 + ty + 16 * q) * C.ld + c0 + cl);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[q][e] = x[e] * scale;
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t r = r0 + ty + 16 * q;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t cc = c0 + cl + e;
+        v[q][e] = (r < C.rows && cc < C.cols) ? load_as_f32(C.src, r * C.ld + cc, L.srcDtype) * scale : 0.f;
+      }
+    }
+  }
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int rl = ty + 16 * q;
     const int64_t r = r0 + rl;
-    const int cl = 4 * tx;
-    float v[4];
-    if (vec) {
-      const float4 x = *(const float4*)((const float*)C.src + r * C.ld + c0 + cl);
-      v[0] = x.x * scale; v[1] = x.y * scale; v[2] = x.z * scale; v[3] = x.w * scale;
-    } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int64_t cc = c0 + cl + e;
-        v[e] = (r < C.rows && cc < C.cols) ? load_as_f32(C.src, r * C.ld + cc, L.srcDtype) * scale : 0.f;
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) tile[rl][cl + e] = v[e];
+    for (int e = 0; e < 4; ++e) tile[rl][cl + e] = v[q][e];
     T* dst = S + r * C.cp + c0 + cl;
     if constexpr (sizeof(T) == 2) {
       half4_t h;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) h[e] = (_Float16)v[e];
+      for (int e = 0; e < 4; ++e) h[e] = (_Float16)v[q][e];
       *(half4_t*)dst = h;
     } else {
-      *(float4*)dst = make_float4(v[0], v[1], v[2], v[3]);
+      *(float4*)dst = make_float4(v[q][0], v[q][1], v[q][2], v[q][3]);
     }
   }
   __syncthreads();
