@@ -141,18 +141,29 @@ def lr_shape_scale(rows: int, cols: int) -> float:
     return math.sqrt(max(1.0, rows / cols))
 
 
-def muon_step(W, g, M, beta, lr, coeffs, steps, eps):
+def muon_step(W, g, M, beta, lr, coeffs, steps, eps, nesterov=False, weight_decay=0.0):
     """One Muon step for one matrix.
 
     W: stored weights (values of a bf16 tensor, any float dtype),
-    g: fp32 gradient, M: fp32 momentum, all rows × cols.
-    Returns (W_new_bf16_values_as_fp64, M_new_fp32, O_fp64).
+    g: gradient values (fp32, or bf16 values), M: fp32 momentum, all
+    rows × cols.  Returns (W_new_bf16_values_as_fp64, M_new_fp32, O_fp64).
+
+    The two options are not part of the pages' method (which is the plain
+    step: nesterov False, weight_decay 0); they are the usual Muon-optimiser
+    variants, written out here from their definitions:
+      nesterov:     the matrix orthogonalised is u = g + β·M' instead of the
+                    updated momentum M' (M' is still the returned state);
+      weight_decay: decoupled, W' = round((1 − lr·wd)·W − lr·sc·O).
     """
     M_new = momentum_update(M, g, beta)
-    O = muon_orthogonalize(M_new, coeffs, steps, eps)
+    U = M_new.astype(np.float64)
+    if nesterov:
+        U = np.asarray(g, dtype=np.float64) + float(beta) * U
+    O = muon_orthogonalize(U, coeffs, steps, eps)
     rows, cols = np.asarray(W).shape
     W64 = np.asarray(W, dtype=np.float64)
-    W_new = bf16_round(W64 - float(lr) * lr_shape_scale(rows, cols) * O)
+    decay = 1.0 - float(lr) * float(weight_decay)
+    W_new = bf16_round(decay * W64 - float(lr) * lr_shape_scale(rows, cols) * O)
     return W_new, M_new, O
 
 

@@ -296,6 +296,95 @@ def test_muon_step_rank_one_closed_form(rows, cols):
     assert np.array_equal(W_new, oracle.bf16_round(W - 0.02 * sc * O_want))
 
 
+# -- the optimiser variants (Nesterov input, decoupled weight decay) ----------
+
+def _two_rank_ones(rows, cols):
+    """e₁ = (1, 1, 0, …), e₂ = (1, −1, 0, …), f₁ = (1, 0, 1, 0, …),
+    f₂ = (0, 1, 0, 1, 0, …): h_i = e_i·f_iᵀ / 2 are rank-one with singular
+    value 1, orthogonal row and column spaces and disjoint supports, so
+    a·h₁ + b·h₂ has singular values |a|, |b|, NS acts on each independently,
+    and every entry is exactly a or ±b (no rounding mixes the two)."""
+    e1 = np.zeros(rows); e1[:2] = [1, 1]
+    e2 = np.zeros(rows); e2[:2] = [1, -1]
+    f1 = np.zeros(cols); f1[[0, 2]] = 1
+    f2 = np.zeros(cols); f2[[1, 3]] = 1
+    return np.outer(e1, f1) / 2, np.outer(e2, f2) / 2
+
+
+@pytest.mark.parametrize("nesterov", [False, True])
+def test_variants_closed_form_on_two_orthogonal_rank_ones(nesterov):
+    """Two steps from M = 0 with g₁ = 4·h₁, then g₂ = 6·h₂ (exact in fp32):
+    M'₂ = b₁·h₁ + 6·h₂ with b₁ = fp32(4β) (the stored state is fp32), so the
+    plain input has singular values (b₁, 6) and the Nesterov input
+    g₂ + β·M'₂ has (β·b₁, 6(1 + β)).  After Frobenius normalisation each
+    singular value maps through φ^5, so O is known in closed form; a
+    Nesterov input taken as M' (or the plain input as g + β·M') changes the
+    ratio of the two singular values and fails."""
+    rows, cols = 9, 14
+    h1, h2 = _two_rank_ones(rows, cols)
+    beta, lr, eps = 0.95, 0.02, 0.0
+    g1, g2 = (4.0 * h1).astype(np.float32), (6.0 * h2).astype(np.float32)
+    W = np.zeros((rows, cols))
+    M = np.zeros((rows, cols), np.float32)
+    _, M, _ = oracle.muon_step(W, g1, M, beta, lr, oracle.QUINTIC, 5, eps, nesterov=nesterov)
+    _, M, O = oracle.muon_step(W, g2, M, beta, lr, oracle.QUINTIC, 5, eps, nesterov=nesterov)
+    b1 = float(np.float32(4.0 * beta))
+    assert np.array_equal(M.astype(np.float64), b1 * h1 + 6.0 * h2)
+
+    def closed(s1, s2):
+        nrm = math.hypot(s1, s2)
+        return (oracle.scalar_map(s1 / nrm, oracle.QUINTIC, 5) * h1 +
+                oracle.scalar_map(s2 / nrm, oracle.QUINTIC, 5) * h2)
+
+    plain, nest = (b1, 6.0), (beta * b1, 6.0 * (1 + beta))
+    want, wrong = (closed(*nest), closed(*plain)) if nesterov else (closed(*plain), closed(*nest))
+    assert np.allclose(O, want, rtol=0, atol=1e-12)
+    assert not np.allclose(O, wrong, rtol=0, atol=1e-3)
+
+
+def test_nesterov_first_step_equals_plain():
+    """From M = 0 the Nesterov input is (1 + β)·g, a positive multiple of the
+    plain input, and Frobenius normalisation removes the factor."""
+    rng = np.random.default_rng(5)
+    g = (rng.standard_normal((12, 30)) * 1e-2).astype(np.float32)
+    W = oracle.bf16_round(rng.standard_normal((12, 30)) * 0.02)
+    M = np.zeros_like(g)
+    a = oracle.muon_step(W, g, M, 0.9, 0.02, oracle.QUINTIC, 5, 0.0, nesterov=False)
+    b = oracle.muon_step(W, g, M, 0.9, 0.02, oracle.QUINTIC, 5, 0.0, nesterov=True)
+    assert np.allclose(a[2], b[2], rtol=0, atol=1e-12)
+    assert np.array_equal(a[1], b[1])
+
+
+def test_weight_decay_zero_gradient_halves_weights():
+    """g = 0 and M = 0 give a zero update (the zero matrix normalises to 0),
+    so W' = round((1 − lr·wd)·W); with lr·wd = 1/2 that is W/2, exact for
+    bf16 values."""
+    rng = np.random.default_rng(8)
+    W = oracle.bf16_round(rng.standard_normal((7, 11)))
+    z = np.zeros((7, 11), np.float32)
+    W_new, M_new, O = oracle.muon_step(W, z, z, 0.95, 0.25, oracle.QUINTIC, 5, 1e-7, weight_decay=2.0)
+    assert not O.any() and not M_new.any()
+    assert np.array_equal(W_new, W / 2)
+
+
+@pytest.mark.parametrize("rows,cols", [(6, 20), (20, 6)])
+def test_weight_decay_rank_one_closed_form(rows, cols):
+    """Rank-one gradient with decoupled decay: W' = bf16((1 − lr·wd)·W −
+    lr·sc·φ^5(1)·g/‖g‖); lr·wd = 1/4 makes the decayed weights exact."""
+    rng = np.random.default_rng(rows * 7 + cols)
+    u = rng.integers(-8, 9, rows).astype(np.float64)
+    v = rng.integers(-8, 9, cols).astype(np.float64) / 64.0
+    u[0], v[0] = 3.0, 0.5
+    g = np.outer(u, v).astype(np.float32)
+    W = oracle.bf16_round(rng.standard_normal((rows, cols)) * 0.02)
+    M = np.zeros((rows, cols), np.float32)
+    W_new, _, O = oracle.muon_step(W, g, M, 0.95, 0.02, oracle.QUINTIC, 5, 0.0, weight_decay=12.5)
+    g64 = g.astype(np.float64)
+    O_want = oracle.scalar_map(1.0, oracle.QUINTIC, 5) * g64 / np.linalg.norm(g64)
+    sc = math.sqrt(max(1.0, rows / cols))
+    assert np.array_equal(W_new, oracle.bf16_round(0.75 * W - 0.02 * sc * O_want))
+
+
 def test_gram_flops_by_enumeration():
     """Walk the product sequence of the Gram recursion (A², then Q-update,
     P·A, P·(P·A) as the step requires) and count 2·K flops per upper-triangle
