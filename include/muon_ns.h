@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define MUON_NS_ABI_VERSION 1
+#define MUON_NS_ABI_VERSION 2
 
 typedef enum muon_status {
   MUON_OK = 0,
@@ -120,7 +120,33 @@ muon_status_t muon_step(void* const* params, const float* const* grads, float* c
                         const float coeffs[3], float eps,
                         void* workspace, size_t workspace_bytes, void* stream);
 
-/* Workspace bytes muon_step needs for these shapes.  Host only. */
+/* Options of muon_step_ex.  The pages define the plain step only (momentum
+ * as above, no weight decay); these are the usual Muon-optimiser variants,
+ * provided for use as a drop-in optimiser (DMuon summary §3: the module
+ * replaces the optimiser without changing the framework):
+ *   nesterov = 1:  the matrix orthogonalised is u = g + beta·M' (M' the
+ *                  updated momentum) instead of M'; the stored state is M'.
+ *   weight_decay:  decoupled, W ← round((1 − lr·weight_decay)·W − lr·sc·O);
+ *                  0 leaves the plain update unchanged.  Finite, ≥ 0.
+ *   grad_dtype:    MUON_DTYPE_F32 or MUON_DTYPE_BF16 gradients (momentum
+ *                  stays fp32; bf16 values are widened exactly). */
+typedef struct muon_step_opts {
+  int32_t nesterov;          /* 0 or 1 */
+  float weight_decay;
+  muon_dtype_t grad_dtype;
+} muon_step_opts_t;
+
+/* muon_step with options; opts = NULL gives exactly muon_step.  grads[i]
+ * has opts->grad_dtype; every other argument, the workspace size and the
+ * error behaviour are those of muon_step (an invalid option returns
+ * MUON_ERR_INVALID_ARG before anything is enqueued). */
+muon_status_t muon_step_ex(void* const* params, const void* const* grads, float* const* momentum,
+                           const int64_t* rows, const int64_t* cols, int32_t count,
+                           muon_dtype_t param_dtype, float beta, float lr, int32_t steps,
+                           const float coeffs[3], float eps, const muon_step_opts_t* opts,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes muon_step (and muon_step_ex) needs for these shapes.  Host only. */
 muon_status_t muon_step_workspace_size(const int64_t* rows, const int64_t* cols, int32_t count,
                                        size_t* bytes);
 

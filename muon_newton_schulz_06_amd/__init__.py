@@ -31,6 +31,7 @@ CUBIC = (1.5, -0.5, 0.0)
 
 MUON_DTYPE_F32 = 0
 MUON_DTYPE_BF16 = 1
+ABI_VERSION = 2
 
 PROFILE_KINDS = {"momentum": 0, "norm": 1, "cast": 2, "syrk": 3, "gram128": 4, "final": 5,
                  "gram256_axpy": 6, "gram256_sq": 7}
@@ -55,6 +56,11 @@ class MuonError(RuntimeError):
 class MuonNsDesc(ctypes.Structure):
     _fields_ = [("x", ctypes.c_void_p), ("out", ctypes.c_void_p), ("rows", ctypes.c_int64),
                 ("cols", ctypes.c_int64), ("ld_x", ctypes.c_int64), ("ld_out", ctypes.c_int64)]
+
+
+class MuonStepOpts(ctypes.Structure):
+    _fields_ = [("nesterov", ctypes.c_int32), ("weight_decay", ctypes.c_float),
+                ("grad_dtype", ctypes.c_int32)]
 
 
 _lib = None
@@ -90,6 +96,11 @@ def load():
                                 ctypes.POINTER(i64), ctypes.POINTER(i64), i32, i32, f32, f32, i32,
                                 ctypes.POINTER(f32), f32, vp, sz, vp]
         L.muon_step.restype = i32
+        L.muon_step_ex.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(vp),
+                                   ctypes.POINTER(i64), ctypes.POINTER(i64), i32, i32, f32, f32,
+                                   i32, ctypes.POINTER(f32), f32, ctypes.POINTER(MuonStepOpts),
+                                   vp, sz, vp]
+        L.muon_step_ex.restype = i32
         L.muon_step_workspace_size.argtypes = [ctypes.POINTER(i64), ctypes.POINTER(i64), i32,
                                                ctypes.POINTER(sz)]
         L.muon_step_workspace_size.restype = i32
@@ -101,8 +112,8 @@ def load():
         L.muon_profile_read.argtypes = [i32, ctypes.POINTER(ctypes.c_double),
                                         ctypes.POINTER(i64), ctypes.POINTER(ctypes.c_double)]
         L.muon_profile_read.restype = i32
-        if L.muon_abi_version() != 1:
-            raise ImportError(f"libmuon_ns ABI {L.muon_abi_version()} != 1")
+        if L.muon_abi_version() != ABI_VERSION:
+            raise ImportError(f"libmuon_ns ABI {L.muon_abi_version()} != {ABI_VERSION}")
         _lib = L
         return L
 
@@ -250,9 +261,12 @@ def muon_ns_batched(xs, outs=None, steps: int = 5, coeffs=QUINTIC, eps: float = 
 
 
 def muon_step(params, grads, momenta, beta: float = 0.95, lr: float = 0.02, steps: int = 5,
-              coeffs=QUINTIC, eps: float = 1e-7, workspace=None, stream=None):
-    """One in-place Muon step over lists of weights (bf16 or fp32), fp32
-    gradients and fp32 momenta (all contiguous, same device)."""
+              coeffs=QUINTIC, eps: float = 1e-7, workspace=None, stream=None,
+              nesterov: bool = False, weight_decay: float = 0.0):
+    """One in-place Muon step over lists of weights (bf16 or fp32), gradients
+    (fp32 or bf16, one dtype per call) and fp32 momenta (all contiguous, same
+    device).  nesterov / weight_decay select the muon_step_ex variants; with
+    their defaults and fp32 gradients the plain muon_step entry point runs."""
     L = load()
     params, grads, momenta = list(params), list(grads), list(momenta)
     n = len(params)
@@ -262,13 +276,18 @@ def muon_step(params, grads, momenta, beta: float = 0.95, lr: float = 0.02, step
         return
     dev = params[0].device
     pdt = params[0].dtype
+    gdt = grads[0].dtype
+    if gdt not in (torch.float32, torch.bfloat16):
+        raise TypeError("grads must be float32 or bfloat16")
     for p, g, m in zip(params, grads, momenta):
         if p.device != dev or g.device != dev or m.device != dev or dev.type != "cuda":
             raise ValueError("all tensors must be on one CUDA/HIP device")
         if p.dtype != pdt:
             raise TypeError("all params must share one dtype")
-        if g.dtype != torch.float32 or m.dtype != torch.float32:
-            raise TypeError("grads and momenta must be float32")
+        if g.dtype != gdt:
+            raise TypeError("all grads must share one dtype")
+        if m.dtype != torch.float32:
+            raise TypeError("momenta must be float32")
         if p.dim() != 2 or tuple(p.shape) != tuple(g.shape) or tuple(p.shape) != tuple(m.shape):
             raise ValueError("param, grad and momentum shapes differ (or not 2-D)")
         if not (p.is_contiguous() and g.is_contiguous() and m.is_contiguous()):
@@ -282,11 +301,18 @@ def muon_step(params, grads, momenta, beta: float = 0.95, lr: float = 0.02, step
     need = ctypes.c_size_t(0)
     _check(L.muon_step_workspace_size(rows, cols, n, ctypes.byref(need)))
     ws, ws_bytes = _workspace(int(need.value), dev, workspace)
+    plain = (not nesterov) and float(weight_decay) == 0.0 and gdt == torch.float32
     with torch.cuda.device(dev):
-        _check(L.muon_step(P, G, M, rows, cols, n, _dtype_code(pdt), float(beta), float(lr),
-                           int(steps), _coeffs(coeffs), float(eps),
-                           ctypes.c_void_p(ws.data_ptr() if ws is not None else 0), ws_bytes,
-                           _stream_handle(stream, dev)))
+        wsp = ctypes.c_void_p(ws.data_ptr() if ws is not None else 0)
+        if plain:
+            _check(L.muon_step(P, G, M, rows, cols, n, _dtype_code(pdt), float(beta), float(lr),
+                               int(steps), _coeffs(coeffs), float(eps), wsp, ws_bytes,
+                               _stream_handle(stream, dev)))
+        else:
+            opts = MuonStepOpts(int(bool(nesterov)), float(weight_decay), _dtype_code(gdt))
+            _check(L.muon_step_ex(P, G, M, rows, cols, n, _dtype_code(pdt), float(beta),
+                                  float(lr), int(steps), _coeffs(coeffs), float(eps),
+                                  ctypes.byref(opts), wsp, ws_bytes, _stream_handle(stream, dev)))
 
 
 def profile_enable(on: bool = True):

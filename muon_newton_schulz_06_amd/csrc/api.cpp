@@ -133,8 +133,15 @@ struct CallerMat {
   int64_t ldSrc;
   void* dst;         // weights (step) or out (ns)
   int64_t ldDst;
-  const float* grad; // step only
+  const void* grad;  // step only
   float lrsc;
+};
+
+// Step options resolved on the host (defaults: the plain step).
+struct StepVariant {
+  int gradDtype = MUON_DTYPE_F32;
+  int nesterov = 0;
+  float decay = 1.f;  // 1 − lr·weight_decay
 };
 
 template <typename T>
@@ -143,7 +150,7 @@ T* at(void* ws, size_t off) {
 }
 
 muon_status_t enqueue(const Plan& P, const std::vector<CallerMat>& cm, int srcDtype, int dstDtype,
-                      float beta, float eps, void* ws, hipStream_t st) {
+                      float beta, float eps, const StepVariant& V, void* ws, hipStream_t st) {
   Launcher Lr{st};
   const int count = (int)P.mats.size();
   const size_t esz = P.op == OP_F32 ? 4 : 2;
@@ -160,7 +167,8 @@ muon_status_t enqueue(const Plan& P, const std::vector<CallerMat>& cm, int srcDt
     EwLaunch L;
     std::memset(&L, 0, sizeof(L));
     L.mode = P.forStep ? 0 : 1;
-    L.xDtype = srcDtype;
+    L.xDtype = P.forStep ? V.gradDtype : srcDtype;
+    L.nesterov = P.forStep ? V.nesterov : 0;
     L.beta = beta;
     L.partials = partials;
     L.vec = 1;
@@ -180,8 +188,9 @@ muon_status_t enqueue(const Plan& P, const std::vector<CallerMat>& cm, int srcDt
         e.x = cm[i].grad;
         e.mom = (float*)cm[i].src;
         e.ld = mp.cols;
-        if ((mp.numel & 3) || ((uintptr_t)e.x & 15) || ((uintptr_t)e.mom & 15)) L.vec = 0;
-        bytes += 12.0 * mp.numel;
+        const uintptr_t galign = V.gradDtype == MUON_DTYPE_BF16 ? 7 : 15;
+        if ((mp.numel & 3) || ((uintptr_t)e.x & galign) || ((uintptr_t)e.mom & 15)) L.vec = 0;
+        bytes += (V.gradDtype == MUON_DTYPE_BF16 ? 10.0 : 12.0) * mp.numel;
       } else {
         e.x = cm[i].src;
         e.ld = cm[i].ldSrc;
@@ -221,6 +230,9 @@ muon_status_t enqueue(const Plan& P, const std::vector<CallerMat>& cm, int srcDt
     L.outOp = P.op;
     L.sX = sc.sX;
     L.alpha = alpha;
+    L.nesterov = P.forStep ? V.nesterov : 0;
+    L.gradDtype = V.gradDtype;
+    L.beta = beta;
     const size_t cn = std::min(live.size() - c0, (size_t)kMaxUser);
     int64_t blocks = 0;
     double bytes = 0;
@@ -230,6 +242,7 @@ muon_status_t enqueue(const Plan& P, const std::vector<CallerMat>& cm, int srcDt
       const BucketPlan& bp = P.buckets[mp.bucket];
       CastMat& C = L.mat[k];
       C.src = cm[i].src;
+      C.grad = cm[i].grad;
       C.rows = mp.rows;
       C.cols = mp.cols;
       C.ld = P.forStep ? mp.cols : cm[i].ldSrc;
@@ -252,6 +265,7 @@ muon_status_t enqueue(const Plan& P, const std::vector<CallerMat>& cm, int srcDt
       blocks += (int64_t)(C.rp / kCastTile) * C.tilesC;
       bytes += (P.forStep ? 4.0 : (srcDtype == MUON_DTYPE_BF16 ? 2.0 : 4.0)) * mp.numel +
                2.0 * esz * (double)bp.Mp * (double)bp.Np;
+      if (L.nesterov) bytes += (V.gradDtype == MUON_DTYPE_BF16 ? 2.0 : 4.0) * mp.numel;
     }
     L.n = (int)cn;
     muon_status_t s = Lr.run(2, bytes, "cast kernel", [&] { return launch_cast(L, blocks, st); });
@@ -272,6 +286,7 @@ muon_status_t enqueue(const Plan& P, const std::vector<CallerMat>& cm, int srcDt
     for (size_t s0 = 0; s0 < segs.size(); s0 += kMaxSegs) {
       GemmLaunch L;
       std::memset(&L, 0, sizeof(L));
+      L.decay = 1.f;
       const size_t ns = std::min(segs.size() - s0, (size_t)kMaxSegs);
       int blocks = 0;
       double work = 0;
@@ -452,6 +467,7 @@ muon_status_t enqueue(const Plan& P, const std::vector<CallerMat>& cm, int srcDt
       GemmLaunch L;
       std::memset(&L, 0, sizeof(L));
       L.userDtype = dstDtype;
+      L.decay = P.forStep ? V.decay : 1.f;
       GemmSeg& S = L.seg[0];
       const char* qh = at<char>(ws, g.offQh[qcur] + g.strideh * (bp.gramStart + c0));
       const char* xth = at<char>(ws, bp.offXTh + bp.strideX * c0);
@@ -634,16 +650,29 @@ muon_status_t muon_ns_batched(const muon_ns_desc_t* desc, int32_t count, int32_t
   }
   muon_status_t s = check_device();
   if (s != MUON_OK) return s;
-  return enqueue(P, cm, dtype, dtype, 0.f, eps, workspace, (hipStream_t)stream);
+  return enqueue(P, cm, dtype, dtype, 0.f, eps, StepVariant{}, workspace, (hipStream_t)stream);
 }
 
-muon_status_t muon_step(void* const* params, const float* const* grads, float* const* momentum,
-                        const int64_t* rows, const int64_t* cols, int32_t count,
-                        muon_dtype_t param_dtype, float beta, float lr, int32_t steps,
-                        const float coeffs[3], float eps, void* workspace, size_t workspace_bytes,
-                        void* stream) {
+muon_status_t muon_step_ex(void* const* params, const void* const* grads, float* const* momentum,
+                           const int64_t* rows, const int64_t* cols, int32_t count,
+                           muon_dtype_t param_dtype, float beta, float lr, int32_t steps,
+                           const float coeffs[3], float eps, const muon_step_opts_t* opts,
+                           void* workspace, size_t workspace_bytes, void* stream) {
   g_err.clear();
   if (count < 0) return fail(MUON_ERR_INVALID_ARG, "count < 0");
+  StepVariant V;
+  float wd = 0.f;
+  if (opts) {
+    if (opts->nesterov != 0 && opts->nesterov != 1)
+      return fail(MUON_ERR_INVALID_ARG, "opts->nesterov must be 0 or 1");
+    if (!std::isfinite(opts->weight_decay) || opts->weight_decay < 0)
+      return fail(MUON_ERR_INVALID_ARG, "opts->weight_decay must be finite and >= 0");
+    if (opts->grad_dtype != MUON_DTYPE_F32 && opts->grad_dtype != MUON_DTYPE_BF16)
+      return fail(MUON_ERR_INVALID_ARG, "unknown opts->grad_dtype");
+    V.nesterov = opts->nesterov;
+    V.gradDtype = opts->grad_dtype;
+    wd = opts->weight_decay;
+  }
   if (count == 0) return MUON_OK;
   if (!params || !grads || !momentum || !rows || !cols)
     return fail(MUON_ERR_INVALID_ARG, "NULL pointer array");
@@ -654,7 +683,10 @@ muon_status_t muon_step(void* const* params, const float* const* grads, float* c
   if (!std::isfinite(beta) || !std::isfinite(lr))
     return fail(MUON_ERR_INVALID_ARG, "beta and lr must be finite");
   if (!std::isfinite(eps) || eps < 0) return fail(MUON_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  V.decay = (float)(1.0 - (double)lr * (double)wd);
+  if (!std::isfinite(V.decay)) return fail(MUON_ERR_INVALID_ARG, "1 - lr*weight_decay is not finite");
   const size_t psz = param_dtype == MUON_DTYPE_F32 ? 4 : 2;
+  const size_t gsz = V.gradDtype == MUON_DTYPE_F32 ? 4 : 2;
   std::vector<Range> ranges;
   for (int i = 0; i < count; ++i) {
     muon_status_t s = check_shape(i, rows[i], cols[i]);
@@ -664,7 +696,7 @@ muon_status_t muon_step(void* const* params, const float* const* grads, float* c
       return fail(MUON_ERR_INVALID_ARG, "matrix " + std::to_string(i) + ": NULL tensor");
     const uintptr_t n = (uintptr_t)(rows[i] * cols[i]);
     ranges.push_back({(uintptr_t)params[i], (uintptr_t)params[i] + n * psz, i});
-    ranges.push_back({(uintptr_t)grads[i], (uintptr_t)grads[i] + n * 4, i});
+    ranges.push_back({(uintptr_t)grads[i], (uintptr_t)grads[i] + n * gsz, i});
     ranges.push_back({(uintptr_t)momentum[i], (uintptr_t)momentum[i] + n * 4, i});
   }
   int oa = 0, ob = 0;
@@ -690,7 +722,16 @@ muon_status_t muon_step(void* const* params, const float* const* grads, float* c
   }
   muon_status_t s = check_device();
   if (s != MUON_OK) return s;
-  return enqueue(P, cm, MUON_DTYPE_F32, param_dtype, beta, eps, workspace, (hipStream_t)stream);
+  return enqueue(P, cm, MUON_DTYPE_F32, param_dtype, beta, eps, V, workspace, (hipStream_t)stream);
+}
+
+muon_status_t muon_step(void* const* params, const float* const* grads, float* const* momentum,
+                        const int64_t* rows, const int64_t* cols, int32_t count,
+                        muon_dtype_t param_dtype, float beta, float lr, int32_t steps,
+                        const float coeffs[3], float eps, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  return muon_step_ex(params, (const void* const*)grads, momentum, rows, cols, count, param_dtype,
+                      beta, lr, steps, coeffs, eps, nullptr, workspace, workspace_bytes, stream);
 }
 
 muon_status_t muon_profile_enable(int32_t on) {

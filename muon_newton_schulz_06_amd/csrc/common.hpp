@@ -30,7 +30,8 @@ enum Epi : int32_t {
   EPI_SQ = 1,
   // Y' = p0·Y + u·acc (Y from inh) → outh = sOut·Y' (mirrored).
   EPI_AXPY = 2,
-  // caller weights W ← round(W − lrsc·u·acc), full tiles, real extent only.
+  // caller weights W ← round(decay·W − lrsc·u·acc), full tiles, real extent
+  // only (decay = 1 − lr·weight_decay, exactly 1 without weight decay).
   EPI_UPDATE = 3,
   // caller output out = round(u·acc), full tiles, real extent only.
   EPI_OUT = 4,
@@ -72,6 +73,7 @@ struct GemmSeg {
 struct GemmLaunch {
   int32_t nseg;
   int32_t userDtype;          // muon_dtype_t of the caller matrices
+  float decay;                // EPI_UPDATE: factor applied to W before the update
   int32_t segStart[kMaxSegs + 1];  // prefix of workgroups per segment
   GemmSeg seg[kMaxSegs];
   void* user[kMaxUser];        // caller weights (EPI_UPDATE) or outputs (EPI_OUT)
@@ -95,10 +97,10 @@ struct EwMat {
 struct EwLaunch {
   int32_t n;
   int32_t mode;        // 0: momentum, 1: sum of squares of x
-  int32_t xDtype;      // muon_dtype_t of x in norm mode
+  int32_t xDtype;      // muon_dtype_t of x (the gradient in momentum mode)
   int32_t vec;         // 1: every matrix contiguous, numel % 4 == 0, 16-B aligned
   float beta;
-  int32_t pad_;
+  int32_t nesterov;    // momentum mode: Σ of (g + β·M')² instead of Σ M'²
   float* partials;
   EwMat mat[kMaxUser];
 };
@@ -118,6 +120,7 @@ constexpr int kCastTile = 64;
 
 struct CastMat {
   const void* src;     // stored rows × cols, row stride ld
+  const void* grad;    // Nesterov input: gradient, same layout as src (else unused)
   void* S;             // same orientation, padded rp × cp
   void* T;             // transposed, padded cp × rp
   int64_t rows, cols, ld;
@@ -132,6 +135,10 @@ struct CastLaunch {
   int32_t srcDtype;    // muon_dtype_t
   int32_t outOp;       // OpType of S and T
   float sX;            // operand scale
+  int32_t nesterov;    // 1: the value cast is g + β·src (src = M', g = grad)
+  int32_t gradDtype;   // muon_dtype_t of grad
+  float beta;
+  int32_t pad_;
   const float* alpha;  // per-matrix 1 / (‖x‖_F + eps)
   CastMat mat[kMaxUser];
 };

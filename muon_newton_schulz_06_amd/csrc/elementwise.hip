@@ -4,7 +4,9 @@
 //    per-workgroup partial Σ M², in one pass over g and M (DeMuon technical
 //    summary, gist.science Korean, Method §1: the momentum is a moving
 //    average of the gradients; DMuon technical summary §1: NS runs on the
-//    momentum-accumulated gradient);
+//    momentum-accumulated gradient).  With the Nesterov option the value
+//    orthogonalised is u = g + β·M (after the update), and Σ u² is summed;
+//    gradients may be fp32 or bf16;
 //  * norm finish: α = 1/(√ΣM² + eps) per matrix, summing the partials in a
 //    fixed order (deterministic, no float atomics);
 //  * scaled cast: X₀ = α·sX·M rounded to the MFMA operand type, written in
@@ -36,6 +38,54 @@ __device__ __forceinline__ float load_as_f32(const void* p, int64_t e, int dtype
   return ((const float*)p)[e];
 }
 
+// Four consecutive values at element e (e % 4 == 0, 8-byte aligned for
+// bf16, 16-byte aligned for fp32), widened to fp32.
+template <int GD>
+__device__ __forceinline__ f32x4 load4(const void* p, int64_t e) {
+  f32x4 r;
+  if constexpr (GD == 1) {
+    const uint2 u = *(const uint2*)((const uint16_t*)p + e);
+    r[0] = __uint_as_float(u.x << 16);
+    r[1] = __uint_as_float(u.x & 0xffff0000u);
+    r[2] = __uint_as_float(u.y << 16);
+    r[3] = __uint_as_float(u.y & 0xffff0000u);
+  } else {
+    r = __builtin_nontemporal_load((const f32x4*)((const float*)p + e));
+  }
+  return r;
+}
+
+// Momentum of one block of kEwElems elements wholly inside the matrix: every
+// load is issued before the first store (the compiler cannot prove that g
+// and M do not overlap, so interleaved load/store pairs would serialise on
+// memory latency).  Returns this thread's part of Σ u².
+template <int GD, bool NEST>
+__device__ __forceinline__ float momentum_block(const void* g, float* m, int64_t e0, float beta,
+                                                int tid) {
+  constexpr int Q = kEwElems / (4 * kEwThreads);
+  f32x4 gv[Q], mv[Q];
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    const int64_t e = e0 + (int64_t)(q * kEwThreads + tid) * 4;
+    gv[q] = load4<GD>(g, e);
+    mv[q] = *(const f32x4*)(m + e);
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    const int64_t e = e0 + (int64_t)(q * kEwThreads + tid) * 4;
+    f32x4 v;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      v[c] = fmaf(beta, mv[q][c], gv[q][c]);
+      const float u = NEST ? fmaf(beta, v[c], gv[q][c]) : v[c];
+      ss += u * u;
+    }
+    *(f32x4*)(m + e) = v;
+  }
+  return ss;
+}
+
 __global__ __launch_bounds__(kEwThreads) void ew_kernel(const EwLaunch L) {
   const int64_t b = blockIdx.x;
   int mi = 0;
@@ -46,53 +96,22 @@ __global__ __launch_bounds__(kEwThreads) void ew_kernel(const EwLaunch L) {
   const int tid = threadIdx.x;
   float ss = 0.f;
   if (L.mode == 0) {
-    const float* g = (const float*)M.x;
+    const void* g = M.x;
     float* m = M.mom;
-    constexpr int Q = kEwElems / (4 * kEwThreads);
     if (L.vec && e0 + kEwElems <= M.numel) {
-      // Whole block inside the matrix: every load is issued before the
-      // first store (the compiler cannot prove that g and M do not overlap,
-      // so interleaved load/store pairs would serialise on memory latency).
-      f32x4 gv[Q], mv[Q];
-#pragma unroll
-      for (int q = 0; q < Q; ++q) {
-        const int64_t e = e0 + (int64_t)(q * kEwThreads + tid) * 4;
-        gv[q] = __builtin_nontemporal_load((const f32x4*)(g + e));
-        mv[q] = *(const f32x4*)(m + e);
-      }
-#pragma unroll
-      for (int q = 0; q < Q; ++q) {
-        const int64_t e = e0 + (int64_t)(q * kEwThreads + tid) * 4;
-        f32x4 v;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          v[c] = fmaf(L.beta, mv[q][c], gv[q][c]);
-          ss += v[c] * v[c];
-        }
-        *(f32x4*)(m + e) = v;
-      }
-    } else if (L.vec) {
-#pragma unroll
-      for (int q = 0; q < Q; ++q) {
-        const int64_t e = e0 + (int64_t)(q * kEwThreads + tid) * 4;
-        if (e < M.numel) {
-          const float4 gv = *(const float4*)(g + e);
-          float4 mv = *(const float4*)(m + e);
-          mv.x = fmaf(L.beta, mv.x, gv.x);
-          mv.y = fmaf(L.beta, mv.y, gv.y);
-          mv.z = fmaf(L.beta, mv.z, gv.z);
-          mv.w = fmaf(L.beta, mv.w, gv.w);
-          *(float4*)(m + e) = mv;
-          ss += mv.x * mv.x + mv.y * mv.y + mv.z * mv.z + mv.w * mv.w;
-        }
-      }
+      if (L.xDtype == 1) ss = L.nesterov ? momentum_block<1, true>(g, m, e0, L.beta, tid)
+                                         : momentum_block<1, false>(g, m, e0, L.beta, tid);
+      else ss = L.nesterov ? momentum_block<0, true>(g, m, e0, L.beta, tid)
+                           : momentum_block<0, false>(g, m, e0, L.beta, tid);
     } else {
       for (int q = 0; q < kEwElems / kEwThreads; ++q) {
         const int64_t e = e0 + q * kEwThreads + tid;
         if (e < M.numel) {
-          const float v = fmaf(L.beta, m[e], g[e]);
+          const float gv = load_as_f32(g, e, L.xDtype);
+          const float v = fmaf(L.beta, m[e], gv);
           m[e] = v;
-          ss += v * v;
+          const float u = L.nesterov ? fmaf(L.beta, v, gv) : v;
+          ss += u * u;
         }
       }
     }
@@ -153,22 +172,36 @@ __device__ void cast_tile(const CastLaunch& L, const CastMat& C, int64_t t) {
   const int tid = threadIdx.x;
   const int tx = tid & 15, ty = tid >> 4;
   const float scale = L.alpha[C.alphaIdx] * L.sX;
+  const bool nest = L.nesterov != 0;
   T* S = (T*)C.S;
   T* Tt = (T*)C.T;
   const int64_t r0 = (int64_t)tr * kCastTile, c0 = (int64_t)tc * kCastTile;
   const bool full = (r0 + kCastTile <= C.rows) && (c0 + kCastTile <= C.cols);
-  const bool vec = full && L.srcDtype == 0 && (C.ld % 4 == 0) && (((uintptr_t)C.src & 15) == 0);
+  const bool vec = full && L.srcDtype == 0 && (C.ld % 4 == 0) && (((uintptr_t)C.src & 15) == 0) &&
+                   (!L.nesterov || (((uintptr_t)C.grad & (L.gradDtype == 1 ? 7 : 15)) == 0));
   // All four source rows are loaded before anything is stored (the
   // compiler cannot prove that the source and the copies do not overlap).
   const int cl = 4 * tx;
   float v[4][4];
-  if (vec) {
+  if (vec && !nest) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const f32x4 x = *(const f32x4*)((const float*)C.src + (r0 + ty + 16 * q) * C.ld + c0 + cl);
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[q][e] = x[e] * scale;
     }
+  } else if (vec) {  // Nesterov: u = g + β·M', M' fp32, g fp32 or bf16 (contiguous)
+    f32x4 x[4], gq[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t e = (r0 + ty + 16 * q) * C.ld + c0 + cl;
+      x[q] = *(const f32x4*)((const float*)C.src + e);
+      gq[q] = L.gradDtype == 1 ? load4<1>(C.grad, e) : load4<0>(C.grad, e);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[q][e] = fmaf(L.beta, x[q][e], gq[q][e]) * scale;
   } else {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -176,7 +209,12 @@ __device__ void cast_tile(const CastLaunch& L, const CastMat& C, int64_t t) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int64_t cc = c0 + cl + e;
-        v[q][e] = (r < C.rows && cc < C.cols) ? load_as_f32(C.src, r * C.ld + cc, L.srcDtype) * scale : 0.f;
+        float x = 0.f;
+        if (r < C.rows && cc < C.cols) {
+          x = load_as_f32(C.src, r * C.ld + cc, L.srcDtype);
+          if (nest) x = fmaf(L.beta, x, load_as_f32(C.grad, r * C.ld + cc, L.gradDtype));
+        }
+        v[q][e] = x * scale;
       }
     }
   }

@@ -133,7 +133,7 @@ struct EpiArgs {
   void* user;
   int64_t userLd;
   int ldc, mReal, nReal, writeIdentity, userDtype;
-  float u, sOut, sOutB, sIn, p0, p1, p2, lrsc;
+  float u, sOut, sOutB, sIn, p0, p1, p2, lrsc, decay;
 };
 
 // Epilogue for one accumulator element (i, j) (register-staged kernel).  EPI
@@ -171,13 +171,13 @@ __device__ __forceinline__ void epilogue(const EpiArgs<T>& E, int i, int j, floa
   } else if constexpr (EPI == EPI_UPDATE) {
     if (i >= E.mReal || j >= E.nReal) return;
     const int64_t e = (int64_t)i * E.userLd + j;
-    const float d = E.lrsc * (E.u * acc);
+    const float o = E.u * acc;
     if (E.userDtype == 1) {
       uint16_t* w = (uint16_t*)E.user;
-      w[e] = f32_to_bf16_rne(bf16_to_f32(w[e]) - d);
+      w[e] = f32_to_bf16_rne(fmaf(-E.lrsc, o, bf16_to_f32(w[e]) * E.decay));
     } else {
       float* w = (float*)E.user;
-      w[e] = w[e] - d;
+      w[e] = fmaf(-E.lrsc, o, w[e] * E.decay);
     }
   } else if constexpr (EPI == EPI_OUT) {
     if (i >= E.mReal || j >= E.nReal) return;
@@ -242,6 +242,7 @@ __device__ __forceinline__ EpiArgs<T> make_epi(const GemmLaunch& L, const GemmSe
   E.user = nullptr;
   E.userLd = 0;
   E.lrsc = 0.f;
+  E.decay = L.decay;
   E.userDtype = L.userDtype;
   if constexpr (EPI == EPI_UPDATE || EPI == EPI_OUT) {
     const int k = S.userBase + mat;
@@ -645,8 +646,8 @@ __device__ __forceinline__ void update_prefetched(const EpiArgs<_Float16>& E, ch
       uint32_t o[2];
 #pragma unroll
       for (int p = 0; p < 2; ++p) {
-        const float a0 = bf16_to_f32((uint16_t)(in[p] & 0xffffu)) - E.lrsc * __uint_as_float(raw[2 * p]);
-        const float a1 = bf16_to_f32((uint16_t)(in[p] >> 16)) - E.lrsc * __uint_as_float(raw[2 * p + 1]);
+        const float a0 = fmaf(-E.lrsc, __uint_as_float(raw[2 * p]), bf16_to_f32((uint16_t)(in[p] & 0xffffu)) * E.decay);
+        const float a1 = fmaf(-E.lrsc, __uint_as_float(raw[2 * p + 1]), bf16_to_f32((uint16_t)(in[p] >> 16)) * E.decay);
         o[p] = (uint32_t)f32_to_bf16_rne(a0) | ((uint32_t)f32_to_bf16_rne(a1) << 16);
       }
       *(uint2*)(w0 + (int64_t)(half * 128 + it * 8) * E.userLd) = make_uint2(o[0], o[1]);
@@ -696,26 +697,26 @@ __device__ __forceinline__ void dense_staged(const EpiArgs<_Float16>& E, char* l
             uint32_t o[2];
 #pragma unroll
             for (int p = 0; p < 2; ++p) {
-              const float a0 = bf16_to_f32((uint16_t)(in[p] & 0xffffu)) - E.lrsc * v[2 * p];
-              const float a1 = bf16_to_f32((uint16_t)(in[p] >> 16)) - E.lrsc * v[2 * p + 1];
+              const float a0 = fmaf(-E.lrsc, v[2 * p], bf16_to_f32((uint16_t)(in[p] & 0xffffu)) * E.decay);
+              const float a1 = fmaf(-E.lrsc, v[2 * p + 1], bf16_to_f32((uint16_t)(in[p] >> 16)) * E.decay);
               o[p] = (uint32_t)f32_to_bf16_rne(a0) | ((uint32_t)f32_to_bf16_rne(a1) << 16);
             }
             *(uint2*)w = make_uint2(o[0], o[1]);
           } else {
             for (int e = 0; e < 4 && j + e < E.nReal; ++e)
-              w[e] = f32_to_bf16_rne(bf16_to_f32(w[e]) - E.lrsc * v[e]);
+              w[e] = f32_to_bf16_rne(fmaf(-E.lrsc, v[e], bf16_to_f32(w[e]) * E.decay));
           }
         } else {
           float* w = (float*)E.user + base;
           if (full) {
             float4 wv = *(const float4*)w;
-            wv.x -= E.lrsc * v[0];
-            wv.y -= E.lrsc * v[1];
-            wv.z -= E.lrsc * v[2];
-            wv.w -= E.lrsc * v[3];
+            wv.x = fmaf(-E.lrsc, v[0], wv.x * E.decay);
+            wv.y = fmaf(-E.lrsc, v[1], wv.y * E.decay);
+            wv.z = fmaf(-E.lrsc, v[2], wv.z * E.decay);
+            wv.w = fmaf(-E.lrsc, v[3], wv.w * E.decay);
             *(float4*)w = wv;
           } else {
-            for (int e = 0; e < 4 && j + e < E.nReal; ++e) w[e] = w[e] - E.lrsc * v[e];
+            for (int e = 0; e < 4 && j + e < E.nReal; ++e) w[e] = fmaf(-E.lrsc, v[e], w[e] * E.decay);
           }
         }
       } else {  // EPI_OUT

@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol():
     assert "muon_ns_batched" in names and "muon_step" in names
     for n in names:
         assert hasattr(L, n), n
-    assert mns.abi_version() == 1
+    assert mns.abi_version() == 2
 
 
 def test_library_binds_hip_runtime_only_by_soname():
@@ -154,6 +154,46 @@ def test_step_rejects_bad_arguments():
     assert _step(wsb=100) == 4
     assert mns.load().muon_step(None, None, None, None, None, 0, 1, 0.9, 0.1, 5, C3, 1e-7,
                                 None, 0, None) == 0
+
+
+def _step_ex(opts, n=2, rows=(4, 8), cols=(8, 4), g=None, gbytes=None, **kw):
+    vp = ctypes.c_void_p
+    P = (vp * n)(*[0x1000000 + i * 0x10000 for i in range(n)])
+    G = (vp * n)(*(g or [0x2000000 + i * 0x10000 for i in range(n)]))
+    M = (vp * n)(*[0x3000000 + i * 0x10000 for i in range(n)])
+    R = (ctypes.c_int64 * n)(*rows[:n])
+    C = (ctypes.c_int64 * n)(*cols[:n])
+    o = ctypes.byref(opts) if opts is not None else None
+    return mns.load().muon_step_ex(P, G, M, R, C, n, kw.get("dtype", 1), kw.get("beta", 0.95),
+                                   kw.get("lr", 0.02), 5, C3, 1e-7, o,
+                                   ctypes.c_void_p(kw.get("ws", 0x100000000)), 1 << 40, None)
+
+
+def test_step_ex_rejects_bad_options():
+    O = mns.MuonStepOpts
+    assert _step_ex(O(2, 0.0, 0)) == 1 and "nesterov" in _err()
+    assert _step_ex(O(0, -0.1, 0)) == 1 and "weight_decay" in _err()
+    assert _step_ex(O(0, float("nan"), 0)) == 1
+    assert _step_ex(O(0, 0.0, 3)) == 1 and "grad_dtype" in _err()
+    # 1 − lr·wd overflows fp32
+    assert _step_ex(O(0, 3e38, 0), lr=1e10) == 1
+    # bf16 gradients are 2 bytes per element: 4×8 bf16 ends at +64, so a
+    # second gradient at +64 does not overlap, one at +62 does
+    assert _step_ex(O(0, 0.0, 1), g=[0x2000000, 0x2000000 + 62]) == 3, _err()
+    st = _step_ex(O(0, 0.0, 1), g=[0x2000000, 0x2000000 + 64])
+    if not torch.cuda.is_available():
+        assert st == 6, _err()
+    # invalid options are reported before count == 0 short-circuits
+    assert mns.load().muon_step_ex(None, None, None, None, None, 0, 1, 0.9, 0.1, 5, C3, 1e-7,
+                                   ctypes.byref(O(5, 0.0, 0)), None, 0, None) == 1
+    assert mns.load().muon_step_ex(None, None, None, None, None, 0, 1, 0.9, 0.1, 5, C3, 1e-7,
+                                   None, None, 0, None) == 0
+
+
+def test_step_ex_null_options_is_the_plain_step():
+    """opts = NULL takes the same validation path as muon_step."""
+    assert _step_ex(None, dtype=5) == _step(dtype=5) == 1
+    assert _step_ex(None, ws=0) == _step(ws=0) == 4
 
 
 # ---------------------------------------------------------------- planning

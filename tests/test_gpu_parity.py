@@ -51,7 +51,7 @@ def oracle_ns(x_cpu, steps=5, coeffs=oracle.QUINTIC, eps=1e-7):
     return oracle.muon_orthogonalize(x_cpu.to(torch.float64).numpy(), c32, steps, eps)
 
 
-def weights_consistent(W0, got, O, lrsc, band=0.1):
+def weights_consistent(W0, got, O, lrsc, band=0.1, decay=1.0):
     """Every updated bf16 weight must be the round-to-nearest-even of
     W0 − lrsc·Õ for some Õ within ±band·rms(O) of the oracle's update O
     (elementwise; 5× the per-element rms that the 2e-2 Frobenius bound
@@ -61,10 +61,10 @@ def weights_consistent(W0, got, O, lrsc, band=0.1):
     the fraction an update error at the tolerance would produce)."""
     rms = float(np.sqrt(np.mean(O * O)))
     b = band * rms
-    lo = oracle.bf16_round(W0 - lrsc * (O + b))
-    hi = oracle.bf16_round(W0 - lrsc * (O - b))
+    lo = oracle.bf16_round(decay * W0 - lrsc * (O + b))
+    hi = oracle.bf16_round(decay * W0 - lrsc * (O - b))
     ok = bool(np.all((got >= lo) & (got <= hi)))
-    frac = float(np.mean(got != oracle.bf16_round(W0 - lrsc * O)))
+    frac = float(np.mean(got != oracle.bf16_round(decay * W0 - lrsc * O)))
     # fraction of elements an update error at the 2e-2 bound (per-element rms
     # 2e-2·rms(O)) would move across a bf16 rounding boundary
     ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(got), 2.0 ** -126))) - 7)
@@ -228,15 +228,21 @@ def test_run_to_run_bitwise_determinism(mns):
 
 
 # ------------------------------------------------------------------ muon_step
-def _check_step(mns, shapes, seed0, check_idx, nsteps=2):
+def _check_step(mns, shapes, seed0, check_idx, nsteps=2, nesterov=False, weight_decay=0.0,
+                grad_dtype=torch.float32):
     inp = W.muon_inputs(shapes, seed0, device="cuda")
     host_W = [p.float().cpu().double().numpy() for p in inp.params]
     host_M = [m.cpu().numpy() for m in inp.momenta]
+    lr32, wd32 = float(np.float32(0.02)), float(np.float32(weight_decay))
+    decay = 1.0 - lr32 * wd32
     for step in range(nsteps):
         grads = inp.grads if step == 0 else W.fresh_grads(shapes, seed0, step, device="cuda")
-        host_g = [g.cpu().numpy() for g in grads]
-        say("muon_step", step, "over", len(shapes), "matrices")
-        mns.muon_step(inp.params, grads, inp.momenta, beta=0.95, lr=0.02, steps=5)
+        grads = [g.to(grad_dtype) for g in grads]
+        host_g = [g.float().cpu().numpy() for g in grads]
+        say("muon_step", step, "over", len(shapes), "matrices", "nesterov", nesterov,
+            "weight_decay", weight_decay, "grads", grad_dtype)
+        mns.muon_step(inp.params, grads, inp.momenta, beta=0.95, lr=0.02, steps=5,
+                      nesterov=nesterov, weight_decay=weight_decay)
         torch.cuda.synchronize()
         for j in range(len(shapes)):
             Mn = oracle.momentum_update(host_M[j], host_g[j], np.float32(0.95))
@@ -245,11 +251,14 @@ def _check_step(mns, shapes, seed0, check_idx, nsteps=2):
             assert np.all(np.abs(got.astype(np.float64) - Mn) <= ulp), ("momentum", j)
             host_M[j] = got
         for j in check_idx:
-            O = oracle.muon_orthogonalize(host_M[j], tuple(float(np.float32(v)) for v in oracle.QUINTIC), 5, 1e-7)
+            U = host_M[j].astype(np.float64)
+            if nesterov:
+                U = host_g[j].astype(np.float64) + float(np.float32(0.95)) * U
+            O = oracle.muon_orthogonalize(U, tuple(float(np.float32(v)) for v in oracle.QUINTIC), 5, 1e-7)
             r, c = shapes[j]
-            lrsc = float(np.float32(0.02)) * oracle.lr_shape_scale(r, c)
+            lrsc = lr32 * oracle.lr_shape_scale(r, c)
             got = inp.params[j].float().cpu().double().numpy()
-            ok, frac, expect = weights_consistent(host_W[j], got, O, lrsc)
+            ok, frac, expect = weights_consistent(host_W[j], got, O, lrsc, decay=decay)
             say("weights", shapes[j], "consistent", ok, "fraction != oracle rounding", frac,
                 "bound", expect)
             assert ok
@@ -265,6 +274,23 @@ def test_muon_step_small_shapes(mns):
 def test_muon_step_qwen_layer(mns):
     shapes = W.qwen_layer_shapes()
     _check_step(mns, shapes, 4001, check_idx=[1, 0], nsteps=2)
+
+
+@pytest.mark.parametrize("nesterov,weight_decay,grad_dtype", [
+    (True, 0.0, torch.float32),
+    (False, 0.1, torch.float32),
+    (False, 0.0, torch.bfloat16),
+    (True, 0.1, torch.bfloat16),
+])
+def test_muon_step_variants(mns, nesterov, weight_decay, grad_dtype):
+    """muon_step_ex: Nesterov input, decoupled weight decay and bf16
+    gradients, against the oracle's definitions, over two steps (the second
+    step is where the Nesterov input differs from the plain one)."""
+    shapes = [(96, 200), (200, 96), (256, 256), (300, 1000), (1, 64), (2304, 512)]
+    if nesterov and weight_decay:
+        shapes.append((2304, 2304))  # the 256-tile kernels (weights prefetched in the update)
+    _check_step(mns, shapes, 950, range(len(shapes)), nsteps=2, nesterov=nesterov,
+                weight_decay=weight_decay, grad_dtype=grad_dtype)
 
 
 def test_muon_step_fp32_params_expose_the_update(mns):
