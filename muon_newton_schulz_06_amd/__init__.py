@@ -326,3 +326,8 @@ def profile_read(kind) -> dict:
     ms, n, w = ctypes.c_double(0), ctypes.c_int64(0), ctypes.c_double(0)
     _check(load().muon_profile_read(k, ctypes.byref(ms), ctypes.byref(n), ctypes.byref(w)))
     return {"ms": ms.value, "launches": n.value, "work": w.value}
+
+
+from .optim import Muon  # noqa: E402  (torch.optim front end)
+
+__all__.append("Muon")

@@ -153,7 +153,6 @@ muon_status_t enqueue(const Plan& P, const std::vector<CallerMat>& cm, int srcDt
                       float beta, float eps, const StepVariant& V, void* ws, hipStream_t st) {
   Launcher Lr{st};
   const int count = (int)P.mats.size();
-  const size_t esz = P.op == OP_F32 ? 4 : 2;
   std::vector<int> live;
   for (int i = 0; i < count; ++i)
     if (!P.mats[i].empty) live.push_back(i);
@@ -222,22 +221,27 @@ muon_status_t enqueue(const Plan& P, const std::vector<CallerMat>& cm, int srcDt
     muon_status_t s = Lr.run(1, bytes, "norm finish kernel", [&] { return launch_norm(L, st); });
     if (s != MUON_OK) return s;
   }
-  // 3. cast into both operand layouts
-  for (size_t c0 = 0; c0 < live.size(); c0 += kMaxUser) {
+  // 3. cast into both operand layouts (one launch sequence per operand type)
+  for (int op : {(int)OP_F16, (int)OP_F32}) {
+  std::vector<int> castMats;
+  for (int i : live)
+    if (P.buckets[P.mats[i].bucket].op == op) castMats.push_back(i);
+  const size_t esz = op == OP_F32 ? 4 : 2;
+  for (size_t c0 = 0; c0 < castMats.size(); c0 += kMaxUser) {
     CastLaunch L;
     std::memset(&L, 0, sizeof(L));
     L.srcDtype = P.forStep ? MUON_DTYPE_F32 : srcDtype;
-    L.outOp = P.op;
+    L.outOp = op;
     L.sX = sc.sX;
     L.alpha = alpha;
     L.nesterov = P.forStep ? V.nesterov : 0;
     L.gradDtype = V.gradDtype;
     L.beta = beta;
-    const size_t cn = std::min(live.size() - c0, (size_t)kMaxUser);
+    const size_t cn = std::min(castMats.size() - c0, (size_t)kMaxUser);
     int64_t blocks = 0;
     double bytes = 0;
     for (size_t k = 0; k < cn; ++k) {
-      const int i = live[c0 + k];
+      const int i = castMats[c0 + k];
       const MatPlan& mp = P.mats[i];
       const BucketPlan& bp = P.buckets[mp.bucket];
       CastMat& C = L.mat[k];
@@ -271,15 +275,19 @@ muon_status_t enqueue(const Plan& P, const std::vector<CallerMat>& cm, int srcDt
     muon_status_t s = Lr.run(2, bytes, "cast kernel", [&] { return launch_cast(L, blocks, st); });
     if (s != MUON_OK) return s;
   }
+  }
 
-  // Tile configurations present, each launched separately.
-  std::vector<int> tiles;
-  for (const GroupPlan& g : P.groups)
-    if (std::find(tiles.begin(), tiles.end(), g.tile) == tiles.end()) tiles.push_back(g.tile);
+  // Kernel configurations (tile, operand type) present, each launched
+  // separately.
+  std::vector<std::pair<int, int>> cfgs;
+  for (const GroupPlan& g : P.groups) {
+    const auto cf = std::make_pair(g.tile, g.op);
+    if (std::find(cfgs.begin(), cfgs.end(), cf) == cfgs.end()) cfgs.push_back(cf);
+  }
 
   // Helper: launch a list of segments (≤ kMaxSegs per launch).
-  auto launch_segs = [&](int tile, std::vector<GemmSeg>& segs, std::vector<double>& works, int kind,
-                         const char* what) -> muon_status_t {
+  auto launch_segs = [&](int tile, int op, std::vector<GemmSeg>& segs, std::vector<double>& works,
+                         int kind, const char* what) -> muon_status_t {
     for (const GemmSeg& S : segs)
       if (tile == 256 && (S.in32 || S.out32))
         return fail(MUON_ERR_UNSUPPORTED, "internal: fp32 state on a 256-tile launch");
@@ -300,7 +308,7 @@ muon_status_t enqueue(const Plan& P, const std::vector<CallerMat>& cm, int srcDt
       L.nseg = (int)ns;
       int k = kind;
       if (kind == 4 && tile == 256) k = (L.seg[0].epi == EPI_AXPY) ? 6 : 7;
-      muon_status_t s = Lr.run(k, work, what, [&] { return launch_gemm(P.op, tile, L, blocks, st); });
+      muon_status_t s = Lr.run(k, work, what, [&] { return launch_gemm(op, tile, L, blocks, st); });
       if (s != MUON_OK) return s;
     }
     return MUON_OK;
@@ -328,11 +336,11 @@ muon_status_t enqueue(const Plan& P, const std::vector<CallerMat>& cm, int srcDt
   auto symflops = [](const GroupPlan& g) { return (double)g.count * g.m * g.m * (double)(g.m + 1); };
 
   // 4. SYRK per stored shape
-  for (int tile : tiles) {
+  for (const auto& [tile, op] : cfgs) {
     std::vector<GemmSeg> segs;
     std::vector<double> works;
     for (const GroupPlan& g : P.groups) {
-      if (g.tile != tile) continue;
+      if (g.tile != tile || g.op != op) continue;
       for (int bi : g.buckets) {
         const BucketPlan& bp = P.buckets[bi];
         GemmSeg S = sym_seg(g, tile);
@@ -355,7 +363,7 @@ muon_status_t enqueue(const Plan& P, const std::vector<CallerMat>& cm, int srcDt
         works.push_back((double)bp.mats.size() * bp.m * (double)(bp.m + 1) * bp.n);
       }
     }
-    muon_status_t s = launch_segs(tile, segs, works, 3, "SYRK kernel");
+    muon_status_t s = launch_segs(tile, op, segs, works, 3, "SYRK kernel");
     if (s != MUON_OK) return s;
   }
 
@@ -365,12 +373,12 @@ muon_status_t enqueue(const Plan& P, const std::vector<CallerMat>& cm, int srcDt
   int qcur = 0;  // Qh buffer holding the current Q
   for (int k = 0; k < P.steps; ++k) {
     const bool hasQ = k >= 1, hasA = k <= P.steps - 2;
-    for (int tile : tiles) {
+    for (const auto& [tile, op] : cfgs) {
       // (i) A² → B (and Q₁ at k = 0)
       std::vector<GemmSeg> segs;
       std::vector<double> works;
       for (const GroupPlan& g : P.groups) {
-        if (g.tile != tile) continue;
+        if (g.tile != tile || g.op != op) continue;
         GemmSeg S = sym_seg(g, tile);
         S.A = S.B = S.inh = at<char>(ws, g.offAh);
         S.in32 = f32(g, g.offA32);
@@ -390,13 +398,13 @@ muon_status_t enqueue(const Plan& P, const std::vector<CallerMat>& cm, int srcDt
         segs.push_back(S);
         works.push_back(symflops(g));
       }
-      muon_status_t s = launch_segs(tile, segs, works, 4, "Gram A^2 kernel");
+      muon_status_t s = launch_segs(tile, op, segs, works, 4, "Gram A^2 kernel");
       if (s != MUON_OK) return s;
       // (ii) Q ← a·Q + B·Q and P·A = a·A + B·A
       segs.clear();
       works.clear();
       for (const GroupPlan& g : P.groups) {
-        if (g.tile != tile) continue;
+        if (g.tile != tile || g.op != op) continue;
         if (hasQ) {
           GemmSeg S = sym_seg(g, tile);
           S.A = at<char>(ws, g.offBh);
@@ -428,14 +436,14 @@ muon_status_t enqueue(const Plan& P, const std::vector<CallerMat>& cm, int srcDt
           works.push_back(symflops(g));
         }
       }
-      s = launch_segs(tile, segs, works, 4, "Gram Q/PA kernel");
+      s = launch_segs(tile, op, segs, works, 4, "Gram Q/PA kernel");
       if (s != MUON_OK) return s;
       // (iii) A ← a·PA + B·PA
       if (hasA) {
         segs.clear();
         works.clear();
         for (const GroupPlan& g : P.groups) {
-          if (g.tile != tile) continue;
+          if (g.tile != tile || g.op != op) continue;
           GemmSeg S = sym_seg(g, tile);
           S.A = at<char>(ws, g.offBh);
           S.B = S.inh = at<char>(ws, g.offPAh);
@@ -451,7 +459,7 @@ muon_status_t enqueue(const Plan& P, const std::vector<CallerMat>& cm, int srcDt
           segs.push_back(S);
           works.push_back(symflops(g));
         }
-        s = launch_segs(tile, segs, works, 4, "Gram A-update kernel");
+        s = launch_segs(tile, op, segs, works, 4, "Gram A-update kernel");
         if (s != MUON_OK) return s;
       }
     }
@@ -510,7 +518,7 @@ muon_status_t enqueue(const Plan& P, const std::vector<CallerMat>& cm, int srcDt
       L.segStart[1] = blocks;
       const double work = 2.0 * (double)cn * bp.m * (double)bp.m * bp.n;
       muon_status_t s = Lr.run(5, work, "final product kernel",
-                               [&] { return launch_gemm(P.op, tile, L, blocks, st); });
+                               [&] { return launch_gemm(g.op, tile, L, blocks, st); });
       if (s != MUON_OK) return s;
     }
   }

@@ -105,12 +105,12 @@ std::string build_plan(const int64_t* rows, const int64_t* cols, int count, int 
   P.b = b;
   P.c = c;
   P.mats.resize(count);
-  const size_t esz = (op == OP_F32) ? 4 : 2;
+  auto esz_of = [](int o) -> size_t { return o == OP_F32 ? 4 : 2; };
 
   // buckets keyed by stored shape, groups keyed by m; both in order of first
   // appearance so the plan is a pure function of the shape list.
   std::map<std::pair<int64_t, int64_t>, int> bucketOf;
-  std::map<int64_t, int> groupOf;
+  std::map<std::pair<int64_t, int>, int> groupOf;  // (m, op)
   for (int i = 0; i < count; ++i) {
     MatPlan& mp = P.mats[i];
     mp.rows = rows[i];
@@ -130,6 +130,7 @@ std::string build_plan(const int64_t* rows, const int64_t* cols, int count, int 
       bp.m = mp.m;
       bp.n = mp.n;
       bp.tall = mp.tall;
+      bp.op = (op == OP_F32 || needs_f32(bp.m, bp.n)) ? OP_F32 : OP_F16;
       it = bucketOf.emplace(key, (int)P.buckets.size()).first;
       P.buckets.push_back(bp);
     }
@@ -139,11 +140,13 @@ std::string build_plan(const int64_t* rows, const int64_t* cols, int count, int 
   }
   for (int bi = 0; bi < (int)P.buckets.size(); ++bi) {
     BucketPlan& bp = P.buckets[bi];
-    auto it = groupOf.find(bp.m);
+    const auto gkey = std::make_pair(bp.m, bp.op);
+    auto it = groupOf.find(gkey);
     if (it == groupOf.end()) {
       GroupPlan gp;
       gp.m = bp.m;
-      it = groupOf.emplace(bp.m, (int)P.groups.size()).first;
+      gp.op = bp.op;
+      it = groupOf.emplace(gkey, (int)P.groups.size()).first;
       P.groups.push_back(gp);
     }
     GroupPlan& gp = P.groups[it->second];
@@ -156,8 +159,8 @@ std::string build_plan(const int64_t* rows, const int64_t* cols, int count, int 
     // fp16 operands lose the relative accuracy of the small eigenvalues of A
     // unless the a·A terms of the A-chain are carried in fp32; only the
     // 128-tile kernel carries that state.
-    gp.state32 = (op == OP_F16) && gp.m <= kState32MaxM;
-    gp.tile = gp.state32 ? 128 : choose_tile(op, gp.m, gp.count);
+    gp.state32 = (gp.op == OP_F16) && gp.m <= kState32MaxM;
+    gp.tile = gp.state32 ? 128 : choose_tile(gp.op, gp.m, gp.count);
     gp.Mp = round_up(gp.m, gp.tile);
   }
   for (BucketPlan& bp : P.buckets) {
@@ -187,7 +190,7 @@ std::string build_plan(const int64_t* rows, const int64_t* cols, int count, int 
   P.offAlpha = off;
   off = align_up(off + size_t(count) * 4);
   for (GroupPlan& gp : P.groups) {
-    gp.strideh = size_t(gp.Mp) * size_t(gp.Mp) * esz;
+    gp.strideh = size_t(gp.Mp) * size_t(gp.Mp) * esz_of(gp.op);
     const size_t nh = gp.strideh * gp.count;
     gp.offAh = off;   off = align_up(off + nh);
     gp.offBh = off;   off = align_up(off + nh);
@@ -201,11 +204,13 @@ std::string build_plan(const int64_t* rows, const int64_t* cols, int count, int 
     }
   }
   for (BucketPlan& bp : P.buckets) {
-    bp.strideX = size_t(bp.Mp) * size_t(bp.Np) * esz;
+    bp.strideX = size_t(bp.Mp) * size_t(bp.Np) * esz_of(bp.op);
     bp.offXh = off;  off = align_up(off + bp.strideX * bp.mats.size());
     bp.offXTh = off; off = align_up(off + bp.strideX * bp.mats.size());
   }
   P.totalBytes = off;
+  // Power-of-two scales are exact in fp32 too, so fp32 groups of a
+  // half-precision plan share its scales.
   P.scales = make_scales(op, steps, a, b, c);
   return std::string();
 }
@@ -219,6 +224,7 @@ std::string Plan::json() const {
   for (size_t g = 0; g < groups.size(); ++g) {
     const GroupPlan& gp = groups[g];
     o << (g ? "," : "") << "{\"m\":" << gp.m << ",\"Mp\":" << gp.Mp << ",\"tile\":" << gp.tile
+      << ",\"op\":\"" << (gp.op == OP_F32 ? "f32" : "f16") << "\""
       << ",\"state32\":" << (gp.state32 ? "true" : "false")
       << ",\"count\":" << gp.count << ",\"buckets\":[";
     for (size_t k = 0; k < gp.buckets.size(); ++k) o << (k ? "," : "") << gp.buckets[k];
@@ -229,7 +235,8 @@ std::string Plan::json() const {
   for (size_t bi = 0; bi < buckets.size(); ++bi) {
     const BucketPlan& bp = buckets[bi];
     o << (bi ? "," : "") << "{\"rows\":" << bp.rows << ",\"cols\":" << bp.cols << ",\"m\":" << bp.m
-      << ",\"n\":" << bp.n << ",\"tall\":" << (bp.tall ? "true" : "false") << ",\"group\":"
+      << ",\"n\":" << bp.n << ",\"tall\":" << (bp.tall ? "true" : "false") << ",\"op\":\""
+      << (bp.op == OP_F32 ? "f32" : "f16") << "\",\"group\":"
       << bp.group << ",\"Mp\":" << bp.Mp << ",\"Np\":" << bp.Np << ",\"gram_start\":"
       << bp.gramStart << ",\"mats\":[";
     for (size_t k = 0; k < bp.mats.size(); ++k) o << (k ? "," : "") << bp.mats[k];

@@ -28,6 +28,7 @@ struct MatPlan {
 struct BucketPlan {
   int64_t rows = 0, cols = 0, m = 0, n = 0;
   bool tall = false;
+  int op = 0;               // OpType of this bucket's operand copies
   int group = -1;
   int64_t Mp = 0, Np = 0;   // padded m, n
   std::vector<int> mats;    // matrix indices in call order
@@ -40,6 +41,7 @@ struct BucketPlan {
 // Matrices of one Gram size m: they share every Gram-space launch.
 struct GroupPlan {
   int64_t m = 0, Mp = 0;
+  int op = 0;               // OpType of the group's MFMA operands
   int tile = 128;
   int count = 0;
   std::vector<int> buckets;
@@ -61,7 +63,7 @@ struct ScalePlan {
 };
 
 struct Plan {
-  int op = 0;              // OpType of the MFMA operands
+  int op = 0;              // requested OpType (groups may use fp32, see below)
   int steps = 0;
   bool forStep = false;
   float a = 0, b = 0, c = 0;
@@ -83,8 +85,17 @@ int tile_override();
 // half-precision path (smaller, worse-conditioned Gram matrices need it).
 constexpr int64_t kState32MaxM = 2048;
 
-// Build the plan.  `op` selects operand type (OP_F16 / OP_F32).  Returns an
-// empty string on success, else a message.
+// Small, nearly square matrices run in fp32 MFMA even on the half-precision
+// path: their smallest singular values sit near zero, where 5 quintic steps
+// amplify input perturbations ≈ a⁵ ≈ 490×, and fp16 operands then miss the
+// bf16 tolerance (measured 1–3% for 32–128 squares).  The fp32 products cost
+// little at these sizes.
+constexpr int64_t kF32NearSquareMaxM = 1024;
+inline bool needs_f32(int64_t m, int64_t n) { return m <= kF32NearSquareMaxM && n <= 2 * m; }
+
+// Build the plan.  `op` selects operand type (OP_F16 / OP_F32); with OP_F16
+// the groups that needs_f32 selects use OP_F32.  Returns an empty string on
+// success, else a message.
 std::string build_plan(const int64_t* rows, const int64_t* cols, int count, int op, int steps,
                        float a, float b, float c, bool forStep, Plan* plan);
 

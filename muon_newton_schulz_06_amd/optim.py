@@ -1,0 +1,130 @@
+"""`torch.optim` front end of the library: Muon for 2-D weight matrices.
+
+The optimiser step is the owner-side update of the DMuon technical summary
+(gist.science, Korean), §1 and §2.2 — momentum, Frobenius normalisation,
+Newton–Schulz in the Gram formulation, shape-scaled update — used as a
+drop-in optimiser module (§3 of the same page: the module replaces the
+optimiser and changes nothing else in the training framework).  Every step
+runs in the library's HIP kernels through `muon_step` / `muon_step_ex`;
+this class only groups tensors and keeps the momentum state.
+
+Only 2-D parameters are accepted (Muon orthogonalises matrices; biases,
+norms and embeddings belong in another optimiser).  Parameters may be bf16
+or fp32, gradients fp32 or bf16; the momentum is always kept in fp32.
+"""
+from __future__ import annotations
+
+import itertools
+import math
+
+import torch
+
+from . import QUINTIC, muon_step
+
+
+class Muon(torch.optim.Optimizer):
+    """Muon with Gram Newton–Schulz orthogonalisation on the GPU.
+
+    Arguments (per parameter group):
+      lr:              learning rate; the update of a rows × cols matrix is
+                       scaled by lr·√max(1, rows/cols)
+      momentum:        β of M ← β·M + g
+      nesterov:        orthogonalise g + β·M (after the update) instead of M
+      weight_decay:    decoupled, W ← (1 − lr·weight_decay)·W − lr·sc·O
+      ns_steps:        Newton–Schulz steps (0–64)
+      ns_coefficients: (a, b, c) of X ← a·X + (b·A + c·A²)·X, A = X·Xᵀ
+      eps:             added to ‖M‖_F before normalising
+    """
+
+    def __init__(self, params, lr: float = 0.02, momentum: float = 0.95, nesterov: bool = False,
+                 weight_decay: float = 0.0, ns_steps: int = 5, ns_coefficients=QUINTIC,
+                 eps: float = 1e-7):
+        defaults = dict(lr=lr, momentum=momentum, nesterov=nesterov, weight_decay=weight_decay,
+                        ns_steps=ns_steps, ns_coefficients=tuple(ns_coefficients), eps=eps)
+        _check_hyper(defaults)
+        super().__init__(params, defaults)
+        for group in self.param_groups:
+            _check_hyper(group)
+            for p in group["params"]:
+                if p.dim() != 2:
+                    raise ValueError(f"Muon takes 2-D parameters only, got shape {tuple(p.shape)}")
+                if p.dtype not in (torch.float32, torch.bfloat16):
+                    raise TypeError(f"parameter dtype {p.dtype} (use float32 or bfloat16)")
+
+    def add_param_group(self, param_group):
+        super().add_param_group(param_group)
+        _check_hyper(self.param_groups[-1])
+
+    @torch.no_grad()
+    def step(self, closure=None):
+        loss = None
+        if closure is not None:
+            with torch.enable_grad():
+                loss = closure()
+        for group in self.param_groups:
+            # one batched library call per (device, param dtype, grad dtype)
+            parts: dict = {}
+            for p in group["params"]:
+                if p.grad is None:
+                    continue
+                g = p.grad
+                if g.is_sparse:
+                    raise RuntimeError("Muon does not support sparse gradients")
+                if g.dtype not in (torch.float32, torch.bfloat16):
+                    raise TypeError(f"gradient dtype {g.dtype} (use float32 or bfloat16)")
+                if not p.is_contiguous():
+                    raise ValueError("Muon updates parameters in place and needs them contiguous")
+                st = self.state[p]
+                buf = st.get("momentum_buffer")
+                if buf is None:
+                    buf = torch.zeros(p.shape, dtype=torch.float32, device=p.device)
+                    st["momentum_buffer"] = buf
+                elif buf.dtype != torch.float32 or not buf.is_contiguous():
+                    buf = buf.to(torch.float32).contiguous()
+                    st["momentum_buffer"] = buf
+                key = (p.device, p.dtype, g.dtype)
+                ps, gs, ms = parts.setdefault(key, ([], [], []))
+                ps.append(p)
+                gs.append(g.contiguous())
+                ms.append(buf)
+            for (dev, _, _), (ps, gs, ms) in parts.items():
+                muon_step(ps, gs, ms, beta=group["momentum"], lr=group["lr"],
+                          steps=group["ns_steps"], coeffs=group["ns_coefficients"],
+                          eps=group["eps"], nesterov=group["nesterov"],
+                          weight_decay=group["weight_decay"],
+                          stream=torch.cuda.current_stream(dev) if dev.type == "cuda" else None)
+        return loss
+
+    def load_state_dict(self, state_dict):
+        """torch's loader casts floating-point state to the parameter dtype;
+        the momentum is fp32 state whatever the parameter dtype, so the saved
+        fp32 buffers are put back after the base class has loaded."""
+        saved = {pid: s["momentum_buffer"] for pid, s in state_dict["state"].items()
+                 if isinstance(s, dict) and "momentum_buffer" in s}
+        super().load_state_dict(state_dict)
+        ids = itertools.chain.from_iterable(g["params"] for g in state_dict["param_groups"])
+        params = itertools.chain.from_iterable(g["params"] for g in self.param_groups)
+        for pid, p in zip(ids, params):
+            if pid in saved:
+                self.state[p]["momentum_buffer"] = saved[pid].to(
+                    device=p.device, dtype=torch.float32).contiguous()
+
+
+def _check_hyper(h):
+    def finite(x):
+        return isinstance(x, (int, float)) and math.isfinite(float(x))
+    if not finite(h["lr"]) or h["lr"] < 0:
+        raise ValueError(f"invalid lr {h['lr']}")
+    if not finite(h["momentum"]):
+        raise ValueError(f"invalid momentum {h['momentum']}")
+    if not finite(h["weight_decay"]) or h["weight_decay"] < 0:
+        raise ValueError(f"invalid weight_decay {h['weight_decay']}")
+    if not finite(h["eps"]) or h["eps"] < 0:
+        raise ValueError(f"invalid eps {h['eps']}")
+    if not isinstance(h["ns_steps"], int) or not 0 <= h["ns_steps"] <= 64:
+        raise ValueError(f"invalid ns_steps {h['ns_steps']}")
+    c = tuple(h["ns_coefficients"])
+    if len(c) != 3 or not all(finite(v) for v in c):
+        raise ValueError(f"invalid ns_coefficients {c}")
+    if not isinstance(h["nesterov"], bool):
+        raise ValueError(f"nesterov must be a bool, got {h['nesterov']!r}")

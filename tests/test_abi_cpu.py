@@ -232,17 +232,42 @@ def test_plan_workspace_matches_layout():
     assert p["workspace_bytes"] == mns.ns_workspace_size(shapes)
     assert p["workspace_bytes"] % 256 == 0
     total = 0
+    esz = {"f16": 2, "f32": 4}
     for g in p["groups"]:
-        total += 10 * g["Mp"] ** 2 * g["count"]  # 5 fp16 m×m operand copies
+        total += 5 * esz[g["op"]] * g["Mp"] ** 2 * g["count"]  # 5 m×m operand copies
         if g["state32"]:
             total += 8 * g["Mp"] ** 2 * g["count"]  # fp32 A and P·A
     for b in p["buckets"]:
-        total += 2 * 2 * b["Mp"] * b["Np"] * len(b["mats"])
+        total += 2 * esz[b["op"]] * b["Mp"] * b["Np"] * len(b["mats"])
     assert p["workspace_bytes"] >= total
     assert p["workspace_bytes"] - total < 256 * (3 + 8 * len(p["groups"]) + 2 * len(p["buckets"])) + 4 * 1000
     # small Gram sizes keep fp32 A-chain state on the 128-tile kernel
     assert all(g["state32"] == (g["m"] <= 2048) and (not g["state32"] or g["tile"] == 128)
                for g in p["groups"])
+
+
+def test_plan_small_near_square_matrices_use_fp32_products():
+    """On the half-precision path, matrices with m ≤ 1024 and n ≤ 2m run in
+    fp32 MFMA (their smallest singular values make fp16 operands miss the
+    bf16 tolerance); a Gram size can then appear in two groups."""
+    shapes = [(64, 64), (300, 500), (1000, 1024), (1024, 3000), (2048, 2048), (96, 200),
+              (512, 512), (3584, 512)]
+    for for_step in (True, False):
+        p = mns.describe_plan(shapes, for_step=for_step)
+        op = {(b["rows"], b["cols"]): b["op"] for b in p["buckets"]}
+        assert op == {(64, 64): "f32", (300, 500): "f32", (1000, 1024): "f32",
+                      (1024, 3000): "f16", (2048, 2048): "f16", (96, 200): "f16",
+                      (512, 512): "f32", (3584, 512): "f16"}
+        for b in p["buckets"]:
+            assert p["groups"][b["group"]]["op"] == b["op"]
+        g512 = sorted(g["op"] for g in p["groups"] if g["m"] == 512)
+        assert g512 == ["f16", "f32"]
+        for g in p["groups"]:
+            if g["op"] == "f32":
+                assert not g["state32"] and g["tile"] == 128
+    # the Qwen2.5-7B set has no such matrix
+    q = mns.describe_plan([(3584, 3584), (512, 3584), (18944, 3584), (3584, 18944)], for_step=True)
+    assert all(g["op"] == "f16" for g in q["groups"])
 
 
 def test_plan_f32_uses_unit_scales():

@@ -314,6 +314,30 @@ def test_muon_step_fp32_params_expose_the_update(mns):
         assert e <= TOL_BF16
 
 
+def test_muon_step_small_near_square_runs_in_fp32(mns):
+    """Small, nearly square matrices take fp32 products (their smallest
+    singular values make fp16 operands miss the bf16 bound): the update
+    recovered from fp32 weights must meet the fp32 bound, over two steps."""
+    shapes = [(32, 32), (64, 64), (128, 128), (300, 500), (700, 400)]
+    inp = W.muon_inputs(shapes, 61, device="cuda", param_dtype=torch.float32)
+    host_M = [m.cpu().numpy() for m in inp.momenta]
+    c32 = tuple(float(np.float32(v)) for v in oracle.QUINTIC)
+    for step in range(2):
+        grads = inp.grads if step == 0 else W.fresh_grads(shapes, 61, step, device="cuda")
+        for p in inp.params:
+            p.zero_()
+        mns.muon_step(inp.params, grads, inp.momenta, beta=0.95, lr=0.02, steps=5)
+        torch.cuda.synchronize()
+        for j, (r, c) in enumerate(shapes):
+            Mn = oracle.momentum_update(host_M[j], grads[j].cpu().numpy(), np.float32(0.95))
+            host_M[j] = Mn
+            lrsc = float(np.float32(0.02)) * oracle.lr_shape_scale(r, c)
+            O_gpu = -inp.params[j].double().cpu().numpy() / lrsc
+            e = rel(O_gpu, oracle.muon_orthogonalize(Mn, c32, 5, 1e-7))
+            say("step", step, shapes[j], "rel err of update", e)
+            assert e <= TOL_F32
+
+
 def test_single_hip_runtime_in_process(mns):
     x = W.gaussian((32, 64), 1, device="cuda")
     mns.muon_ns_batched([x])
