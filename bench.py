@@ -11,8 +11,11 @@ parameters, bf16 weights, fp32 gradients and momentum (seeded synthetic data).
 
 Prints one JSON line: whole-step throughput in algorithmic TFLOP/s (Gram
 formulation; symmetric products count their upper triangle only), the
-roofline of the dominant kernel (HIP events over the timed region) and the
-fp64 CPU oracle timed on a bounded sample of the same workload.
+roofline of the dominant kernel (HIP events over the timed region), the
+fp64 CPU oracle timed on a bounded sample of the same workload, and (under
+"other_configs", unless --no-other-configs) the smaller workloads timed in
+the same run: one 256×1024 fp32 matrix, 32 × 1024×4096 bf16, the
+176-matrix small-shape mix and one Qwen2.5-7B-shaped layer.
 """
 from __future__ import annotations
 
@@ -104,6 +107,52 @@ def cpu_baseline(budget_s=30.0):
                       f"(fp64 numpy, standard NS), {dt:.2f} s; algorithmic Gram flops / time"}
 
 
+def other_configs(mns, W, torch):
+    """ms per call, matrices/s and algorithmic TFLOP/s of the smaller
+    workloads (HIP events on the current stream, after one warm-up call)."""
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        e1.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    def entry(name, ms, shapes, peak, note):
+        fl = gram_flops(shapes)
+        return {"workload": name, "ms": ms, "matrices_per_s": len(shapes) / (ms / 1e3),
+                "tflops": fl / (ms / 1e3) / 1e12, "frac_peak": fl / (ms / 1e3) / 1e12 / peak,
+                "note": note}
+
+    out = []
+    x = W.ns_single(device="cuda")
+    out.append(entry("single 256x1024 fp32", timed(lambda: mns.muon_ns_batched([x], steps=5), 50),
+                     [(256, 1024)], MFMA_PEAK_F32, "muon_ns_batched, fp32 MFMA, latency-bound"))
+    xs = W.ns_uniform_batch(device="cuda")
+    outs = [torch.empty_like(t) for t in xs]
+    out.append(entry("uniform 32x(1024x4096) bf16",
+                     timed(lambda: mns.muon_ns_batched(xs, outs=outs, steps=5), 10),
+                     [tuple(t.shape) for t in xs], MFMA_PEAK_F16, "muon_ns_batched"))
+    del xs, outs
+    ms_ = W.ns_small_mix(device="cuda")
+    outs = [torch.empty_like(t) for t in ms_]
+    out.append(entry("small mix 176 bf16",
+                     timed(lambda: mns.muon_ns_batched(ms_, outs=outs, steps=5), 20),
+                     [tuple(t.shape) for t in ms_], MFMA_PEAK_F16, "muon_ns_batched"))
+    del ms_, outs
+    shapes = W.qwen_model_shapes(1)
+    inp = W.muon_inputs(shapes, 4001, device="cuda")
+    out.append(entry("one Qwen2.5-7B layer muon_step",
+                     timed(lambda: mns.muon_step(inp.params, inp.grads, inp.momenta, steps=5), 10),
+                     shapes, MFMA_PEAK_F16, "muon_step"))
+    del inp
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -111,6 +160,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="qwen_full")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="time only the main workload (profiling runs)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB read + 1 GiB write kernel (counter calibration)")
     args = ap.parse_args()
@@ -196,6 +247,12 @@ def main():
                 "frac": achieved / MFMA_PEAK_F16, "traffic": traffic_for(dom, args.workload),
                 "avg_launch_ms": avg_s * 1e3, "algorithmic_flops_per_launch": per_launch,
                 "launches": d["launches"]}
+    others = None
+    if not args.no_other_configs:
+        del inp, ws
+        torch.cuda.empty_cache()
+        print("[bench] timing the smaller workloads", file=sys.stderr, flush=True)
+        others = other_configs(mns, W, torch)
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
@@ -211,7 +268,10 @@ def main():
                    "mfma_operands": "f16 (power-of-two scaled)", "accumulate": "f32",
                    "algorithmic_tflop_per_step": F / 1e12, "parallelism": "single GPU"},
         "frac_mfma_peak": tflops / MFMA_PEAK_F16,
+        "matrices_per_s": len(shapes) / (ms / 1e3),
+        "elementwise_gbs": {k: breakdown[k]["gbs"] for k in ("momentum", "cast") if k in breakdown},
         "roofline": roofline, "breakdown": breakdown, "cpu_baseline": cpu,
+        "other_configs": others,
     }
     print(json.dumps(line), flush=True)
 

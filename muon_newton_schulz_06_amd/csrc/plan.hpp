@@ -82,7 +82,7 @@ struct Plan {
 int tile_override();
 
 // Largest Gram size m that keeps fp32 state for the A-chain on the
-// half-precision path (smaller, worse-conditioned Gram matrices need it).
+// half-precision path, for groups holding nearly square matrices (n ≤ 2m).
 constexpr int64_t kState32MaxM = 2048;
 
 // Small, nearly square matrices run in fp32 MFMA even on the half-precision

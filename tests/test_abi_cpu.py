@@ -241,9 +241,13 @@ def test_plan_workspace_matches_layout():
         total += 2 * esz[b["op"]] * b["Mp"] * b["Np"] * len(b["mats"])
     assert p["workspace_bytes"] >= total
     assert p["workspace_bytes"] - total < 256 * (3 + 8 * len(p["groups"]) + 2 * len(p["buckets"])) + 4 * 1000
-    # small Gram sizes keep fp32 A-chain state on the 128-tile kernel
-    assert all(g["state32"] == (g["m"] <= 2048) and (not g["state32"] or g["tile"] == 128)
-               for g in p["groups"])
+    # fp16 groups of nearly square matrices with m ≤ 2048 keep fp32 A-chain
+    # state on the 128-tile kernel; wide matrices run state-free
+    assert not any(g["state32"] for g in p["groups"])
+    q = mns.describe_plan([(1500, 1600), (1500, 6000), (2100, 2100), (512, 4096)], for_step=True)
+    st = {g["m"]: (g["state32"], g["tile"], g["op"]) for g in q["groups"]}
+    assert st[1500] == (True, 128, "f16")    # holds a nearly square bucket
+    assert st[2100][0] is False and st[512][0] is False
 
 
 def test_plan_small_near_square_matrices_use_fp32_products():
