@@ -960,6 +960,8 @@ hipError_t launch_epi(int op, int tile, const GemmLaunch& L, int blocks, hipStre
     hipLaunchKernelGGL((gemm_kernel<_Float16, 128, 128, 2, 2, EPI>), dim3(blocks), dim3(256), 0, st, L);
   } else if (op == OP_F32 && tile == 128) {
     hipLaunchKernelGGL((gemm_kernel<float, 128, 128, 2, 2, EPI>), dim3(blocks), dim3(256), 0, st, L);
+  } else if (op == OP_F32 && tile == 64) {
+    hipLaunchKernelGGL((gemm_kernel<float, 64, 64, 2, 2, EPI>), dim3(blocks), dim3(256), 0, st, L);
   } else {
     return hipErrorInvalidValue;
   }

@@ -32,8 +32,12 @@ float pow2_scale(double bound) {
 }
 
 int choose_tile(int op, int64_t m, int count) {
-  (void)count;
-  if (op == OP_F32) return 128;
+  if (op == OP_F32) {
+    // fp32 products are latency-bound for small groups: 64-tiles give four
+    // times the workgroups when 128-tiles would not fill the 256 CUs twice.
+    const int64_t t = (m + 127) / 128;
+    return double(count) * double(t * (t + 1) / 2) < 512.0 ? 64 : 128;
+  }
   int ov = tile_override();
   if (ov) return ov;
   // The 256-tile kernel (direct-to-LDS ring, staged epilogues) is several
