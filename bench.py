@@ -121,16 +121,33 @@ def other_configs(mns, W, torch):
         e1.synchronize()
         return e0.elapsed_time(e1) / reps
 
-    def entry(name, ms, shapes, peak, note):
+    def entry(name, ms, shapes, peak, note, ms_graph=None):
         fl = gram_flops(shapes)
-        return {"workload": name, "ms": ms, "matrices_per_s": len(shapes) / (ms / 1e3),
-                "tflops": fl / (ms / 1e3) / 1e12, "frac_peak": fl / (ms / 1e3) / 1e12 / peak,
-                "note": note}
+        e = {"workload": name, "ms": ms, "matrices_per_s": len(shapes) / (ms / 1e3),
+             "tflops": fl / (ms / 1e3) / 1e12, "frac_peak": fl / (ms / 1e3) / 1e12 / peak,
+             "note": note}
+        if ms_graph is not None:
+            e["ms_graph_replay"] = ms_graph
+            e["matrices_per_s_graph_replay"] = len(shapes) / (ms_graph / 1e3)
+        return e
+
+    def graph_ms(fn, reps):
+        """The same call captured once into a HIP graph, then replayed."""
+        fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        return timed(g.replay, reps)
 
     out = []
     x = W.ns_single(device="cuda")
-    out.append(entry("single 256x1024 fp32", timed(lambda: mns.muon_ns_batched([x], steps=5), 50),
-                     [(256, 1024)], MFMA_PEAK_F32, "muon_ns_batched, fp32 MFMA, latency-bound"))
+    xo = [torch.empty_like(x)]
+    wsx = torch.empty(mns.ns_workspace_size([tuple(x.shape)], dtype=torch.float32),
+                      dtype=torch.uint8, device="cuda")
+    f1 = lambda: mns.muon_ns_batched([x], outs=xo, steps=5, workspace=wsx)  # noqa: E731
+    out.append(entry("single 256x1024 fp32", timed(f1, 50), [(256, 1024)], MFMA_PEAK_F32,
+                     "muon_ns_batched, fp32 MFMA, latency-bound", graph_ms(f1, 50)))
     xs = W.ns_uniform_batch(device="cuda")
     outs = [torch.empty_like(t) for t in xs]
     out.append(entry("uniform 32x(1024x4096) bf16",
@@ -139,9 +156,11 @@ def other_configs(mns, W, torch):
     del xs, outs
     ms_ = W.ns_small_mix(device="cuda")
     outs = [torch.empty_like(t) for t in ms_]
-    out.append(entry("small mix 176 bf16",
-                     timed(lambda: mns.muon_ns_batched(ms_, outs=outs, steps=5), 20),
-                     [tuple(t.shape) for t in ms_], MFMA_PEAK_F16, "muon_ns_batched"))
+    wsm = torch.empty(mns.ns_workspace_size([tuple(t.shape) for t in ms_]), dtype=torch.uint8,
+                      device="cuda")
+    f3 = lambda: mns.muon_ns_batched(ms_, outs=outs, steps=5, workspace=wsm)  # noqa: E731
+    out.append(entry("small mix 176 bf16", timed(f3, 20), [tuple(t.shape) for t in ms_],
+                     MFMA_PEAK_F16, "muon_ns_batched", graph_ms(f3, 20)))
     del ms_, outs
     shapes = W.qwen_model_shapes(1)
     inp = W.muon_inputs(shapes, 4001, device="cuda")

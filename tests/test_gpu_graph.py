@@ -1,0 +1,56 @@
+"""The entry points enqueue only kernel launches on the caller's stream (no
+allocation, no memset, no host synchronisation), so a whole muon_step can be
+captured into a HIP graph and replayed.  Each replay is checked bitwise
+against the eager step it stands for, with eager work and synchronisations
+between the replays."""
+import pytest
+import torch
+
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def mns():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a HIP device")
+    import muon_newton_schulz_06_amd as m
+    m.load()
+    return m
+
+
+def test_muon_step_graph_replays_match_eager(mns):
+    shapes = [(256, 1024), (1024, 256), (128, 128), (512, 3584), (300, 700)]
+    base = W.muon_inputs(shapes, 123, device="cuda")
+    ws = torch.empty(mns.step_workspace_size(shapes), dtype=torch.uint8, device="cuda")
+
+    def clone(inp):
+        return ([p.clone() for p in inp.params], [g.clone() for g in inp.grads],
+                [m.clone() for m in inp.momenta])
+
+    # eager reference: three steps with the same gradients
+    ep, eg, em = clone(base)
+    eager = []
+    for _ in range(3):
+        mns.muon_step(ep, eg, em, workspace=ws, nesterov=True, weight_decay=0.01)
+        eager.append(([p.clone() for p in ep], [m.clone() for m in em]))
+    torch.cuda.synchronize()
+
+    gp, gg, gm = clone(base)
+    ws2 = torch.empty_like(ws)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        mns.muon_step(gp, gg, gm, workspace=ws2, nesterov=True, weight_decay=0.01)
+    # capture records the launches without running them
+    assert all(torch.equal(p, q) for p, q in zip(gp, base.params))
+    for step in range(3):
+        graph.replay()
+        torch.cuda.synchronize()
+        junk = torch.randn(1 << 20, device="cuda").sum()  # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.isfinite(junk)
+        for j in range(len(shapes)):
+            assert torch.equal(gp[j], eager[step][0][j]), ("weights", step, j)
+            assert torch.equal(gm[j], eager[step][1][j]), ("momentum", step, j)
