@@ -159,6 +159,26 @@ muon_status_t muon_describe_plan(const int64_t* rows, const int64_t* cols, int32
                                  int32_t for_step, muon_dtype_t dtype, int32_t steps,
                                  const float coeffs[3], char* buf, size_t buf_len);
 
+/* Tile table: the tile edge the planner uses for a Gram group, keyed by the
+ * group's size m, operand type (0: fp16 operands, 1: fp32 operands) and
+ * batch-size class floor(log2(number of matrices in the group)).  DMuon
+ * summary §2.4 tunes kernel configurations per shape at start-up and keeps
+ * them in a cache; `python -m muon_newton_schulz_06_amd.autotune` measures
+ * such a table and installs it with this call.
+ *   tile: 128 or 256 for fp16 groups, 64 or 128 for fp32 groups;
+ *   m ≥ 1, 0 ≤ count_class ≤ 31, at most 4096 entries.
+ * The table replaces the previous one process-wide (n = 0 clears it); groups
+ * without an entry use the built-in choice.  Groups that carry fp32 A-chain
+ * state always use 128.  An invalid entry leaves the table unchanged. */
+typedef struct muon_tile_entry {
+  int64_t m;
+  int32_t op;
+  int32_t count_class;
+  int32_t tile;
+} muon_tile_entry_t;
+
+muon_status_t muon_set_tile_table(const muon_tile_entry_t* entries, int32_t n);
+
 /* Kernel-time instrumentation.  While enabled, every launch the library
  * makes is bracketed by a pair of HIP events on the launch's stream and its
  * algorithmic work is recorded.  muon_profile_read waits for the recorded

@@ -23,7 +23,7 @@ import torch
 __all__ = [
     "QUINTIC", "CUBIC", "MuonError", "lib_path", "load", "muon_ns_batched", "muon_step",
     "ns_workspace_size", "step_workspace_size", "describe_plan", "profile_enable",
-    "profile_read", "abi_version", "PROFILE_KINDS",
+    "profile_read", "abi_version", "PROFILE_KINDS", "set_tile_table",
 ]
 
 QUINTIC = (3.4445, -4.7750, 2.0315)
@@ -56,6 +56,11 @@ class MuonError(RuntimeError):
 class MuonNsDesc(ctypes.Structure):
     _fields_ = [("x", ctypes.c_void_p), ("out", ctypes.c_void_p), ("rows", ctypes.c_int64),
                 ("cols", ctypes.c_int64), ("ld_x", ctypes.c_int64), ("ld_out", ctypes.c_int64)]
+
+
+class MuonTileEntry(ctypes.Structure):
+    _fields_ = [("m", ctypes.c_int64), ("op", ctypes.c_int32), ("count_class", ctypes.c_int32),
+                ("tile", ctypes.c_int32)]
 
 
 class MuonStepOpts(ctypes.Structure):
@@ -107,6 +112,8 @@ def load():
         L.muon_describe_plan.argtypes = [ctypes.POINTER(i64), ctypes.POINTER(i64), i32, i32, i32,
                                          i32, ctypes.POINTER(f32), ctypes.c_char_p, sz]
         L.muon_describe_plan.restype = i32
+        L.muon_set_tile_table.argtypes = [ctypes.POINTER(MuonTileEntry), i32]
+        L.muon_set_tile_table.restype = i32
         L.muon_profile_enable.argtypes = [i32]
         L.muon_profile_enable.restype = i32
         L.muon_profile_read.argtypes = [i32, ctypes.POINTER(ctypes.c_double),
@@ -313,6 +320,21 @@ def muon_step(params, grads, momenta, beta: float = 0.95, lr: float = 0.02, step
             _check(L.muon_step_ex(P, G, M, rows, cols, n, _dtype_code(pdt), float(beta),
                                   float(lr), int(steps), _coeffs(coeffs), float(eps),
                                   ctypes.byref(opts), wsp, ws_bytes, _stream_handle(stream, dev)))
+
+
+def set_tile_table(entries):
+    """Install the planner's tile table: an iterable of dicts with keys m, op
+    ("f16" or "f32"), count_class (floor(log2(matrices in the group))) and
+    tile.  An empty iterable clears it."""
+    entries = list(entries)
+    arr = (MuonTileEntry * max(len(entries), 1))()
+    for i, e in enumerate(entries):
+        op = e["op"]
+        arr[i].m = int(e["m"])
+        arr[i].op = {"f16": 0, "f32": 1}[op] if isinstance(op, str) else int(op)
+        arr[i].count_class = int(e["count_class"])
+        arr[i].tile = int(e["tile"])
+    _check(load().muon_set_tile_table(arr, len(entries)))
 
 
 def profile_enable(on: bool = True):

@@ -742,6 +742,23 @@ muon_status_t muon_step(void* const* params, const float* const* grads, float* c
                       beta, lr, steps, coeffs, eps, nullptr, workspace, workspace_bytes, stream);
 }
 
+muon_status_t muon_set_tile_table(const muon_tile_entry_t* entries, int32_t n) {
+  g_err.clear();
+  if (n < 0 || n > 4096) return fail(MUON_ERR_INVALID_ARG, "n outside [0, 4096]");
+  if (n > 0 && !entries) return fail(MUON_ERR_INVALID_ARG, "entries is NULL");
+  std::vector<std::pair<TileKey, int>> v;
+  for (int i = 0; i < n; ++i) {
+    const muon_tile_entry_t& e = entries[i];
+    const bool okTile = e.op == OP_F16 ? (e.tile == 128 || e.tile == 256)
+                                       : (e.op == OP_F32 && (e.tile == 64 || e.tile == 128));
+    if (e.m < 1 || e.count_class < 0 || e.count_class > 31 || !okTile)
+      return fail(MUON_ERR_INVALID_ARG, "tile entry " + std::to_string(i) + " is invalid");
+    v.push_back({TileKey{e.m, e.op, e.count_class}, e.tile});
+  }
+  set_tile_table(v);
+  return MUON_OK;
+}
+
 muon_status_t muon_profile_enable(int32_t on) {
   g_err.clear();
   g_prof_on = on != 0;

@@ -11,6 +11,7 @@
 #include <cmath>
 #include <cstdlib>
 #include <map>
+#include <mutex>
 #include <sstream>
 
 #include "common.hpp"
@@ -31,7 +32,11 @@ float pow2_scale(double bound) {
   return std::ldexp(1.0f, e);
 }
 
+std::mutex g_table_mu;
+std::map<TileKey, int> g_table;
+
 int choose_tile(int op, int64_t m, int count) {
+  if (const int t = tile_from_table(m, op, count)) return t;
   if (op == OP_F32) {
     // fp32 products are latency-bound for small groups: 64-tiles give four
     // times the workgroups when 128-tiles would not fill the 256 CUs twice.
@@ -51,6 +56,27 @@ int choose_tile(int op, int64_t m, int count) {
 }
 
 }  // namespace
+
+int count_class(int count) {
+  int c = 0;
+  while (count > 1) {
+    count >>= 1;
+    ++c;
+  }
+  return c;
+}
+
+void set_tile_table(const std::vector<std::pair<TileKey, int>>& entries) {
+  std::lock_guard<std::mutex> lk(g_table_mu);
+  g_table.clear();
+  for (const auto& e : entries) g_table[e.first] = e.second;
+}
+
+int tile_from_table(int64_t m, int op, int count) {
+  std::lock_guard<std::mutex> lk(g_table_mu);
+  auto it = g_table.find(TileKey{m, op, count_class(count)});
+  return it == g_table.end() ? 0 : it->second;
+}
 
 int tile_override() {
   const char* s = std::getenv("MUON_TILE");

@@ -81,6 +81,18 @@ struct Plan {
 // Environment override of the tile (MUON_TILE=128|256), 0 when unset.
 int tile_override();
 
+// Tile table installed through the C ABI: (m, op, count class) → tile.
+struct TileKey {
+  int64_t m;
+  int op, countClass;
+  bool operator<(const TileKey& o) const {
+    return m != o.m ? m < o.m : (op != o.op ? op < o.op : countClass < o.countClass);
+  }
+};
+void set_tile_table(const std::vector<std::pair<TileKey, int>>& entries);
+int tile_from_table(int64_t m, int op, int count);  // 0 when absent
+int count_class(int count);
+
 // Largest Gram size m that keeps fp32 state for the A-chain on the
 // half-precision path, for groups holding nearly square matrices (n ≤ 2m).
 constexpr int64_t kState32MaxM = 2048;
