@@ -328,7 +328,20 @@ muon_status_t enqueue(const Plan& P, const std::vector<CallerMat>& cm, int srcDt
     S.strideInh = S.strideOuth = g.Mp * g.Mp;
     S.strideIn32 = S.strideOut32 = g.Mp * g.Mp;
     S.mReal = S.nReal = (int32_t)g.m;
+    S.mirrorOut = 1;
     return S;
+  };
+  // On the 256-tile kernel every Gram-space iterate is stored block-upper
+  // (tile only, no mirror) and read back through transposed panels; only
+  // the last Q, which the final product reads as a dense operand, is
+  // written in full.  The 128-tile kernel always works on full matrices.
+  auto upper = [](GemmSeg& S, int tile, bool lastQ) {
+    if (tile != 256) return;
+    S.mirrorOut = lastQ ? 1 : 0;
+  };
+  auto upper_in = [](GemmSeg& S, int tile) {
+    if (tile != 256) return;
+    S.upperA = S.upperB = 1;
   };
   auto f32 = [&](const GroupPlan& g, size_t off) -> float* {
     return g.state32 ? at<float>(ws, off) : nullptr;
@@ -350,6 +363,7 @@ muon_status_t enqueue(const Plan& P, const std::vector<CallerMat>& cm, int srcDt
         S.lda = S.ldb = (int32_t)bp.Np;
         S.K = (int32_t)bp.Np;
         S.epi = EPI_SYRK;
+        upper(S, tile, false);
         S.u = 1.0f / (sc.sX * sc.sX);
         S.sOut = sc.sA[0];
         S.outh = at<char>(ws, g.offAh + g.strideh * bp.gramStart);
@@ -385,6 +399,8 @@ muon_status_t enqueue(const Plan& P, const std::vector<CallerMat>& cm, int srcDt
         S.inIsB = 1;
         S.sIn = 1.0f / sc.sA[k];
         S.epi = EPI_SQ;
+        upper_in(S, tile);
+        upper(S, tile, k == 0 && P.steps == 1);  // Q₁ is written here and is last when s = 1
         S.u = 1.0f / (sc.sA[k] * sc.sA[k]);
         S.p0 = a;
         S.p1 = b;
@@ -412,6 +428,8 @@ muon_status_t enqueue(const Plan& P, const std::vector<CallerMat>& cm, int srcDt
           S.inIsB = 1;
           S.sIn = 1.0f / sc.sQ[k];
           S.epi = EPI_AXPY;
+          upper_in(S, tile);
+          upper(S, tile, k + 1 == P.steps);
           S.u = 1.0f / (sc.sB[k] * sc.sQ[k]);
           S.p0 = a;
           S.outh = at<char>(ws, g.offQh[qcur ^ 1]);
@@ -428,6 +446,8 @@ muon_status_t enqueue(const Plan& P, const std::vector<CallerMat>& cm, int srcDt
           S.inIsB = 1;
           S.sIn = 1.0f / sc.sA[k];
           S.epi = EPI_AXPY;
+          upper_in(S, tile);
+          upper(S, tile, false);
           S.u = 1.0f / (sc.sB[k] * sc.sA[k]);
           S.p0 = a;
           S.outh = at<char>(ws, g.offPAh);
@@ -452,6 +472,8 @@ muon_status_t enqueue(const Plan& P, const std::vector<CallerMat>& cm, int srcDt
           S.inIsB = 1;
           S.sIn = 1.0f / sc.sPA[k];
           S.epi = EPI_AXPY;
+          upper_in(S, tile);
+          upper(S, tile, false);
           S.u = 1.0f / (sc.sB[k] * sc.sPA[k]);
           S.p0 = a;
           S.outh = at<char>(ws, g.offAh);

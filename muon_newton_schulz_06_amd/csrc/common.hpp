@@ -67,7 +67,14 @@ struct GemmSeg {
   int64_t strideOuth;
   void* outhb;         // second result copy (EPI_SQ first step, EPI_SYRK zero steps)
   int32_t userBase;    // first caller-table entry of this segment
-  int32_t pad_;
+  // 256-tile kernel only.  A symmetric matrix may be stored "block-upper":
+  // only its 256×256 blocks (bi, bj) with bi ≤ bj are valid (diagonal blocks
+  // in full).  An operand stored that way reads the k-tiles left of its
+  // diagonal block transposed (rows k of the stored matrix).
+  int32_t upperA, upperB;
+  // symmetric outputs: 1 writes the tile and its mirror (full matrix),
+  // 0 writes the tile only (block-upper, diagonal tiles in full)
+  int32_t mirrorOut;
 };
 
 struct GemmLaunch {

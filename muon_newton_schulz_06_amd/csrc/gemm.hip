@@ -441,8 +441,34 @@ __device__ __forceinline__ uint32_t lds_addr(const char* p) {
   return (uint32_t)(uintptr_t)(lds_ptr_t)p;
 }
 
-// ----- staged epilogues of the 256-tile kernel ------------------------------
+// ----- transposed operand panels ---------------------------------------------
+// A block-upper symmetric operand (only blocks bi ≤ bj stored) supplies the
+// k-tiles left of its diagonal block from the transposed position: rows k of
+// the stored matrix, 256 values each.  Such a panel sits in the same 16 KiB
+// of the ring slot as 32 k-rows of 512 bytes; 16-byte chunk c of row k is
+// stored at c ^ 4·(k & 3), so the four k-rows read together by one 16-lane
+// group of a transposed read cover the 64 banks once.
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) short4_t* lds_s4_t;
+
+__device__ __forceinline__ int tpan_off(int k, int i) {
+  return k * 512 + (((i >> 3) ^ (4 * (k & 3))) << 4) + (i & 7) * 2;
+}
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane j supplies the
+// address of 4 consecutive 16-bit values; lane i of the group receives
+// value i % 4 of the chunks of lanes i/4, 4 + i/4, 8 + i/4, 12 + i/4.  With
+// lane j pointing at (k0 + j/4, c0 + 4·(j%4)) of a k-major panel, lane i
+// receives column c0 + i at rows k0 .. k0+3: four consecutive k of one row
+// of the operand, which is the MFMA operand layout.
+__device__ __forceinline__ half4 tr_read4(const char* pan, int k0, int c0, int j) {
+  const short4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s4_t)(pan + tpan_off(k0 + (j >> 2), c0 + 4 * (j & 3))));
+  return __builtin_bit_cast(half4, v);
+}
+
+// ----- staged epilogues of the 256-tile kernel ------------------------------
 
 // Symmetric results: every value is written through LDS twice, once as the
 // tile itself (rows of C) and once transposed (the mirrored tile), each time
@@ -554,11 +580,14 @@ template <int FM, int FN, bool kTwo>
 __device__ __forceinline__ void write_symmetric(_Float16* dst, int ldc, char* lds, int ti, int tj,
                                                 int wm, int wn, int lr, int lh, int tid,
                                                 const floatx16 (&acc)[FM][FN],
-                                                const SecondCopy& sc) {
+                                                const SecondCopy& sc, bool mirror) {
   const bool diag = ti == tj;
   stage_rows<FM, FN>(lds, wm, wn, lr, lh, acc);
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   store_staged<true, kTwo>(dst, ldc, lds, ti, tj, diag, tid, sc);
+  // Block-upper output: an off-diagonal tile alone; a diagonal tile still
+  // gets its lower half from the transposed staging (exactly symmetric).
+  if (!mirror && !diag) return;
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   stage_cols<FM, FN>(lds, wm, wn, lr, lh, acc);
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -782,13 +811,43 @@ __global__ __launch_bounds__(512) void gemm256_kernel(const GemmLaunch L) {
     gB[p] = Bg + (int64_t)r * S.ldb + lc * 8;
   }
   const int dstA = wave * 32 * kRowB;
-  auto issue = [&gA, &gB, dstA](char* st, int kt) {
-    const int k0 = kt * BK;
-    const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(st) + dstA);
+  // Block-upper operands: k-tiles kt < dA (dB) of A (B) come from the
+  // transposed position, k-rows kt·32 .. kt·32+31 of the stored matrix at
+  // columns ti·256 (tj·256) onwards.  Wave w fills k-rows 4w .. 4w+3, two
+  // rows (1 KiB) per instruction, so the instruction count per k-tile (and
+  // hence every vmcnt below) is the same in both layouts.
+  // Only the Gram-space products (square operands, lda = ldb = Mp ≤ 32768,
+  // so a lane's offset inside a panel fits 32 bits) take this path.
+  const int dA = (kCapture && S.upperA) ? ti * (BM / BK) : 0;
+  const int dB = (kCapture && S.upperB) ? tj * (BN / BK) : 0;
+  const T* const baseAT = (const T*)S.A + mat * S.strideA + ti * BM;
+  const T* const baseBT = (const T*)S.B + mat * S.strideB + tj * BN;
+  int offT[2];
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      dma16(gA[p] + k0, base + p * 16 * kRowB);
-      dma16(gB[p] + k0, base + kStageA + p * 16 * kRowB);
+  for (int p = 0; p < 2; ++p) {
+    const int r = wave * 4 + 2 * p + (lane >> 5);
+    offT[p] = r * S.lda + (((lane & 31) ^ (4 * (r & 3))) << 3);
+  }
+  const int dstT = wave * 4 * 512;
+  const int ldT = S.lda;
+  auto issue = [&gA, &gB, offT, baseAT, baseBT, ldT, dstA, dstT, dA, dB](char* st, int kt) __attribute__((always_inline)) {
+    const int k0 = kt * BK;
+    const uint32_t sbase = __builtin_amdgcn_readfirstlane(lds_addr(st));
+    if (kt < dA) {
+      const T* b = baseAT + (int64_t)k0 * ldT;
+#pragma unroll
+      for (int p = 0; p < 2; ++p) dma16(b + offT[p], __builtin_amdgcn_readfirstlane(sbase + dstT + p * 1024));
+    } else {
+#pragma unroll
+      for (int p = 0; p < 2; ++p) dma16(gA[p] + k0, __builtin_amdgcn_readfirstlane(sbase + dstA + p * 16 * kRowB));
+    }
+    if (kt < dB) {
+      const T* b = baseBT + (int64_t)k0 * ldT;
+#pragma unroll
+      for (int p = 0; p < 2; ++p) dma16(b + offT[p], __builtin_amdgcn_readfirstlane(sbase + kStageA + dstT + p * 1024));
+    } else {
+#pragma unroll
+      for (int p = 0; p < 2; ++p) dma16(gB[p] + k0, __builtin_amdgcn_readfirstlane(sbase + kStageA + dstA + p * 16 * kRowB));
     }
   };
 
@@ -801,19 +860,32 @@ __global__ __launch_bounds__(512) void gemm256_kernel(const GemmLaunch L) {
       for (int e = 0; e < 16; ++e) acc[fi][fj][e] = 0.f;
 
   // Fragment addresses: rows base + lr with base a multiple of 32, so the
-  // swizzle depends on lr only.
+  // swizzle depends on lr only.  A transposed panel gives the same fragment
+  // (row lr, k = 16·kk + 8·lh + 0..7) from two transposed reads; the 16-lane
+  // group g = lane/16 covers rows 16·(g&1) .. +15 and k-half g/2.
   const int sw = swz4(lr);
-  auto compute = [&acc, wm, wn, lr, lh, sw](const char* st) {
+  const int tg = lane >> 4, tjl = lane & 15;
+  auto frag_n = [lr, lh, sw](const char* pan, int row0, int kk) __attribute__((always_inline)) {
+    return *(const half8*)(pan + (row0 + lr) * kRowB + (((2 * kk + lh) ^ sw) * 16));
+  };
+  auto frag_t = [tg, tjl](const char* pan, int row0, int kk) __attribute__((always_inline)) {
+    const int c0 = row0 + 16 * (tg & 1), k0 = kk * 16 + 8 * (tg >> 1);
+    const half4 lo = tr_read4(pan, k0, c0, tjl);
+    const half4 hi = tr_read4(pan, k0 + 4, c0, tjl);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+  auto compute_m = [&acc, frag_n, frag_t, wm, wn](const char* st, auto tac, auto tbc) __attribute__((always_inline)) {
+    constexpr bool TA = decltype(tac)::value, TB = decltype(tbc)::value;
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
-      const int pc = ((2 * kk + lh) ^ sw) * 16;
       half8 af[FM], bf[FN];
 #pragma unroll
       for (int fi = 0; fi < FM; ++fi)
-        af[fi] = *(const half8*)(st + (wm * WTM + fi * 32 + lr) * kRowB + pc);
+        af[fi] = TA ? frag_t(st, wm * WTM + fi * 32, kk) : frag_n(st, wm * WTM + fi * 32, kk);
 #pragma unroll
       for (int fj = 0; fj < FN; ++fj)
-        bf[fj] = *(const half8*)(st + kStageA + (wn * WTN + fj * 32 + lr) * kRowB + pc);
+        bf[fj] = TB ? frag_t(st + kStageA, wn * WTN + fj * 32, kk)
+                    : frag_n(st + kStageA, wn * WTN + fj * 32, kk);
 #pragma unroll
       for (int fi = 0; fi < FM; ++fi)
 #pragma unroll
@@ -827,26 +899,40 @@ __global__ __launch_bounds__(512) void gemm256_kernel(const GemmLaunch L) {
   // the ring holds k-tile ti·8 + wm·4 + fi, its B tile contains
   // Y[tj·256 + jl][k] = Y[i][j] for this wave's rows i of block fi: each lane
   // copies its four consecutive i of each column (one 8-byte LDS read).
+  // In a transposed B panel the same four values (rows k = 8q + 4·lh .. +3,
+  // column jl) are one transposed read.
+  // The k-tiles of block ti are in the phase with B transposed when ti < tj
+  // and in the direct phase when ti == tj (never in the first phase), so the
+  // layout of the capture is fixed by the phase.
   half4 ycap[kCapture ? FM : 1][FN][4];
   const int capBase = ti * 8 + wm * 4;
-  auto capture_fi = [&ycap, wn, lr, lh, sw](const char* st, auto fic) {
+  auto capture_fi = [&ycap, wn, lr, lh, sw, tg, tjl](const char* st, auto fic, auto tbc) __attribute__((always_inline)) {
     constexpr int fi = decltype(fic)::value;
     if constexpr (kCapture) {
+      if constexpr (decltype(tbc)::value) {
 #pragma unroll
-      for (int fj = 0; fj < FN; ++fj)
+        for (int fj = 0; fj < FN; ++fj)
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          ycap[fi][fj][q] = *(const half4*)(st + kStageA + (wn * WTN + fj * 32 + lr) * kRowB +
-                                            ((q ^ sw) << 4) + lh * 8);
+          for (int q = 0; q < 4; ++q)
+            ycap[fi][fj][q] = tr_read4(st + kStageA, 8 * q + 4 * (tg >> 1),
+                                       wn * WTN + fj * 32 + 16 * (tg & 1), tjl);
+      } else {
+#pragma unroll
+        for (int fj = 0; fj < FN; ++fj)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            ycap[fi][fj][q] = *(const half4*)(st + kStageA + (wn * WTN + fj * 32 + lr) * kRowB +
+                                              ((q ^ sw) << 4) + lh * 8);
+      }
     }
   };
-  auto capture = [&](const char* st, int k) {
-    if constexpr (kCapture) {
+  auto capture = [&](const char* st, int k, auto tac, auto tbc) __attribute__((always_inline)) {
+    if constexpr (kCapture && !decltype(tac)::value) {
       switch (k - capBase) {
-        case 0: capture_fi(st, std::integral_constant<int, 0>{}); break;
-        case 1: capture_fi(st, std::integral_constant<int, 1>{}); break;
-        case 2: capture_fi(st, std::integral_constant<int, 2>{}); break;
-        case 3: capture_fi(st, std::integral_constant<int, 3>{}); break;
+        case 0: capture_fi(st, std::integral_constant<int, 0>{}, tbc); break;
+        case 1: capture_fi(st, std::integral_constant<int, 1>{}, tbc); break;
+        case 2: capture_fi(st, std::integral_constant<int, 2>{}, tbc); break;
+        case 3: capture_fi(st, std::integral_constant<int, 3>{}, tbc); break;
         default: break;
       }
     }
@@ -871,7 +957,7 @@ __global__ __launch_bounds__(512) void gemm256_kernel(const GemmLaunch L) {
   // "memory" clobber keeps the compiler from moving LDS accesses across it;
   // every wave's own ds_reads of the slot about to be refilled completed
   // before its MFMAs, hence before it reached the barrier.
-  auto step = [&](const char* cur, char* nxt, int k) {
+  auto step = [&](const char* cur, char* nxt, int k, auto tac, auto tbc) __attribute__((always_inline)) {
     const int ahead = min(2, KT - 1 - k);
     const bool wpend = pref && k >= KT - 2;  // weight loads younger than k-tile k
     if (ahead >= 2) asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
@@ -883,18 +969,30 @@ __global__ __launch_bounds__(512) void gemm256_kernel(const GemmLaunch L) {
     if constexpr (EPI == EPI_UPDATE) {
       if (pref && k == KT - 3) weight_prefetch<0>(Ew, ti, tj, tid, wpf);
     }
-    capture(cur, k);
-    compute(cur);
+    capture(cur, k, tac, tbc);
+    compute_m(cur, tac, tbc);
+  };
+  // k-tiles in three phases of fixed operand layouts: [0, dA) both
+  // transposed, [dA, dB) B transposed, [dB, KT) both direct (dA ≤ dB since
+  // ti ≤ tj; both are multiples of 8, so every phase starts on ring slot 0).
+  auto phase = [&](int k0, int k1, auto tac, auto tbc) __attribute__((always_inline)) {
+    for (int kt = k0; kt < k1; kt += 4) {
+      step(st0, st3, kt, tac, tbc);
+      if (kt + 1 < k1) step(st1, st0, kt + 1, tac, tbc);
+      if (kt + 2 < k1) step(st2, st1, kt + 2, tac, tbc);
+      if (kt + 3 < k1) step(st3, st2, kt + 3, tac, tbc);
+    }
   };
 
   issue(st0, 0);
   if (KT > 1) issue(st1, 1);
   if (KT > 2) issue(st2, 2);
-  for (int kt = 0; kt < KT; kt += 4) {
-    step(st0, st3, kt);
-    if (kt + 1 < KT) step(st1, st0, kt + 1);
-    if (kt + 2 < KT) step(st2, st1, kt + 2);
-    if (kt + 3 < KT) step(st3, st2, kt + 3);
+  if constexpr (kCapture) {
+    phase(0, dA, std::true_type{}, std::true_type{});
+    phase(dA, dB, std::false_type{}, std::true_type{});
+    phase(dB, KT, std::false_type{}, std::false_type{});
+  } else {
+    phase(0, KT, std::false_type{}, std::false_type{});
   }
 
   // Every wave is done with the ring before it is reused for staging.
@@ -921,9 +1019,11 @@ __global__ __launch_bounds__(512) void gemm256_kernel(const GemmLaunch L) {
     SecondCopy sc{E.outhb, E.sOutB / E.sOut, E.sOutB * E.p0, E.mReal};
     if (EPI == EPI_SQ && E.outhb) {
       // first step: Q₁ = a·I + B₀ written from the same staged B₀ values
-      write_symmetric<FM, FN, true>(E.outh, E.ldc, lds, ti, tj, wm, wn, lr, lh, tid, acc, sc);
+      write_symmetric<FM, FN, true>(E.outh, E.ldc, lds, ti, tj, wm, wn, lr, lh, tid, acc, sc,
+                                    S.mirrorOut != 0);
     } else {
-      write_symmetric<FM, FN, false>(E.outh, E.ldc, lds, ti, tj, wm, wn, lr, lh, tid, acc, sc);
+      write_symmetric<FM, FN, false>(E.outh, E.ldc, lds, ti, tj, wm, wn, lr, lh, tid, acc, sc,
+                                     S.mirrorOut != 0);
     }
     if constexpr (EPI == EPI_SYRK) {
       if (E.writeIdentity) {  // zero steps: Q₀ = I (rare; element by element)
