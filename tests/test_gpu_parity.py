@@ -217,6 +217,26 @@ def test_edge_cases(mns):
     assert rel(o, ref) <= TOL_F32
 
 
+@pytest.mark.parametrize("steps", [0, 1, 2, 3, 7])
+def test_step_counts_on_the_256_tile_path(mns, steps):
+    """bf16 matrices with m = 600 (3×3 blocks of 256 after padding) and
+    m = 2300 (9×9): the Gram iterates are stored as their upper blocks and
+    read back through transposed panels; which products run, and which one
+    writes the last Q in full for the final product, depend on the step
+    count."""
+    xs = [W.gaussian((600, 1500), 40 + steps, dtype=torch.bfloat16, device="cuda"),
+          W.gaussian((4700, 2300), 50 + steps, dtype=torch.bfloat16, device="cuda")]
+    plan = mns.describe_plan([tuple(x.shape) for x in xs], for_step=False)
+    assert all(g["tile"] == 256 and not g["state32"] for g in plan["groups"])
+    say("steps", steps, "shapes", [tuple(x.shape) for x in xs])
+    outs = mns.muon_ns_batched(xs, steps=steps)
+    torch.cuda.synchronize()
+    for x, o in zip(xs, outs):
+        e = rel(o.float(), oracle_ns(x.float().cpu(), steps=steps))
+        say("steps", steps, tuple(x.shape), "rel err", e)
+        assert e <= TOL_BF16
+
+
 def test_run_to_run_bitwise_determinism(mns):
     say("determinism")
     xs = W.ns_small_mix(device="cuda", mix=[(4, 256, 1024), (3, 512, 2048)])
