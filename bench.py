@@ -76,10 +76,11 @@ def gram_flops(shapes, steps=5):
     return tot
 
 
-def cpu_baseline(budget_s=30.0):
-    """The oracle as it stands, on a bounded sample of the workload: one
-    q-shaped (3584×3584) and one k-shaped (512×3584) matrix of layer 0, one
-    full muon_step each (momentum, fp64 standard Newton–Schulz, update)."""
+def cpu_baseline(budget_s=15.0):
+    """The oracle as it stands, on a bounded sample of the workload: the
+    matrices of layer 0 in the order k, q, down, v, o, gate, up, one full
+    muon_step each (momentum, fp64 standard Newton–Schulz, update), until
+    about `budget_s` seconds of CPU work have been spent."""
     import numpy as np
     import torch
 
@@ -90,20 +91,23 @@ def cpu_baseline(budget_s=30.0):
         threads = max([d.get("num_threads", 0) for d in threadpool_info()] or [os.cpu_count()])
     except Exception:
         threads = os.cpu_count()
-    shapes = [(512, 3584), (3584, 3584)]
-    inp = W.muon_inputs(shapes, 5001, device="cpu")
+    layer = W.qwen_model_shapes(1)            # q, k, v, o, gate, up, down
+    order = [1, 0, 6, 2, 3, 4, 5]
+    shapes = [layer[i] for i in order]
+    inp = W.muon_inputs(layer, 5001, device="cpu")
     t0 = time.perf_counter()
     done = []
-    for j, (r, c) in enumerate(shapes):
-        oracle.muon_step(inp.params[j].float().numpy(), inp.grads[j].numpy(),
-                         inp.momenta[j].numpy(), np.float32(0.95), 0.02, oracle.QUINTIC, 5, 1e-7)
+    for i in order:
+        r, c = layer[i]
+        oracle.muon_step(inp.params[i].float().numpy(), inp.grads[i].numpy(),
+                         inp.momenta[i].numpy(), np.float32(0.95), 0.02, oracle.QUINTIC, 5, 1e-7)
         done.append((r, c))
         if time.perf_counter() - t0 > budget_s:
             break
     dt = time.perf_counter() - t0
     fl = gram_flops(done)
     return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"muon_step on {len(done)} matrices {done} of layer 0 "
+            "sample": f"muon_step on {len(done)} of the {len(shapes)} matrices of layer 0 {done} "
                       f"(fp64 numpy, standard NS), {dt:.2f} s; algorithmic Gram flops / time"}
 
 
