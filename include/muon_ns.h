@@ -24,8 +24,14 @@
  *     stream), asynchronously: results are valid once the stream reaches
  *     the enqueued work.  No entry point synchronises the host with the GPU.
  *   - `workspace` is caller-allocated device memory of at least the size
- *     the matching *_workspace_size query returns, 256-byte aligned.  Its
- *     contents on entry do not matter and are garbage on exit.
+ *     the matching *_workspace_size query returns, 256-byte aligned, that
+ *     overlaps no tensor of the call (MUON_ERR_ALIAS otherwise).  Its
+ *     contents on entry do not matter and are garbage on exit.  Calls that
+ *     share a workspace must be ordered (same stream, or synchronised).
+ *   - Thread safety: entry points may be called from several threads; the
+ *     tile table and the profiling records are process-wide and guarded.
+ *     Do not enable profiling while a stream is being captured into a graph
+ *     (the event records would be captured too).
  *   - Argument checks run on the host BEFORE any HIP call.  On any error
  *     nothing is enqueued and a status other than MUON_OK is returned; the
  *     message is available from muon_last_error() (per thread).

@@ -17,8 +17,10 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -44,11 +46,13 @@ struct ProfRec {
   hipEvent_t e0, e1;
   double work;
 };
-bool g_prof_on = false;
+// Shared by every thread that calls the library: guarded by g_prof_mu.
+std::atomic<bool> g_prof_on{false};
+std::mutex g_prof_mu;
 std::vector<ProfRec> g_prof;
 std::vector<hipEvent_t> g_event_pool;
 
-hipEvent_t take_event() {
+hipEvent_t take_event() {  // g_prof_mu held
   if (!g_event_pool.empty()) {
     hipEvent_t e = g_event_pool.back();
     g_event_pool.pop_back();
@@ -64,15 +68,22 @@ struct Launcher {
   template <typename F>
   muon_status_t run(int kind, double work, const char* what, F&& f) {
     hipEvent_t e0 = nullptr, e1 = nullptr;
-    if (g_prof_on) {
+    const bool prof = g_prof_on.load();
+    if (prof) {
+      std::lock_guard<std::mutex> lk(g_prof_mu);
       e0 = take_event();
       e1 = take_event();
-      if (e0) hipEventRecord(e0, st);
     }
+    if (e0) hipEventRecord(e0, st);
     hipError_t err = f();
-    if (g_prof_on && e0 && e1) {
+    if (prof && e0 && e1) {
       hipEventRecord(e1, st);
+      std::lock_guard<std::mutex> lk(g_prof_mu);
       g_prof.push_back({kind, e0, e1, work});
+    } else if (prof) {
+      std::lock_guard<std::mutex> lk(g_prof_mu);
+      if (e0) g_event_pool.push_back(e0);
+      if (e1) g_event_pool.push_back(e1);
     }
     if (err != hipSuccess)
       return fail(MUON_ERR_HIP, std::string(what) + ": " + hipGetErrorString(err));
@@ -96,6 +107,17 @@ bool overlaps(std::vector<Range> v, int* a, int* b) {
       return true;
     }
   }
+  return false;
+}
+
+// The workspace must not overlap any caller tensor (it is scratch the
+// kernels overwrite while the tensors are read).
+bool workspace_overlaps(const std::vector<Range>& v, uintptr_t lo, uintptr_t hi, int* who) {
+  for (const Range& r : v)
+    if (r.lo < hi && lo < r.hi) {
+      *who = r.owner;
+      return true;
+    }
   return false;
 }
 
@@ -639,7 +661,7 @@ muon_status_t muon_ns_batched(const muon_ns_desc_t* desc, int32_t count, int32_t
   if (!std::isfinite(eps) || eps < 0) return fail(MUON_ERR_INVALID_ARG, "eps must be finite and >= 0");
   const size_t esz = dtype == MUON_DTYPE_F32 ? 4 : 2;
   std::vector<int64_t> r(count), c(count);
-  std::vector<Range> outs;
+  std::vector<Range> outs, ins;
   for (int i = 0; i < count; ++i) {
     const muon_ns_desc_t& d = desc[i];
     muon_status_t s = check_shape(i, d.rows, d.cols);
@@ -652,6 +674,8 @@ muon_status_t muon_ns_batched(const muon_ns_desc_t* desc, int32_t count, int32_t
       return fail(MUON_ERR_INVALID_ARG, "matrix " + std::to_string(i) + ": ld < cols");
     const uintptr_t lo = (uintptr_t)d.out;
     outs.push_back({lo, lo + (uintptr_t)(((d.rows - 1) * d.ld_out + d.cols) * esz), i});
+    const uintptr_t xl = (uintptr_t)d.x;
+    ins.push_back({xl, xl + (uintptr_t)(((d.rows - 1) * d.ld_x + d.cols) * esz), i});
   }
   int oa = 0, ob = 0;
   if (overlaps(outs, &oa, &ob))
@@ -668,6 +692,10 @@ muon_status_t muon_ns_batched(const muon_ns_desc_t* desc, int32_t count, int32_t
     if (workspace_bytes < P.totalBytes)
       return fail(MUON_ERR_WORKSPACE, "workspace too small: need " + std::to_string(P.totalBytes) +
                                           " bytes, got " + std::to_string(workspace_bytes));
+    const uintptr_t wl = (uintptr_t)workspace, wh = wl + P.totalBytes;
+    int who = 0;
+    if (workspace_overlaps(outs, wl, wh, &who) || workspace_overlaps(ins, wl, wh, &who))
+      return fail(MUON_ERR_ALIAS, "workspace overlaps matrix " + std::to_string(who));
   }
   std::vector<CallerMat> cm(count);
   for (int i = 0; i < count; ++i) {
@@ -741,6 +769,11 @@ muon_status_t muon_step_ex(void* const* params, const void* const* grads, float*
   if (workspace_bytes < P.totalBytes)
     return fail(MUON_ERR_WORKSPACE, "workspace too small: need " + std::to_string(P.totalBytes) +
                                         " bytes, got " + std::to_string(workspace_bytes));
+  {
+    int who = 0;
+    if (workspace_overlaps(ranges, (uintptr_t)workspace, (uintptr_t)workspace + P.totalBytes, &who))
+      return fail(MUON_ERR_ALIAS, "workspace overlaps a tensor of matrix " + std::to_string(who));
+  }
   std::vector<CallerMat> cm(count);
   for (int i = 0; i < count; ++i) {
     cm[i].src = momentum[i];
@@ -783,7 +816,7 @@ muon_status_t muon_set_tile_table(const muon_tile_entry_t* entries, int32_t n) {
 
 muon_status_t muon_profile_enable(int32_t on) {
   g_err.clear();
-  g_prof_on = on != 0;
+  g_prof_on.store(on != 0);
   return MUON_OK;
 }
 
@@ -792,16 +825,21 @@ muon_status_t muon_profile_read(int32_t kind, double* total_ms, int64_t* launche
   if (!total_ms || !launches || !work) return fail(MUON_ERR_INVALID_ARG, "NULL output");
   double ms = 0, w = 0;
   int64_t n = 0;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
   std::vector<ProfRec> keep;
+  const char* err = nullptr;
   for (ProfRec& r : g_prof) {
-    if (r.kind != kind) {
+    if (r.kind != kind || err) {  // other kinds, and everything after a failure, stay recorded
       keep.push_back(r);
       continue;
     }
-    if (hipEventSynchronize(r.e1) != hipSuccess) return fail(MUON_ERR_HIP, "hipEventSynchronize failed");
     float t = 0;
-    if (hipEventElapsedTime(&t, r.e0, r.e1) != hipSuccess)
-      return fail(MUON_ERR_HIP, "hipEventElapsedTime failed");
+    if (hipEventSynchronize(r.e1) != hipSuccess) err = "hipEventSynchronize failed";
+    else if (hipEventElapsedTime(&t, r.e0, r.e1) != hipSuccess) err = "hipEventElapsedTime failed";
+    if (err) {
+      keep.push_back(r);
+      continue;
+    }
     ms += t;
     w += r.work;
     ++n;
@@ -809,6 +847,7 @@ muon_status_t muon_profile_read(int32_t kind, double* total_ms, int64_t* launche
     g_event_pool.push_back(r.e1);
   }
   g_prof.swap(keep);
+  if (err) return fail(MUON_ERR_HIP, err);
   *total_ms = ms;
   *launches = n;
   *work = w;

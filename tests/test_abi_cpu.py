@@ -313,3 +313,12 @@ def test_tile_choice_for_qwen_set():
     p = mns.describe_plan(shapes, for_step=True)
     tiles = {g["m"]: g["tile"] for g in p["groups"]}
     assert tiles[3584] == 256
+
+
+def test_workspace_must_not_overlap_tensors():
+    # muon_step: workspace overlapping a gradient
+    assert _step(ws=0x2000000) == 3 and "workspace" in _err()
+    # muon_ns_batched: workspace overlapping an input or an output
+    arr = _desc(1)
+    assert _ns(arr, 1, ws=0x10000 - 0x100, wsb=1 << 40) == 3 and "workspace" in _err()
+    assert _ns(arr, 1, ws=0x900000, wsb=1 << 40) == 3
