@@ -34,10 +34,10 @@ HBM_PEAK = 8000.0        # GB/s
 
 METRIC = "Muon step ms & NS TFLOP/s (% MFMA peak), Qwen2.5-7B-shaped matrix set"
 
-KERNEL_SYMBOLS = {"gram256_axpy": "void muon::gemm256_kernel<2>(muon::GemmLaunch)",
-                  "gram256_sq": "void muon::gemm256_kernel<1>(muon::GemmLaunch)",
-                  "syrk": "void muon::gemm256_kernel<0>(muon::GemmLaunch)",
-                  "final": "void muon::gemm256_kernel<3>(muon::GemmLaunch)"}
+KERNEL_SYMBOLS = {"gram256_axpy": "void muon::gemm256_kernel<2, 0>(muon::GemmLaunch)",
+                  "gram256_sq": "void muon::gemm256_kernel<1, 0>(muon::GemmLaunch)",
+                  "syrk": "void muon::gemm256_kernel<0, 0>(muon::GemmLaunch)",
+                  "final": "void muon::gemm256_kernel<3, 1|2>(muon::GemmLaunch)"}
 
 
 def traffic_for(kind, workload):

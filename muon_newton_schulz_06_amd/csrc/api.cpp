@@ -273,7 +273,7 @@ muon_status_t enqueue(const Plan& P, const std::vector<CallerMat>& cm, int srcDt
       C.cols = mp.cols;
       C.ld = P.forStep ? mp.cols : cm[i].ldSrc;
       void* xh = at<char>(ws, bp.offXh + bp.strideX * mp.posBucket);
-      void* xth = at<char>(ws, bp.offXTh + bp.strideX * mp.posBucket);
+      void* xth = bp.xT ? at<char>(ws, bp.offXTh + bp.strideX * mp.posBucket) : nullptr;
       if (!mp.tall) {  // stored = X₀ (m × n)
         C.S = xh;
         C.T = xth;
@@ -290,7 +290,7 @@ muon_status_t enqueue(const Plan& P, const std::vector<CallerMat>& cm, int srcDt
       C.blockStart = blocks;
       blocks += (int64_t)(C.rp / kCastTile) * C.tilesC;
       bytes += (P.forStep ? 4.0 : (srcDtype == MUON_DTYPE_BF16 ? 2.0 : 4.0)) * mp.numel +
-               2.0 * esz * (double)bp.Mp * (double)bp.Np;
+               (bp.xT ? 2.0 : 1.0) * esz * (double)bp.Mp * (double)bp.Np;
       if (L.nesterov) bytes += (V.gradDtype == MUON_DTYPE_BF16 ? 2.0 : 4.0) * mp.numel;
     }
     L.n = (int)cn;
@@ -522,27 +522,36 @@ muon_status_t enqueue(const Plan& P, const std::vector<CallerMat>& cm, int srcDt
       L.decay = P.forStep ? V.decay : 1.f;
       GemmSeg& S = L.seg[0];
       const char* qh = at<char>(ws, g.offQh[qcur] + g.strideh * (bp.gramStart + c0));
-      const char* xth = at<char>(ws, bp.offXTh + bp.strideX * c0);
+      // X₀ᵀ as rows (128-tile kernel), or X₀ read through transposed panels
+      // (256-tile kernel; its rows are k, so the row stride is Np).
+      const char* xop = bp.xT ? at<char>(ws, bp.offXTh + bp.strideX * c0)
+                              : at<char>(ws, bp.offXh + bp.strideX * c0);
+      const int32_t ldx = (int32_t)(bp.xT ? bp.Mp : bp.Np);
       if (!bp.tall) {  // O = Q·X₀ : rows of Q, rows of X₀ᵀ
         S.A = qh;
         S.strideA = bp.Mp * bp.Mp;
-        S.B = xth;
+        S.B = xop;
         S.strideB = bp.Np * bp.Mp;
+        S.lda = (int32_t)bp.Mp;
+        S.ldb = ldx;
+        S.transB = bp.xT ? 0 : 1;
         S.tilesM = (int32_t)(bp.Mp / tile);
         S.tilesN = (int32_t)(bp.Np / tile);
         S.mReal = (int32_t)bp.m;
         S.nReal = (int32_t)bp.n;
       } else {         // Oᵀ = X₀ᵀ·Q : rows of X₀ᵀ, rows of Q
-        S.A = xth;
+        S.A = xop;
         S.strideA = bp.Np * bp.Mp;
         S.B = qh;
         S.strideB = bp.Mp * bp.Mp;
+        S.lda = ldx;
+        S.ldb = (int32_t)bp.Mp;
+        S.transA = bp.xT ? 0 : 1;
         S.tilesM = (int32_t)(bp.Np / tile);
         S.tilesN = (int32_t)(bp.Mp / tile);
         S.mReal = (int32_t)bp.n;
         S.nReal = (int32_t)bp.m;
       }
-      S.lda = S.ldb = (int32_t)bp.Mp;
       S.K = (int32_t)bp.Mp;
       S.tilesPerMat = S.tilesM * S.tilesN;
       S.count = (int)cn;

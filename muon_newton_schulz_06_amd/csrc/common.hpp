@@ -75,6 +75,10 @@ struct GemmSeg {
   // symmetric outputs: 1 writes the tile and its mirror (full matrix),
   // 0 writes the tile only (block-upper, diagonal tiles in full)
   int32_t mirrorOut;
+  // dense products: 1 reads every k-tile of A (B) transposed, i.e. A[i][k]
+  // from row k of the stored matrix (X₀ for the final product)
+  int32_t transA, transB;
+  int32_t pad_;
 };
 
 struct GemmLaunch {
@@ -128,8 +132,8 @@ constexpr int kCastTile = 64;
 struct CastMat {
   const void* src;     // stored rows × cols, row stride ld
   const void* grad;    // Nesterov input: gradient, same layout as src (else unused)
-  void* S;             // same orientation, padded rp × cp
-  void* T;             // transposed, padded cp × rp
+  void* S;             // same orientation, padded rp × cp (null: not written)
+  void* T;             // transposed, padded cp × rp (null: not written)
   int64_t rows, cols, ld;
   int32_t rp, cp;      // padded extents (multiples of kCastTile)
   int32_t alphaIdx;

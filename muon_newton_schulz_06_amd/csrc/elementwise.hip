@@ -218,22 +218,30 @@ __device__ void cast_tile(const CastLaunch& L, const CastMat& C, int64_t t) {
       }
     }
   }
+  // Either copy may be absent (a null pointer): the operand layouts a
+  // bucket keeps depend on the kernel that reads them.
+  if (Tt) {
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int rl = ty + 16 * q;
-    const int64_t r = r0 + rl;
+    for (int q = 0; q < 4; ++q)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) tile[rl][cl + e] = v[q][e];
-    T* dst = S + r * C.cp + c0 + cl;
-    if constexpr (sizeof(T) == 2) {
-      half4_t h;
+      for (int e = 0; e < 4; ++e) tile[ty + 16 * q][cl + e] = v[q][e];
+  }
+  if (S) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) h[e] = (_Float16)v[q][e];
-      *(half4_t*)dst = h;
-    } else {
-      *(float4*)dst = make_float4(v[q][0], v[q][1], v[q][2], v[q][3]);
+    for (int q = 0; q < 4; ++q) {
+      const int64_t r = r0 + ty + 16 * q;
+      T* dst = S + r * C.cp + c0 + cl;
+      if constexpr (sizeof(T) == 2) {
+        half4_t h;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) h[e] = (_Float16)v[q][e];
+        *(half4_t*)dst = h;
+      } else {
+        *(float4*)dst = make_float4(v[q][0], v[q][1], v[q][2], v[q][3]);
+      }
     }
   }
+  if (!Tt) return;
   __syncthreads();
 #pragma unroll
   for (int p = 0; p < 2; ++p) {

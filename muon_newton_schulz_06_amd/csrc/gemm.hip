@@ -769,7 +769,9 @@ __device__ __forceinline__ void dense_staged(const EpiArgs<_Float16>& E, char* l
   }
 }
 
-template <int EPI>
+// TR (dense products only): 0 both operands direct, 1 A read transposed,
+// 2 B read transposed, for every k-tile.
+template <int EPI, int TR = 0>
 __global__ __launch_bounds__(512) void gemm256_kernel(const GemmLaunch L) {
   using T = _Float16;
   constexpr int BM = 256, BN = 256, BK = 32, WN = 4;
@@ -816,35 +818,50 @@ __global__ __launch_bounds__(512) void gemm256_kernel(const GemmLaunch L) {
   // columns ti·256 (tj·256) onwards.  Wave w fills k-rows 4w .. 4w+3, two
   // rows (1 KiB) per instruction, so the instruction count per k-tile (and
   // hence every vmcnt below) is the same in both layouts.
-  // Only the Gram-space products (square operands, lda = ldb = Mp ≤ 32768,
-  // so a lane's offset inside a panel fits 32 bits) take this path.
-  const int dA = (kCapture && S.upperA) ? ti * (BM / BK) : 0;
-  const int dB = (kCapture && S.upperB) ? tj * (BN / BK) : 0;
+  // The final product reads X₀ transposed for every k-tile instead (transA
+  // or transB).  A lane's offset inside a 32-row transposed panel,
+  // r·ld + column, fits 32 bits for every supported shape (ld < 2^25).
+  const int KT = S.K / BK;
+  const int dA = kCapture ? (S.upperA ? ti * (BM / BK) : 0) : (TR == 1 ? KT : 0);
+  const int dB = kCapture ? (S.upperB ? tj * (BN / BK) : 0) : (TR == 2 ? KT : 0);
   const T* const baseAT = (const T*)S.A + mat * S.strideA + ti * BM;
   const T* const baseBT = (const T*)S.B + mat * S.strideB + tj * BN;
+  // Gram products (lda = ldb) keep both offsets in registers; the final
+  // product recomputes them per issue from the lane index.
   int offT[2];
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
     const int r = wave * 4 + 2 * p + (lane >> 5);
     offT[p] = r * S.lda + (((lane & 31) ^ (4 * (r & 3))) << 3);
   }
+  auto tr_off = [wave, lane, offT](int p, int ld) __attribute__((always_inline)) {
+    if constexpr (kCapture) {
+      (void)ld;
+      return offT[p];
+    } else {
+      const int r = wave * 4 + 2 * p + (lane >> 5);
+      return r * ld + ((((lane & 31) ^ (4 * (r & 3)))) << 3);
+    }
+  };
   const int dstT = wave * 4 * 512;
-  const int ldT = S.lda;
-  auto issue = [&gA, &gB, offT, baseAT, baseBT, ldT, dstA, dstT, dA, dB](char* st, int kt) __attribute__((always_inline)) {
+  const int ldTA = S.lda, ldTB = kCapture ? S.lda : S.ldb;
+  auto issue = [&gA, &gB, tr_off, baseAT, baseBT, ldTA, ldTB, dstA, dstT, dA, dB](char* st, int kt) __attribute__((always_inline)) {
     const int k0 = kt * BK;
     const uint32_t sbase = __builtin_amdgcn_readfirstlane(lds_addr(st));
     if (kt < dA) {
-      const T* b = baseAT + (int64_t)k0 * ldT;
+      const T* b = baseAT + (int64_t)k0 * ldTA;
 #pragma unroll
-      for (int p = 0; p < 2; ++p) dma16(b + offT[p], __builtin_amdgcn_readfirstlane(sbase + dstT + p * 1024));
+      for (int p = 0; p < 2; ++p)
+        dma16(b + tr_off(p, ldTA), __builtin_amdgcn_readfirstlane(sbase + dstT + p * 1024));
     } else {
 #pragma unroll
       for (int p = 0; p < 2; ++p) dma16(gA[p] + k0, __builtin_amdgcn_readfirstlane(sbase + dstA + p * 16 * kRowB));
     }
     if (kt < dB) {
-      const T* b = baseBT + (int64_t)k0 * ldT;
+      const T* b = baseBT + (int64_t)k0 * ldTB;
 #pragma unroll
-      for (int p = 0; p < 2; ++p) dma16(b + offT[p], __builtin_amdgcn_readfirstlane(sbase + kStageA + dstT + p * 1024));
+      for (int p = 0; p < 2; ++p)
+        dma16(b + tr_off(p, ldTB), __builtin_amdgcn_readfirstlane(sbase + kStageA + dstT + p * 1024));
     } else {
 #pragma unroll
       for (int p = 0; p < 2; ++p) dma16(gB[p] + k0, __builtin_amdgcn_readfirstlane(sbase + kStageA + dstA + p * 16 * kRowB));
@@ -938,16 +955,15 @@ __global__ __launch_bounds__(512) void gemm256_kernel(const GemmLaunch L) {
     }
   };
 
-  const int KT = S.K / BK;
   // Weight update: the first half of the tile's bf16 weights is loaded at
-  // k-tile KT − 3, after the last k-tile's operand loads, and lands while the
-  // last three k-tiles are multiplied.
+  // k-tile KT − 2, after the last k-tile's operand loads, and lands while the
+  // last two k-tiles are multiplied.
   [[maybe_unused]] WeightPrefetch wpf;
   [[maybe_unused]] EpiArgs<T> Ew;
   bool pref = false;
   if constexpr (EPI == EPI_UPDATE) {
     Ew = make_epi<T, EPI>(L, S, mat);
-    pref = KT >= 3 && weight_prefetch_ok(Ew, ti, tj);
+    pref = KT >= 2 && weight_prefetch_ok(Ew, ti, tj);
   }
   // Each k-tile is 4 load instructions per wave; wait until the oldest
   // outstanding k-tile has landed, leaving the younger ones in flight (and
@@ -959,7 +975,7 @@ __global__ __launch_bounds__(512) void gemm256_kernel(const GemmLaunch L) {
   // before its MFMAs, hence before it reached the barrier.
   auto step = [&](const char* cur, char* nxt, int k, auto tac, auto tbc) __attribute__((always_inline)) {
     const int ahead = min(2, KT - 1 - k);
-    const bool wpend = pref && k >= KT - 2;  // weight loads younger than k-tile k
+    const bool wpend = pref && k >= KT - 1;  // weight loads younger than k-tile k
     if (ahead >= 2) asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
     else if (ahead == 1 && wpend) asm volatile("s_waitcnt vmcnt(20)\n\ts_barrier" ::: "memory");
     else if (ahead == 1) asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
@@ -967,7 +983,7 @@ __global__ __launch_bounds__(512) void gemm256_kernel(const GemmLaunch L) {
     else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
     if (k + 3 < KT) issue(nxt, k + 3);
     if constexpr (EPI == EPI_UPDATE) {
-      if (pref && k == KT - 3) weight_prefetch<0>(Ew, ti, tj, tid, wpf);
+      if (pref && k == KT - 2) weight_prefetch<0>(Ew, ti, tj, tid, wpf);
     }
     capture(cur, k, tac, tbc);
     compute_m(cur, tac, tbc);
@@ -991,6 +1007,10 @@ __global__ __launch_bounds__(512) void gemm256_kernel(const GemmLaunch L) {
     phase(0, dA, std::true_type{}, std::true_type{});
     phase(dA, dB, std::false_type{}, std::true_type{});
     phase(dB, KT, std::false_type{}, std::false_type{});
+  } else if constexpr (TR == 1) {
+    phase(0, KT, std::true_type{}, std::false_type{});
+  } else if constexpr (TR == 2) {
+    phase(0, KT, std::false_type{}, std::true_type{});
   } else {
     phase(0, KT, std::false_type{}, std::false_type{});
   }
@@ -1055,7 +1075,17 @@ __global__ __launch_bounds__(512) void gemm256_kernel(const GemmLaunch L) {
 template <int EPI>
 hipError_t launch_epi(int op, int tile, const GemmLaunch& L, int blocks, hipStream_t st) {
   if (op == OP_F16 && tile == 256) {
-    hipLaunchKernelGGL((gemm256_kernel<EPI>), dim3(blocks), dim3(512), 0, st, L);
+    if constexpr (EPI == EPI_UPDATE || EPI == EPI_OUT) {
+      // one bucket per launch, so every segment shares the operand layout
+      if (L.seg[0].transA)
+        hipLaunchKernelGGL((gemm256_kernel<EPI, 1>), dim3(blocks), dim3(512), 0, st, L);
+      else if (L.seg[0].transB)
+        hipLaunchKernelGGL((gemm256_kernel<EPI, 2>), dim3(blocks), dim3(512), 0, st, L);
+      else
+        hipLaunchKernelGGL((gemm256_kernel<EPI, 0>), dim3(blocks), dim3(512), 0, st, L);
+    } else {
+      hipLaunchKernelGGL((gemm256_kernel<EPI>), dim3(blocks), dim3(512), 0, st, L);
+    }
   } else if (op == OP_F16 && tile == 128) {
     hipLaunchKernelGGL((gemm_kernel<_Float16, 128, 128, 2, 2, EPI>), dim3(blocks), dim3(256), 0, st, L);
   } else if (op == OP_F32 && tile == 128) {

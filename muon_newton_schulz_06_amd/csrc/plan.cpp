@@ -238,8 +238,11 @@ std::string build_plan(const int64_t* rows, const int64_t* cols, int count, int 
   }
   for (BucketPlan& bp : P.buckets) {
     bp.strideX = size_t(bp.Mp) * size_t(bp.Np) * esz_of(bp.op);
+    bp.xT = P.groups[bp.group].tile != 256;
     bp.offXh = off;  off = align_up(off + bp.strideX * bp.mats.size());
-    bp.offXTh = off; off = align_up(off + bp.strideX * bp.mats.size());
+    if (bp.xT) {
+      bp.offXTh = off; off = align_up(off + bp.strideX * bp.mats.size());
+    }
   }
   P.totalBytes = off;
   // Power-of-two scales are exact in fp32 too, so fp32 groups of a
@@ -269,7 +272,8 @@ std::string Plan::json() const {
     const BucketPlan& bp = buckets[bi];
     o << (bi ? "," : "") << "{\"rows\":" << bp.rows << ",\"cols\":" << bp.cols << ",\"m\":" << bp.m
       << ",\"n\":" << bp.n << ",\"tall\":" << (bp.tall ? "true" : "false") << ",\"op\":\""
-      << (bp.op == OP_F32 ? "f32" : "f16") << "\",\"group\":"
+      << (bp.op == OP_F32 ? "f32" : "f16") << "\",\"x_transposed_copy\":" << (bp.xT ? "true" : "false")
+      << ",\"group\":"
       << bp.group << ",\"Mp\":" << bp.Mp << ",\"Np\":" << bp.Np << ",\"gram_start\":"
       << bp.gramStart << ",\"mats\":[";
     for (size_t k = 0; k < bp.mats.size(); ++k) o << (k ? "," : "") << bp.mats[k];

@@ -34,8 +34,11 @@ struct BucketPlan {
   std::vector<int> mats;    // matrix indices in call order
   int gramStart = 0;        // position of mats[0] inside its group
   size_t offXh = 0;         // X₀  (Mp × Np), operand type
-  size_t offXTh = 0;        // X₀ᵀ (Np × Mp), operand type
+  size_t offXTh = 0;        // X₀ᵀ (Np × Mp), operand type; only when xT
   size_t strideX = 0;       // bytes per matrix of either buffer
+  // The 128-tile kernel reads X₀ᵀ for the final product; the 256-tile kernel
+  // reads X₀ through transposed panels, so its buckets keep X₀ alone.
+  bool xT = true;
 };
 
 // Matrices of one Gram size m: they share every Gram-space launch.

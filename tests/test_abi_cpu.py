@@ -238,7 +238,9 @@ def test_plan_workspace_matches_layout():
         if g["state32"]:
             total += 8 * g["Mp"] ** 2 * g["count"]  # fp32 A and P·A
     for b in p["buckets"]:
-        total += 2 * esz[b["op"]] * b["Mp"] * b["Np"] * len(b["mats"])
+        copies = 2 if b["x_transposed_copy"] else 1   # X₀, and X₀ᵀ for the 128-tile kernel
+        total += copies * esz[b["op"]] * b["Mp"] * b["Np"] * len(b["mats"])
+        assert b["x_transposed_copy"] == (p["groups"][b["group"]]["tile"] != 256)
     assert p["workspace_bytes"] >= total
     assert p["workspace_bytes"] - total < 256 * (3 + 8 * len(p["groups"]) + 2 * len(p["buckets"])) + 4 * 1000
     # fp16 groups of nearly square matrices with m ≤ 2048 keep fp32 A-chain
