@@ -6,23 +6,25 @@
 //   * the symmetric Gram-space products A², B·Q, B·A, B·(P·A),
 //   * the final product Q·X₀ (or X₀ᵀ·Q for tall matrices) with the weight
 //     update fused into its epilogue.
-// Every product has the form C[i][j] = Σ_k A[i][k]·B[j][k] with both operands
-// stored row-major with k contiguous: for the Gram-space products this holds
-// because every operand is symmetric (a polynomial in G), for the SYRK and
-// the final product because X₀ is kept in both layouts.
+// Every product has the form C[i][j] = Σ_k A[i][k]·B[j][k]: the Gram-space
+// operands are symmetric (polynomials in G), so a row of one is also its
+// column.
 //
 // Symmetric outputs (every Gram-space product is a product of commuting
 // polynomials in G, hence symmetric) are computed on upper-triangle tiles
-// only; the fp16 operand copy is written mirrored so the next product can
-// read whole rows, and the fp32 state is kept on the upper triangle.
-// Diagonal tiles store the element of the upper half into both (i, j) and
-// (j, i), so every stored iterate is exactly symmetric.
+// only.  Diagonal tiles store the element of the upper half into both (i, j)
+// and (j, i), so every stored iterate is exactly symmetric.
 //
 // Two kernels share the tile mapping and the epilogues:
 //  * gemm256_kernel: 256×256 fp16 tiles, 8 waves, direct global→LDS loads
-//    into a 4-slot ring (the large Gram sizes);
-//  * gemm_kernel: 128×128 tiles (fp16 or fp32), 4 waves, register-staged
-//    double buffering (small Gram sizes, fp32 state, the fp32 path).
+//    into a 4-slot ring.  Gram-space iterates are stored block-upper (only
+//    the 256×256 blocks on or above the diagonal, except the last Q, which
+//    the final product reads whole); a product reads an operand's k-tiles
+//    left of its diagonal block from the transposed position, and the final
+//    product reads X₀ᵀ as transposed panels of X₀ (X₀ is kept in one layout);
+//  * gemm_kernel: 128×128 (fp32: also 64×64) tiles, 4 waves, register-staged
+//    double buffering (fp32 groups and groups carrying fp32 state); full,
+//    mirrored operands and both layouts of X₀.
 // Both keep k-rows in LDS with a 16-byte-chunk XOR swizzle chosen for the
 // 64-bank LDS (conflict-free ds_read_b128 fragment reads).
 #include <hip/hip_runtime.h>
@@ -977,7 +979,6 @@ __global__ __launch_bounds__(512) void gemm256_kernel(const GemmLaunch L) {
     const int ahead = min(2, KT - 1 - k);
     const bool wpend = pref && k >= KT - 1;  // weight loads younger than k-tile k
     if (ahead >= 2) asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
-    else if (ahead == 1 && wpend) asm volatile("s_waitcnt vmcnt(20)\n\ts_barrier" ::: "memory");
     else if (ahead == 1) asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
     else if (wpend) asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
     else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
