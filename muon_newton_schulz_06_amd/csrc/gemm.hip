@@ -780,9 +780,11 @@ __global__ __launch_bounds__(512) void gemm256_kernel(const GemmLaunch L) {
   constexpr int WTM = 128, WTN = 64, FM = 4, FN = 2;
   constexpr bool kSym = EPI == EPI_SYRK || EPI == EPI_SQ || EPI == EPI_AXPY;
   constexpr bool kCapture = EPI == EPI_SQ || EPI == EPI_AXPY;
-  // 4-slot ring for the main loop; reused by the staged epilogue.
-  __shared__ __attribute__((aligned(1024))) char lds[128 * kDensePitch];
-  static_assert(128 * kDensePitch >= 4 * kStage, "ring must fit");
+  // 4-slot ring for the main loop (plus one more slot's worth for the Y
+  // tile of the symmetric epilogues); reused by the staged epilogue.
+  constexpr int kLds = kCapture ? 5 * kStage : 128 * kDensePitch;
+  __shared__ __attribute__((aligned(1024))) char lds[kLds];
+  static_assert(128 * kDensePitch >= 4 * kStage && kLds >= 4 * kStage, "ring must fit");
   char* const st0 = lds;
   char* const st1 = lds + kStage;
   char* const st2 = lds + 2 * kStage;
@@ -828,25 +830,22 @@ __global__ __launch_bounds__(512) void gemm256_kernel(const GemmLaunch L) {
   const int dB = kCapture ? (S.upperB ? tj * (BN / BK) : 0) : (TR == 2 ? KT : 0);
   const T* const baseAT = (const T*)S.A + mat * S.strideA + ti * BM;
   const T* const baseBT = (const T*)S.B + mat * S.strideB + tj * BN;
-  // Gram products (lda = ldb) keep both offsets in registers; the final
-  // product recomputes them per issue from the lane index.
+  // Only one leading dimension is ever read transposed in a launch (Gram
+  // products have lda = ldb; the final product transposes one operand), so
+  // a lane's two offsets are computed once.
+  const int ldTA = S.lda, ldTB = kCapture ? S.lda : S.ldb;
+  const int ldT = TR == 2 ? ldTB : ldTA;  // the one transposed operand's (Gram: lda = ldb)
   int offT[2];
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
     const int r = wave * 4 + 2 * p + (lane >> 5);
-    offT[p] = r * S.lda + (((lane & 31) ^ (4 * (r & 3))) << 3);
+    offT[p] = r * ldT + (((lane & 31) ^ (4 * (r & 3))) << 3);
   }
-  auto tr_off = [wave, lane, offT](int p, int ld) __attribute__((always_inline)) {
-    if constexpr (kCapture) {
-      (void)ld;
-      return offT[p];
-    } else {
-      const int r = wave * 4 + 2 * p + (lane >> 5);
-      return r * ld + ((((lane & 31) ^ (4 * (r & 3)))) << 3);
-    }
+  auto tr_off = [offT](int p, int ld) __attribute__((always_inline)) {
+    (void)ld;
+    return offT[p];
   };
   const int dstT = wave * 4 * 512;
-  const int ldTA = S.lda, ldTB = kCapture ? S.lda : S.ldb;
   auto issue = [&gA, &gB, tr_off, baseAT, baseBT, ldTA, ldTB, dstA, dstT, dA, dB](char* st, int kt) __attribute__((always_inline)) {
     const int k0 = kt * BK;
     const uint32_t sbase = __builtin_amdgcn_readfirstlane(lds_addr(st));
@@ -893,131 +892,191 @@ __global__ __launch_bounds__(512) void gemm256_kernel(const GemmLaunch L) {
     const half4 hi = tr_read4(pan, k0 + 4, c0, tjl);
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   };
-  auto compute_m = [&acc, frag_n, frag_t, wm, wn](const char* st, auto tac, auto tbc) __attribute__((always_inline)) {
+
+  // Two register sets of operand fragments, one per 16-wide k-step: the set
+  // of the next k-step is read from LDS while the MFMAs of the current one
+  // run, across k-tile boundaries too, so LDS latency stays off the MFMA
+  // pipe.  The layout (direct or transposed panel) of each operand is a
+  // template argument wherever it is known at compile time.
+  half8 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
+  auto load = [&](half8 (&fa)[FM], half8 (&fb)[FN], const char* st, int kk, auto tac,
+                  auto tbc) __attribute__((always_inline)) {
     constexpr bool TA = decltype(tac)::value, TB = decltype(tbc)::value;
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      half8 af[FM], bf[FN];
+    for (int fi = 0; fi < FM; ++fi)
+      fa[fi] = TA ? frag_t(st, wm * WTM + fi * 32, kk) : frag_n(st, wm * WTM + fi * 32, kk);
 #pragma unroll
-      for (int fi = 0; fi < FM; ++fi)
-        af[fi] = TA ? frag_t(st, wm * WTM + fi * 32, kk) : frag_n(st, wm * WTM + fi * 32, kk);
+    for (int fj = 0; fj < FN; ++fj)
+      fb[fj] = TB ? frag_t(st + kStageA, wn * WTN + fj * 32, kk)
+                  : frag_n(st + kStageA, wn * WTN + fj * 32, kk);
+  };
+  auto mma = [&acc](const half8 (&fa)[FM], const half8 (&fb)[FN]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int fi = 0; fi < FM; ++fi)
 #pragma unroll
       for (int fj = 0; fj < FN; ++fj)
-        bf[fj] = TB ? frag_t(st + kStageA, wn * WTN + fj * 32, kk)
-                    : frag_n(st + kStageA, wn * WTN + fj * 32, kk);
+        acc[fi][fj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[fi], fb[fj], acc[fi][fj], 0, 0, 0);
+  };
+
+  // The epilogues of A², B·Q, B·A and B·(P·A) need the previous iterate Y
+  // (the B operand, block-upper) at the output positions: block (ti, tj) of
+  // Y, which is stored since ti ≤ tj.  It is fetched into LDS during the last
+  // four k-tiles as eight transposed-format panels of 32 rows, in pairs
+  // (32 KiB, four loads per wave, like a k-tile): pair 3 into the LDS beyond
+  // the ring when k-tile KT − 1 is issued, pairs 0, 1, 2 into the ring slots
+  // of k-tiles KT − 4, KT − 3, KT − 2 as each is released.  KT is a multiple
+  // of 8 for these products (K is m padded to the tile).
+  auto issue_y = [&](char* dst, int q) __attribute__((always_inline)) {
+    const uint32_t sbase = __builtin_amdgcn_readfirstlane(lds_addr(dst));
 #pragma unroll
-      for (int fi = 0; fi < FM; ++fi)
+    for (int h = 0; h < 2; ++h) {
+      const T* b = baseBT + (int64_t)(ti * BM + 64 * q + 32 * h) * ldTB;
 #pragma unroll
-        for (int fj = 0; fj < FN; ++fj)
-          acc[fi][fj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[fi], bf[fj], acc[fi][fj], 0, 0, 0);
+      for (int p = 0; p < 2; ++p)
+        dma16(b + tr_off(p, ldTB), __builtin_amdgcn_readfirstlane(sbase + h * kStageA + dstT + p * 1024));
     }
   };
 
-  // The epilogues of A², B·Q, B·A and B·(P·A) need the previous iterate Y at
-  // the output positions.  Y is the B operand (a symmetric matrix), so when
-  // the ring holds k-tile ti·8 + wm·4 + fi, its B tile contains
-  // Y[tj·256 + jl][k] = Y[i][j] for this wave's rows i of block fi: each lane
-  // copies its four consecutive i of each column (one 8-byte LDS read).
-  // In a transposed B panel the same four values (rows k = 8q + 4·lh .. +3,
-  // column jl) are one transposed read.
-  // The k-tiles of block ti are in the phase with B transposed when ti < tj
-  // and in the direct phase when ti == tj (never in the first phase), so the
-  // layout of the capture is fixed by the phase.
-  half4 ycap[kCapture ? FM : 1][FN][4];
-  const int capBase = ti * 8 + wm * 4;
-  auto capture_fi = [&ycap, wn, lr, lh, sw, tg, tjl](const char* st, auto fic, auto tbc) __attribute__((always_inline)) {
-    constexpr int fi = decltype(fic)::value;
-    if constexpr (kCapture) {
-      if constexpr (decltype(tbc)::value) {
-#pragma unroll
-        for (int fj = 0; fj < FN; ++fj)
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            ycap[fi][fj][q] = tr_read4(st + kStageA, 8 * q + 4 * (tg >> 1),
-                                       wn * WTN + fj * 32 + 16 * (tg & 1), tjl);
-      } else {
-#pragma unroll
-        for (int fj = 0; fj < FN; ++fj)
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            ycap[fi][fj][q] = *(const half4*)(st + kStageA + (wn * WTN + fj * 32 + lr) * kRowB +
-                                              ((q ^ sw) << 4) + lh * 8);
-      }
-    }
-  };
-  auto capture = [&](const char* st, int k, auto tac, auto tbc) __attribute__((always_inline)) {
-    if constexpr (kCapture && !decltype(tac)::value) {
-      switch (k - capBase) {
-        case 0: capture_fi(st, std::integral_constant<int, 0>{}, tbc); break;
-        case 1: capture_fi(st, std::integral_constant<int, 1>{}, tbc); break;
-        case 2: capture_fi(st, std::integral_constant<int, 2>{}, tbc); break;
-        case 3: capture_fi(st, std::integral_constant<int, 3>{}, tbc); break;
-        default: break;
-      }
-    }
-  };
-
-  // Weight update: the first half of the tile's bf16 weights is loaded at
-  // k-tile KT − 2, after the last k-tile's operand loads, and lands while the
-  // last two k-tiles are multiplied.
+  // Weight update: the first half of the tile's bf16 weights is loaded after
+  // the loads of k-tile KT − 1 are issued (in k-tile KT − 3) and lands while
+  // the last k-tiles are multiplied.
   [[maybe_unused]] WeightPrefetch wpf;
   [[maybe_unused]] EpiArgs<T> Ew;
   bool pref = false;
   if constexpr (EPI == EPI_UPDATE) {
     Ew = make_epi<T, EPI>(L, S, mat);
-    pref = KT >= 2 && weight_prefetch_ok(Ew, ti, tj);
+    pref = KT >= 4 && weight_prefetch_ok(Ew, ti, tj);
   }
-  // Each k-tile is 4 load instructions per wave; wait until the oldest
-  // outstanding k-tile has landed, leaving the younger ones in flight (and
-  // the 16 weight loads, when they were issued after it).
+
+  // One k-tile k (ring slot cur; nxt holds k + 1; fill held k − 1):
+  //   read the fragments of the second k-step of k;  MFMAs of the first;
+  //   wait until k-tile k + 1 has landed for every wave (each k-tile is four
+  //   loads per wave; younger loads stay in flight) — the barrier also means
+  //   every wave is done with slot fill;  refill fill with k + 3 (and the
+  //   tail loads);  read the first k-step of k + 1 (same phase);  MFMAs of
+  //   the second k-step of k.
   // The barrier is a bare s_barrier: a __syncthreads() would also wait for
-  // every outstanding load (the loads of the younger k-tiles included).  The
-  // "memory" clobber keeps the compiler from moving LDS accesses across it;
-  // every wave's own ds_reads of the slot about to be refilled completed
-  // before its MFMAs, hence before it reached the barrier.
-  auto step = [&](const char* cur, char* nxt, int k, auto tac, auto tbc) __attribute__((always_inline)) {
-    const int ahead = min(2, KT - 1 - k);
-    const bool wpend = pref && k >= KT - 1;  // weight loads younger than k-tile k
-    if (ahead >= 2) asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
-    else if (ahead == 1) asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
-    else if (wpend) asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-    if (k + 3 < KT) issue(nxt, k + 3);
-    if constexpr (EPI == EPI_UPDATE) {
-      if (pref && k == KT - 2) weight_prefetch<0>(Ew, ti, tj, tid, wpf);
+  // every outstanding load.  The "memory" clobber keeps the compiler from
+  // moving LDS accesses across it; sched_barrier keeps the MFMAs in place.
+  auto first_half = [&](const char* cur, auto tac, auto tbc) __attribute__((always_inline)) {
+    load(fa1, fb1, cur, 1, tac, tbc);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(fa0, fb0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto second_half = [&](const char* nxt, auto tan, auto tbn) __attribute__((always_inline)) {
+    load(fa0, fb0, nxt, 0, tan, tbn);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(fa1, fb1);
+  };
+  // Steps with k + 1 in the same phase and at least four k-tiles after k.
+  auto plain = [&](const char* cur, const char* nxt, char* fill, int k, auto tac, auto tbc) __attribute__((always_inline)) {
+    first_half(cur, tac, tbc);
+    asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
+    issue(fill, k + 3);
+    second_half(nxt, tac, tbc);
+  };
+  // Any step: phase ends and the last k-tiles (tail loads, shorter waits).
+  auto step = [&](const char* cur, const char* nxt, char* fill, int k, int k1, auto tac,
+                  auto tbc) __attribute__((always_inline)) {
+    first_half(cur, tac, tbc);
+    const int r = KT - 1 - k;  // k-tiles after this one
+    if (kCapture && (r == 1 || r == 2)) {
+      asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+    } else if (r >= 2) {
+      asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
+    } else if (r == 1) {
+      if (pref) asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    } else if (kCapture) {
+      asm volatile("s_barrier" ::: "memory");
     }
-    capture(cur, k, tac, tbc);
-    compute_m(cur, tac, tbc);
+    if (r >= 3) issue(fill, k + 3);
+    if constexpr (kCapture) {
+      if (r == 3) issue_y(lds + 4 * kStage, 3);
+      else if (r <= 2) issue_y(fill, 2 - r);
+    }
+    if constexpr (EPI == EPI_UPDATE) {
+      if (pref && r == 2) weight_prefetch<0>(Ew, ti, tj, tid, wpf);
+    }
+    if (k + 1 < k1) load(fa0, fb0, nxt, 0, tac, tbc);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(fa1, fb1);
   };
   // k-tiles in three phases of fixed operand layouts: [0, dA) both
   // transposed, [dA, dB) B transposed, [dB, KT) both direct (dA ≤ dB since
-  // ti ≤ tj; both are multiples of 8, so every phase starts on ring slot 0).
+  // ti ≤ tj).  Phase lengths are multiples of 8 (KT, dA, dB are), so every
+  // phase starts on ring slot 0 and runs in whole groups of four k-tiles.
+  // The first k-step of a phase is read at its start (the step before it
+  // does not know the layout).
   auto phase = [&](int k0, int k1, auto tac, auto tbc) __attribute__((always_inline)) {
-    for (int kt = k0; kt < k1; kt += 4) {
-      step(st0, st3, kt, tac, tbc);
-      if (kt + 1 < k1) step(st1, st0, kt + 1, tac, tbc);
-      if (kt + 2 < k1) step(st2, st1, kt + 2, tac, tbc);
-      if (kt + 3 < k1) step(st3, st2, kt + 3, tac, tbc);
+    if (k0 < k1) load(fa0, fb0, st0, 0, tac, tbc);
+    int kt = k0;
+    for (; kt + 4 < k1 && kt + 8 <= KT; kt += 4) {
+      plain(st0, st1, st3, kt, tac, tbc);
+      plain(st1, st2, st0, kt + 1, tac, tbc);
+      plain(st2, st3, st1, kt + 2, tac, tbc);
+      plain(st3, st0, st2, kt + 3, tac, tbc);
+    }
+    for (; kt < k1; kt += 4) {
+      step(st0, st1, st3, kt, k1, tac, tbc);
+      step(st1, st2, st0, kt + 1, k1, tac, tbc);
+      step(st2, st3, st1, kt + 2, k1, tac, tbc);
+      step(st3, st0, st2, kt + 3, k1, tac, tbc);
     }
   };
 
   issue(st0, 0);
   if (KT > 1) issue(st1, 1);
   if (KT > 2) issue(st2, 2);
+  if (KT > 2) asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+  else if (KT > 1) asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
   if constexpr (kCapture) {
     phase(0, dA, std::true_type{}, std::true_type{});
     phase(dA, dB, std::false_type{}, std::true_type{});
     phase(dB, KT, std::false_type{}, std::false_type{});
-  } else if constexpr (TR == 1) {
-    phase(0, KT, std::true_type{}, std::false_type{});
-  } else if constexpr (TR == 2) {
-    phase(0, KT, std::false_type{}, std::true_type{});
   } else {
-    phase(0, KT, std::false_type{}, std::false_type{});
+    // One layout for every k-tile: KT ≥ 8, so the loop of whole groups runs
+    // at least once (written so, which keeps the accumulators in place).
+    constexpr auto ta = std::bool_constant<TR == 1>{};
+    constexpr auto tb = std::bool_constant<TR == 2>{};
+    load(fa0, fb0, st0, 0, ta, tb);
+    int kt = 0;
+    do {
+      plain(st0, st1, st3, kt, ta, tb);
+      plain(st1, st2, st0, kt + 1, ta, tb);
+      plain(st2, st3, st1, kt + 2, ta, tb);
+      plain(st3, st0, st2, kt + 3, ta, tb);
+      kt += 4;
+    } while (kt + 4 < KT);
+    step(st0, st1, st3, kt, KT, ta, tb);
+    step(st1, st2, st0, kt + 1, KT, ta, tb);
+    step(st2, st3, st1, kt + 2, KT, ta, tb);
+    step(st3, st0, st2, kt + 3, KT, ta, tb);
   }
 
-  // Every wave is done with the ring before it is reused for staging.
+  // Every wave is done with the ring (and the tail loads have landed) before
+  // it is read for Y or reused for staging.
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  half4 ycap[kCapture ? FM : 1][FN][4];
+  if constexpr (kCapture) {
+    // Panel c (rows 32c .. 32c+31 of the Y block) is in pair c/2: pairs 0-2
+    // in the ring slots of k-tiles KT − 4 .. KT − 2, pair 3 beyond the ring.
+    // Lane (lr, lh) takes Y at rows 8q + 4·lh .. +3 of panel wm·4 + fi,
+    // column wn·64 + fj·32 + lr: one transposed read each.
+#pragma unroll
+    for (int fi = 0; fi < FM; ++fi) {
+      const int c = wm * 4 + fi, q = c >> 1;
+      const char* pan = (q == 3 ? lds + 4 * kStage : lds + ((KT - 4 + q) & 3) * kStage) + (c & 1) * kStageA;
+#pragma unroll
+      for (int fj = 0; fj < FN; ++fj)
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq)
+          ycap[fi][fj][qq] = tr_read4(pan, 8 * qq + 4 * (tg >> 1), wn * WTN + fj * 32 + 16 * (tg & 1), tjl);
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  }
   const EpiArgs<T> E = make_epi<T, EPI>(L, S, mat);
   if constexpr (kSym) {
     // acc ← storage value of the result: sOut·y(i, j).
@@ -1076,6 +1135,9 @@ __global__ __launch_bounds__(512) void gemm256_kernel(const GemmLaunch L) {
 template <int EPI>
 hipError_t launch_epi(int op, int tile, const GemmLaunch& L, int blocks, hipStream_t st) {
   if (op == OP_F16 && tile == 256) {
+    // the main loop runs whole groups of four k-tiles, phases of eight
+    for (int k = 0; k < L.nseg; ++k)
+      if (L.seg[k].K <= 0 || L.seg[k].K % 256 != 0) return hipErrorInvalidValue;
     if constexpr (EPI == EPI_UPDATE || EPI == EPI_OUT) {
       // one bucket per launch, so every segment shares the operand layout
       if (L.seg[0].transA)
