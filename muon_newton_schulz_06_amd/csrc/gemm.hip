@@ -40,6 +40,7 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 // Native 16-byte vector (scalarisable, unlike HIP's uint4 class type).
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 // Compile-time loop: f(std::integral_constant<int, P>) for P in [B, E).  The
 // index reaches the body as a constant, so register arrays indexed by it are
@@ -443,6 +444,20 @@ __device__ __forceinline__ uint32_t lds_addr(const char* p) {
   return (uint32_t)(uintptr_t)(lds_ptr_t)p;
 }
 
+// acc += a·bᵀ with a 16×16×32 fp16 MFMA whose result register is its
+// accumulator input.  Written as inline asm with a tied operand: the
+// built-in lets the register allocator give each result a fresh register
+// (a rotating accumulator), which at 128 accumulator registers per lane
+// leaves too few for the operand pipeline.  The asm is opaque to the
+// compiler's hazard tracking, so the kernel keeps the rules itself: the
+// accumulators are written only by these MFMAs between the wait after
+// their initialisation and the wait before the epilogue reads them
+// (s_nop, below), and operand registers are only overwritten by LDS reads,
+// which read-after-MFMA ordering does not constrain.
+__device__ __forceinline__ void mfma16_acc(floatx4& acc, const half8& a, const half8& b) {
+  asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+
 // ----- transposed operand panels ---------------------------------------------
 // A block-upper symmetric operand (only blocks bi ≤ bj stored) supplies the
 // k-tiles left of its diagonal block from the transposed position: rows k of
@@ -481,16 +496,20 @@ __device__ __forceinline__ int stage_off(int row, int col) {
   return row * 512 + ((((col >> 3) ^ (row & 31))) << 4) + (col & 7) * 2;
 }
 
+// Accumulators of the 256-tile kernel: 16×16×32 MFMAs, block (fi, fj) of a
+// wave's 128×64 region; lane l, register r holds row 16·fi + 4·(l/16) + r,
+// column 16·fj + l%16 (lc = l%16, lg = l/16 below).
+
 // acc → LDS as rows of C (one 2-byte write per element).
 template <int FM, int FN>
-__device__ __forceinline__ void stage_rows(char* lds, int wm, int wn, int lr, int lh,
-                                           const floatx16 (&acc)[FM][FN]) {
+__device__ __forceinline__ void stage_rows(char* lds, int wm, int wn, int lc, int lg,
+                                           const floatx4 (&acc)[FM][FN]) {
   static_for<0, FM>([&](auto fi) {
     static_for<0, FN>([&](auto fj) {
-      static_for<0, 16>([&](auto rc) {
+      static_for<0, 4>([&](auto rc) {
         constexpr int r = decltype(rc)::value;
-        const int il = wm * 128 + fi * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-        const int jl = wn * 64 + fj * 32 + lr;
+        const int il = wm * 128 + fi * 16 + 4 * lg + r;
+        const int jl = wn * 64 + fj * 16 + lc;
         *(_Float16*)(lds + stage_off(il, jl)) = (_Float16)acc[fi][fj][r];
       });
     });
@@ -500,20 +519,18 @@ __device__ __forceinline__ void stage_rows(char* lds, int wm, int wn, int lr, in
 // acc → LDS as rows of Cᵀ: a lane's four consecutive rows of one column are
 // one 8-byte write.
 template <int FM, int FN>
-__device__ __forceinline__ void stage_cols(char* lds, int wm, int wn, int lr, int lh,
-                                           const floatx16 (&acc)[FM][FN]) {
+__device__ __forceinline__ void stage_cols(char* lds, int wm, int wn, int lc, int lg,
+                                           const floatx4 (&acc)[FM][FN]) {
   static_for<0, FM>([&](auto fi) {
     static_for<0, FN>([&](auto fj) {
-      static_for<0, 4>([&](auto q) {
-        const int jl = wn * 64 + fj * 32 + lr;
-        const int il = wm * 128 + fi * 32 + 8 * q + 4 * lh;
-        half4 v;
-        v[0] = (_Float16)acc[fi][fj][4 * q + 0];
-        v[1] = (_Float16)acc[fi][fj][4 * q + 1];
-        v[2] = (_Float16)acc[fi][fj][4 * q + 2];
-        v[3] = (_Float16)acc[fi][fj][4 * q + 3];
-        *(half4*)(lds + stage_off(jl, il)) = v;
-      });
+      const int jl = wn * 64 + fj * 16 + lc;
+      const int il = wm * 128 + fi * 16 + 4 * lg;
+      half4 v;
+      v[0] = (_Float16)acc[fi][fj][0];
+      v[1] = (_Float16)acc[fi][fj][1];
+      v[2] = (_Float16)acc[fi][fj][2];
+      v[3] = (_Float16)acc[fi][fj][3];
+      *(half4*)(lds + stage_off(jl, il)) = v;
     });
   });
 }
@@ -580,18 +597,18 @@ __device__ __forceinline__ void store_staged(_Float16* dst, int ldc, const char*
 // dst: the tile (ti, tj) from its rows, the tile (tj, ti) from its columns.
 template <int FM, int FN, bool kTwo>
 __device__ __forceinline__ void write_symmetric(_Float16* dst, int ldc, char* lds, int ti, int tj,
-                                                int wm, int wn, int lr, int lh, int tid,
-                                                const floatx16 (&acc)[FM][FN],
+                                                int wm, int wn, int lc, int lg, int tid,
+                                                const floatx4 (&acc)[FM][FN],
                                                 const SecondCopy& sc, bool mirror) {
   const bool diag = ti == tj;
-  stage_rows<FM, FN>(lds, wm, wn, lr, lh, acc);
+  stage_rows<FM, FN>(lds, wm, wn, lc, lg, acc);
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   store_staged<true, kTwo>(dst, ldc, lds, ti, tj, diag, tid, sc);
   // Block-upper output: an off-diagonal tile alone; a diagonal tile still
   // gets its lower half from the transposed staging (exactly symmetric).
   if (!mirror && !diag) return;
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  stage_cols<FM, FN>(lds, wm, wn, lr, lh, acc);
+  stage_cols<FM, FN>(lds, wm, wn, lc, lg, acc);
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   store_staged<false, kTwo>(dst, ldc, lds, tj, ti, diag, tid, sc);
   // The kernel ends here (LDS is not used again), so no closing barrier.
@@ -638,15 +655,15 @@ __device__ __forceinline__ void weight_prefetch(const EpiArgs<_Float16>& E, int 
 // acc of the waves of row half `half` → LDS as fp32 rows (u applied).
 template <int FM, int FN>
 __device__ __forceinline__ void stage_dense_half(char* lds, int half, float u, int wm, int wn,
-                                                 int lr, int lh, const floatx16 (&acc)[FM][FN]) {
+                                                 int lc, int lg, const floatx4 (&acc)[FM][FN]) {
   if (half) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   if (wm == half) {
     static_for<0, FM>([&](auto fi) {
       static_for<0, FN>([&](auto fj) {
-        static_for<0, 16>([&](auto rc) {
+        static_for<0, 4>([&](auto rc) {
           constexpr int r = decltype(rc)::value;
-          const int row = fi * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-          const int jl = wn * 64 + fj * 32 + lr;
+          const int row = fi * 16 + 4 * lg + r;
+          const int jl = wn * 64 + fj * 16 + lc;
           *(float*)(lds + row * kDensePitch + jl * 4) = u * acc[fi][fj][r];
         });
       });
@@ -658,8 +675,8 @@ __device__ __forceinline__ void stage_dense_half(char* lds, int half, float u, i
 // Weight update of a tile inside the matrix with prefetched bf16 weights.
 template <int FM, int FN>
 __device__ __forceinline__ void update_prefetched(const EpiArgs<_Float16>& E, char* lds, int ti,
-                                                  int tj, int wm, int wn, int lr, int lh, int tid,
-                                                  const floatx16 (&acc)[FM][FN],
+                                                  int tj, int wm, int wn, int lc, int lg, int tid,
+                                                  const floatx4 (&acc)[FM][FN],
                                                   WeightPrefetch& W) {
   weight_prefetch<1>(E, ti, tj, tid, W);
   const int c = tid & 63;
@@ -667,7 +684,7 @@ __device__ __forceinline__ void update_prefetched(const EpiArgs<_Float16>& E, ch
                        (int64_t)tj * 256 + c * 4;
   static_for<0, 2>([&](auto hc) {
     constexpr int half = decltype(hc)::value;
-    stage_dense_half<FM, FN>(lds, half, E.u, wm, wn, lr, lh, acc);
+    stage_dense_half<FM, FN>(lds, half, E.u, wm, wn, lc, lg, acc);
 #pragma unroll
     for (int it = 0; it < kDenseIters; ++it) {
       const int row = it * 8 + (tid >> 6);
@@ -688,18 +705,18 @@ __device__ __forceinline__ void update_prefetched(const EpiArgs<_Float16>& E, ch
 
 template <int EPI, int FM, int FN>
 __device__ __forceinline__ void dense_staged(const EpiArgs<_Float16>& E, char* lds, int ti, int tj,
-                                             int wm, int wn, int lr, int lh, int tid,
-                                             const floatx16 (&acc)[FM][FN]) {
+                                             int wm, int wn, int lc, int lg, int tid,
+                                             const floatx4 (&acc)[FM][FN]) {
   const bool vec_ok = (E.userLd % 4 == 0) && (((uintptr_t)E.user & 15) == 0);
   for (int half = 0; half < 2; ++half) {
     if (half) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     if (wm == half) {
       static_for<0, FM>([&](auto fi) {
         static_for<0, FN>([&](auto fj) {
-          static_for<0, 16>([&](auto rc) {
+          static_for<0, 4>([&](auto rc) {
             constexpr int r = decltype(rc)::value;
-            const int row = fi * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-            const int jl = wn * 64 + fj * 32 + lr;
+            const int row = fi * 16 + 4 * lg + r;
+            const int jl = wn * 64 + fj * 16 + lc;
             *(float*)(lds + row * kDensePitch + jl * 4) = E.u * acc[fi][fj][r];
           });
         });
@@ -777,7 +794,7 @@ template <int EPI, int TR = 0>
 __global__ __launch_bounds__(512) void gemm256_kernel(const GemmLaunch L) {
   using T = _Float16;
   constexpr int BM = 256, BN = 256, BK = 32, WN = 4;
-  constexpr int WTM = 128, WTN = 64, FM = 4, FN = 2;
+  constexpr int WTM = 128, WTN = 64, FM = 8, FN = 4;  // 16×16 blocks per wave
   constexpr bool kSym = EPI == EPI_SYRK || EPI == EPI_SQ || EPI == EPI_AXPY;
   constexpr bool kCapture = EPI == EPI_SQ || EPI == EPI_AXPY;
   // 4-slot ring for the main loop (plus one more slot's worth for the Y
@@ -798,7 +815,7 @@ __global__ __launch_bounds__(512) void gemm256_kernel(const GemmLaunch L) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave - wm * WN;
-  const int lr = lane & 31, lh = lane >> 5;
+  const int lc = lane & 15, lg = lane >> 4;
 
   const T* Ag = (const T*)S.A + mat * S.strideA + (int64_t)ti * BM * S.lda;
   const T* Bg = (const T*)S.B + mat * S.strideB + (int64_t)tj * BN * S.ldb;
@@ -869,54 +886,73 @@ __global__ __launch_bounds__(512) void gemm256_kernel(const GemmLaunch L) {
     }
   };
 
-  floatx16 acc[FM][FN];
+  floatx4 acc[FM][FN];
 #pragma unroll
   for (int fi = 0; fi < FM; ++fi)
 #pragma unroll
     for (int fj = 0; fj < FN; ++fj)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[fi][fj][e] = 0.f;
+      for (int e = 0; e < 4; ++e) acc[fi][fj][e] = 0.f;
+  // The zeros are written (in order) before the wait that precedes the
+  // first MFMA reading them.
+#pragma unroll
+  for (int fi = 0; fi < FM; ++fi)
+#pragma unroll
+    for (int fj = 0; fj < FN; ++fj) asm volatile("" : "+v"(acc[fi][fj]));
+  asm volatile("s_nop 7");
 
-  // Fragment addresses: rows base + lr with base a multiple of 32, so the
-  // swizzle depends on lr only.  A transposed panel gives the same fragment
-  // (row lr, k = 16·kk + 8·lh + 0..7) from two transposed reads; the 16-lane
-  // group g = lane/16 covers rows 16·(g&1) .. +15 and k-half g/2.
-  const int sw = swz4(lr);
-  const int tg = lane >> 4, tjl = lane & 15;
-  auto frag_n = [lr, lh, sw](const char* pan, int row0, int kk) __attribute__((always_inline)) {
-    return *(const half8*)(pan + (row0 + lr) * kRowB + (((2 * kk + lh) ^ sw) * 16));
+  // Operand fragments of a 16×16×32 MFMA: lane l holds row row0 + l%16 at
+  // k = 8·(l/16) .. +7 of the k-tile, i.e. 16-byte chunk l/16 of the row
+  // (row0 is a multiple of 16, so the swizzle depends on l%16 only).  A
+  // transposed panel gives the same fragment from two transposed reads.
+  const int sw = swz4(lc);
+  auto frag_n = [lc, lg, sw](const char* pan, int row0) __attribute__((always_inline)) {
+    return *(const half8*)(pan + (row0 + lc) * kRowB + ((lg ^ sw) << 4));
   };
-  auto frag_t = [tg, tjl](const char* pan, int row0, int kk) __attribute__((always_inline)) {
-    const int c0 = row0 + 16 * (tg & 1), k0 = kk * 16 + 8 * (tg >> 1);
-    const half4 lo = tr_read4(pan, k0, c0, tjl);
-    const half4 hi = tr_read4(pan, k0 + 4, c0, tjl);
+  auto frag_t = [lc, lg](const char* pan, int row0) __attribute__((always_inline)) {
+    const half4 lo = tr_read4(pan, 8 * lg, row0, lc);
+    const half4 hi = tr_read4(pan, 8 * lg + 4, row0, lc);
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   };
 
-  // Two register sets of operand fragments, one per 16-wide k-step: the set
-  // of the next k-step is read from LDS while the MFMAs of the current one
-  // run, across k-tile boundaries too, so LDS latency stays off the MFMA
-  // pipe.  The layout (direct or transposed panel) of each operand is a
-  // template argument wherever it is known at compile time.
-  half8 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
-  auto load = [&](half8 (&fa)[FM], half8 (&fb)[FN], const char* st, int kk, auto tac,
-                  auto tbc) __attribute__((always_inline)) {
-    constexpr bool TA = decltype(tac)::value, TB = decltype(tbc)::value;
-#pragma unroll
-    for (int fi = 0; fi < FM; ++fi)
-      fa[fi] = TA ? frag_t(st, wm * WTM + fi * 32, kk) : frag_n(st, wm * WTM + fi * 32, kk);
-#pragma unroll
-    for (int fj = 0; fj < FN; ++fj)
-      fb[fj] = TB ? frag_t(st + kStageA, wn * WTN + fj * 32, kk)
-                  : frag_n(st + kStageA, wn * WTN + fj * 32, kk);
+  // A k-tile is one 32-wide k-step: 8 × 4 MFMAs per wave, in four
+  // quarters by rows (A blocks 2q, 2q+1).  Registers: the B fragments of the
+  // current and of the next k-tile (alternating by k-tile parity) and two
+  // sets of A-quarter fragments; the fragments of the next quarter are read
+  // from LDS while the MFMAs of the current one run, across k-tile
+  // boundaries too.  The layout (direct or transposed panel) of each
+  // operand is a template argument wherever it is known at compile time.
+  half8 fb0[FN], fb1[FN], fax[2], fay[2];
+  auto bset = [&](auto pc) -> half8 (&)[FN] {
+    if constexpr (decltype(pc)::value) return fb1;
+    else return fb0;
   };
-  auto mma = [&acc](const half8 (&fa)[FM], const half8 (&fb)[FN]) __attribute__((always_inline)) {
+  auto load_a = [&](half8 (&fa)[2], const char* st, int q, auto tac) __attribute__((always_inline)) {
 #pragma unroll
-    for (int fi = 0; fi < FM; ++fi)
+    for (int f = 0; f < 2; ++f) {
+      const int row0 = wm * WTM + (2 * q + f) * 16;
+      fa[f] = decltype(tac)::value ? frag_t(st, row0) : frag_n(st, row0);
+    }
+  };
+  auto load_b = [&](half8 (&fb)[FN], const char* st, auto tbc) __attribute__((always_inline)) {
+#pragma unroll
+    for (int fj = 0; fj < FN; ++fj) {
+      const int row0 = wn * WTN + fj * 16;
+      fb[fj] = decltype(tbc)::value ? frag_t(st + kStageA, row0) : frag_n(st + kStageA, row0);
+    }
+  };
+  auto mma = [&acc](const half8 (&fa)[2], const half8 (&fb)[FN], auto qc) __attribute__((always_inline)) {
+    constexpr int q = decltype(qc)::value;
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
 #pragma unroll
       for (int fj = 0; fj < FN; ++fj)
-        acc[fi][fj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[fi], fb[fj], acc[fi][fj], 0, 0, 0);
+        mfma16_acc(acc[2 * q + f][fj], fa[f], fb[fj]);
   };
+  constexpr auto kQ0 = std::integral_constant<int, 0>{};
+  constexpr auto kQ1 = std::integral_constant<int, 1>{};
+  constexpr auto kQ2 = std::integral_constant<int, 2>{};
+  constexpr auto kQ3 = std::integral_constant<int, 3>{};
 
   // The epilogues of A², B·Q, B·A and B·(P·A) need the previous iterate Y
   // (the B operand, block-upper) at the output positions: block (ti, tj) of
@@ -948,38 +984,54 @@ __global__ __launch_bounds__(512) void gemm256_kernel(const GemmLaunch L) {
     pref = KT >= 4 && weight_prefetch_ok(Ew, ti, tj);
   }
 
-  // One k-tile k (ring slot cur; nxt holds k + 1; fill held k − 1):
-  //   read the fragments of the second k-step of k;  MFMAs of the first;
+  // One k-tile k (ring slot cur; nxt holds k + 1; fill held k − 1; pc its
+  // parity, selecting the B registers):
+  //   quarters 0-2: read the next A quarter of k while the MFMAs of the
+  //   current one run;
   //   wait until k-tile k + 1 has landed for every wave (each k-tile is four
   //   loads per wave; younger loads stay in flight) — the barrier also means
   //   every wave is done with slot fill;  refill fill with k + 3 (and the
-  //   tail loads);  read the first k-step of k + 1 (same phase);  MFMAs of
-  //   the second k-step of k.
+  //   tail loads);
+  //   quarter 3: read B and A quarter 0 of k + 1 (same phase) while its
+  //   MFMAs run.
   // The barrier is a bare s_barrier: a __syncthreads() would also wait for
   // every outstanding load.  The "memory" clobber keeps the compiler from
   // moving LDS accesses across it; sched_barrier keeps the MFMAs in place.
-  auto first_half = [&](const char* cur, auto tac, auto tbc) __attribute__((always_inline)) {
-    load(fa1, fb1, cur, 1, tac, tbc);
+  auto first_half = [&](const char* cur, auto pc, auto tac) __attribute__((always_inline)) {
+    half8 (&fb)[FN] = bset(pc);
+    load_a(fay, cur, 1, tac);
     __builtin_amdgcn_sched_barrier(0);
-    mma(fa0, fb0);
+    mma(fax, fb, kQ0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_a(fax, cur, 2, tac);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(fay, fb, kQ1);
+    __builtin_amdgcn_sched_barrier(0);
+    load_a(fay, cur, 3, tac);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(fax, fb, kQ2);
     __builtin_amdgcn_sched_barrier(0);
   };
-  auto second_half = [&](const char* nxt, auto tan, auto tbn) __attribute__((always_inline)) {
-    load(fa0, fb0, nxt, 0, tan, tbn);
+  auto head = [&](const char* st, auto pc, auto tac, auto tbc) __attribute__((always_inline)) {
+    load_b(bset(pc), st, tbc);
+    load_a(fax, st, 0, tac);
+  };
+  auto second_half = [&](const char* nxt, auto pc, auto tac, auto tbc) __attribute__((always_inline)) {
+    head(nxt, std::bool_constant<!decltype(pc)::value>{}, tac, tbc);
     __builtin_amdgcn_sched_barrier(0);
-    mma(fa1, fb1);
+    mma(fay, bset(pc), kQ3);
   };
   // Steps with k + 1 in the same phase and at least four k-tiles after k.
-  auto plain = [&](const char* cur, const char* nxt, char* fill, int k, auto tac, auto tbc) __attribute__((always_inline)) {
-    first_half(cur, tac, tbc);
+  auto plain = [&](const char* cur, const char* nxt, char* fill, int k, auto pc, auto tac, auto tbc) __attribute__((always_inline)) {
+    first_half(cur, pc, tac);
     asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
     issue(fill, k + 3);
-    second_half(nxt, tac, tbc);
+    second_half(nxt, pc, tac, tbc);
   };
   // Any step: phase ends and the last k-tiles (tail loads, shorter waits).
-  auto step = [&](const char* cur, const char* nxt, char* fill, int k, int k1, auto tac,
+  auto step = [&](const char* cur, const char* nxt, char* fill, int k, int k1, auto pc, auto tac,
                   auto tbc) __attribute__((always_inline)) {
-    first_half(cur, tac, tbc);
+    first_half(cur, pc, tac);
     const int r = KT - 1 - k;  // k-tiles after this one
     if (kCapture && (r == 1 || r == 2)) {
       asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
@@ -999,30 +1051,32 @@ __global__ __launch_bounds__(512) void gemm256_kernel(const GemmLaunch L) {
     if constexpr (EPI == EPI_UPDATE) {
       if (pref && r == 2) weight_prefetch<0>(Ew, ti, tj, tid, wpf);
     }
-    if (k + 1 < k1) load(fa0, fb0, nxt, 0, tac, tbc);
+    if (k + 1 < k1) head(nxt, std::bool_constant<!decltype(pc)::value>{}, tac, tbc);
     __builtin_amdgcn_sched_barrier(0);
-    mma(fa1, fb1);
+    mma(fay, bset(pc), kQ3);
   };
+  constexpr auto kEven = std::false_type{};
+  constexpr auto kOdd = std::true_type{};
   // k-tiles in three phases of fixed operand layouts: [0, dA) both
   // transposed, [dA, dB) B transposed, [dB, KT) both direct (dA ≤ dB since
   // ti ≤ tj).  Phase lengths are multiples of 8 (KT, dA, dB are), so every
-  // phase starts on ring slot 0 and runs in whole groups of four k-tiles.
-  // The first k-step of a phase is read at its start (the step before it
-  // does not know the layout).
+  // phase starts on ring slot 0 with an even k-tile and runs in whole groups
+  // of four k-tiles.  The first fragments of a phase are read at its start
+  // (the step before it does not know the layout).
   auto phase = [&](int k0, int k1, auto tac, auto tbc) __attribute__((always_inline)) {
-    if (k0 < k1) load(fa0, fb0, st0, 0, tac, tbc);
+    if (k0 < k1) head(st0, kEven, tac, tbc);
     int kt = k0;
     for (; kt + 4 < k1 && kt + 8 <= KT; kt += 4) {
-      plain(st0, st1, st3, kt, tac, tbc);
-      plain(st1, st2, st0, kt + 1, tac, tbc);
-      plain(st2, st3, st1, kt + 2, tac, tbc);
-      plain(st3, st0, st2, kt + 3, tac, tbc);
+      plain(st0, st1, st3, kt, kEven, tac, tbc);
+      plain(st1, st2, st0, kt + 1, kOdd, tac, tbc);
+      plain(st2, st3, st1, kt + 2, kEven, tac, tbc);
+      plain(st3, st0, st2, kt + 3, kOdd, tac, tbc);
     }
     for (; kt < k1; kt += 4) {
-      step(st0, st1, st3, kt, k1, tac, tbc);
-      step(st1, st2, st0, kt + 1, k1, tac, tbc);
-      step(st2, st3, st1, kt + 2, k1, tac, tbc);
-      step(st3, st0, st2, kt + 3, k1, tac, tbc);
+      step(st0, st1, st3, kt, k1, kEven, tac, tbc);
+      step(st1, st2, st0, kt + 1, k1, kOdd, tac, tbc);
+      step(st2, st3, st1, kt + 2, k1, kEven, tac, tbc);
+      step(st3, st0, st2, kt + 3, k1, kOdd, tac, tbc);
     }
   };
 
@@ -1041,39 +1095,46 @@ __global__ __launch_bounds__(512) void gemm256_kernel(const GemmLaunch L) {
     // at least once (written so, which keeps the accumulators in place).
     constexpr auto ta = std::bool_constant<TR == 1>{};
     constexpr auto tb = std::bool_constant<TR == 2>{};
-    load(fa0, fb0, st0, 0, ta, tb);
+    head(st0, kEven, ta, tb);
     int kt = 0;
     do {
-      plain(st0, st1, st3, kt, ta, tb);
-      plain(st1, st2, st0, kt + 1, ta, tb);
-      plain(st2, st3, st1, kt + 2, ta, tb);
-      plain(st3, st0, st2, kt + 3, ta, tb);
+      plain(st0, st1, st3, kt, kEven, ta, tb);
+      plain(st1, st2, st0, kt + 1, kOdd, ta, tb);
+      plain(st2, st3, st1, kt + 2, kEven, ta, tb);
+      plain(st3, st0, st2, kt + 3, kOdd, ta, tb);
       kt += 4;
     } while (kt + 4 < KT);
-    step(st0, st1, st3, kt, KT, ta, tb);
-    step(st1, st2, st0, kt + 1, KT, ta, tb);
-    step(st2, st3, st1, kt + 2, KT, ta, tb);
-    step(st3, st0, st2, kt + 3, KT, ta, tb);
+    step(st0, st1, st3, kt, KT, kEven, ta, tb);
+    step(st1, st2, st0, kt + 1, KT, kOdd, ta, tb);
+    step(st2, st3, st1, kt + 2, KT, kEven, ta, tb);
+    step(st3, st0, st2, kt + 3, KT, kOdd, ta, tb);
   }
+
+  // Wait states between the last MFMA writing an accumulator and the first
+  // other instruction reading it (more than the deepest MFMA needs); the
+  // empty statements order every later use of acc after them.
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
+#pragma unroll
+  for (int fi = 0; fi < FM; ++fi)
+#pragma unroll
+    for (int fj = 0; fj < FN; ++fj) asm volatile("" : "+v"(acc[fi][fj]));
 
   // Every wave is done with the ring (and the tail loads have landed) before
   // it is read for Y or reused for staging.
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  half4 ycap[kCapture ? FM : 1][FN][4];
+  half4 ycap[kCapture ? FM : 1][FN];
   if constexpr (kCapture) {
     // Panel c (rows 32c .. 32c+31 of the Y block) is in pair c/2: pairs 0-2
     // in the ring slots of k-tiles KT − 4 .. KT − 2, pair 3 beyond the ring.
-    // Lane (lr, lh) takes Y at rows 8q + 4·lh .. +3 of panel wm·4 + fi,
-    // column wn·64 + fj·32 + lr: one transposed read each.
+    // Lane (lc, lg) takes Y at rows 16·(fi&1) + 4·lg .. +3 of panel
+    // wm·4 + fi/2, column wn·64 + fj·16 + lc: one transposed read each.
 #pragma unroll
     for (int fi = 0; fi < FM; ++fi) {
-      const int c = wm * 4 + fi, q = c >> 1;
+      const int c = wm * 4 + (fi >> 1), q = c >> 1;
       const char* pan = (q == 3 ? lds + 4 * kStage : lds + ((KT - 4 + q) & 3) * kStage) + (c & 1) * kStageA;
 #pragma unroll
       for (int fj = 0; fj < FN; ++fj)
-#pragma unroll
-        for (int qq = 0; qq < 4; ++qq)
-          ycap[fi][fj][qq] = tr_read4(pan, 8 * qq + 4 * (tg >> 1), wn * WTN + fj * 32 + 16 * (tg & 1), tjl);
+        ycap[fi][fj] = tr_read4(pan, 16 * (fi & 1) + 4 * lg, wn * WTN + fj * 16, lc);
     }
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   }
@@ -1082,14 +1143,14 @@ __global__ __launch_bounds__(512) void gemm256_kernel(const GemmLaunch L) {
     // acc ← storage value of the result: sOut·y(i, j).
     static_for<0, FM>([&](auto fi) {
       static_for<0, FN>([&](auto fj) {
-        static_for<0, 16>([&](auto rc) {
+        static_for<0, 4>([&](auto rc) {
           constexpr int r = decltype(rc)::value;
           const float a = E.u * acc[fi][fj][r];
           float y;
           if constexpr (EPI == EPI_SYRK) {
             y = a;
           } else {
-            const float prev = E.sIn * (float)ycap[fi][fj][r >> 2][r & 3];
+            const float prev = E.sIn * (float)ycap[fi][fj][r];
             y = (EPI == EPI_SQ) ? E.p1 * prev + E.p2 * a : E.p0 * prev + a;
           }
           acc[fi][fj][r] = E.sOut * y;
@@ -1099,10 +1160,10 @@ __global__ __launch_bounds__(512) void gemm256_kernel(const GemmLaunch L) {
     SecondCopy sc{E.outhb, E.sOutB / E.sOut, E.sOutB * E.p0, E.mReal};
     if (EPI == EPI_SQ && E.outhb) {
       // first step: Q₁ = a·I + B₀ written from the same staged B₀ values
-      write_symmetric<FM, FN, true>(E.outh, E.ldc, lds, ti, tj, wm, wn, lr, lh, tid, acc, sc,
+      write_symmetric<FM, FN, true>(E.outh, E.ldc, lds, ti, tj, wm, wn, lc, lg, tid, acc, sc,
                                     S.mirrorOut != 0);
     } else {
-      write_symmetric<FM, FN, false>(E.outh, E.ldc, lds, ti, tj, wm, wn, lr, lh, tid, acc, sc,
+      write_symmetric<FM, FN, false>(E.outh, E.ldc, lds, ti, tj, wm, wn, lc, lg, tid, acc, sc,
                                      S.mirrorOut != 0);
     }
     if constexpr (EPI == EPI_SYRK) {
@@ -1110,10 +1171,10 @@ __global__ __launch_bounds__(512) void gemm256_kernel(const GemmLaunch L) {
         const int gi0 = ti * BM + wm * WTM, gj0 = tj * BN + wn * WTN;
         static_for<0, FM>([&](auto fi) {
           static_for<0, FN>([&](auto fj) {
-            static_for<0, 16>([&](auto rc) {
+            static_for<0, 4>([&](auto rc) {
               constexpr int r = decltype(rc)::value;
-              const int i = gi0 + fi * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-              const int j = gj0 + fj * 32 + lr;
+              const int i = gi0 + fi * 16 + 4 * lg + r;
+              const int j = gj0 + fj * 16 + lc;
               if (i <= j)
                 store_mirror<T>(E.outhb, E.ldc, i, j, (T)((i == j && i < E.mReal) ? E.sOutB : 0.f));
             });
@@ -1124,11 +1185,11 @@ __global__ __launch_bounds__(512) void gemm256_kernel(const GemmLaunch L) {
   } else {
     if constexpr (EPI == EPI_UPDATE) {
       if (pref) {
-        update_prefetched<FM, FN>(E, lds, ti, tj, wm, wn, lr, lh, tid, acc, wpf);
+        update_prefetched<FM, FN>(E, lds, ti, tj, wm, wn, lc, lg, tid, acc, wpf);
         return;
       }
     }
-    dense_staged<EPI, FM, FN>(E, lds, ti, tj, wm, wn, lr, lh, tid, acc);
+    dense_staged<EPI, FM, FN>(E, lds, ti, tj, wm, wn, lc, lg, tid, acc);
   }
 }
 
