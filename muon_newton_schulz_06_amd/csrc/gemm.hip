@@ -407,7 +407,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const GemmLaunch L) 
 // ---------------------------------------------------------------------------
 // 256×256 fp16 kernel with direct global→LDS loads.
 //
-// 8 waves (2 × 4, each a 128×64 block of 32×32×16 MFMAs), k-tile 32, and a
+// 8 waves (2 × 4, each a 128×64 block of 16×16×32 MFMAs), k-tile 32, and a
 // 4-stage LDS ring (4 × 32 KiB): the loads of k-tile kt+3 are in flight
 // while k-tile kt is multiplied, so about three k-tiles of latency are
 // covered without registers for staging.  Each 16-byte load lands straight
