@@ -26,4 +26,5 @@ from .ns_oracle import (  # noqa: F401
     muon_step,
     gram_flops,
 )
+from .selected import muon_step_selected, selected_count, select_rows, row_scores  # noqa: F401
 from . import rational  # noqa: F401
