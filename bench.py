@@ -176,6 +176,55 @@ def other_configs(mns, W, torch):
     return out
 
 
+def selected_step(mns, torch, inp, shapes, stream, fraction, warmup=1, steps=3):
+    """The row/column-selected step with error feedback over the same
+    matrices (state continues from the main run): ms per step and the
+    per-kind HIP-event breakdown; its passes over M, g and W are HBM-bound,
+    so the roofline entry is the accumulate pass (B = M + g with row scores)
+    against HBM bandwidth."""
+    ws = torch.empty(mns.step_selected_workspace_size(shapes, fraction), dtype=torch.uint8,
+                     device=inp.params[0].device)
+
+    def step():
+        mns.muon_step_selected(inp.params, inp.grads, inp.momenta, fraction=fraction, beta=0.95,
+                               lr=0.02, steps=5, workspace=ws, stream=stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    mns.profile_enable(True)
+    for k in mns.PROFILE_KINDS:
+        mns.profile_read(k)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    mns.profile_enable(False)
+    kinds = {k: mns.profile_read(k) for k in mns.PROFILE_KINDS}
+    ms = (t1 - t0) * 1e3 / steps
+    per_kind = {}
+    for k, v in kinds.items():
+        if v["launches"]:
+            e = {"ms_per_step": v["ms"] / steps, "launches_per_step": v["launches"] // steps}
+            if k in ("syrk", "gram128", "gram256_sq", "gram256_axpy", "final"):
+                e["tflops"] = v["work"] / (v["ms"] / 1e3) / 1e12
+            else:
+                e["gbs"] = v["work"] / (v["ms"] / 1e3) / 1e9
+            per_kind[k] = e
+    acc = kinds["sel_accum"]
+    gbs = acc["work"] / (acc["ms"] / 1e3) / 1e9
+    del ws
+    return {"workload": f"muon_step_selected, fraction {fraction}, same {len(shapes)} matrices",
+            "ms_per_step": ms, "matrices_per_s": len(shapes) / (ms / 1e3), "steps": steps,
+            "roofline": {"bound": "hbm", "kernel": "sel_accum",
+                         "symbol": "muon::(anonymous namespace)::sel_accum_kernel(muon::SelLaunch)",
+                         "achieved": gbs, "peak": HBM_PEAK, "unit": "GB/s", "frac": gbs / HBM_PEAK,
+                         "avg_launch_ms": acc["ms"] / acc["launches"],
+                         "algorithmic_bytes_per_launch": acc["work"] / acc["launches"]},
+            "breakdown": per_kind}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -185,6 +234,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-configs", action="store_true",
                     help="time only the main workload (profiling runs)")
+    ap.add_argument("--no-selected", action="store_true",
+                    help="skip the row/column-selected step timing")
+    ap.add_argument("--selected-fraction", type=float, default=0.25)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB read + 1 GiB write kernel (counter calibration)")
     args = ap.parse_args()
@@ -270,6 +322,10 @@ def main():
                 "frac": achieved / MFMA_PEAK_F16, "traffic": traffic_for(dom, args.workload),
                 "avg_launch_ms": avg_s * 1e3, "algorithmic_flops_per_launch": per_launch,
                 "launches": d["launches"]}
+    selected = None
+    if not args.no_selected:
+        print("[bench] timing the selected-row step", file=sys.stderr, flush=True)
+        selected = selected_step(mns, torch, inp, shapes, stream, args.selected_fraction)
     others = None
     if not args.no_other_configs:
         del inp, ws
@@ -294,7 +350,7 @@ def main():
         "matrices_per_s": len(shapes) / (ms / 1e3),
         "elementwise_gbs": {k: breakdown[k]["gbs"] for k in ("momentum", "cast") if k in breakdown},
         "roofline": roofline, "breakdown": breakdown, "cpu_baseline": cpu,
-        "other_configs": others,
+        "selected_step": selected, "other_configs": others,
     }
     print(json.dumps(line), flush=True)
 

@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define MUON_NS_ABI_VERSION 2
+#define MUON_NS_ABI_VERSION 3
 
 typedef enum muon_status {
   MUON_OK = 0,
@@ -152,6 +152,43 @@ muon_status_t muon_step_ex(void* const* params, const void* const* grads, float*
                            const float coeffs[3], float eps, const muon_step_opts_t* opts,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/* Row/column-selected Muon step with error feedback, in place.
+ * Dion3 review (blog.secrett2633.cloud), §3 "Method & Key Results": the
+ * update rule uses only part of the rows / columns of the momentum matrix to
+ * shrink the orthogonalisation; §1 "Key Terms & Definitions", Error
+ * Feedback: what a reduced-size update leaves out is corrected in later
+ * steps.  The page gives no formula; this entry point computes, per matrix
+ * (stored rows × cols, m = min(rows, cols)):
+ *   B = momentum[i] + grads[i]                                   (fp32 add)
+ *   score of each row of the oriented m×n view of B (stored rows when
+ *   rows ≤ cols, stored columns when rows > cols) = its squared ℓ2 norm,
+ *   summed in fp32; S = the k = max(1, ⌈fraction·m⌉) highest scores (ρ·m
+ *   formed in double), equal scores taken lowest index first;
+ *   O_S = NS_steps(B_S / (‖B_S‖_F + eps))  on the k×n block (Gram size k);
+ *   params[i] rows (columns) in S ← round(W − lr·√max(1, rows/cols)·O_S),
+ *   all other weights unchanged bit for bit;
+ *   momentum[i] ← β·B on S and B elsewhere (the unused rows are carried at
+ *   full weight: error feedback).
+ * With fraction = 1 the update equals muon_step's (B then follows
+ * B ← β·B + g) and the stored buffer is β·B.
+ * Tensors are contiguous row-major: params[i] param_dtype (BF16 or F32),
+ * grads[i] float32 (read), momentum[i] float32 (read + written).
+ * 0 < fraction ≤ 1 (MUON_ERR_INVALID_ARG otherwise); every other argument,
+ * the aliasing rules and the error behaviour are those of muon_step.  The
+ * selection is made in fp32 on the GPU: rows whose scores differ by less
+ * than fp32 summation error may be selected either way.  The k×n blocks go
+ * through the half-precision MFMA pipeline of muon_ns_batched. */
+muon_status_t muon_step_selected(void* const* params, const float* const* grads,
+                                 float* const* momentum, const int64_t* rows, const int64_t* cols,
+                                 int32_t count, muon_dtype_t param_dtype, float beta, float lr,
+                                 int32_t steps, const float coeffs[3], float eps, double fraction,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes muon_step_selected needs for these shapes and fraction.
+ * Host only. */
+muon_status_t muon_step_selected_workspace_size(const int64_t* rows, const int64_t* cols,
+                                                int32_t count, double fraction, size_t* bytes);
+
 /* Workspace bytes muon_step (and muon_step_ex) needs for these shapes.  Host only. */
 muon_status_t muon_step_workspace_size(const int64_t* rows, const int64_t* cols, int32_t count,
                                        size_t* bytes);
@@ -192,8 +229,11 @@ muon_status_t muon_set_tile_table(const muon_tile_entry_t* entries, int32_t n);
  * Kinds: 0 momentum / sum of squares, 1 norm finish, 2 cast + transpose,
  *        3 SYRK, 4 symmetric Gram-space products on 128×128 tiles,
  *        5 final product + update, 6 Gram-space a·Y + B·Y products on
- *        256×256 tiles, 7 Gram-space A² products on 256×256 tiles.
- * work is algorithmic flops for kinds 3–7 and algorithmic HBM bytes for 0–2. */
+ *        256×256 tiles, 7 Gram-space A² products on 256×256 tiles,
+ *        8 selected step: B = M + g and row scores, 9 its top-k,
+ *        10 its gather, 11 its scatter of the update.
+ * work is algorithmic flops for kinds 3–7 and algorithmic HBM bytes for the
+ * others. */
 muon_status_t muon_profile_enable(int32_t on);
 muon_status_t muon_profile_read(int32_t kind, double* total_ms, int64_t* launches, double* work);
 

@@ -23,7 +23,8 @@ import torch
 __all__ = [
     "QUINTIC", "CUBIC", "MuonError", "lib_path", "load", "muon_ns_batched", "muon_step",
     "ns_workspace_size", "step_workspace_size", "describe_plan", "profile_enable",
-    "profile_read", "abi_version", "PROFILE_KINDS", "set_tile_table",
+    "profile_read", "abi_version", "PROFILE_KINDS", "set_tile_table", "muon_step_selected",
+    "step_selected_workspace_size",
 ]
 
 QUINTIC = (3.4445, -4.7750, 2.0315)
@@ -31,10 +32,11 @@ CUBIC = (1.5, -0.5, 0.0)
 
 MUON_DTYPE_F32 = 0
 MUON_DTYPE_BF16 = 1
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 PROFILE_KINDS = {"momentum": 0, "norm": 1, "cast": 2, "syrk": 3, "gram128": 4, "final": 5,
-                 "gram256_axpy": 6, "gram256_sq": 7}
+                 "gram256_axpy": 6, "gram256_sq": 7, "sel_accum": 8, "sel_topk": 9,
+                 "sel_gather": 10, "sel_scatter": 11}
 
 _STATUS = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "ALIAS", 4: "WORKSPACE",
            5: "HIP", 6: "NO_DEVICE"}
@@ -109,6 +111,14 @@ def load():
         L.muon_step_workspace_size.argtypes = [ctypes.POINTER(i64), ctypes.POINTER(i64), i32,
                                                ctypes.POINTER(sz)]
         L.muon_step_workspace_size.restype = i32
+        L.muon_step_selected.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(vp),
+                                         ctypes.POINTER(i64), ctypes.POINTER(i64), i32, i32, f32,
+                                         f32, i32, ctypes.POINTER(f32), f32, ctypes.c_double, vp,
+                                         sz, vp]
+        L.muon_step_selected.restype = i32
+        L.muon_step_selected_workspace_size.argtypes = [ctypes.POINTER(i64), ctypes.POINTER(i64),
+                                                        i32, ctypes.c_double, ctypes.POINTER(sz)]
+        L.muon_step_selected_workspace_size.restype = i32
         L.muon_describe_plan.argtypes = [ctypes.POINTER(i64), ctypes.POINTER(i64), i32, i32, i32,
                                          i32, ctypes.POINTER(f32), ctypes.c_char_p, sz]
         L.muon_describe_plan.restype = i32
@@ -221,6 +231,16 @@ def step_workspace_size(shapes) -> int:
     return int(out.value)
 
 
+def step_selected_workspace_size(shapes, fraction: float) -> int:
+    L = load()
+    n = len(shapes)
+    rows = (ctypes.c_int64 * max(n, 1))(*[int(r) for r, _ in shapes])
+    cols = (ctypes.c_int64 * max(n, 1))(*[int(c) for _, c in shapes])
+    out = ctypes.c_size_t(0)
+    _check(L.muon_step_selected_workspace_size(rows, cols, n, float(fraction), ctypes.byref(out)))
+    return int(out.value)
+
+
 def describe_plan(shapes, for_step=True, dtype=torch.bfloat16, steps=5, coeffs=QUINTIC) -> dict:
     L = load()
     n = len(shapes)
@@ -320,6 +340,49 @@ def muon_step(params, grads, momenta, beta: float = 0.95, lr: float = 0.02, step
             _check(L.muon_step_ex(P, G, M, rows, cols, n, _dtype_code(pdt), float(beta),
                                   float(lr), int(steps), _coeffs(coeffs), float(eps),
                                   ctypes.byref(opts), wsp, ws_bytes, _stream_handle(stream, dev)))
+
+
+def muon_step_selected(params, grads, momenta, fraction: float, beta: float = 0.95, lr: float = 0.02,
+                       steps: int = 5, coeffs=QUINTIC, eps: float = 1e-7, workspace=None, stream=None):
+    """One in-place row/column-selected Muon step with error feedback (the
+    muon_step_selected entry point): per matrix only the ⌈fraction·m⌉
+    highest-norm rows of B = M + g along the short side are orthogonalised
+    and applied; the buffer keeps B elsewhere and β·B on the selection.
+    params bf16 or fp32, grads and momenta fp32, all contiguous on one device."""
+    L = load()
+    params, grads, momenta = list(params), list(grads), list(momenta)
+    n = len(params)
+    if not (len(grads) == len(momenta) == n):
+        raise ValueError("params, grads and momenta differ in length")
+    if n == 0:
+        return
+    dev = params[0].device
+    pdt = params[0].dtype
+    for p, g, m in zip(params, grads, momenta):
+        if p.device != dev or g.device != dev or m.device != dev or dev.type != "cuda":
+            raise ValueError("all tensors must be on one CUDA/HIP device")
+        if p.dtype != pdt:
+            raise TypeError("all params must share one dtype")
+        if g.dtype != torch.float32 or m.dtype != torch.float32:
+            raise TypeError("grads and momenta must be float32")
+        if p.dim() != 2 or tuple(p.shape) != tuple(g.shape) or tuple(p.shape) != tuple(m.shape):
+            raise ValueError("param, grad and momentum shapes differ (or not 2-D)")
+        if not (p.is_contiguous() and g.is_contiguous() and m.is_contiguous()):
+            raise ValueError("params, grads and momenta must be contiguous")
+    vp = ctypes.c_void_p
+    P = (vp * n)(*[p.data_ptr() for p in params])
+    G = (vp * n)(*[g.data_ptr() for g in grads])
+    M = (vp * n)(*[m.data_ptr() for m in momenta])
+    rows = (ctypes.c_int64 * n)(*[int(p.shape[0]) for p in params])
+    cols = (ctypes.c_int64 * n)(*[int(p.shape[1]) for p in params])
+    need = ctypes.c_size_t(0)
+    _check(L.muon_step_selected_workspace_size(rows, cols, n, float(fraction), ctypes.byref(need)))
+    ws, ws_bytes = _workspace(int(need.value), dev, workspace)
+    with torch.cuda.device(dev):
+        wsp = ctypes.c_void_p(ws.data_ptr() if ws is not None else 0)
+        _check(L.muon_step_selected(P, G, M, rows, cols, n, _dtype_code(pdt), float(beta), float(lr),
+                                    int(steps), _coeffs(coeffs), float(eps), float(fraction), wsp,
+                                    ws_bytes, _stream_handle(stream, dev)))
 
 
 def set_tile_table(entries):

@@ -578,6 +578,176 @@ muon_status_t enqueue(const Plan& P, const std::vector<CallerMat>& cm, int srcDt
   return MUON_OK;
 }
 
+
+// ----------------------------------------------------------------------------
+// Row/column-selected step (Dion3 review, §3 "Method & Key Results" and §1
+// "Key Terms & Definitions", Error Feedback): per matrix the k = ⌈ρ·m⌉
+// highest-scoring rows of the oriented buffer are gathered into a dense fp32
+// block, orthogonalised by the batched pipeline above (in place) and
+// scattered back into the weights.
+
+struct SelMatLayout {
+  int64_t m = 0, k = 0, gr = 0, gc = 0;  // short side, kept rows, block shape
+  int tall = 0, nChunks = 0;
+  size_t offXs = 0, offScore = 0, offIdx = 0;
+};
+
+struct SelLayout {
+  Plan ns;                     // plan of the batched NS over the blocks
+  std::vector<SelMatLayout> mats;
+  size_t totalBytes = 0;
+};
+
+size_t sel_align(size_t x) { return (x + 255) / 256 * 256; }
+
+int64_t sel_count(int64_t m, double fraction) {
+  if (m == 0) return 0;
+  const int64_t k = (int64_t)std::ceil(fraction * (double)m);
+  return std::max<int64_t>(1, std::min<int64_t>(m, k));
+}
+
+std::string sel_layout(const int64_t* rows, const int64_t* cols, int count, double fraction,
+                       int steps, const float* coeffs, SelLayout* out) {
+  SelLayout& Lo = *out;
+  Lo.mats.assign(count, SelMatLayout{});
+  std::vector<int64_t> gr(count), gc(count);
+  for (int i = 0; i < count; ++i) {
+    SelMatLayout& s = Lo.mats[i];
+    const int64_t r = rows[i], c = cols[i];
+    s.tall = r > c ? 1 : 0;
+    s.m = std::min(r, c);
+    s.k = (r == 0 || c == 0) ? 0 : sel_count(s.m, fraction);
+    s.gr = s.tall ? r : s.k;
+    s.gc = s.tall ? s.k : c;
+    s.nChunks = s.tall ? (int)((r + kSelChunk - 1) / kSelChunk) : 1;
+    gr[i] = s.k ? s.gr : 0;
+    gc[i] = s.k ? s.gc : 0;
+  }
+  std::string e = build_plan(gr.data(), gc.data(), count, OP_F16, steps, coeffs[0], coeffs[1],
+                             coeffs[2], false, &Lo.ns);
+  if (!e.empty()) return e;
+  size_t off = sel_align(Lo.ns.totalBytes);
+  for (SelMatLayout& s : Lo.mats) {
+    if (!s.k) continue;
+    s.offXs = off;    off = sel_align(off + 4 * (size_t)s.gr * (size_t)s.gc);
+    s.offScore = off; off = sel_align(off + 4 * (size_t)s.nChunks * (size_t)s.m);
+    s.offIdx = off;   off = sel_align(off + 4 * (size_t)s.k);
+  }
+  Lo.totalBytes = off;
+  return "";
+}
+
+muon_status_t enqueue_selected(const SelLayout& Lo, void* const* params, const float* const* grads,
+                               float* const* momentum, const int64_t* rows, const int64_t* cols,
+                               int count, int paramDtype, float beta, float lr, float eps,
+                               void* ws, hipStream_t st) {
+  Launcher Lr{st};
+  std::vector<int> live;
+  for (int i = 0; i < count; ++i)
+    if (Lo.mats[i].k) live.push_back(i);
+  if (live.empty()) return MUON_OK;
+  int vec = 1;
+  for (int i : live)
+    if ((cols[i] & 3) || ((uintptr_t)grads[i] & 15) || ((uintptr_t)momentum[i] & 15)) vec = 0;
+  const size_t psz = paramDtype == MUON_DTYPE_F32 ? 4 : 2;
+
+  auto fill = [&](SelLaunch& L, size_t c0, size_t cn) {
+    std::memset(&L, 0, sizeof(L));
+    L.n = (int)cn;
+    L.paramDtype = paramDtype;
+    L.beta = beta;
+    L.vec = vec;
+    for (size_t q = 0; q < cn; ++q) {
+      const int i = live[c0 + q];
+      const SelMatLayout& s = Lo.mats[i];
+      SelMat& M = L.mat[q];
+      M.g = grads[i];
+      M.mom = momentum[i];
+      M.w = params[i];
+      M.xs = at<float>(ws, s.offXs);
+      M.score = at<float>(ws, s.offScore);
+      M.idx = at<int32_t>(ws, s.offIdx);
+      M.rows = rows[i];
+      M.cols = cols[i];
+      M.m = (int32_t)s.m;
+      M.k = (int32_t)s.k;
+      M.tall = s.tall;
+      M.nChunks = s.nChunks;
+      M.lrsc = (float)(lr * std::sqrt(std::max(1.0, (double)rows[i] / (double)cols[i])));
+    }
+  };
+  // 1. B = M + g and the row scores
+  for (size_t c0 = 0; c0 < live.size(); c0 += kMaxUser) {
+    SelLaunch L;
+    const size_t cn = std::min(live.size() - c0, (size_t)kMaxUser);
+    fill(L, c0, cn);
+    int64_t blocks = 0;
+    double bytes = 0;
+    for (size_t q = 0; q < cn; ++q) {
+      SelMat& M = L.mat[q];
+      M.blockStart = blocks;
+      blocks += M.tall ? (int64_t)M.nChunks * ((M.cols + kSelThreads - 1) / kSelThreads)
+                       : (M.rows + 3) / 4;
+      bytes += 12.0 * (double)M.rows * (double)M.cols + 4.0 * M.nChunks * (double)M.m;
+    }
+    muon_status_t s = Lr.run(8, bytes, "selected accumulate kernel",
+                             [&] { return launch_sel_accum(L, blocks, st); });
+    if (s != MUON_OK) return s;
+  }
+  // 2. top-k per matrix, 3. gather
+  for (size_t c0 = 0; c0 < live.size(); c0 += kMaxUser) {
+    SelLaunch L;
+    const size_t cn = std::min(live.size() - c0, (size_t)kMaxUser);
+    fill(L, c0, cn);
+    double bytes = 0;
+    for (size_t q = 0; q < cn; ++q)
+      bytes += 4.0 * L.mat[q].nChunks * (double)L.mat[q].m + 4.0 * L.mat[q].k;
+    muon_status_t s = Lr.run(9, bytes, "selected top-k kernel", [&] { return launch_sel_topk(L, st); });
+    if (s != MUON_OK) return s;
+    int64_t blocks = 0;
+    bytes = 0;
+    for (size_t q = 0; q < cn; ++q) {
+      SelMat& M = L.mat[q];
+      M.blockStart = blocks;
+      blocks += ((M.tall ? M.rows : (int64_t)M.k) + 3) / 4;
+      bytes += 8.0 * (double)(M.tall ? M.rows : M.k) * (double)(M.tall ? M.k : M.cols);
+    }
+    s = Lr.run(10, bytes, "selected gather kernel", [&] { return launch_sel_gather(L, blocks, st); });
+    if (s != MUON_OK) return s;
+  }
+  // 4. orthogonalise every block in place
+  std::vector<CallerMat> cm(count);
+  for (int i = 0; i < count; ++i) {
+    const SelMatLayout& s = Lo.mats[i];
+    cm[i].src = s.k ? at<float>(ws, s.offXs) : nullptr;
+    cm[i].ldSrc = std::max<int64_t>(s.gc, 1);
+    cm[i].dst = s.k ? at<float>(ws, s.offXs) : nullptr;
+    cm[i].ldDst = std::max<int64_t>(s.gc, 1);
+    cm[i].grad = nullptr;
+    cm[i].lrsc = 0.f;
+  }
+  muon_status_t s = enqueue(Lo.ns, cm, MUON_DTYPE_F32, MUON_DTYPE_F32, 0.f, eps, StepVariant{}, ws, st);
+  if (s != MUON_OK) return s;
+  // 5. scatter the update and decay the selected buffer rows
+  for (size_t c0 = 0; c0 < live.size(); c0 += kMaxUser) {
+    SelLaunch L;
+    const size_t cn = std::min(live.size() - c0, (size_t)kMaxUser);
+    fill(L, c0, cn);
+    int64_t blocks = 0;
+    double bytes = 0;
+    for (size_t q = 0; q < cn; ++q) {
+      SelMat& M = L.mat[q];
+      M.blockStart = blocks;
+      blocks += ((M.tall ? M.rows : (int64_t)M.k) + 3) / 4;
+      bytes += (4.0 + 2.0 * psz + 8.0) * (double)(M.tall ? M.rows : M.k) *
+               (double)(M.tall ? M.k : M.cols);
+    }
+    s = Lr.run(11, bytes, "selected scatter kernel", [&] { return launch_sel_scatter(L, blocks, st); });
+    if (s != MUON_OK) return s;
+  }
+  return MUON_OK;
+}
+
 }  // namespace
 }  // namespace muon
 
@@ -804,6 +974,81 @@ muon_status_t muon_step(void* const* params, const float* const* grads, float* c
                         void* stream) {
   return muon_step_ex(params, (const void* const*)grads, momentum, rows, cols, count, param_dtype,
                       beta, lr, steps, coeffs, eps, nullptr, workspace, workspace_bytes, stream);
+}
+
+muon_status_t muon_step_selected_workspace_size(const int64_t* rows, const int64_t* cols,
+                                                int32_t count, double fraction, size_t* bytes) {
+  g_err.clear();
+  if (!bytes) return fail(MUON_ERR_INVALID_ARG, "bytes is NULL");
+  if (count < 0) return fail(MUON_ERR_INVALID_ARG, "count < 0");
+  if (count > 0 && (!rows || !cols)) return fail(MUON_ERR_INVALID_ARG, "rows/cols is NULL");
+  if (!std::isfinite(fraction) || !(fraction > 0.0) || fraction > 1.0)
+    return fail(MUON_ERR_INVALID_ARG, "fraction must lie in (0, 1]");
+  for (int i = 0; i < count; ++i) {
+    muon_status_t s = check_shape(i, rows[i], cols[i]);
+    if (s != MUON_OK) return s;
+  }
+  const float unit[3] = {1.f, 0.f, 0.f};
+  SelLayout Lo;
+  std::string e = sel_layout(rows, cols, count, fraction, 5, unit, &Lo);
+  if (!e.empty()) return fail(MUON_ERR_INVALID_ARG, e);
+  *bytes = Lo.totalBytes;
+  return MUON_OK;
+}
+
+muon_status_t muon_step_selected(void* const* params, const float* const* grads,
+                                 float* const* momentum, const int64_t* rows, const int64_t* cols,
+                                 int32_t count, muon_dtype_t param_dtype, float beta, float lr,
+                                 int32_t steps, const float coeffs[3], float eps, double fraction,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  if (count < 0) return fail(MUON_ERR_INVALID_ARG, "count < 0");
+  if (!std::isfinite(fraction) || !(fraction > 0.0) || fraction > 1.0)
+    return fail(MUON_ERR_INVALID_ARG, "fraction must lie in (0, 1]");
+  if (count == 0) return MUON_OK;
+  if (!params || !grads || !momentum || !rows || !cols)
+    return fail(MUON_ERR_INVALID_ARG, "NULL pointer array");
+  if (param_dtype != MUON_DTYPE_F32 && param_dtype != MUON_DTYPE_BF16)
+    return fail(MUON_ERR_INVALID_ARG, "unknown param dtype");
+  if (steps < 0 || steps > kMaxSteps) return fail(MUON_ERR_INVALID_ARG, "steps out of range [0, 64]");
+  if (!finite3(coeffs)) return fail(MUON_ERR_INVALID_ARG, "coeffs NULL or not finite");
+  if (!std::isfinite(beta) || !std::isfinite(lr))
+    return fail(MUON_ERR_INVALID_ARG, "beta and lr must be finite");
+  if (!std::isfinite(eps) || eps < 0) return fail(MUON_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  const size_t psz = param_dtype == MUON_DTYPE_F32 ? 4 : 2;
+  std::vector<Range> ranges;
+  for (int i = 0; i < count; ++i) {
+    muon_status_t s = check_shape(i, rows[i], cols[i]);
+    if (s != MUON_OK) return s;
+    if (rows[i] == 0 || cols[i] == 0) continue;
+    if (!params[i] || !grads[i] || !momentum[i])
+      return fail(MUON_ERR_INVALID_ARG, "matrix " + std::to_string(i) + ": NULL tensor");
+    const uintptr_t n = (uintptr_t)(rows[i] * cols[i]);
+    ranges.push_back({(uintptr_t)params[i], (uintptr_t)params[i] + n * psz, i});
+    ranges.push_back({(uintptr_t)grads[i], (uintptr_t)grads[i] + n * 4, i});
+    ranges.push_back({(uintptr_t)momentum[i], (uintptr_t)momentum[i] + n * 4, i});
+  }
+  int oa = 0, ob = 0;
+  if (overlaps(ranges, &oa, &ob))
+    return fail(MUON_ERR_ALIAS, "tensors of matrices " + std::to_string(oa) + " and " +
+                                    std::to_string(ob) + " overlap");
+  SelLayout Lo;
+  std::string e = sel_layout(rows, cols, count, fraction, steps, coeffs, &Lo);
+  if (!e.empty()) return fail(MUON_ERR_INVALID_ARG, e);
+  if (!workspace) return fail(MUON_ERR_WORKSPACE, "workspace is NULL");
+  if ((uintptr_t)workspace & 255) return fail(MUON_ERR_WORKSPACE, "workspace not 256-byte aligned");
+  if (workspace_bytes < Lo.totalBytes)
+    return fail(MUON_ERR_WORKSPACE, "workspace too small: need " + std::to_string(Lo.totalBytes) +
+                                        " bytes, got " + std::to_string(workspace_bytes));
+  {
+    int who = 0;
+    if (workspace_overlaps(ranges, (uintptr_t)workspace, (uintptr_t)workspace + Lo.totalBytes, &who))
+      return fail(MUON_ERR_ALIAS, "workspace overlaps a tensor of matrix " + std::to_string(who));
+  }
+  muon_status_t s = check_device();
+  if (s != MUON_OK) return s;
+  return enqueue_selected(Lo, params, grads, momentum, rows, cols, count, param_dtype, beta, lr, eps,
+                          workspace, (hipStream_t)stream);
 }
 
 muon_status_t muon_set_tile_table(const muon_tile_entry_t* entries, int32_t n) {

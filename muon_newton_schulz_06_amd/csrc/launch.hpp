@@ -16,4 +16,11 @@ hipError_t launch_norm(const NormLaunch& L, hipStream_t st);
 // Scaled cast into the two operand layouts (and zero padding).
 hipError_t launch_cast(const CastLaunch& L, int64_t blocks, hipStream_t st);
 
+// Selected-row step: B = M + g with row scores; top-k per matrix; gather of
+// the selected block; scatter of the update and the buffer decay.
+hipError_t launch_sel_accum(const SelLaunch& L, int64_t blocks, hipStream_t st);
+hipError_t launch_sel_topk(const SelLaunch& L, hipStream_t st);
+hipError_t launch_sel_gather(const SelLaunch& L, int64_t blocks, hipStream_t st);
+hipError_t launch_sel_scatter(const SelLaunch& L, int64_t blocks, hipStream_t st);
+
 }  // namespace muon

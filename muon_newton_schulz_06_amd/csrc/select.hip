@@ -1,0 +1,327 @@
+// Row/column-selected Muon step with error feedback on gfx950.
+//
+// Dion3 review (blog.secrett2633.cloud), §3 "Method & Key Results": the update
+// rule uses only part of the rows / columns of the momentum matrix, which
+// shrinks the orthogonalisation; §1 "Key Terms & Definitions", Error
+// Feedback: what a reduced-size update leaves out is carried into later
+// steps.  Per matrix, with m = min(rows, cols) and the oriented m×n view
+// (stored rows of a wide or square matrix, stored columns of a tall one):
+//
+//   B = M + g                       (one pass, with the squared ℓ2 norm of
+//                                     every oriented row as its score)
+//   S = the k = ⌈ρ·m⌉ highest scores, equal scores to the lower index
+//   X_S = B restricted to S          (gathered into a dense fp32 block)
+//   O_S = NS(X_S / (‖X_S‖_F + eps))  (the batched Gram pipeline, in place)
+//   W_S ← round(W_S − lr·√max(1, rows/cols)·O_S),  M_S ← β·B_S,
+//   M elsewhere keeps B (the error that later steps pick up).
+//
+// The passes here are HBM-bound; the top-k is one workgroup per matrix and
+// works on at most 32768 scores: an MSB-first 8-bit radix select over the
+// fp32 bit patterns (non-negative floats order like their bits) finds the
+// k-th largest score exactly, then two block-wide scans write the selected
+// indices in ascending order.  Integer counts only, so the selection is
+// deterministic.
+#include <hip/hip_runtime.h>
+
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace muon {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float sel_wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ uint16_t to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ int find_mat(const SelLaunch& L, int64_t b) {
+  int mi = 0;
+  while (mi + 1 < L.n && b >= L.mat[mi + 1].blockStart) ++mi;
+  return mi;
+}
+
+// ---------------------------------------------------------------------------
+// B = M + g and the row scores.
+//  * wide / square (rows ≤ cols): one wave per stored row, 16-byte accesses
+//    when allowed, lane sums then a wavefront butterfly → score[row];
+//  * tall: one thread per stored column over a chunk of kSelChunk rows (a
+//    wave reads 256 contiguous bytes per row) → score[chunk·m + col]; the
+//    top-k kernel adds the chunks in order.
+__global__ __launch_bounds__(kSelThreads) void sel_accum_kernel(const SelLaunch L) {
+  const int64_t b = blockIdx.x;
+  const SelMat& S = L.mat[find_mat(L, b)];
+  const int64_t blk = b - S.blockStart;
+  const int tid = threadIdx.x, lane = tid & 63;
+  if (!S.tall) {
+    const int64_t r = blk * (kSelThreads / 64) + (tid >> 6);
+    if (r >= S.rows) return;  // whole wave: no cross-lane work follows
+    const float* g = S.g + r * S.cols;
+    float* mo = S.mom + r * S.cols;
+    float ss = 0.f;
+    if (L.vec) {
+      for (int64_t c0 = (int64_t)lane * 4; c0 < S.cols; c0 += 4 * 256) {
+        f32x4 gv[4], mv[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int64_t c = c0 + q * 256;
+          if (c < S.cols) {
+            gv[q] = __builtin_nontemporal_load((const f32x4*)(g + c));
+            mv[q] = *(const f32x4*)(mo + c);
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int64_t c = c0 + q * 256;
+          if (c < S.cols) {
+            const f32x4 v = mv[q] + gv[q];
+            *(f32x4*)(mo + c) = v;
+            ss += v[0] * v[0];
+            ss += v[1] * v[1];
+            ss += v[2] * v[2];
+            ss += v[3] * v[3];
+          }
+        }
+      }
+    } else {
+      for (int64_t c = lane; c < S.cols; c += 64) {
+        const float v = mo[c] + g[c];
+        mo[c] = v;
+        ss += v * v;
+      }
+    }
+    ss = sel_wave_sum(ss);
+    if (lane == 0) S.score[r] = ss;
+  } else {
+    const int64_t colBlocks = (S.cols + kSelThreads - 1) / kSelThreads;
+    const int64_t chunk = blk / colBlocks;
+    const int64_t c = (blk - chunk * colBlocks) * kSelThreads + tid;
+    if (c >= S.cols) return;
+    const int64_t r0 = chunk * kSelChunk;
+    const int64_t r1 = r0 + kSelChunk < S.rows ? r0 + kSelChunk : S.rows;
+    float ss = 0.f;
+    for (int64_t rb = r0; rb < r1; rb += 8) {
+      float gv[8], mv[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        if (rb + q < r1) {
+          gv[q] = __builtin_nontemporal_load(S.g + (rb + q) * S.cols + c);
+          mv[q] = S.mom[(rb + q) * S.cols + c];
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        if (rb + q < r1) {
+          const float v = mv[q] + gv[q];
+          S.mom[(rb + q) * S.cols + c] = v;
+          ss += v * v;
+        }
+      }
+    }
+    S.score[chunk * S.m + c] = ss;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Top-k: one workgroup of 1024 threads per matrix; thread t owns the
+// contiguous scores [t·per, t·per + per), per = ⌈m / 1024⌉ ≤ 32.
+
+// Exclusive prefix sum of one int per thread over the workgroup, in thread
+// order.  `sh` holds one slot per wave.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* sh) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) sh[w] = x;
+  __syncthreads();
+  int base = 0;
+  for (int i = 0; i < w; ++i) base += sh[i];
+  __syncthreads();  // sh is reused by the next scan
+  return base + x - v;
+}
+
+__global__ __launch_bounds__(kSelTopThreads) void sel_topk_kernel(const SelLaunch L) {
+  const SelMat& S = L.mat[blockIdx.x];
+  const int tid = threadIdx.x;
+  const int m = S.m;
+  const int per = (m + kSelTopThreads - 1) / kSelTopThreads;
+  const int j0 = tid * per;
+  const int cnt = m - j0 < 0 ? 0 : (m - j0 < per ? m - j0 : per);
+
+  uint32_t key[kSelMaxPer];
+#pragma unroll
+  for (int q = 0; q < kSelMaxPer; ++q) {
+    float s = 0.f;
+    if (q < cnt)
+      for (int c = 0; c < S.nChunks; ++c) s += S.score[(int64_t)c * m + j0 + q];
+    key[q] = __float_as_uint(s);
+  }
+
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t shPrefix, shKrem;
+  __shared__ int shScan[kSelTopThreads / 64];
+  uint32_t prefix = 0, mask = 0, krem = (uint32_t)S.k;
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    if (tid < 256) hist[tid] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < kSelMaxPer; ++q)
+      if (q < cnt && (key[q] & mask) == prefix) atomicAdd(&hist[(key[q] >> shift) & 255u], 1u);
+    __syncthreads();
+    if (tid == 0) {
+      // Largest digit d with (keys of digit > d) < krem ≤ (keys of digit ≥ d);
+      // the keys matching the prefix number at least krem, so d exists.
+      uint32_t above = 0;
+      int d = 255;
+      for (; d > 0; --d) {
+        if (above + hist[d] >= krem) break;
+        above += hist[d];
+      }
+      shPrefix = prefix | ((uint32_t)d << shift);
+      shKrem = krem - above;
+    }
+    __syncthreads();
+    prefix = shPrefix;
+    krem = shKrem;
+    mask |= 255u << shift;
+  }
+  // prefix is the k-th largest key T; krem of the keys equal to T are taken,
+  // lowest indices first, together with every key above T.
+  const uint32_t T = prefix;
+  int eqc = 0;
+#pragma unroll
+  for (int q = 0; q < kSelMaxPer; ++q)
+    if (q < cnt && key[q] == T) ++eqc;
+  int eqSeen = block_exclusive_scan(eqc, shScan);
+  uint32_t take = 0;
+  int selc = 0;
+#pragma unroll
+  for (int q = 0; q < kSelMaxPer; ++q) {
+    if (q < cnt) {
+      bool t = key[q] > T;
+      if (key[q] == T) {
+        t = eqSeen < (int)krem;
+        ++eqSeen;
+      }
+      if (t) {
+        take |= 1u << q;
+        ++selc;
+      }
+    }
+  }
+  int pos = block_exclusive_scan(selc, shScan);
+#pragma unroll
+  for (int q = 0; q < kSelMaxPer; ++q)
+    if (((take >> q) & 1u) && pos < S.k) S.idx[pos++] = j0 + q;
+}
+
+// ---------------------------------------------------------------------------
+// Gather: one wave per row of the selected block.
+//  * wide: block row i = B row idx[i] (a contiguous row copy);
+//  * tall: block row r = B row r at the columns idx[0..k).
+__global__ __launch_bounds__(kSelThreads) void sel_gather_kernel(const SelLaunch L) {
+  const int64_t b = blockIdx.x;
+  const SelMat& S = L.mat[find_mat(L, b)];
+  const int64_t row = (b - S.blockStart) * (kSelThreads / 64) + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (!S.tall) {
+    if (row >= S.k) return;
+    const float* src = S.mom + (int64_t)S.idx[row] * S.cols;
+    float* dst = S.xs + row * S.cols;
+    if (L.vec) {
+      for (int64_t c = (int64_t)lane * 4; c < S.cols; c += 256)
+        *(f32x4*)(dst + c) = *(const f32x4*)(src + c);
+    } else {
+      for (int64_t c = lane; c < S.cols; c += 64) dst[c] = src[c];
+    }
+  } else {
+    if (row >= S.rows) return;
+    const float* src = S.mom + row * S.cols;
+    float* dst = S.xs + row * S.k;
+    for (int i = lane; i < S.k; i += 64) dst[i] = src[S.idx[i]];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Scatter: W_S ← round(W_S − lrsc·O_S) and M_S ← β·B_S, one wave per row of
+// the block (same mapping as the gather).
+template <int PD>
+__device__ __forceinline__ void update_w(void* w, int64_t e, float lrsc, float o) {
+  if constexpr (PD == 1) {
+    uint16_t* p = (uint16_t*)w + e;
+    *p = to_bf16_rne(fmaf(-lrsc, o, __uint_as_float((uint32_t)*p << 16)));
+  } else {
+    float* p = (float*)w + e;
+    *p = fmaf(-lrsc, o, *p);
+  }
+}
+
+template <int PD>
+__device__ __forceinline__ void scatter_row(const SelLaunch& L, const SelMat& S, int64_t row, int lane) {
+  if (!S.tall) {
+    const int64_t r = S.idx[row];
+    const float* o = S.xs + row * S.cols;
+    for (int64_t c = lane; c < S.cols; c += 64) {
+      update_w<PD>(S.w, r * S.cols + c, S.lrsc, o[c]);
+      S.mom[r * S.cols + c] = L.beta * S.mom[r * S.cols + c];
+    }
+  } else {
+    const float* o = S.xs + row * S.k;
+    for (int i = lane; i < S.k; i += 64) {
+      const int64_t e = row * S.cols + S.idx[i];
+      update_w<PD>(S.w, e, S.lrsc, o[i]);
+      S.mom[e] = L.beta * S.mom[e];
+    }
+  }
+}
+
+__global__ __launch_bounds__(kSelThreads) void sel_scatter_kernel(const SelLaunch L) {
+  const int64_t b = blockIdx.x;
+  const SelMat& S = L.mat[find_mat(L, b)];
+  const int64_t row = (b - S.blockStart) * (kSelThreads / 64) + (threadIdx.x >> 6);
+  if (row >= (S.tall ? S.rows : (int64_t)S.k)) return;
+  if (L.paramDtype == 1) scatter_row<1>(L, S, row, threadIdx.x & 63);
+  else scatter_row<0>(L, S, row, threadIdx.x & 63);
+}
+
+}  // namespace
+
+hipError_t launch_sel_accum(const SelLaunch& L, int64_t blocks, hipStream_t st) {
+  if (blocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(sel_accum_kernel, dim3((unsigned)blocks), dim3(kSelThreads), 0, st, L);
+  return hipGetLastError();
+}
+
+hipError_t launch_sel_topk(const SelLaunch& L, hipStream_t st) {
+  if (L.n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(sel_topk_kernel, dim3((unsigned)L.n), dim3(kSelTopThreads), 0, st, L);
+  return hipGetLastError();
+}
+
+hipError_t launch_sel_gather(const SelLaunch& L, int64_t blocks, hipStream_t st) {
+  if (blocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(sel_gather_kernel, dim3((unsigned)blocks), dim3(kSelThreads), 0, st, L);
+  return hipGetLastError();
+}
+
+hipError_t launch_sel_scatter(const SelLaunch& L, int64_t blocks, hipStream_t st) {
+  if (blocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(sel_scatter_kernel, dim3((unsigned)blocks), dim3(kSelThreads), 0, st, L);
+  return hipGetLastError();
+}
+
+}  // namespace muon

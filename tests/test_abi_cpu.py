@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol():
     assert "muon_ns_batched" in names and "muon_step" in names
     for n in names:
         assert hasattr(L, n), n
-    assert mns.abi_version() == 2
+    assert mns.abi_version() == 3
 
 
 def test_library_binds_hip_runtime_only_by_soname():
@@ -324,3 +324,51 @@ def test_workspace_must_not_overlap_tensors():
     arr = _desc(1)
     assert _ns(arr, 1, ws=0x10000 - 0x100, wsb=1 << 40) == 3 and "workspace" in _err()
     assert _ns(arr, 1, ws=0x900000, wsb=1 << 40) == 3
+
+
+# ------------------------------------------------- selected-row step (host side)
+def _sel(fraction=0.25, n=2, rows=(4, 8), cols=(8, 4), g=None, dtype=1, steps=5, ws=0x100000000,
+         wsb=1 << 40, beta=0.95):
+    vp = ctypes.c_void_p
+    P = (vp * n)(*[0x1000000 + i * 0x10000 for i in range(n)])
+    G = (vp * n)(*(g or [0x2000000 + i * 0x10000 for i in range(n)]))
+    M = (vp * n)(*[0x3000000 + i * 0x10000 for i in range(n)])
+    R = (ctypes.c_int64 * n)(*rows[:n])
+    C = (ctypes.c_int64 * n)(*cols[:n])
+    return mns.load().muon_step_selected(P, G, M, R, C, n, dtype, beta, 0.02, steps, C3, 1e-7,
+                                         float(fraction), ctypes.c_void_p(ws), wsb, None)
+
+
+def test_selected_step_rejects_bad_arguments():
+    for f in (0.0, -0.5, 1.5, float("nan"), float("inf")):
+        assert _sel(fraction=f) == 1 and "fraction" in _err()
+    assert _sel(dtype=7) == 1
+    assert _sel(steps=65) == 1
+    assert _sel(beta=float("nan")) == 1
+    assert _sel(rows=(-2, 8)) == 1
+    assert _sel(g=[0x3000000 + 4, 0x2010000]) == 3     # gradient overlaps a buffer
+    assert _sel(ws=0) == 4
+    assert _sel(ws=0x100000080) == 4                    # misaligned
+    assert _sel(wsb=64) == 4
+    assert _sel(ws=0x2000000) == 3                      # workspace over a gradient
+    st = _sel()
+    if not torch.cuda.is_available():
+        assert st == 6, _err()
+    # count 0 is a no-op, an invalid fraction is still reported
+    L = mns.load()
+    assert L.muon_step_selected(None, None, None, None, None, 0, 1, 0.9, 0.1, 5, C3, 1e-7, 0.5,
+                                None, 0, None) == 0
+    assert L.muon_step_selected(None, None, None, None, None, 0, 1, 0.9, 0.1, 5, C3, 1e-7, 2.0,
+                                None, 0, None) == 1
+
+
+def test_selected_workspace_grows_with_the_fraction():
+    shapes = [(3584, 3584), (512, 3584), (18944, 3584), (3584, 18944)]
+    sizes = [mns.step_selected_workspace_size(shapes, f) for f in (0.1, 0.25, 0.5, 1.0)]
+    assert sizes == sorted(sizes) and sizes[0] > 0
+    # the fp32 selected blocks alone: k × n floats per matrix, k = ⌈ρ·m⌉
+    blocks = sum(4 * math.ceil(0.25 * min(r, c)) * max(r, c) for r, c in shapes)
+    assert sizes[1] >= blocks
+    assert mns.step_selected_workspace_size([(0, 5), (7, 0)], 0.5) <= 512   # no blocks, no scores
+    with pytest.raises(mns.MuonError):
+        mns.step_selected_workspace_size(shapes, 0.0)

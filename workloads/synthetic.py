@@ -133,3 +133,35 @@ def fresh_grads(shapes, seed0: int, offset: int, device="cpu", g_std=1e-2):
 
 
 __all__.append("fresh_grads")
+
+
+def row_scales(rows: int, cols: int, seed: int, device="cpu"):
+    """Distinct per-row factors 0.5 + π(i)/m along the short side (π a seeded
+    permutation of 0..m−1, m = min(rows, cols)), shaped to broadcast over a
+    rows × cols matrix: the selected-row step's inputs get row norms that are
+    well separated (relative gaps ≥ 1/m), as real gradients' rows differ in
+    size, so the selection does not hinge on rounding."""
+    m = min(rows, cols)
+    perm = torch.randperm(m, generator=_gen(seed, "cpu")).to(torch.float32)
+    s = (0.5 + perm / m).to(device)
+    return s[None, :] if rows > cols else s[:, None]
+
+
+def selected_inputs(shapes, seed0: int, device="cpu", w_std=0.02, g_std=1e-2, m_std=0.0,
+                    param_dtype=torch.bfloat16):
+    """Inputs of the selected-row step: ``muon_inputs`` with every gradient
+    (and, for ``m_std`` > 0, an N(0, m_std²) starting buffer) scaled by
+    ``row_scales`` (seed ``seed0 + j + 7_000_001``)."""
+    inp = muon_inputs(shapes, seed0, device=device, w_std=w_std, g_std=g_std,
+                      param_dtype=param_dtype)
+    for j, (r, c) in enumerate(shapes):
+        if r == 0 or c == 0:
+            continue
+        s = row_scales(r, c, seed0 + j + 7_000_001, device=device)
+        inp.grads[j].mul_(s)
+        if m_std > 0:
+            inp.momenta[j] = gaussian((r, c), seed0 + j + 3_000_017, std=m_std, device=device).mul_(s)
+    return inp
+
+
+__all__ += ["row_scales", "selected_inputs"]
