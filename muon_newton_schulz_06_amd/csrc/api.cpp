@@ -589,7 +589,7 @@ muon_status_t enqueue(const Plan& P, const std::vector<CallerMat>& cm, int srcDt
 struct SelMatLayout {
   int64_t m = 0, k = 0, gr = 0, gc = 0;  // short side, kept rows, block shape
   int tall = 0, nChunks = 0;
-  size_t offXs = 0, offScore = 0, offIdx = 0;
+  size_t offXs = 0, offScore = 0, offIdx = 0, offPos = 0;
 };
 
 struct SelLayout {
@@ -632,6 +632,7 @@ std::string sel_layout(const int64_t* rows, const int64_t* cols, int count, doub
     s.offXs = off;    off = sel_align(off + 4 * (size_t)s.gr * (size_t)s.gc);
     s.offScore = off; off = sel_align(off + 4 * (size_t)s.nChunks * (size_t)s.m);
     s.offIdx = off;   off = sel_align(off + 4 * (size_t)s.k);
+    s.offPos = off;   off = sel_align(off + 4 * (size_t)s.m);
   }
   Lo.totalBytes = off;
   return "";
@@ -646,10 +647,12 @@ muon_status_t enqueue_selected(const SelLayout& Lo, void* const* params, const f
   for (int i = 0; i < count; ++i)
     if (Lo.mats[i].k) live.push_back(i);
   if (live.empty()) return MUON_OK;
+  const size_t psz = paramDtype == MUON_DTYPE_F32 ? 4 : 2;
   int vec = 1;
   for (int i : live)
-    if ((cols[i] & 3) || ((uintptr_t)grads[i] & 15) || ((uintptr_t)momentum[i] & 15)) vec = 0;
-  const size_t psz = paramDtype == MUON_DTYPE_F32 ? 4 : 2;
+    if ((cols[i] & 3) || ((uintptr_t)grads[i] & 15) || ((uintptr_t)momentum[i] & 15) ||
+        ((uintptr_t)params[i] & (4 * psz - 1)))
+      vec = 0;
 
   auto fill = [&](SelLaunch& L, size_t c0, size_t cn) {
     std::memset(&L, 0, sizeof(L));
@@ -667,6 +670,7 @@ muon_status_t enqueue_selected(const SelLayout& Lo, void* const* params, const f
       M.xs = at<float>(ws, s.offXs);
       M.score = at<float>(ws, s.offScore);
       M.idx = at<int32_t>(ws, s.offIdx);
+      M.pos = at<int32_t>(ws, s.offPos);
       M.rows = rows[i];
       M.cols = cols[i];
       M.m = (int32_t)s.m;
@@ -686,8 +690,8 @@ muon_status_t enqueue_selected(const SelLayout& Lo, void* const* params, const f
     for (size_t q = 0; q < cn; ++q) {
       SelMat& M = L.mat[q];
       M.blockStart = blocks;
-      blocks += M.tall ? (int64_t)M.nChunks * ((M.cols + kSelThreads - 1) / kSelThreads)
-                       : (M.rows + 3) / 4;
+      const int64_t span = (int64_t)kSelThreads * (vec ? 4 : 1);  // columns per workgroup (tall)
+      blocks += M.tall ? (int64_t)M.nChunks * ((M.cols + span - 1) / span) : (M.rows + 3) / 4;
       bytes += 12.0 * (double)M.rows * (double)M.cols + 4.0 * M.nChunks * (double)M.m;
     }
     muon_status_t s = Lr.run(8, bytes, "selected accumulate kernel",
@@ -701,7 +705,7 @@ muon_status_t enqueue_selected(const SelLayout& Lo, void* const* params, const f
     fill(L, c0, cn);
     double bytes = 0;
     for (size_t q = 0; q < cn; ++q)
-      bytes += 4.0 * L.mat[q].nChunks * (double)L.mat[q].m + 4.0 * L.mat[q].k;
+      bytes += 4.0 * L.mat[q].nChunks * (double)L.mat[q].m + 4.0 * L.mat[q].k + 4.0 * L.mat[q].m;
     muon_status_t s = Lr.run(9, bytes, "selected top-k kernel", [&] { return launch_sel_topk(L, st); });
     if (s != MUON_OK) return s;
     int64_t blocks = 0;

@@ -159,7 +159,7 @@ struct CastLaunch {
 // scoring rows of the oriented m×n buffer (stored rows of a wide matrix,
 // stored columns of a tall one) are orthogonalised and applied.
 constexpr int kSelThreads = 256;      // accumulate / gather / scatter: 4 waves
-constexpr int kSelChunk = 64;         // stored rows per workgroup, column pass of a tall matrix
+constexpr int kSelChunk = 256;        // stored rows per workgroup, column pass of a tall matrix
 constexpr int kSelTopThreads = 1024;  // top-k: one workgroup per matrix
 constexpr int kSelMaxPer = 32;        // scores per top-k thread (m ≤ 32768)
 
@@ -170,6 +170,7 @@ struct SelMat {
   float* xs;           // selected block, fp32: k × cols (wide) or rows × k (tall)
   float* score;        // partial scores, nChunks × m (nChunks = 1 for a wide matrix)
   int32_t* idx;        // the k selected indices along the short side, ascending
+  int32_t* pos;        // inverse map, m entries: position in idx, or −1
   int64_t rows, cols;
   int32_t m, k, tall, nChunks;
   int64_t blockStart;  // first workgroup of this matrix in the launch
@@ -181,7 +182,7 @@ struct SelLaunch {
   int32_t n;
   int32_t paramDtype;  // muon_dtype_t of the weights
   float beta;
-  int32_t vec;         // 1: every matrix has cols % 4 == 0 and 16-byte aligned rows
+  int32_t vec;         // 1: every matrix has cols % 4 == 0 and 4-element aligned rows
   SelMat mat[kMaxUser];
 };
 

@@ -54,9 +54,9 @@ __device__ __forceinline__ int find_mat(const SelLaunch& L, int64_t b) {
 // B = M + g and the row scores.
 //  * wide / square (rows ≤ cols): one wave per stored row, 16-byte accesses
 //    when allowed, lane sums then a wavefront butterfly → score[row];
-//  * tall: one thread per stored column over a chunk of kSelChunk rows (a
-//    wave reads 256 contiguous bytes per row) → score[chunk·m + col]; the
-//    top-k kernel adds the chunks in order.
+//  * tall: one thread per 4 stored columns (1 without 16-byte alignment)
+//    over a chunk of kSelChunk rows, so a wave reads 1 KiB contiguous per
+//    row → score[chunk·m + col]; the top-k kernel adds the chunks in order.
 __global__ __launch_bounds__(kSelThreads) void sel_accum_kernel(const SelLaunch L) {
   const int64_t b = blockIdx.x;
   const SelMat& S = L.mat[find_mat(L, b)];
@@ -102,32 +102,60 @@ __global__ __launch_bounds__(kSelThreads) void sel_accum_kernel(const SelLaunch 
     ss = sel_wave_sum(ss);
     if (lane == 0) S.score[r] = ss;
   } else {
-    const int64_t colBlocks = (S.cols + kSelThreads - 1) / kSelThreads;
+    // V consecutive columns per thread (16-byte accesses when allowed)
+    const int V = L.vec ? 4 : 1;
+    const int64_t colBlocks = (S.cols + kSelThreads * V - 1) / (kSelThreads * V);
     const int64_t chunk = blk / colBlocks;
-    const int64_t c = (blk - chunk * colBlocks) * kSelThreads + tid;
+    const int64_t c = (blk - chunk * colBlocks) * kSelThreads * V + (int64_t)tid * V;
     if (c >= S.cols) return;
     const int64_t r0 = chunk * kSelChunk;
     const int64_t r1 = r0 + kSelChunk < S.rows ? r0 + kSelChunk : S.rows;
-    float ss = 0.f;
-    for (int64_t rb = r0; rb < r1; rb += 8) {
-      float gv[8], mv[8];
+    if (V == 4) {
+      f32x4 ss = {0.f, 0.f, 0.f, 0.f};
+      for (int64_t rb = r0; rb < r1; rb += 4) {
+        f32x4 gv[4], mv[4];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        if (rb + q < r1) {
-          gv[q] = __builtin_nontemporal_load(S.g + (rb + q) * S.cols + c);
-          mv[q] = S.mom[(rb + q) * S.cols + c];
+        for (int q = 0; q < 4; ++q) {
+          if (rb + q < r1) {
+            gv[q] = __builtin_nontemporal_load((const f32x4*)(S.g + (rb + q) * S.cols + c));
+            mv[q] = *(const f32x4*)(S.mom + (rb + q) * S.cols + c);
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (rb + q < r1) {
+            const f32x4 v = mv[q] + gv[q];
+            *(f32x4*)(S.mom + (rb + q) * S.cols + c) = v;
+            ss[0] += v[0] * v[0];
+            ss[1] += v[1] * v[1];
+            ss[2] += v[2] * v[2];
+            ss[3] += v[3] * v[3];
+          }
         }
       }
+      *(f32x4*)(S.score + chunk * S.m + c) = ss;
+    } else {
+      float ss = 0.f;
+      for (int64_t rb = r0; rb < r1; rb += 8) {
+        float gv[8], mv[8];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        if (rb + q < r1) {
-          const float v = mv[q] + gv[q];
-          S.mom[(rb + q) * S.cols + c] = v;
-          ss += v * v;
+        for (int q = 0; q < 8; ++q) {
+          if (rb + q < r1) {
+            gv[q] = __builtin_nontemporal_load(S.g + (rb + q) * S.cols + c);
+            mv[q] = S.mom[(rb + q) * S.cols + c];
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          if (rb + q < r1) {
+            const float v = mv[q] + gv[q];
+            S.mom[(rb + q) * S.cols + c] = v;
+            ss += v * v;
+          }
         }
       }
+      S.score[chunk * S.m + c] = ss;
     }
-    S.score[chunk * S.m + c] = ss;
   }
 }
 
@@ -225,8 +253,13 @@ __global__ __launch_bounds__(kSelTopThreads) void sel_topk_kernel(const SelLaunc
   }
   int pos = block_exclusive_scan(selc, shScan);
 #pragma unroll
-  for (int q = 0; q < kSelMaxPer; ++q)
-    if (((take >> q) & 1u) && pos < S.k) S.idx[pos++] = j0 + q;
+  for (int q = 0; q < kSelMaxPer; ++q) {
+    if (q < cnt) {
+      const bool t = ((take >> q) & 1u) && pos < S.k;
+      S.pos[j0 + q] = t ? pos : -1;
+      if (t) S.idx[pos++] = j0 + q;
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -258,15 +291,47 @@ __global__ __launch_bounds__(kSelThreads) void sel_gather_kernel(const SelLaunch
 
 // ---------------------------------------------------------------------------
 // Scatter: W_S ← round(W_S − lrsc·O_S) and M_S ← β·B_S, one wave per row of
-// the block (same mapping as the gather).
+// the block.
+//  * wide: block row i → stored row idx[i], a contiguous row update;
+//  * tall: block row r → stored row r at the selected columns.  The row is
+//    walked densely through the inverse map (selected columns are spread
+//    over every 64-byte segment, so a dense walk moves no more data than a
+//    gather would, with full-width accesses); groups of 4 columns with no
+//    selected column are skipped.
 template <int PD>
-__device__ __forceinline__ void update_w(void* w, int64_t e, float lrsc, float o) {
+__device__ __forceinline__ float w_load(const void* w, int64_t e) {
+  if constexpr (PD == 1) return __uint_as_float((uint32_t)((const uint16_t*)w)[e] << 16);
+  else return ((const float*)w)[e];
+}
+template <int PD>
+__device__ __forceinline__ void w_store(void* w, int64_t e, float v) {
+  if constexpr (PD == 1) ((uint16_t*)w)[e] = to_bf16_rne(v);
+  else ((float*)w)[e] = v;
+}
+
+// Four consecutive weights at e (e % 4 == 0, aligned), widened to fp32.
+template <int PD>
+__device__ __forceinline__ f32x4 w_load4(const void* w, int64_t e) {
+  f32x4 r;
   if constexpr (PD == 1) {
-    uint16_t* p = (uint16_t*)w + e;
-    *p = to_bf16_rne(fmaf(-lrsc, o, __uint_as_float((uint32_t)*p << 16)));
+    const uint2 u = *(const uint2*)((const uint16_t*)w + e);
+    r[0] = __uint_as_float(u.x << 16);
+    r[1] = __uint_as_float(u.x & 0xffff0000u);
+    r[2] = __uint_as_float(u.y << 16);
+    r[3] = __uint_as_float(u.y & 0xffff0000u);
   } else {
-    float* p = (float*)w + e;
-    *p = fmaf(-lrsc, o, *p);
+    r = *(const f32x4*)((const float*)w + e);
+  }
+  return r;
+}
+template <int PD>
+__device__ __forceinline__ void w_store4(void* w, int64_t e, f32x4 v) {
+  if constexpr (PD == 1) {
+    const uint32_t p0 = (uint32_t)to_bf16_rne(v[0]) | ((uint32_t)to_bf16_rne(v[1]) << 16);
+    const uint32_t p1 = (uint32_t)to_bf16_rne(v[2]) | ((uint32_t)to_bf16_rne(v[3]) << 16);
+    *(uint2*)((uint16_t*)w + e) = make_uint2(p0, p1);
+  } else {
+    *(f32x4*)((float*)w + e) = v;
   }
 }
 
@@ -275,16 +340,54 @@ __device__ __forceinline__ void scatter_row(const SelLaunch& L, const SelMat& S,
   if (!S.tall) {
     const int64_t r = S.idx[row];
     const float* o = S.xs + row * S.cols;
-    for (int64_t c = lane; c < S.cols; c += 64) {
-      update_w<PD>(S.w, r * S.cols + c, S.lrsc, o[c]);
-      S.mom[r * S.cols + c] = L.beta * S.mom[r * S.cols + c];
+    float* mo = S.mom + r * S.cols;
+    const int64_t wb = r * S.cols;
+    if (L.vec) {
+      for (int64_t c = (int64_t)lane * 4; c < S.cols; c += 256) {
+        const f32x4 ov = *(const f32x4*)(o + c);
+        f32x4 wv = w_load4<PD>(S.w, wb + c);
+        f32x4 mv = *(const f32x4*)(mo + c);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          wv[e] = fmaf(-S.lrsc, ov[e], wv[e]);
+          mv[e] = L.beta * mv[e];
+        }
+        w_store4<PD>(S.w, wb + c, wv);
+        *(f32x4*)(mo + c) = mv;
+      }
+    } else {
+      for (int64_t c = lane; c < S.cols; c += 64) {
+        w_store<PD>(S.w, wb + c, fmaf(-S.lrsc, o[c], w_load<PD>(S.w, wb + c)));
+        mo[c] = L.beta * mo[c];
+      }
     }
   } else {
     const float* o = S.xs + row * S.k;
-    for (int i = lane; i < S.k; i += 64) {
-      const int64_t e = row * S.cols + S.idx[i];
-      update_w<PD>(S.w, e, S.lrsc, o[i]);
-      S.mom[e] = L.beta * S.mom[e];
+    float* mo = S.mom + row * S.cols;
+    const int64_t wb = row * S.cols;
+    if (L.vec) {
+      for (int64_t c = (int64_t)lane * 4; c < S.cols; c += 256) {
+        const int4 p = *(const int4*)(S.pos + c);
+        if ((p.x & p.y & p.z & p.w) < 0) continue;  // no selected column here
+        f32x4 wv = w_load4<PD>(S.w, wb + c);
+        f32x4 mv = *(const f32x4*)(mo + c);
+        const int pp[4] = {p.x, p.y, p.z, p.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (pp[e] >= 0) {
+            wv[e] = fmaf(-S.lrsc, o[pp[e]], wv[e]);
+            mv[e] = L.beta * mv[e];
+          }
+        }
+        w_store4<PD>(S.w, wb + c, wv);
+        *(f32x4*)(mo + c) = mv;
+      }
+    } else {
+      for (int i = lane; i < S.k; i += 64) {
+        const int64_t c = S.idx[i];
+        w_store<PD>(S.w, wb + c, fmaf(-S.lrsc, o[i], w_load<PD>(S.w, wb + c)));
+        mo[c] = L.beta * mo[c];
+      }
     }
   }
 }
