@@ -164,6 +164,9 @@ struct StepVariant {
   int gradDtype = MUON_DTYPE_F32;
   int nesterov = 0;
   float decay = 1.f;  // 1 − lr·weight_decay
+  // 1: each matrix's Σx² is already in its first partial (the selected
+  // step's top-k writes it), so the sum-of-squares pass is skipped
+  int presummed = 0;
 };
 
 template <typename T>
@@ -184,7 +187,7 @@ muon_status_t enqueue(const Plan& P, const std::vector<CallerMat>& cm, int srcDt
   const ScalePlan& sc = P.scales;
 
   // 1. momentum / sum of squares
-  for (size_t c0 = 0; c0 < live.size(); c0 += kMaxUser) {
+  for (size_t c0 = 0; c0 < (V.presummed ? 0 : live.size()); c0 += kMaxUser) {
     EwLaunch L;
     std::memset(&L, 0, sizeof(L));
     L.mode = P.forStep ? 0 : 1;
@@ -235,7 +238,7 @@ muon_status_t enqueue(const Plan& P, const std::vector<CallerMat>& cm, int srcDt
     for (size_t k = 0; k < cn; ++k) {
       const int i = live[c0 + k];
       L.off[k] = P.mats[i].partialOff;
-      L.cnt[k] = P.mats[i].partialCnt;
+      L.cnt[k] = V.presummed ? 1 : P.mats[i].partialCnt;
       L.alphaIdx[k] = i;
       bytes += 4.0 * P.mats[i].partialCnt;
     }
@@ -671,6 +674,7 @@ muon_status_t enqueue_selected(const SelLayout& Lo, void* const* params, const f
       M.score = at<float>(ws, s.offScore);
       M.idx = at<int32_t>(ws, s.offIdx);
       M.pos = at<int32_t>(ws, s.offPos);
+      M.nsSum = at<float>(ws, Lo.ns.offPartials) + Lo.ns.mats[i].partialOff;
       M.rows = rows[i];
       M.cols = cols[i];
       M.m = (int32_t)s.m;
@@ -690,7 +694,7 @@ muon_status_t enqueue_selected(const SelLayout& Lo, void* const* params, const f
     for (size_t q = 0; q < cn; ++q) {
       SelMat& M = L.mat[q];
       M.blockStart = blocks;
-      const int64_t span = (int64_t)kSelThreads * (vec ? 4 : 1);  // columns per workgroup (tall)
+      const int64_t span = 64 * (vec ? 4 : 1);  // columns per workgroup (tall)
       blocks += M.tall ? (int64_t)M.nChunks * ((M.cols + span - 1) / span) : (M.rows + 3) / 4;
       bytes += 12.0 * (double)M.rows * (double)M.cols + 4.0 * M.nChunks * (double)M.m;
     }
@@ -714,7 +718,7 @@ muon_status_t enqueue_selected(const SelLayout& Lo, void* const* params, const f
       SelMat& M = L.mat[q];
       M.blockStart = blocks;
       blocks += ((M.tall ? M.rows : (int64_t)M.k) + 3) / 4;
-      bytes += 8.0 * (double)(M.tall ? M.rows : M.k) * (double)(M.tall ? M.k : M.cols);
+      bytes += 12.0 * (double)(M.tall ? M.rows : M.k) * (double)(M.tall ? M.k : M.cols);
     }
     s = Lr.run(10, bytes, "selected gather kernel", [&] { return launch_sel_gather(L, blocks, st); });
     if (s != MUON_OK) return s;
@@ -730,9 +734,11 @@ muon_status_t enqueue_selected(const SelLayout& Lo, void* const* params, const f
     cm[i].grad = nullptr;
     cm[i].lrsc = 0.f;
   }
-  muon_status_t s = enqueue(Lo.ns, cm, MUON_DTYPE_F32, MUON_DTYPE_F32, 0.f, eps, StepVariant{}, ws, st);
+  StepVariant V;
+  V.presummed = 1;  // ‖B_S‖²_F = Σ of the selected scores, written by the top-k
+  muon_status_t s = enqueue(Lo.ns, cm, MUON_DTYPE_F32, MUON_DTYPE_F32, 0.f, eps, V, ws, st);
   if (s != MUON_OK) return s;
-  // 5. scatter the update and decay the selected buffer rows
+  // 5. scatter the update (the gather has already decayed the buffer on S)
   for (size_t c0 = 0; c0 < live.size(); c0 += kMaxUser) {
     SelLaunch L;
     const size_t cn = std::min(live.size() - c0, (size_t)kMaxUser);
@@ -743,8 +749,7 @@ muon_status_t enqueue_selected(const SelLayout& Lo, void* const* params, const f
       SelMat& M = L.mat[q];
       M.blockStart = blocks;
       blocks += ((M.tall ? M.rows : (int64_t)M.k) + 3) / 4;
-      bytes += (4.0 + 2.0 * psz + 8.0) * (double)(M.tall ? M.rows : M.k) *
-               (double)(M.tall ? M.k : M.cols);
+      bytes += (4.0 + 2.0 * psz) * (double)(M.tall ? M.rows : M.k) * (double)(M.tall ? M.k : M.cols);
     }
     s = Lr.run(11, bytes, "selected scatter kernel", [&] { return launch_sel_scatter(L, blocks, st); });
     if (s != MUON_OK) return s;

@@ -171,6 +171,7 @@ struct SelMat {
   float* score;        // partial scores, nChunks × m (nChunks = 1 for a wide matrix)
   int32_t* idx;        // the k selected indices along the short side, ascending
   int32_t* pos;        // inverse map, m entries: position in idx, or −1
+  float* nsSum;        // Σ of the selected scores = ‖B_S‖²_F (the block's norm partial)
   int64_t rows, cols;
   int32_t m, k, tall, nChunks;
   int64_t blockStart;  // first workgroup of this matrix in the launch

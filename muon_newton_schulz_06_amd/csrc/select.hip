@@ -11,7 +11,9 @@
 //                                     every oriented row as its score)
 //   S = the k = ⌈ρ·m⌉ highest scores, equal scores to the lower index
 //   X_S = B restricted to S          (gathered into a dense fp32 block)
-//   O_S = NS(X_S / (‖X_S‖_F + eps))  (the batched Gram pipeline, in place)
+//   O_S = NS(X_S / (‖X_S‖_F + eps))  (the batched Gram pipeline, in place;
+//                                     ‖X_S‖²_F is the sum of the selected
+//                                     scores, so it needs no pass of its own)
 //   W_S ← round(W_S − lr·√max(1, rows/cols)·O_S),  M_S ← β·B_S,
 //   M elsewhere keeps B (the error that later steps pick up).
 //
@@ -54,9 +56,10 @@ __device__ __forceinline__ int find_mat(const SelLaunch& L, int64_t b) {
 // B = M + g and the row scores.
 //  * wide / square (rows ≤ cols): one wave per stored row, 16-byte accesses
 //    when allowed, lane sums then a wavefront butterfly → score[row];
-//  * tall: one thread per 4 stored columns (1 without 16-byte alignment)
-//    over a chunk of kSelChunk rows, so a wave reads 1 KiB contiguous per
-//    row → score[chunk·m + col]; the top-k kernel adds the chunks in order.
+//  * tall: a workgroup covers 256 stored columns (4 per lane; 64 without
+//    16-byte alignment) of a chunk of kSelChunk rows, each wave a quarter of
+//    the rows, so a wave reads 1 KiB contiguous per row → score[chunk·m +
+//    col]; the top-k kernel adds the chunks in order.
 __global__ __launch_bounds__(kSelThreads) void sel_accum_kernel(const SelLaunch L) {
   const int64_t b = blockIdx.x;
   const SelMat& S = L.mat[find_mat(L, b)];
@@ -102,59 +105,70 @@ __global__ __launch_bounds__(kSelThreads) void sel_accum_kernel(const SelLaunch 
     ss = sel_wave_sum(ss);
     if (lane == 0) S.score[r] = ss;
   } else {
-    // V consecutive columns per thread (16-byte accesses when allowed)
+    // V consecutive columns per lane (16-byte accesses when allowed); the
+    // four waves take rows r0 + w, r0 + w + 4, … of the chunk and their sums
+    // are added in wave order through LDS.
     const int V = L.vec ? 4 : 1;
-    const int64_t colBlocks = (S.cols + kSelThreads * V - 1) / (kSelThreads * V);
+    const int64_t span = 64 * V;
+    const int64_t colBlocks = (S.cols + span - 1) / span;
     const int64_t chunk = blk / colBlocks;
-    const int64_t c = (blk - chunk * colBlocks) * kSelThreads * V + (int64_t)tid * V;
-    if (c >= S.cols) return;
+    const int64_t c = (blk - chunk * colBlocks) * span + (int64_t)lane * V;
+    const int w = tid >> 6;
     const int64_t r0 = chunk * kSelChunk;
     const int64_t r1 = r0 + kSelChunk < S.rows ? r0 + kSelChunk : S.rows;
-    if (V == 4) {
-      f32x4 ss = {0.f, 0.f, 0.f, 0.f};
-      for (int64_t rb = r0; rb < r1; rb += 4) {
-        f32x4 gv[4], mv[4];
+    __shared__ f32x4 part[kSelThreads / 64][64];
+    f32x4 ss = {0.f, 0.f, 0.f, 0.f};
+    if (c < S.cols) {
+      if (V == 4) {
+        for (int64_t rb = r0 + w; rb < r1; rb += 16) {
+          f32x4 gv[4], mv[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          if (rb + q < r1) {
-            gv[q] = __builtin_nontemporal_load((const f32x4*)(S.g + (rb + q) * S.cols + c));
-            mv[q] = *(const f32x4*)(S.mom + (rb + q) * S.cols + c);
+          for (int q = 0; q < 4; ++q) {
+            if (rb + 4 * q < r1) {
+              gv[q] = __builtin_nontemporal_load((const f32x4*)(S.g + (rb + 4 * q) * S.cols + c));
+              mv[q] = *(const f32x4*)(S.mom + (rb + 4 * q) * S.cols + c);
+            }
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            if (rb + 4 * q < r1) {
+              const f32x4 v = mv[q] + gv[q];
+              *(f32x4*)(S.mom + (rb + 4 * q) * S.cols + c) = v;
+              ss[0] += v[0] * v[0];
+              ss[1] += v[1] * v[1];
+              ss[2] += v[2] * v[2];
+              ss[3] += v[3] * v[3];
+            }
           }
         }
+      } else {
+        for (int64_t rb = r0 + w; rb < r1; rb += 16) {
+          float gv[4], mv[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          if (rb + q < r1) {
-            const f32x4 v = mv[q] + gv[q];
-            *(f32x4*)(S.mom + (rb + q) * S.cols + c) = v;
-            ss[0] += v[0] * v[0];
-            ss[1] += v[1] * v[1];
-            ss[2] += v[2] * v[2];
-            ss[3] += v[3] * v[3];
+          for (int q = 0; q < 4; ++q) {
+            if (rb + 4 * q < r1) {
+              gv[q] = __builtin_nontemporal_load(S.g + (rb + 4 * q) * S.cols + c);
+              mv[q] = S.mom[(rb + 4 * q) * S.cols + c];
+            }
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            if (rb + 4 * q < r1) {
+              const float v = mv[q] + gv[q];
+              S.mom[(rb + 4 * q) * S.cols + c] = v;
+              ss[0] += v * v;
+            }
           }
         }
       }
-      *(f32x4*)(S.score + chunk * S.m + c) = ss;
-    } else {
-      float ss = 0.f;
-      for (int64_t rb = r0; rb < r1; rb += 8) {
-        float gv[8], mv[8];
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          if (rb + q < r1) {
-            gv[q] = __builtin_nontemporal_load(S.g + (rb + q) * S.cols + c);
-            mv[q] = S.mom[(rb + q) * S.cols + c];
-          }
-        }
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          if (rb + q < r1) {
-            const float v = mv[q] + gv[q];
-            S.mom[(rb + q) * S.cols + c] = v;
-            ss += v * v;
-          }
-        }
-      }
-      S.score[chunk * S.m + c] = ss;
+    }
+    part[w][lane] = ss;
+    __syncthreads();
+    if (w == 0 && c < S.cols) {
+      const f32x4 t = part[0][lane] + part[1][lane] + part[2][lane] + part[3][lane];
+      float* dst = S.score + chunk * S.m + c;
+      if (V == 4) *(f32x4*)dst = t;
+      else dst[0] = t[0];
     }
   }
 }
@@ -252,20 +266,37 @@ __global__ __launch_bounds__(kSelTopThreads) void sel_topk_kernel(const SelLaunc
     }
   }
   int pos = block_exclusive_scan(selc, shScan);
+  float tsum = 0.f;
 #pragma unroll
   for (int q = 0; q < kSelMaxPer; ++q) {
     if (q < cnt) {
       const bool t = ((take >> q) & 1u) && pos < S.k;
       S.pos[j0 + q] = t ? pos : -1;
-      if (t) S.idx[pos++] = j0 + q;
+      if (t) {
+        S.idx[pos++] = j0 + q;
+        tsum += __uint_as_float(key[q]);
+      }
     }
+  }
+  // ‖B_S‖²_F for the normalisation of the block: thread sums in index
+  // order, then a fixed butterfly per wave and the waves in order.
+  tsum = sel_wave_sum(tsum);
+  __shared__ float shSum[kSelTopThreads / 64];
+  if ((tid & 63) == 0) shSum[tid >> 6] = tsum;
+  __syncthreads();
+  if (tid == 0) {
+    float t = 0.f;
+    for (int w = 0; w < kSelTopThreads / 64; ++w) t += shSum[w];
+    *S.nsSum = t;
   }
 }
 
 // ---------------------------------------------------------------------------
-// Gather: one wave per row of the selected block.
-//  * wide: block row i = B row idx[i] (a contiguous row copy);
-//  * tall: block row r = B row r at the columns idx[0..k).
+// Gather, with the buffer's decay on the selection: one wave per row of the
+// block; X_S takes B_S and the buffer keeps β·B_S there (the rows are read
+// here anyway, so the decay costs only the write).
+//  * wide: block row i = B row idx[i] (contiguous);
+//  * tall: block row r = B row r at the columns idx[0..k) (ascending).
 __global__ __launch_bounds__(kSelThreads) void sel_gather_kernel(const SelLaunch L) {
   const int64_t b = blockIdx.x;
   const SelMat& S = L.mat[find_mat(L, b)];
@@ -273,25 +304,45 @@ __global__ __launch_bounds__(kSelThreads) void sel_gather_kernel(const SelLaunch
   const int lane = threadIdx.x & 63;
   if (!S.tall) {
     if (row >= S.k) return;
-    const float* src = S.mom + (int64_t)S.idx[row] * S.cols;
+    float* src = S.mom + (int64_t)S.idx[row] * S.cols;
     float* dst = S.xs + row * S.cols;
     if (L.vec) {
-      for (int64_t c = (int64_t)lane * 4; c < S.cols; c += 256)
-        *(f32x4*)(dst + c) = *(const f32x4*)(src + c);
+      for (int64_t c0 = (int64_t)lane * 4; c0 < S.cols; c0 += 4 * 256) {
+        f32x4 v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (c0 + q * 256 < S.cols) v[q] = *(const f32x4*)(src + c0 + q * 256);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int64_t c = c0 + q * 256;
+          if (c < S.cols) {
+            *(f32x4*)(dst + c) = v[q];
+            *(f32x4*)(src + c) = L.beta * v[q];
+          }
+        }
+      }
     } else {
-      for (int64_t c = lane; c < S.cols; c += 64) dst[c] = src[c];
+      for (int64_t c = lane; c < S.cols; c += 64) {
+        const float v = src[c];
+        dst[c] = v;
+        src[c] = L.beta * v;
+      }
     }
   } else {
     if (row >= S.rows) return;
-    const float* src = S.mom + row * S.cols;
+    float* src = S.mom + row * S.cols;
     float* dst = S.xs + row * S.k;
-    for (int i = lane; i < S.k; i += 64) dst[i] = src[S.idx[i]];
+    for (int i = lane; i < S.k; i += 64) {
+      const int c = S.idx[i];
+      const float v = src[c];
+      dst[i] = v;
+      src[c] = L.beta * v;
+    }
   }
 }
 
 // ---------------------------------------------------------------------------
-// Scatter: W_S ← round(W_S − lrsc·O_S) and M_S ← β·B_S, one wave per row of
-// the block.
+// Scatter: W_S ← round(W_S − lrsc·O_S), one wave per row of the block.
 //  * wide: block row i → stored row idx[i], a contiguous row update;
 //  * tall: block row r → stored row r at the selected columns.  The row is
 //    walked densely through the inverse map (selected columns are spread
@@ -340,53 +391,68 @@ __device__ __forceinline__ void scatter_row(const SelLaunch& L, const SelMat& S,
   if (!S.tall) {
     const int64_t r = S.idx[row];
     const float* o = S.xs + row * S.cols;
-    float* mo = S.mom + r * S.cols;
     const int64_t wb = r * S.cols;
     if (L.vec) {
-      for (int64_t c = (int64_t)lane * 4; c < S.cols; c += 256) {
-        const f32x4 ov = *(const f32x4*)(o + c);
-        f32x4 wv = w_load4<PD>(S.w, wb + c);
-        f32x4 mv = *(const f32x4*)(mo + c);
+      // four 4-column groups per lane per iteration, every load first
+      for (int64_t c0 = (int64_t)lane * 4; c0 < S.cols; c0 += 4 * 256) {
+        f32x4 ov[4], wv[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          wv[e] = fmaf(-S.lrsc, ov[e], wv[e]);
-          mv[e] = L.beta * mv[e];
+        for (int q = 0; q < 4; ++q) {
+          const int64_t c = c0 + q * 256;
+          if (c < S.cols) {
+            ov[q] = *(const f32x4*)(o + c);
+            wv[q] = w_load4<PD>(S.w, wb + c);
+          }
         }
-        w_store4<PD>(S.w, wb + c, wv);
-        *(f32x4*)(mo + c) = mv;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int64_t c = c0 + q * 256;
+          if (c < S.cols) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) wv[q][e] = fmaf(-S.lrsc, ov[q][e], wv[q][e]);
+            w_store4<PD>(S.w, wb + c, wv[q]);
+          }
+        }
       }
     } else {
-      for (int64_t c = lane; c < S.cols; c += 64) {
+      for (int64_t c = lane; c < S.cols; c += 64)
         w_store<PD>(S.w, wb + c, fmaf(-S.lrsc, o[c], w_load<PD>(S.w, wb + c)));
-        mo[c] = L.beta * mo[c];
-      }
     }
   } else {
     const float* o = S.xs + row * S.k;
-    float* mo = S.mom + row * S.cols;
     const int64_t wb = row * S.cols;
     if (L.vec) {
-      for (int64_t c = (int64_t)lane * 4; c < S.cols; c += 256) {
-        const int4 p = *(const int4*)(S.pos + c);
-        if ((p.x & p.y & p.z & p.w) < 0) continue;  // no selected column here
-        f32x4 wv = w_load4<PD>(S.w, wb + c);
-        f32x4 mv = *(const f32x4*)(mo + c);
-        const int pp[4] = {p.x, p.y, p.z, p.w};
+      for (int64_t c0 = (int64_t)lane * 4; c0 < S.cols; c0 += 4 * 256) {
+        int4 p[4];
+        f32x4 wv[4];
+        bool any[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if (pp[e] >= 0) {
-            wv[e] = fmaf(-S.lrsc, o[pp[e]], wv[e]);
-            mv[e] = L.beta * mv[e];
+        for (int q = 0; q < 4; ++q) {
+          const int64_t c = c0 + q * 256;
+          any[q] = false;
+          if (c < S.cols) {
+            p[q] = *(const int4*)(S.pos + c);
+            any[q] = (p[q].x & p[q].y & p[q].z & p[q].w) >= 0;  // some entry is not −1
           }
         }
-        w_store4<PD>(S.w, wb + c, wv);
-        *(f32x4*)(mo + c) = mv;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (any[q]) wv[q] = w_load4<PD>(S.w, wb + c0 + q * 256);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (any[q]) {
+            const int pp[4] = {p[q].x, p[q].y, p[q].z, p[q].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (pp[e] >= 0) wv[q][e] = fmaf(-S.lrsc, o[pp[e]], wv[q][e]);
+            w_store4<PD>(S.w, wb + c0 + q * 256, wv[q]);
+          }
+        }
       }
     } else {
       for (int i = lane; i < S.k; i += 64) {
         const int64_t c = S.idx[i];
         w_store<PD>(S.w, wb + c, fmaf(-S.lrsc, o[i], w_load<PD>(S.w, wb + c)));
-        mo[c] = L.beta * mo[c];
       }
     }
   }
