@@ -6,7 +6,10 @@ Newton–Schulz in the Gram formulation, shape-scaled update — used as a
 drop-in optimiser module (§3 of the same page: the module replaces the
 optimiser and changes nothing else in the training framework).  Every step
 runs in the library's HIP kernels through `muon_step` / `muon_step_ex`;
-this class only groups tensors and keeps the momentum state.
+this class only groups tensors and keeps the momentum state.  A group with
+`selected_fraction` set runs the row/column-selected step with error
+feedback instead (`muon_step_selected`; Dion3 review, blog.secrett2633.cloud,
+§3 "Method & Key Results" and §1 "Error Feedback").
 
 Only 2-D parameters are accepted (Muon orthogonalises matrices; biases,
 norms and embeddings belong in another optimiser).  Parameters may be bf16
@@ -19,7 +22,7 @@ import math
 
 import torch
 
-from . import QUINTIC, muon_step
+from . import QUINTIC, muon_step, muon_step_selected
 
 
 class Muon(torch.optim.Optimizer):
@@ -34,13 +37,20 @@ class Muon(torch.optim.Optimizer):
       ns_steps:        Newton–Schulz steps (0–64)
       ns_coefficients: (a, b, c) of X ← a·X + (b·A + c·A²)·X, A = X·Xᵀ
       eps:             added to ‖M‖_F before normalising
+      selected_fraction: None for the plain step; ρ in (0, 1] for the
+                       row/column-selected step: only the ⌈ρ·m⌉ highest-norm
+                       rows of B = M + g along the short side are
+                       orthogonalised and applied, the buffer keeps β·B there
+                       and B elsewhere (not combinable with nesterov or
+                       weight_decay; bf16 gradients are widened to fp32)
     """
 
     def __init__(self, params, lr: float = 0.02, momentum: float = 0.95, nesterov: bool = False,
                  weight_decay: float = 0.0, ns_steps: int = 5, ns_coefficients=QUINTIC,
-                 eps: float = 1e-7):
+                 eps: float = 1e-7, selected_fraction=None):
         defaults = dict(lr=lr, momentum=momentum, nesterov=nesterov, weight_decay=weight_decay,
-                        ns_steps=ns_steps, ns_coefficients=tuple(ns_coefficients), eps=eps)
+                        ns_steps=ns_steps, ns_coefficients=tuple(ns_coefficients), eps=eps,
+                        selected_fraction=selected_fraction)
         _check_hyper(defaults)
         super().__init__(params, defaults)
         for group in self.param_groups:
@@ -88,11 +98,19 @@ class Muon(torch.optim.Optimizer):
                 gs.append(g.contiguous())
                 ms.append(buf)
             for (dev, _, _), (ps, gs, ms) in parts.items():
+                stream = torch.cuda.current_stream(dev) if dev.type == "cuda" else None
+                if group["selected_fraction"] is not None:
+                    muon_step_selected(ps, [g.float() for g in gs], ms,
+                                       fraction=group["selected_fraction"], beta=group["momentum"],
+                                       lr=group["lr"], steps=group["ns_steps"],
+                                       coeffs=group["ns_coefficients"], eps=group["eps"],
+                                       stream=stream)
+                    continue
                 muon_step(ps, gs, ms, beta=group["momentum"], lr=group["lr"],
                           steps=group["ns_steps"], coeffs=group["ns_coefficients"],
                           eps=group["eps"], nesterov=group["nesterov"],
                           weight_decay=group["weight_decay"],
-                          stream=torch.cuda.current_stream(dev) if dev.type == "cuda" else None)
+                          stream=stream)
         return loss
 
     def load_state_dict(self, state_dict):
@@ -128,3 +146,9 @@ def _check_hyper(h):
         raise ValueError(f"invalid ns_coefficients {c}")
     if not isinstance(h["nesterov"], bool):
         raise ValueError(f"nesterov must be a bool, got {h['nesterov']!r}")
+    f = h.get("selected_fraction")
+    if f is not None:
+        if not finite(f) or not 0.0 < float(f) <= 1.0:
+            raise ValueError(f"invalid selected_fraction {f} (use a value in (0, 1])")
+        if h["nesterov"] or h["weight_decay"] != 0:
+            raise ValueError("selected_fraction does not combine with nesterov or weight_decay")

@@ -54,3 +54,40 @@ def test_muon_step_graph_replays_match_eager(mns):
         for j in range(len(shapes)):
             assert torch.equal(gp[j], eager[step][0][j]), ("weights", step, j)
             assert torch.equal(gm[j], eager[step][1][j]), ("momentum", step, j)
+
+
+def test_selected_step_graph_replays_match_eager(mns):
+    """muon_step_selected also enqueues kernels only (score pass, top-k,
+    gather, the batched pipeline, scatter): three graph replays equal three
+    eager steps bit for bit."""
+    shapes = [(256, 1024), (1024, 256), (300, 700), (64, 64)]
+    base = W.selected_inputs(shapes, 321, device="cuda", m_std=1e-2)
+    ws = torch.empty(mns.step_selected_workspace_size(shapes, 0.25), dtype=torch.uint8, device="cuda")
+
+    def clone(inp):
+        return ([p.clone() for p in inp.params], [g.clone() for g in inp.grads],
+                [m.clone() for m in inp.momenta])
+
+    ep, eg, em = clone(base)
+    eager = []
+    for _ in range(3):
+        mns.muon_step_selected(ep, eg, em, fraction=0.25, workspace=ws)
+        eager.append(([p.clone() for p in ep], [m.clone() for m in em]))
+    torch.cuda.synchronize()
+
+    gp, gg, gm = clone(base)
+    ws2 = torch.empty_like(ws)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        mns.muon_step_selected(gp, gg, gm, fraction=0.25, workspace=ws2)
+    assert all(torch.equal(p, q) for p, q in zip(gp, base.params))
+    for step in range(3):
+        graph.replay()
+        torch.cuda.synchronize()
+        junk = torch.randn(1 << 20, device="cuda").sum()
+        torch.cuda.synchronize()
+        assert torch.isfinite(junk)
+        for j in range(len(shapes)):
+            assert torch.equal(gp[j], eager[step][0][j]), ("weights", step, j)
+            assert torch.equal(gm[j], eager[step][1][j]), ("buffer", step, j)

@@ -109,3 +109,26 @@ def test_optimizer_follows_the_oracle(mns):
                 assert ok
             host_W[j] = got
             host_M[j] = got_M
+
+
+def test_selected_optimizer_equals_direct_library_call(mns):
+    """selected_fraction runs muon_step_selected (bf16 gradients widened to
+    fp32); two steps match the direct call bit for bit."""
+    ps = _model(91)
+    ref_w = [p.detach().clone() for p in ps]
+    ref_m = [torch.zeros(p.shape, dtype=torch.float32, device="cuda") for p in ps]
+    opt = mns.Muon(ps, lr=0.02, momentum=0.9, selected_fraction=0.3)
+    for step in range(2):
+        gs = _grads(ps, 700, step)
+        for p, g in zip(ps, gs):
+            p.grad = g
+        opt.step()
+        for dt in (torch.bfloat16, torch.float32):
+            idx = [j for j, p in enumerate(ps) if p.dtype == dt]
+            mns.muon_step_selected([ref_w[j] for j in idx], [gs[j].float() for j in idx],
+                                   [ref_m[j] for j in idx], fraction=0.3, beta=0.9, lr=0.02)
+        torch.cuda.synchronize()
+        for j, p in enumerate(ps):
+            assert torch.equal(p.detach(), ref_w[j]), ("weights", step, j)
+            assert torch.equal(opt.state[p]["momentum_buffer"], ref_m[j]), ("buffer", step, j)
+    say("selected optimizer == muon_step_selected over 2 steps")

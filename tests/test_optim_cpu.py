@@ -74,3 +74,17 @@ def test_state_dict_round_trip_keeps_fp32_momentum():
         assert b.dtype == torch.float32 and torch.equal(b, v)
     g = opt2.param_groups[0]
     assert g["lr"] == 0.01 and g["nesterov"] is True and g["weight_decay"] == 0.1
+
+
+@pytest.mark.parametrize("kw", [
+    dict(selected_fraction=0.0), dict(selected_fraction=1.5), dict(selected_fraction=float("nan")),
+    dict(selected_fraction=0.5, nesterov=True), dict(selected_fraction=0.5, weight_decay=0.1),
+])
+def test_rejects_bad_selected_fraction(kw):
+    with pytest.raises(ValueError):
+        mns.Muon(_params(), **kw)
+
+
+def test_selected_fraction_default_and_accepted():
+    assert mns.Muon(_params()).param_groups[0]["selected_fraction"] is None
+    assert mns.Muon(_params(), selected_fraction=0.25).param_groups[0]["selected_fraction"] == 0.25
