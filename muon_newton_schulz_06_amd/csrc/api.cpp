@@ -14,6 +14,12 @@
 //      one launch per product serving every matrix of every Gram group.
 //   6. O = Q_s·X₀ (X₀ᵀ·Q_s for tall matrices) with the output / weight
 //      update fused in the epilogue.
+//
+// muon_step_selected (Dion3 review, §3 and §1 "Error Feedback") runs, per
+// chunk of matrices: B = M + g with row scores, top-k (which also writes the
+// block's Σx²), gather of the selected block with the buffer's β decay; then
+// steps 2–6 above on the fp32 blocks (step 1 skipped), writing O_S in place;
+// then the scatter of the weight update.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
