@@ -205,3 +205,33 @@ def test_qwen_layer_shapes_sampled(mns):
         assert np.array_equal(Go[rest], Wo[rest])
         assert band_ok(Wo[S], Go[S], OS, LR * oracle.lr_shape_scale(r, c))
         say(f"  {name} {r}x{c}: k={k} ok")
+
+
+def test_full_set_sampled(mns):
+    """The benchmark's configuration: one selected step (ρ = 0.25) over all
+    196 Qwen2.5-7B-shaped matrices in one call (the same chunked launches and
+    Gram groups the benchmark times); seven matrices from the first and the
+    last layer are checked against the oracle."""
+    shapes = W.qwen_model_shapes(28)
+    inp = W.selected_inputs(shapes, 5001, device="cuda")
+    sample = {0: "L0 q", 1: "L0 k", 4: "L0 gate", 6: "L0 down", 27 * 7 + 2: "L27 v", 27 * 7 + 3: "L27 o",
+              27 * 7 + 5: "L27 up"}
+    Wc = {j: inp.params[j].float().double().cpu().numpy() for j in sample}
+    gc = {j: inp.grads[j].cpu().numpy() for j in sample}
+    say("full set, 196 matrices, fraction 0.25")
+    mns.muon_step_selected(inp.params, inp.grads, inp.momenta, fraction=0.25, beta=float(BETA), lr=LR,
+                           steps=5)
+    torch.cuda.synchronize()
+    for j, name in sample.items():
+        r, c = shapes[j]
+        k = oracle.selected_count(min(r, c), 0.25)
+        assert unique_margin(gc[j], k) > 1e-5, f"{name}: inputs do not fix the selection"
+        Wn, Mn, S, OS = oracle.muon_step_selected(Wc[j], gc[j], np.zeros((r, c), np.float32), BETA, LR,
+                                                  Q32, 5, EPS, 0.25)
+        assert np.array_equal(inp.momenta[j].cpu().numpy(), Mn), name
+        got = inp.params[j].float().double().cpu().numpy()
+        Go, Wo = (got.T, Wc[j].T) if r > c else (got, Wc[j])
+        rest = np.setdiff1d(np.arange(min(r, c)), S)
+        assert np.array_equal(Go[rest], Wo[rest]), name
+        assert band_ok(Wo[S], Go[S], OS, LR * oracle.lr_shape_scale(r, c)), name
+        say(f"  {name} {r}x{c}: k={k} ok")
