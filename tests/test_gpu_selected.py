@@ -78,7 +78,7 @@ def step_grads(shapes, seed, t):
     return g
 
 
-def run_and_check(mns, shapes, fraction, seed, steps_of_training=2, m_std=1e-2):
+def run_and_check(mns, shapes, fraction, seed, steps_of_training=2, m_std=1e-2, ns_steps=5):
     inp = to_gpu(W.selected_inputs(shapes, seed, m_std=m_std))
     Wc = [p.float().double().cpu().numpy() for p in inp.params]
     Mc = [m.cpu().numpy().copy() for m in inp.momenta]
@@ -88,7 +88,7 @@ def run_and_check(mns, shapes, fraction, seed, steps_of_training=2, m_std=1e-2):
         gc = [g.cpu().numpy() for g in inp.grads]
         say(f"selected step t={t} shapes={shapes} fraction={fraction} seed={seed}")
         mns.muon_step_selected(inp.params, inp.grads, inp.momenta, fraction=fraction, beta=float(BETA),
-                               lr=LR, steps=5)
+                               lr=LR, steps=ns_steps)
         torch.cuda.synchronize()
         for j, (r, c) in enumerate(shapes):
             if r == 0 or c == 0:
@@ -96,7 +96,7 @@ def run_and_check(mns, shapes, fraction, seed, steps_of_training=2, m_std=1e-2):
             B = (Mc[j].astype(np.float64) + gc[j]).astype(np.float32)
             k = oracle.selected_count(min(r, c), fraction)
             assert unique_margin(B, k) > 1e-4, "inputs do not fix the selection"
-            Wn, Mn, S, OS = oracle.muon_step_selected(Wc[j], gc[j], Mc[j], BETA, LR, Q32, 5, EPS,
+            Wn, Mn, S, OS = oracle.muon_step_selected(Wc[j], gc[j], Mc[j], BETA, LR, Q32, ns_steps, EPS,
                                                       fraction)
             got_M = inp.momenta[j].cpu().numpy()
             got_W = inp.params[j].float().double().cpu().numpy()
@@ -116,6 +116,14 @@ def run_and_check(mns, shapes, fraction, seed, steps_of_training=2, m_std=1e-2):
 def test_small_shapes_two_steps(mns, fraction):
     shapes = [(96, 200), (200, 96), (128, 128), (37, 501), (501, 37), (300, 1030), (1, 50), (50, 1)]
     run_and_check(mns, shapes, fraction, 61)
+
+
+@pytest.mark.parametrize("ns_steps", [0, 1, 2])
+def test_other_step_counts(mns, ns_steps):
+    """steps = 0 applies the normalised selected block itself; 1 and 2 steps
+    exercise the short recursions (the first-step Q and the A chain)."""
+    run_and_check(mns, [(96, 200), (200, 96), (300, 1030)], 0.25, 131, steps_of_training=1,
+                  ns_steps=ns_steps)
 
 
 def test_single_row_and_empty_matrices(mns):
