@@ -224,6 +224,7 @@ muon_status_t enqueue(const Plan& P, const std::vector<CallerMat>& cm, int srcDt
       } else {
         e.x = cm[i].src;
         e.ld = cm[i].ldSrc;
+        if (e.ld != mp.cols || ((uintptr_t)e.x & 15)) L.vec = 0;
         bytes += (srcDtype == MUON_DTYPE_BF16 ? 2.0 : 4.0) * mp.numel;
       }
       blocks += mp.partialCnt;

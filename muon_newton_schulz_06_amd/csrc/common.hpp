@@ -109,7 +109,8 @@ struct EwLaunch {
   int32_t n;
   int32_t mode;        // 0: momentum, 1: sum of squares of x
   int32_t xDtype;      // muon_dtype_t of x (the gradient in momentum mode)
-  int32_t vec;         // 1: every matrix contiguous, numel % 4 == 0, 16-B aligned
+  int32_t vec;         // 1: every matrix contiguous (ld == cols) and 16-B aligned (momentum
+                       //    mode: also numel % 4 == 0); partial blocks take the scalar path
   float beta;
   int32_t nesterov;    // momentum mode: Σ of (g + β·M')² instead of Σ M'²
   float* partials;

@@ -32,6 +32,7 @@ __device__ __forceinline__ double wave_sum_d(double v) {
 }
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float load_as_f32(const void* p, int64_t e, int dtype) {
   if (dtype == 1) return __uint_as_float((uint32_t)((const uint16_t*)p)[e] << 16);
@@ -115,6 +116,35 @@ __global__ __launch_bounds__(kEwThreads) void ew_kernel(const EwLaunch L) {
         }
       }
     }
+  } else if (L.vec && e0 + kEwElems <= M.numel) {
+    // contiguous input (ld == cols): 16-byte loads of the flat block, every
+    // load of the block issued before the first product
+    constexpr int Q = kEwElems / (4 * kEwThreads);
+    if (L.xDtype == 1) {
+      u32x4 u[Q / 2];
+#pragma unroll
+      for (int q = 0; q < Q / 2; ++q)
+        u[q] = __builtin_nontemporal_load((const u32x4*)((const uint16_t*)M.x + e0 + (int64_t)(q * kEwThreads + tid) * 8));
+#pragma unroll
+      for (int q = 0; q < Q / 2; ++q) {
+        const uint32_t w[4] = {u[q][0], u[q][1], u[q][2], u[q][3]};
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          const float a = __uint_as_float(w[h] << 16), b = __uint_as_float(w[h] & 0xffff0000u);
+          ss += a * a;
+          ss += b * b;
+        }
+      }
+    } else {
+      f32x4 x[Q];
+#pragma unroll
+      for (int q = 0; q < Q; ++q)
+        x[q] = __builtin_nontemporal_load((const f32x4*)((const float*)M.x + e0 + (int64_t)(q * kEwThreads + tid) * 4));
+#pragma unroll
+      for (int q = 0; q < Q; ++q)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) ss += x[q][c] * x[q][c];
+    }
   } else {
     for (int q = 0; q < kEwElems / kEwThreads; ++q) {
       const int64_t e = e0 + q * kEwThreads + tid;
@@ -181,9 +211,24 @@ __device__ void cast_tile(const CastLaunch& L, const CastMat& C, int64_t t) {
                    (!L.nesterov || (((uintptr_t)C.grad & (L.gradDtype == 1 ? 7 : 15)) == 0));
   // All four source rows are loaded before anything is stored (the
   // compiler cannot prove that the source and the copies do not overlap).
+  // bf16 input (the batched orthogonalisation of bf16 matrices): 8-byte loads
+  const bool vecb = full && !nest && L.srcDtype == 1 && (C.ld % 4 == 0) &&
+                    (((uintptr_t)C.src & 7) == 0);
   const int cl = 4 * tx;
   float v[4][4];
-  if (vec && !nest) {
+  if (vecb) {
+    uint2 x[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      x[q] = *(const uint2*)((const uint16_t*)C.src + (r0 + ty + 16 * q) * C.ld + c0 + cl);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      v[q][0] = __uint_as_float(x[q].x << 16) * scale;
+      v[q][1] = __uint_as_float(x[q].x & 0xffff0000u) * scale;
+      v[q][2] = __uint_as_float(x[q].y << 16) * scale;
+      v[q][3] = __uint_as_float(x[q].y & 0xffff0000u) * scale;
+    }
+  } else if (vec && !nest) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const f32x4 x = *(const f32x4*)((const float*)C.src + (r0 + ty + 16 * q) * C.ld + c0 + cl);
