@@ -203,12 +203,24 @@ __global__ __launch_bounds__(kSelTopThreads) void sel_topk_kernel(const SelLaunc
   const int j0 = tid * per;
   const int cnt = m - j0 < 0 ? 0 : (m - j0 < per ? m - j0 : per);
 
+  // A key is the sum of its chunk partials (one chunk for a wide matrix), in
+  // eight interleaved running sums added in a fixed tree at the end, so
+  // eight loads are in flight per thread.
   uint32_t key[kSelMaxPer];
 #pragma unroll
   for (int q = 0; q < kSelMaxPer; ++q) {
     float s = 0.f;
-    if (q < cnt)
-      for (int c = 0; c < S.nChunks; ++c) s += S.score[(int64_t)c * m + j0 + q];
+    if (q < cnt) {
+      const float* sp = S.score + j0 + q;
+      float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      int c = 0;
+      for (; c + 8 <= S.nChunks; c += 8) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) a[u] += sp[(int64_t)(c + u) * m];
+      }
+      for (; c < S.nChunks; ++c) a[0] += sp[(int64_t)c * m];
+      s = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
+    }
     key[q] = __float_as_uint(s);
   }
 
