@@ -53,7 +53,7 @@ extern "C" {
 typedef enum muon_status {
   MUON_OK = 0,
   MUON_ERR_INVALID_ARG = 1, /* null pointer, bad size, bad stride, bad scalar */
-  MUON_ERR_UNSUPPORTED = 2, /* a valid request this build does not handle   */
+  MUON_ERR_UNSUPPORTED = 2, /* a valid request the library does not handle  */
   MUON_ERR_ALIAS = 3,       /* writable ranges that overlap                  */
   MUON_ERR_WORKSPACE = 4,   /* workspace missing, too small or misaligned    */
   MUON_ERR_HIP = 5,         /* a HIP call or kernel launch failed            */
