@@ -368,3 +368,30 @@ def test_single_hip_runtime_in_process(mns):
             if "libamdhip64" in line:
                 libs.add(line.split()[-1])
     assert len(libs) == 1, libs
+
+
+@pytest.mark.parametrize("dtype,seed", [(torch.bfloat16, 7), (torch.float32, 8)])
+def test_seeded_random_shapes(mns, dtype, seed):
+    """Forty shapes drawn from a seeded generator (each side 1–600, a third of
+    them tall, some repeated so groups hold several matrices), orthogonalised
+    in one call against the oracle: the planner's groups, padding and tile
+    choices meet shapes nobody picked by hand."""
+    import random
+    rng = random.Random(seed)
+    shapes = []
+    while len(shapes) < 40:
+        r, c = rng.randint(1, 600), rng.randint(1, 600)
+        shapes.append((r, c))
+        if rng.random() < 0.25:
+            shapes.append((r, c))
+    say(f"{dtype} seeded random shapes", shapes)
+    xs = [W.gaussian(s, 700 + i, dtype=dtype) for i, s in enumerate(shapes)]
+    outs = mns.muon_ns_batched([x.cuda() for x in xs], steps=5)
+    torch.cuda.synchronize()
+    tol = TOL_BF16 if dtype == torch.bfloat16 else TOL_F32
+    worst = 0.0
+    for x, o in zip(xs, outs):
+        e = rel(o.float(), oracle_ns(x.float()))
+        worst = max(worst, e)
+        assert e <= tol, (tuple(x.shape), e)
+    say("worst", worst)
