@@ -291,6 +291,14 @@ def test_muon_step_small_shapes(mns):
     _check_step(mns, shapes, 900, range(len(shapes)))
 
 
+def test_muon_step_seeded_random_shapes(mns):
+    """Thirty seeded random shapes (each side 1–500) through two full steps."""
+    import random
+    rng = random.Random(11)
+    shapes = [(rng.randint(1, 500), rng.randint(1, 500)) for _ in range(30)]
+    _check_step(mns, shapes, 1300, range(len(shapes)))
+
+
 def test_muon_step_qwen_layer(mns):
     shapes = W.qwen_layer_shapes()
     _check_step(mns, shapes, 4001, check_idx=[1, 0], nsteps=2)

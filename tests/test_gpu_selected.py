@@ -126,6 +126,15 @@ def test_other_step_counts(mns, ns_steps):
                   ns_steps=ns_steps)
 
 
+def test_seeded_random_shapes(mns):
+    """Twenty-four seeded random shapes (each side 2–400) at ρ = 0.3 over two
+    training steps."""
+    import random
+    rng = random.Random(23)
+    shapes = [(rng.randint(2, 400), rng.randint(2, 400)) for _ in range(24)]
+    run_and_check(mns, shapes, 0.3, 151)
+
+
 def test_single_row_and_empty_matrices(mns):
     # fraction so small that k = 1 everywhere; an empty matrix in the list
     run_and_check(mns, [(64, 256), (0, 7), (256, 64), (5, 0)], 1e-6, 71, steps_of_training=1)
