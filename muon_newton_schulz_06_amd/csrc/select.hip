@@ -227,8 +227,42 @@ __global__ __launch_bounds__(kSelTopThreads) void sel_topk_kernel(const SelLaunc
   __shared__ uint32_t hist[256];
   __shared__ uint32_t shPrefix, shKrem;
   __shared__ int shScan[kSelTopThreads / 64];
+  __shared__ uint32_t shOr[kSelTopThreads / 64], shAnd[kSelTopThreads / 64];
+  // Scores of one matrix usually share their top byte (sign and high
+  // exponent bits), which would send every key of the first pass to one
+  // histogram bin; a byte common to all keys is taken without a pass (it
+  // changes neither the prefix's rank nor krem).
+  uint32_t kor = 0u, kand = 0xffffffffu;
+#pragma unroll
+  for (int q = 0; q < kSelMaxPer; ++q)
+    if (q < cnt) {
+      kor |= key[q];
+      kand &= key[q];
+    }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    kor |= (uint32_t)__shfl_xor((int)kor, o, 64);
+    kand &= (uint32_t)__shfl_xor((int)kand, o, 64);
+  }
+  if ((tid & 63) == 0) {
+    shOr[tid >> 6] = kor;
+    shAnd[tid >> 6] = kand;
+  }
+  __syncthreads();
+  kor = 0u;
+  kand = 0xffffffffu;
+  for (int w = 0; w < kSelTopThreads / 64; ++w) {
+    kor |= shOr[w];
+    kand &= shAnd[w];
+  }
   uint32_t prefix = 0, mask = 0, krem = (uint32_t)S.k;
-  for (int pass = 0; pass < 4; ++pass) {
+  int pass0 = 0;
+  if (((kor ^ kand) >> 24) == 0u) {
+    prefix = kand & 0xff000000u;
+    mask = 0xff000000u;
+    pass0 = 1;
+  }
+  for (int pass = pass0; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
     if (tid < 256) hist[tid] = 0;
     __syncthreads();
