@@ -91,10 +91,17 @@ typedef struct muon_ns_desc {
  * Precision:
  *   MUON_DTYPE_F32:  fp32 MFMA products on fp32 operand copies;
  *   MUON_DTYPE_BF16: half-precision MFMA products (fp16 operands scaled by
- *                    powers of two, fp32 accumulation).  The Gram-space
- *                    iterates live as those scaled fp16 copies, plus fp32
- *                    copies of A and P·A when m ≤ 2048 (small Gram matrices
- *                    are the worst conditioned).
+ *                    powers of two, fp32 accumulation), with one exception
+ *                    and one addition, decided per group of matrices that
+ *                    share m (nearly square means n ≤ 2m):
+ *                    - m ≤ 1024 and nearly square: the whole recursion runs
+ *                      on fp32 operands with fp32 MFMA (small square Gram
+ *                      matrices are the worst conditioned);
+ *                    - 1024 < m ≤ 2048 and at least one nearly square
+ *                      matrix in the group: fp16 operands plus fp32 copies
+ *                      of A and P·A (the a·Y terms of the A-chain);
+ *                    - every other group (all wide matrices, n > 2m, and
+ *                      every m > 2048): fp16 operands only, no fp32 state.
  * The matrices are grouped by shape: one launch per stage serves every
  * matrix of a group. */
 muon_status_t muon_ns_batched(const muon_ns_desc_t* desc, int32_t count, int32_t steps,

@@ -178,27 +178,40 @@ def _ld(t: torch.Tensor) -> int:
 
 
 _ws_cache: dict = {}
+_ws_lock = threading.Lock()
 
 
-def _workspace(nbytes: int, device, user):
+def _workspace(nbytes: int, device, user, stream=None):
+    """The workspace of a call: the caller's buffer, or a cached one.
+
+    Cached buffers are kept per (device, stream) and allocated while that
+    stream is current, so the caching allocator files them under the stream
+    the library's kernels use: calls on one stream reuse its buffer in stream
+    order, calls on different streams never share one, and a buffer dropped
+    for a larger one is only handed out again for work on that same stream
+    (after the kernels already enqueued there)."""
     if nbytes == 0:
         return None, 0
     if user is not None:
         if user.device != device:
             raise ValueError("workspace on another device")
         return user, user.numel() * user.element_size()
-    key = (device.type, device.index)
-    buf = _ws_cache.get(key)
-    if buf is None or buf.numel() < nbytes:
-        _ws_cache.pop(key, None)
-        buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
-        _ws_cache[key] = buf
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    key = (device.type, device.index, s.cuda_stream)
+    with _ws_lock:
+        buf = _ws_cache.get(key)
+        if buf is None or buf.numel() < nbytes:
+            _ws_cache.pop(key, None)
+            with torch.cuda.stream(s):
+                buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+            _ws_cache[key] = buf
     return buf, buf.numel()
 
 
 def release_workspace():
     """Drop the cached workspace buffers (the next call allocates anew)."""
-    _ws_cache.clear()
+    with _ws_lock:
+        _ws_cache.clear()
 
 
 def _ns_descs(xs, outs):
@@ -279,7 +292,7 @@ def muon_ns_batched(xs, outs=None, steps: int = 5, coeffs=QUINTIC, eps: float = 
     arr = _ns_descs(xs, outs)
     need = ctypes.c_size_t(0)
     _check(L.muon_ns_workspace_size(arr, len(xs), code, ctypes.byref(need)))
-    ws, ws_bytes = _workspace(int(need.value), dev, workspace)
+    ws, ws_bytes = _workspace(int(need.value), dev, workspace, stream)
     with torch.cuda.device(dev):
         _check(L.muon_ns_batched(arr, len(xs), int(steps), _coeffs(coeffs), code, float(eps),
                                  ctypes.c_void_p(ws.data_ptr() if ws is not None else 0),
@@ -327,7 +340,7 @@ def muon_step(params, grads, momenta, beta: float = 0.95, lr: float = 0.02, step
     cols = (ctypes.c_int64 * n)(*[int(p.shape[1]) for p in params])
     need = ctypes.c_size_t(0)
     _check(L.muon_step_workspace_size(rows, cols, n, ctypes.byref(need)))
-    ws, ws_bytes = _workspace(int(need.value), dev, workspace)
+    ws, ws_bytes = _workspace(int(need.value), dev, workspace, stream)
     plain = (not nesterov) and float(weight_decay) == 0.0 and gdt == torch.float32
     with torch.cuda.device(dev):
         wsp = ctypes.c_void_p(ws.data_ptr() if ws is not None else 0)
@@ -377,7 +390,7 @@ def muon_step_selected(params, grads, momenta, fraction: float, beta: float = 0.
     cols = (ctypes.c_int64 * n)(*[int(p.shape[1]) for p in params])
     need = ctypes.c_size_t(0)
     _check(L.muon_step_selected_workspace_size(rows, cols, n, float(fraction), ctypes.byref(need)))
-    ws, ws_bytes = _workspace(int(need.value), dev, workspace)
+    ws, ws_bytes = _workspace(int(need.value), dev, workspace, stream)
     with torch.cuda.device(dev):
         wsp = ctypes.c_void_p(ws.data_ptr() if ws is not None else 0)
         _check(L.muon_step_selected(P, G, M, rows, cols, n, _dtype_code(pdt), float(beta), float(lr),

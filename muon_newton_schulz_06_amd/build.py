@@ -12,6 +12,7 @@ import shutil
 import subprocess
 import sys
 import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
@@ -37,8 +38,7 @@ def flags():
 def build(verbose: bool = False) -> str:
     cc = hipcc()
     with tempfile.TemporaryDirectory(prefix="muon_build_") as tmp:
-        objs = []
-        for src in SOURCES:
+        def compile_one(src):
             obj = os.path.join(tmp, src + ".o")
             cmd = [cc, *flags(), "-c", os.path.join(CSRC, src), "-o", obj]
             if verbose:
@@ -46,7 +46,10 @@ def build(verbose: bool = False) -> str:
             r = subprocess.run(cmd, capture_output=True, text=True)
             if r.returncode != 0:
                 raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
-            objs.append(obj)
+            return obj
+        # one compiler process per source, at most four at once
+        with ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
+            objs = list(ex.map(compile_one, SOURCES))
         out_tmp = LIB + ".tmp"
         cmd = [cc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", out_tmp, *objs]
         r = subprocess.run(cmd, capture_output=True, text=True)

@@ -15,8 +15,17 @@ import muon_newton_schulz_06_amd as mns
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "muon_ns.h")
 
-pytestmark = pytest.mark.skipif(not os.path.exists(mns.lib_path()),
-                                reason="libmuon_ns.so not built (run __graft_entry__.build())")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def built_library():
+    """These tests need the library itself: it is built here (hipcc
+    cross-compiles for gfx950 without a GPU) when absent, and a failed build
+    fails the tests instead of skipping them."""
+    if not os.path.exists(mns.lib_path()):
+        from muon_newton_schulz_06_amd import build
+        build.build()
+    assert os.path.exists(mns.lib_path())
 
 
 def header_functions():

@@ -17,6 +17,7 @@ import torch
 
 import oracle
 import workloads as W
+from checks import weights_consistent
 
 pytestmark = pytest.mark.gpu
 
@@ -49,27 +50,6 @@ def rel(gpu, ref):
 def oracle_ns(x_cpu, steps=5, coeffs=oracle.QUINTIC, eps=1e-7):
     c32 = tuple(float(np.float32(v)) for v in coeffs)  # what the library receives
     return oracle.muon_orthogonalize(x_cpu.to(torch.float64).numpy(), c32, steps, eps)
-
-
-def weights_consistent(W0, got, O, lrsc, band=0.1, decay=1.0):
-    """Every updated bf16 weight must be the round-to-nearest-even of
-    W0 − lrsc·Õ for some Õ within ±band·rms(O) of the oracle's update O
-    (elementwise; 5× the per-element rms that the 2e-2 Frobenius bound
-    allows).  A plain "≤ 1 ulp" test is wrong where W0 − lrsc·O cancels
-    towards zero: there the bf16 ulp is far below the update's own error.
-    Returns (all consistent, fraction differing from round(W0 − lrsc·O),
-    the fraction an update error at the tolerance would produce)."""
-    rms = float(np.sqrt(np.mean(O * O)))
-    b = band * rms
-    lo = oracle.bf16_round(decay * W0 - lrsc * (O + b))
-    hi = oracle.bf16_round(decay * W0 - lrsc * (O - b))
-    ok = bool(np.all((got >= lo) & (got <= hi)))
-    frac = float(np.mean(got != oracle.bf16_round(decay * W0 - lrsc * O)))
-    # fraction of elements an update error at the 2e-2 bound (per-element rms
-    # 2e-2·rms(O)) would move across a bf16 rounding boundary
-    ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(got), 2.0 ** -126))) - 7)
-    expect = float(np.mean(np.minimum(1.0, 2.0 * lrsc * 2e-2 * rms / ulp)))
-    return ok, frac, expect
 
 
 # ------------------------------------------------------------------ fp32 path

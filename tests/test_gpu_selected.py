@@ -20,6 +20,7 @@ import torch
 
 import oracle
 import workloads as W
+from checks import weights_consistent
 
 pytestmark = pytest.mark.gpu
 
@@ -54,10 +55,11 @@ def unique_margin(B, k):
 
 
 def band_ok(W0, got, O, lrsc, band=0.1):
-    rms = float(np.sqrt(np.mean(O * O)))
-    lo = oracle.bf16_round(W0 - lrsc * (O + band * rms))
-    hi = oracle.bf16_round(W0 - lrsc * (O - band * rms))
-    return bool(np.all((got >= lo) & (got <= hi)))
+    """Selected weights inside the rounding band of the oracle's update, and
+    no more of them off the oracle's rounding than an update error at the
+    2e-2 bound would move."""
+    ok, frac, expect = weights_consistent(W0, got, O, lrsc, band=band)
+    return ok and frac <= expect
 
 
 def to_gpu(inp):
@@ -252,3 +254,53 @@ def test_full_set_sampled(mns):
         assert np.array_equal(Go[rest], Wo[rest]), name
         assert band_ok(Wo[S], Go[S], OS, LR * oracle.lr_shape_scale(r, c)), name
         say(f"  {name} {r}x{c}: k={k} ok")
+
+
+def _scores_in_one_byte(shape, seed):
+    """A gradient whose squared row norms along the short side are exactly
+    0.6 + 1.2·π(i)/m (π a seeded permutation): every score lies in [0.5, 2),
+    so all fp32 keys share their top byte and the top-k takes its shortcut
+    branch, while neighbouring scores stay 1.2/m apart."""
+    r, c = shape
+    g = W.gaussian(shape, seed).double()
+    m = min(r, c)
+    perm = torch.randperm(m, generator=torch.Generator().manual_seed(seed + 1)).double()
+    target = 0.6 + 1.2 * perm / m
+    if r > c:
+        g = g / g.norm(dim=0, keepdim=True) * target.sqrt()[None, :]
+    else:
+        g = g / g.norm(dim=1, keepdim=True) * target.sqrt()[:, None]
+    return g.float()
+
+
+def test_scores_sharing_the_top_byte(mns):
+    """Scores confined to [0.5, 2) (the benchmark's unscaled gradients also
+    fall in one such byte): the top-k's shortcut branch, checked like every
+    other selected step — buffer bit-exact, unselected weights unchanged,
+    selected weights within the update band."""
+    shapes = [(512, 3584), (3584, 512), (2048, 4096), (40, 700)]
+    inp = W.selected_inputs(shapes, 171)
+    inp.grads = [_scores_in_one_byte(s, 180 + j) for j, s in enumerate(shapes)]
+    inp.momenta = [torch.zeros(s, dtype=torch.float32) for s in shapes]
+    Wc = [p.float().double().numpy() for p in inp.params]
+    gc = [g.numpy() for g in inp.grads]
+    for j, (r, c) in enumerate(shapes):
+        Bo = gc[j].T if r > c else gc[j]
+        sc = np.sum(Bo.astype(np.float32) ** 2, axis=1, dtype=np.float32)
+        assert np.all((sc >= 0.5) & (sc < 2.0)), "scores must share the top byte"
+        assert unique_margin(gc[j], oracle.selected_count(min(r, c), 0.25)) > 1e-4
+    inp = to_gpu(inp)
+    say("scores sharing their top byte", shapes)
+    mns.muon_step_selected(inp.params, inp.grads, inp.momenta, fraction=0.25, beta=float(BETA), lr=LR,
+                           steps=5)
+    torch.cuda.synchronize()
+    for j, (r, c) in enumerate(shapes):
+        Wn, Mn, S, OS = oracle.muon_step_selected(Wc[j], gc[j], np.zeros((r, c), np.float32), BETA, LR,
+                                                  Q32, 5, EPS, 0.25)
+        assert np.array_equal(inp.momenta[j].cpu().numpy(), Mn), (r, c)
+        got = inp.params[j].float().double().cpu().numpy()
+        Go, Wo = (got.T, Wc[j].T) if r > c else (got, Wc[j])
+        rest = np.setdiff1d(np.arange(min(r, c)), S)
+        assert np.array_equal(Go[rest], Wo[rest]), (r, c)
+        assert band_ok(Wo[S], Go[S], OS, LR * oracle.lr_shape_scale(r, c)), (r, c)
+        say(f"  {r}x{c}: k={len(S)} ok")
