@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define MUON_NS_ABI_VERSION 3
+#define MUON_NS_ABI_VERSION 4
 
 typedef enum muon_status {
   MUON_OK = 0,
@@ -107,6 +107,32 @@ typedef struct muon_ns_desc {
 muon_status_t muon_ns_batched(const muon_ns_desc_t* desc, int32_t count, int32_t steps,
                               const float coeffs[3], muon_dtype_t dtype, float eps,
                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* Size of the static device scratch of muon_ns_batched_noalloc (64 MiB per
+ * device the library runs on, held from module load until the process
+ * ends). */
+#define MUON_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* muon_ns_batched for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments, results and errors as muon_ns_batched, with
+ * no workspace argument: the workspace is a fixed array of
+ * MUON_NOALLOC_SCRATCH_BYTES in the library's own device memory, one per
+ * device.  Neither this call nor anything it calls allocates device memory
+ * (no hipMalloc / hipFree, no allocating library routine), and it records no
+ * profiling events.
+ *   - A request whose workspace (muon_ns_workspace_size) exceeds
+ *     MUON_NOALLOC_SCRATCH_BYTES returns MUON_ERR_WORKSPACE before any HIP
+ *     call; nothing is enqueued.
+ *   - Every call on one device uses that device's single scratch array, and
+ *     the array keeps the last call's contents (no call relies on its
+ *     contents at entry).  Calls that may overlap on one device race: order
+ *     them on one stream or synchronise them.
+ *   - The first call on a device looks up that device's copy of the array
+ *     (hipGetSymbolAddress) with the device current; later calls reuse it. */
+muon_status_t muon_ns_batched_noalloc(const muon_ns_desc_t* desc, int32_t count, int32_t steps,
+                                      const float coeffs[3], muon_dtype_t dtype, float eps,
+                                      void* stream);
 
 /* Workspace bytes muon_ns_batched needs for this list of matrices (only the
  * rows/cols of desc are read; pointers may be NULL).  Host only. */

@@ -24,7 +24,7 @@ __all__ = [
     "QUINTIC", "CUBIC", "MuonError", "lib_path", "load", "muon_ns_batched", "muon_step",
     "ns_workspace_size", "step_workspace_size", "describe_plan", "profile_enable",
     "profile_read", "abi_version", "PROFILE_KINDS", "set_tile_table", "muon_step_selected",
-    "step_selected_workspace_size",
+    "step_selected_workspace_size", "muon_ns_batched_noalloc", "NOALLOC_SCRATCH_BYTES",
 ]
 
 QUINTIC = (3.4445, -4.7750, 2.0315)
@@ -32,7 +32,8 @@ CUBIC = (1.5, -0.5, 0.0)
 
 MUON_DTYPE_F32 = 0
 MUON_DTYPE_BF16 = 1
-ABI_VERSION = 3
+ABI_VERSION = 4
+NOALLOC_SCRATCH_BYTES = 64 << 20  # MUON_NOALLOC_SCRATCH_BYTES
 
 PROFILE_KINDS = {"momentum": 0, "norm": 1, "cast": 2, "syrk": 3, "gram128": 4, "final": 5,
                  "gram256_axpy": 6, "gram256_sq": 7, "sel_accum": 8, "sel_topk": 9,
@@ -96,6 +97,9 @@ def load():
         L.muon_ns_batched.argtypes = [ctypes.POINTER(MuonNsDesc), i32, i32, ctypes.POINTER(f32),
                                       i32, f32, vp, sz, vp]
         L.muon_ns_batched.restype = i32
+        L.muon_ns_batched_noalloc.argtypes = [ctypes.POINTER(MuonNsDesc), i32, i32,
+                                              ctypes.POINTER(f32), i32, f32, vp]
+        L.muon_ns_batched_noalloc.restype = i32
         L.muon_ns_workspace_size.argtypes = [ctypes.POINTER(MuonNsDesc), i32, i32,
                                              ctypes.POINTER(sz)]
         L.muon_ns_workspace_size.restype = i32
@@ -297,6 +301,34 @@ def muon_ns_batched(xs, outs=None, steps: int = 5, coeffs=QUINTIC, eps: float = 
         _check(L.muon_ns_batched(arr, len(xs), int(steps), _coeffs(coeffs), code, float(eps),
                                  ctypes.c_void_p(ws.data_ptr() if ws is not None else 0),
                                  ws_bytes, _stream_handle(stream, dev)))
+    return outs
+
+
+def muon_ns_batched_noalloc(xs, outs, steps: int = 5, coeffs=QUINTIC, eps: float = 1e-7,
+                            stream=None):
+    """muon_ns_batched through the entry point that allocates nothing: the
+    library's static per-device scratch serves as workspace, and the caller
+    supplies the outputs (nothing is allocated here either).  Calls that may
+    overlap on one device race for that scratch."""
+    L = load()
+    xs, outs = list(xs), list(outs)
+    if len(outs) != len(xs):
+        raise ValueError("xs and outs differ in length")
+    if not xs:
+        return outs
+    dev = xs[0].device
+    dt = xs[0].dtype
+    for x, o in zip(xs, outs):
+        if x.device != dev or o.device != dev or dev.type != "cuda":
+            raise ValueError("all tensors must be on one CUDA/HIP device")
+        if x.dtype != dt or o.dtype != dt:
+            raise TypeError("all tensors must share one dtype")
+        if tuple(x.shape) != tuple(o.shape):
+            raise ValueError("out shape differs from x shape")
+    arr = _ns_descs(xs, outs)
+    with torch.cuda.device(dev):
+        _check(L.muon_ns_batched_noalloc(arr, len(xs), int(steps), _coeffs(coeffs), _dtype_code(dt),
+                                         float(eps), _stream_handle(stream, dev)))
     return outs
 
 

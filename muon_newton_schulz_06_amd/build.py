@@ -17,7 +17,7 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmuon_ns.so")
-SOURCES = ["gemm.hip", "elementwise.hip", "select.hip", "plan.cpp", "api.cpp"]
+SOURCES = ["gemm.hip", "elementwise.hip", "select.hip", "noalloc.hip", "plan.cpp", "api.cpp"]
 
 
 def hipcc() -> str:

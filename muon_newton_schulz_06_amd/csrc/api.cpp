@@ -39,6 +39,9 @@ namespace muon {
 namespace {
 
 thread_local std::string g_err;
+// Set by entry points that must not create HIP objects: no event pairs are
+// recorded for their launches even while profiling is enabled.
+thread_local bool g_no_events = false;
 
 muon_status_t fail(muon_status_t st, const std::string& msg) {
   g_err = msg;
@@ -74,7 +77,7 @@ struct Launcher {
   template <typename F>
   muon_status_t run(int kind, double work, const char* what, F&& f) {
     hipEvent_t e0 = nullptr, e1 = nullptr;
-    const bool prof = g_prof_on.load();
+    const bool prof = g_prof_on.load() && !g_no_events;
     if (prof) {
       std::lock_guard<std::mutex> lk(g_prof_mu);
       e0 = take_event();
@@ -765,6 +768,10 @@ muon_status_t enqueue_selected(const SelLayout& Lo, void* const* params, const f
 }
 
 }  // namespace
+
+void set_last_error(const std::string& msg) { g_err = msg; }
+void set_no_events(bool on) { g_no_events = on; }
+
 }  // namespace muon
 
 using namespace muon;

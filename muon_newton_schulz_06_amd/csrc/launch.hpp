@@ -3,6 +3,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <string>
+
 #include "common.hpp"
 
 namespace muon {
@@ -22,5 +24,11 @@ hipError_t launch_sel_accum(const SelLaunch& L, int64_t blocks, hipStream_t st);
 hipError_t launch_sel_topk(const SelLaunch& L, hipStream_t st);
 hipError_t launch_sel_gather(const SelLaunch& L, int64_t blocks, hipStream_t st);
 hipError_t launch_sel_scatter(const SelLaunch& L, int64_t blocks, hipStream_t st);
+
+// Library state shared across translation units (implemented in api.cpp):
+// the calling thread's last-error message, and whether launches made by this
+// thread record profiling events.
+void set_last_error(const std::string& msg);
+void set_no_events(bool on);
 
 }  // namespace muon

@@ -40,7 +40,7 @@ def test_exports_every_declared_symbol():
     assert "muon_ns_batched" in names and "muon_step" in names
     for n in names:
         assert hasattr(L, n), n
-    assert mns.abi_version() == 3
+    assert mns.abi_version() == 4
 
 
 def test_library_binds_hip_runtime_only_by_soname():
@@ -135,6 +135,28 @@ def test_empty_matrices_skip_pointer_checks():
     st = _ns(arr, 2)
     if not torch.cuda.is_available():
         assert st == 6, _err()
+
+
+def _noalloc(arr, n, steps=5, coeffs=C3, dtype=1, eps=1e-7):
+    return mns.load().muon_ns_batched_noalloc(arr, n, steps, coeffs, dtype, eps, None)
+
+
+def test_noalloc_rejects_before_any_device_call():
+    """The no-allocation entry point validates on the host first: a request
+    whose workspace exceeds the static scratch, and bad scalars, fail before
+    the device lookup (this test has no device)."""
+    assert _noalloc(None, 0) == 0
+    big = _desc(1, rows=2048, cols=8192)          # needs 72 MiB of workspace
+    assert _noalloc(big, 1) == 4 and "static scratch" in _err()
+    need = mns.ns_workspace_size([(2048, 8192)])
+    assert need > mns.NOALLOC_SCRATCH_BYTES
+    small = _desc(1)
+    assert _noalloc(small, 1, steps=65) == 1
+    assert _noalloc(small, 1, eps=-1.0) == 1
+    bad = (ctypes.c_float * 3)(1.0, float("nan"), 0.0)
+    assert _noalloc(small, 1, coeffs=bad) == 1
+    neg = _desc(1, rows=-1)
+    assert _noalloc(neg, 1) == 1
 
 
 def _step(n=2, rows=(4, 8), cols=(8, 4), p=None, g=None, m=None, dtype=1, beta=0.95, lr=0.02,
