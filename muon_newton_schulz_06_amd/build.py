@@ -17,7 +17,8 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmuon_ns.so")
-SOURCES = ["gemm.hip", "elementwise.hip", "select.hip", "noalloc.hip", "plan.cpp", "api.cpp"]
+SOURCES = ["gemm_axpy.hip", "gemm_sq.hip", "gemm_final.hip", "gemm_syrk.hip", "elementwise.hip",
+           "select.hip", "noalloc.hip", "plan.cpp", "api.cpp"]
 
 
 def hipcc() -> str:
@@ -47,8 +48,8 @@ def build(verbose: bool = False) -> str:
             if r.returncode != 0:
                 raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
             return obj
-        # one compiler process per source, at most four at once
-        with ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
+        # one compiler process per source, at most six at once
+        with ThreadPoolExecutor(max_workers=min(6, len(SOURCES))) as ex:
             objs = list(ex.map(compile_one, SOURCES))
         out_tmp = LIB + ".tmp"
         cmd = [cc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", out_tmp, *objs]

@@ -440,6 +440,9 @@ muon_status_t enqueue(const Plan& P, const std::vector<CallerMat>& cm, int srcDt
         S.p0 = a;
         S.p1 = b;
         S.p2 = c;
+        S.ylam = c * S.u;
+        S.ymu = b * S.sIn;
+        if (c == 0.f && tile == 256) S.K = 0;  // B = b·A: no product, a scaled copy
         S.outh = at<char>(ws, g.offBh);
         S.sOut = sc.sB[k];
         if (k == 0) {
@@ -467,6 +470,8 @@ muon_status_t enqueue(const Plan& P, const std::vector<CallerMat>& cm, int srcDt
           upper(S, tile, k + 1 == P.steps);
           S.u = 1.0f / (sc.sB[k] * sc.sQ[k]);
           S.p0 = a;
+          S.ylam = S.u;
+          S.ymu = a * S.sIn;
           S.outh = at<char>(ws, g.offQh[qcur ^ 1]);
           S.sOut = sc.sQ[k + 1];
           segs.push_back(S);
@@ -485,6 +490,8 @@ muon_status_t enqueue(const Plan& P, const std::vector<CallerMat>& cm, int srcDt
           upper(S, tile, false);
           S.u = 1.0f / (sc.sB[k] * sc.sA[k]);
           S.p0 = a;
+          S.ylam = S.u;
+          S.ymu = a * S.sIn;
           S.outh = at<char>(ws, g.offPAh);
           S.sOut = sc.sPA[k];
           segs.push_back(S);
@@ -511,6 +518,8 @@ muon_status_t enqueue(const Plan& P, const std::vector<CallerMat>& cm, int srcDt
           upper(S, tile, false);
           S.u = 1.0f / (sc.sB[k] * sc.sPA[k]);
           S.p0 = a;
+          S.ylam = S.u;
+          S.ymu = a * S.sIn;
           S.outh = at<char>(ws, g.offAh);
           S.sOut = sc.sA[k + 1];
           segs.push_back(S);

@@ -20,7 +20,7 @@ enum OpType : int32_t { OP_F16 = 0, OP_F32 = 1 };
 // its unscale factor (operands are stored multiplied by powers of two).  An
 // epilogue that needs the previous iterate Y reads it as in32[i][j] when the
 // group keeps fp32 state for the A-chain (A and P·A), else as sIn·inh[i][j]
-// from the scaled operand copy.
+// from the scaled operand copy (on the 256-tile kernel: see ylam, ymu).
 enum Epi : int32_t {
   // G = u·acc → outh = sOut·G (mirrored).
   // writeIdentity: also outhb = sOutB·I (zero steps: Q₀ = I).
@@ -78,6 +78,11 @@ struct GemmSeg {
   // dense products: 1 reads every k-tile of A (B) transposed, i.e. A[i][k]
   // from row k of the stored matrix (X₀ for the final product)
   int32_t transA, transB;
+  // 256-tile Gram-space products: the result is ylam·acc + ymu·Y (Y = inh
+  // at the output position, as stored):
+  //   EPI_AXPY: ylam = u,    ymu = p0·sIn
+  //   EPI_SQ:   ylam = p2·u, ymu = p1·sIn (with p2 = 0 the launch has K = 0)
+  float ylam, ymu;
   int32_t pad_;
 };
 

@@ -27,6 +27,12 @@
 //    mirrored operands and both layouts of X₀.
 // Both keep k-rows in LDS with a 16-byte-chunk XOR swizzle chosen for the
 // 64-bank LDS (conflict-free ds_read_b128 fragment reads).
+//
+// This header holds the kernel templates; each gemm_*.hip translation unit
+// instantiates the launches of one epilogue family (so they compile in
+// parallel), and gemm_final.hip also holds the dispatcher launch_gemm.
+#pragma once
+
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -496,41 +502,56 @@ __device__ __forceinline__ int stage_off(int row, int col) {
   return row * 512 + ((((col >> 3) ^ (row & 31))) << 4) + (col & 7) * 2;
 }
 
-// Accumulators of the 256-tile kernel: 16×16×32 MFMAs, block (fi, fj) of a
-// wave's 128×64 region; lane l, register r holds row 16·fi + 4·(l/16) + r,
-// column 16·fj + l%16 (lc = l%16, lg = l/16 below).
+// Gram-space products fetch the previous iterate's block into this staged
+// format during their last k-tiles (see issue_y): rows 0..191 into ring
+// slots 0..2 as those are released, rows 192..255 one slot beyond the ring
+// (they are fetched while slot 3 still holds the last k-tile).  kY selects
+// that placement for every staged access of the tile.
+template <bool kY>
+__device__ __forceinline__ int soff(int row, int col) {
+  return stage_off(row, col) + ((kY && row >= 192) ? kStage : 0);
+}
 
-// acc → LDS as rows of C (one 2-byte write per element).
-template <int FM, int FN>
+// Accumulators of the 256-tile kernel: 16×16×32 MFMAs, block (fi, fj) of a
+// wave's 128×64 region (lc = l%16, lg = l/16 below).
+//  * dense products (A fragments as the MFMA's first operand): lane l,
+//    register r holds row 16·fi + 4·lg + r, column 16·fj + lc;
+//  * symmetric products (operand roles swapped, B fragments first): lane l,
+//    register r holds row 16·fi + lc, column 16·fj + 4·lg + r — four
+//    consecutive columns of one row, which is what lets the previous iterate
+//    enter as the accumulators' start and off-diagonal tiles leave with one
+//    8-byte store per block.
+
+// Symmetric layout: acc → LDS as rows of C (one 8-byte write per block).
+template <bool kY, int FM, int FN>
 __device__ __forceinline__ void stage_rows(char* lds, int wm, int wn, int lc, int lg,
                                            const floatx4 (&acc)[FM][FN]) {
   static_for<0, FM>([&](auto fi) {
     static_for<0, FN>([&](auto fj) {
-      static_for<0, 4>([&](auto rc) {
-        constexpr int r = decltype(rc)::value;
-        const int il = wm * 128 + fi * 16 + 4 * lg + r;
-        const int jl = wn * 64 + fj * 16 + lc;
-        *(_Float16*)(lds + stage_off(il, jl)) = (_Float16)acc[fi][fj][r];
-      });
-    });
-  });
-}
-
-// acc → LDS as rows of Cᵀ: a lane's four consecutive rows of one column are
-// one 8-byte write.
-template <int FM, int FN>
-__device__ __forceinline__ void stage_cols(char* lds, int wm, int wn, int lc, int lg,
-                                           const floatx4 (&acc)[FM][FN]) {
-  static_for<0, FM>([&](auto fi) {
-    static_for<0, FN>([&](auto fj) {
-      const int jl = wn * 64 + fj * 16 + lc;
-      const int il = wm * 128 + fi * 16 + 4 * lg;
+      const int il = wm * 128 + fi * 16 + lc;
+      const int jl = wn * 64 + fj * 16 + 4 * lg;
       half4 v;
       v[0] = (_Float16)acc[fi][fj][0];
       v[1] = (_Float16)acc[fi][fj][1];
       v[2] = (_Float16)acc[fi][fj][2];
       v[3] = (_Float16)acc[fi][fj][3];
-      *(half4*)(lds + stage_off(jl, il)) = v;
+      *(half4*)(lds + soff<kY>(il, jl)) = v;
+    });
+  });
+}
+
+// Symmetric layout: acc → LDS as rows of Cᵀ (one 2-byte write per element).
+template <bool kY, int FM, int FN>
+__device__ __forceinline__ void stage_cols(char* lds, int wm, int wn, int lc, int lg,
+                                           const floatx4 (&acc)[FM][FN]) {
+  static_for<0, FM>([&](auto fi) {
+    static_for<0, FN>([&](auto fj) {
+      static_for<0, 4>([&](auto rc) {
+        constexpr int r = decltype(rc)::value;
+        const int il = wm * 128 + fi * 16 + lc;
+        const int jl = wn * 64 + fj * 16 + 4 * lg + r;
+        *(_Float16*)(lds + soff<kY>(jl, il)) = (_Float16)acc[fi][fj][r];
+      });
     });
   });
 }
@@ -557,14 +578,14 @@ __device__ __forceinline__ u32x4 second_value(u32x4 v, const SecondCopy& sc, int
 // Staged tile → global tile (tr, tc) of dst (and of sc.dst2 when kTwo).  On a
 // diagonal tile only the upper elements (cl ≥ rl, kUpper) or the strictly
 // lower ones (cl < rl) belong to this copy.
-template <bool kUpper, bool kTwo>
+template <bool kUpper, bool kTwo, bool kY>
 __device__ __forceinline__ void store_staged(_Float16* dst, int ldc, const char* lds, int tr,
                                              int tc, bool diag, int tid, const SecondCopy& sc) {
 #pragma unroll
   for (int it = 0; it < 16; ++it) {
     const int idx = it * 512 + tid;
     const int rl = idx >> 5, c = idx & 31;
-    const u32x4 v = *(const u32x4*)(lds + rl * 512 + ((c ^ (rl & 31)) << 4));
+    const u32x4 v = *(const u32x4*)(lds + soff<kY>(rl, c * 8));
     const int64_t off = ((int64_t)tr * 256 + rl) * ldc + (int64_t)tc * 256 + c * 8;
     _Float16* p = dst + off;
     u32x4 v2 = v;
@@ -595,22 +616,24 @@ __device__ __forceinline__ void store_staged(_Float16* dst, int ldc, const char*
 
 // Writes the symmetric result held in acc (already scaled for storage) to
 // dst: the tile (ti, tj) from its rows, the tile (tj, ti) from its columns.
-template <int FM, int FN, bool kTwo>
+// kY (Gram-space products): the rows are already in LDS, in the Y placement
+// (written there while the previous iterate was added).
+template <int FM, int FN, bool kTwo, bool kY>
 __device__ __forceinline__ void write_symmetric(_Float16* dst, int ldc, char* lds, int ti, int tj,
                                                 int wm, int wn, int lc, int lg, int tid,
                                                 const floatx4 (&acc)[FM][FN],
                                                 const SecondCopy& sc, bool mirror) {
   const bool diag = ti == tj;
-  stage_rows<FM, FN>(lds, wm, wn, lc, lg, acc);
+  if constexpr (!kY) stage_rows<kY, FM, FN>(lds, wm, wn, lc, lg, acc);
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  store_staged<true, kTwo>(dst, ldc, lds, ti, tj, diag, tid, sc);
+  store_staged<true, kTwo, kY>(dst, ldc, lds, ti, tj, diag, tid, sc);
   // Block-upper output: an off-diagonal tile alone; a diagonal tile still
   // gets its lower half from the transposed staging (exactly symmetric).
   if (!mirror && !diag) return;
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  stage_cols<FM, FN>(lds, wm, wn, lc, lg, acc);
+  stage_cols<kY, FM, FN>(lds, wm, wn, lc, lg, acc);
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  store_staged<false, kTwo>(dst, ldc, lds, tj, ti, diag, tid, sc);
+  store_staged<false, kTwo, kY>(dst, ldc, lds, tj, ti, diag, tid, sc);
   // The kernel ends here (LDS is not used again), so no closing barrier.
 }
 
@@ -796,12 +819,16 @@ __global__ __launch_bounds__(512) void gemm256_kernel(const GemmLaunch L) {
   constexpr int BM = 256, BN = 256, BK = 32, WN = 4;
   constexpr int WTM = 128, WTN = 64, FM = 8, FN = 4;  // 16×16 blocks per wave
   constexpr bool kSym = EPI == EPI_SYRK || EPI == EPI_SQ || EPI == EPI_AXPY;
-  constexpr bool kCapture = EPI == EPI_SQ || EPI == EPI_AXPY;
-  // 4-slot ring for the main loop (plus one more slot's worth for the Y
-  // tile of the symmetric epilogues); reused by the staged epilogue.
-  constexpr int kLds = kCapture ? 5 * kStage : 128 * kDensePitch;
+  // Gram-space products: block-upper operands, and the previous iterate Y
+  // (their B operand) added in the epilogue.
+  constexpr bool kGram = EPI == EPI_SQ || EPI == EPI_AXPY;
+  // 4-slot ring for the main loop, plus one slot for the last quarter of
+  // the Y block (Gram products); reused by the staged epilogues (one
+  // 256×256 fp16 tile for symmetric results, two fp32 half-tiles for dense).
+  constexpr int kLds = kGram ? 5 * kStage : kSym ? 4 * kStage : 128 * kDensePitch;
   __shared__ __attribute__((aligned(1024))) char lds[kLds];
   static_assert(128 * kDensePitch >= 4 * kStage && kLds >= 4 * kStage, "ring must fit");
+  static_assert(4 * kStage >= 256 * 512, "a staged symmetric tile must fit");
   char* const st0 = lds;
   char* const st1 = lds + kStage;
   char* const st2 = lds + 2 * kStage;
@@ -843,14 +870,14 @@ __global__ __launch_bounds__(512) void gemm256_kernel(const GemmLaunch L) {
   // or transB).  A lane's offset inside a 32-row transposed panel,
   // r·ld + column, fits 32 bits for every supported shape (ld < 2^25).
   const int KT = S.K / BK;
-  const int dA = kCapture ? (S.upperA ? ti * (BM / BK) : 0) : (TR == 1 ? KT : 0);
-  const int dB = kCapture ? (S.upperB ? tj * (BN / BK) : 0) : (TR == 2 ? KT : 0);
+  const int dA = kGram ? (S.upperA ? ti * (BM / BK) : 0) : (TR == 1 ? KT : 0);
+  const int dB = kGram ? (S.upperB ? tj * (BN / BK) : 0) : (TR == 2 ? KT : 0);
   const T* const baseAT = (const T*)S.A + mat * S.strideA + ti * BM;
   const T* const baseBT = (const T*)S.B + mat * S.strideB + tj * BN;
   // Only one leading dimension is ever read transposed in a launch (Gram
   // products have lda = ldb; the final product transposes one operand), so
   // a lane's two offsets are computed once.
-  const int ldTA = S.lda, ldTB = kCapture ? S.lda : S.ldb;
+  const int ldTA = S.lda, ldTB = kGram ? S.lda : S.ldb;
   const int ldT = TR == 2 ? ldTB : ldTA;  // the one transposed operand's (Gram: lda = ldb)
   int offT[2];
 #pragma unroll
@@ -901,6 +928,35 @@ __global__ __launch_bounds__(512) void gemm256_kernel(const GemmLaunch L) {
     for (int fj = 0; fj < FN; ++fj) asm volatile("" : "+v"(acc[fi][fj]));
   asm volatile("s_nop 7");
 
+  // The Gram products' epilogue adds the previous iterate Y (the B operand,
+  // block-upper) at the output positions: block (ti, tj) of Y, stored since
+  // ti ≤ tj.  It is fetched into LDS during the last four k-tiles, in the
+  // staged format of the output tile (row r at r·512, 16-byte chunk c at
+  // c ^ (r & 31); see soff), a quarter of 64 rows (32 KiB, four loads per
+  // wave, like a k-tile) at a time: rows 192..255 beyond the ring when
+  // k-tile KT − 1 is issued, rows 0..63, 64..127, 128..191 into ring slots
+  // 0, 1, 2 as k-tiles KT − 4, KT − 3, KT − 2 release them.  Wave w fetches
+  // rows 8w .. 8w + 7 of a quarter, two 512-byte rows per instruction; a
+  // lane fetches the logical chunk that lands at its physical position.
+  [[maybe_unused]] int offY[4];
+  [[maybe_unused]] const T* ybase = nullptr;
+  if constexpr (kGram) {
+    ybase = (const T*)S.inh + mat * S.strideInh + (int64_t)ti * BM * S.ldc + (int64_t)tj * BN;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int r = wave * 8 + 2 * p + (lane >> 5);
+      offY[p] = r * S.ldc + (((lane & 31) ^ (r & 31)) << 3);
+    }
+  }
+  auto issue_y = [&](int q) __attribute__((always_inline)) {
+    char* dst = q == 3 ? lds + 4 * kStage : lds + q * kStage;
+    const uint32_t sbase = __builtin_amdgcn_readfirstlane(lds_addr(dst));
+    const T* b = ybase + (int64_t)(64 * q) * S.ldc;
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+      dma16(b + offY[p], __builtin_amdgcn_readfirstlane(sbase + (wave * 8 + 2 * p) * 512));
+  };
+
   // Operand fragments of a 16×16×32 MFMA: lane l holds row row0 + l%16 at
   // k = 8·(l/16) .. +7 of the k-tile, i.e. 16-byte chunk l/16 of the row
   // (row0 is a multiple of 16, so the swizzle depends on l%16 only).  A
@@ -941,37 +997,22 @@ __global__ __launch_bounds__(512) void gemm256_kernel(const GemmLaunch L) {
       fb[fj] = decltype(tbc)::value ? frag_t(st + kStageA, row0) : frag_n(st + kStageA, row0);
     }
   };
+  // Symmetric products swap the operand roles (B fragments first), which
+  // transposes the accumulator layout (see stage_rows).
   auto mma = [&acc](const half8 (&fa)[2], const half8 (&fb)[FN], auto qc) __attribute__((always_inline)) {
     constexpr int q = decltype(qc)::value;
 #pragma unroll
     for (int f = 0; f < 2; ++f)
 #pragma unroll
-      for (int fj = 0; fj < FN; ++fj)
-        mfma16_acc(acc[2 * q + f][fj], fa[f], fb[fj]);
+      for (int fj = 0; fj < FN; ++fj) {
+        if constexpr (kSym) mfma16_acc(acc[2 * q + f][fj], fb[fj], fa[f]);
+        else mfma16_acc(acc[2 * q + f][fj], fa[f], fb[fj]);
+      }
   };
   constexpr auto kQ0 = std::integral_constant<int, 0>{};
   constexpr auto kQ1 = std::integral_constant<int, 1>{};
   constexpr auto kQ2 = std::integral_constant<int, 2>{};
   constexpr auto kQ3 = std::integral_constant<int, 3>{};
-
-  // The epilogues of A², B·Q, B·A and B·(P·A) need the previous iterate Y
-  // (the B operand, block-upper) at the output positions: block (ti, tj) of
-  // Y, which is stored since ti ≤ tj.  It is fetched into LDS during the last
-  // four k-tiles as eight transposed-format panels of 32 rows, in pairs
-  // (32 KiB, four loads per wave, like a k-tile): pair 3 into the LDS beyond
-  // the ring when k-tile KT − 1 is issued, pairs 0, 1, 2 into the ring slots
-  // of k-tiles KT − 4, KT − 3, KT − 2 as each is released.  KT is a multiple
-  // of 8 for these products (K is m padded to the tile).
-  auto issue_y = [&](char* dst, int q) __attribute__((always_inline)) {
-    const uint32_t sbase = __builtin_amdgcn_readfirstlane(lds_addr(dst));
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const T* b = baseBT + (int64_t)(ti * BM + 64 * q + 32 * h) * ldTB;
-#pragma unroll
-      for (int p = 0; p < 2; ++p)
-        dma16(b + tr_off(p, ldTB), __builtin_amdgcn_readfirstlane(sbase + h * kStageA + dstT + p * 1024));
-    }
-  };
 
   // Weight update: the first half of the tile's bf16 weights is loaded after
   // the loads of k-tile KT − 1 are issued (in k-tile KT − 3) and lands while
@@ -1033,20 +1074,23 @@ __global__ __launch_bounds__(512) void gemm256_kernel(const GemmLaunch L) {
                   auto tbc) __attribute__((always_inline)) {
     first_half(cur, pc, tac);
     const int r = KT - 1 - k;  // k-tiles after this one
-    if (kCapture && (r == 1 || r == 2)) {
+    if (kGram && (r == 1 || r == 2)) {
+      // k-tile k + 1 has landed once at most the younger loads (k-tile
+      // KT − 1 or the first Y quarter, and one more Y quarter) are pending
       asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
     } else if (r >= 2) {
       asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
     } else if (r == 1) {
       if (pref) asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
       else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-    } else if (kCapture) {
+    } else if (kGram) {
+      // every wave is done with slot KT − 2 before Y refills it
       asm volatile("s_barrier" ::: "memory");
     }
     if (r >= 3) issue(fill, k + 3);
-    if constexpr (kCapture) {
-      if (r == 3) issue_y(lds + 4 * kStage, 3);
-      else if (r <= 2) issue_y(fill, 2 - r);
+    if constexpr (kGram) {
+      if (r == 3) issue_y(3);
+      else if (r <= 2) issue_y(2 - r);
     }
     if constexpr (EPI == EPI_UPDATE) {
       if (pref && r == 2) weight_prefetch<0>(Ew, ti, tj, tid, wpf);
@@ -1080,17 +1124,30 @@ __global__ __launch_bounds__(512) void gemm256_kernel(const GemmLaunch L) {
     }
   };
 
-  issue(st0, 0);
-  if (KT > 1) issue(st1, 1);
-  if (KT > 2) issue(st2, 2);
-  if (KT > 2) asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
-  else if (KT > 1) asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
-  else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-  if constexpr (kCapture) {
-    phase(0, dA, std::true_type{}, std::true_type{});
-    phase(dA, dB, std::false_type{}, std::true_type{});
-    phase(dB, KT, std::false_type{}, std::false_type{});
+  if constexpr (kGram) {
+    // KT is a multiple of 8 (K = m padded to the tile), or 0 for the A²
+    // launch with c = 0 (B = b·A: no product, Y is fetched below)
+    if (KT > 0) {
+      issue(st0, 0);
+      issue(st1, 1);
+      issue(st2, 2);
+      asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+      phase(0, dA, std::true_type{}, std::true_type{});
+      phase(dA, dB, std::false_type{}, std::true_type{});
+      phase(dB, KT, std::false_type{}, std::false_type{});
+    } else {
+      issue_y(0);
+      issue_y(1);
+      issue_y(2);
+      issue_y(3);
+    }
   } else {
+    issue(st0, 0);
+    if (KT > 1) issue(st1, 1);
+    if (KT > 2) issue(st2, 2);
+    if (KT > 2) asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+    else if (KT > 1) asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
     // One layout for every k-tile: KT ≥ 8, so the loop of whole groups runs
     // at least once (written so, which keeps the accumulators in place).
     constexpr auto ta = std::bool_constant<TR == 1>{};
@@ -1119,52 +1176,50 @@ __global__ __launch_bounds__(512) void gemm256_kernel(const GemmLaunch L) {
 #pragma unroll
     for (int fj = 0; fj < FN; ++fj) asm volatile("" : "+v"(acc[fi][fj]));
 
-  // Every wave is done with the ring (and the tail loads have landed) before
-  // it is read for Y or reused for staging.
-  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  half4 ycap[kCapture ? FM : 1][FN];
-  if constexpr (kCapture) {
-    // Panel c (rows 32c .. 32c+31 of the Y block) is in pair c/2: pairs 0-2
-    // in the ring slots of k-tiles KT − 4 .. KT − 2, pair 3 beyond the ring.
-    // Lane (lc, lg) takes Y at rows 16·(fi&1) + 4·lg .. +3 of panel
-    // wm·4 + fi/2, column wn·64 + fj·16 + lc: one transposed read each.
-#pragma unroll
-    for (int fi = 0; fi < FM; ++fi) {
-      const int c = wm * 4 + (fi >> 1), q = c >> 1;
-      const char* pan = (q == 3 ? lds + 4 * kStage : lds + ((KT - 4 + q) & 3) * kStage) + (c & 1) * kStageA;
-#pragma unroll
-      for (int fj = 0; fj < FN; ++fj)
-        ycap[fi][fj] = tr_read4(pan, 16 * (fi & 1) + 4 * lg, wn * WTN + fj * 16, lc);
-    }
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  }
   const EpiArgs<T> E = make_epi<T, EPI>(L, S, mat);
   if constexpr (kSym) {
-    // acc ← storage value of the result: sOut·y(i, j).
-    static_for<0, FM>([&](auto fi) {
-      static_for<0, FN>([&](auto fj) {
-        static_for<0, 4>([&](auto rc) {
-          constexpr int r = decltype(rc)::value;
-          const float a = E.u * acc[fi][fj][r];
-          float y;
-          if constexpr (EPI == EPI_SYRK) {
-            y = a;
-          } else {
-            const float prev = E.sIn * (float)ycap[fi][fj][r];
-            y = (EPI == EPI_SQ) ? E.p1 * prev + E.p2 * a : E.p0 * prev + a;
-          }
-          acc[fi][fj][r] = E.sOut * y;
+    // Every wave is done with the ring, and every load (the Y block of the
+    // Gram products included) has landed, before LDS is read or reused.
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if constexpr (kGram) {
+      // y = λ·acc + μ·Y (a·Y + u·B·Y, or b·A + c·u·A²), stored as sOut·y.
+      // A lane reads Y at its four consecutive columns of a row and writes
+      // the result back to the same LDS address: no other lane touches it,
+      // so the rows of the output tile are staged with no barrier between.
+      const float lam = E.sOut * S.ylam, mu = E.sOut * S.ymu;
+      static_for<0, FM>([&](auto fi) {
+        static_for<0, FN>([&](auto fj) {
+          char* p = lds + soff<true>(wm * WTM + fi * 16 + lc, wn * WTN + fj * 16 + 4 * lg);
+          const half4 y = *(const half4*)p;
+          half4 h;
+          static_for<0, 4>([&](auto rc) {
+            constexpr int r = decltype(rc)::value;
+            acc[fi][fj][r] = lam * acc[fi][fj][r] + mu * (float)y[r];
+            h[r] = (_Float16)acc[fi][fj][r];
+          });
+          *(half4*)p = h;
         });
       });
-    });
+    } else {
+      // acc ← storage value of the result, sOut·u·acc
+      const float scale = E.sOut * E.u;
+      static_for<0, FM>([&](auto fi) {
+        static_for<0, FN>([&](auto fj) {
+          static_for<0, 4>([&](auto rc) {
+            constexpr int r = decltype(rc)::value;
+            acc[fi][fj][r] *= scale;
+          });
+        });
+      });
+    }
     SecondCopy sc{E.outhb, E.sOutB / E.sOut, E.sOutB * E.p0, E.mReal};
     if (EPI == EPI_SQ && E.outhb) {
       // first step: Q₁ = a·I + B₀ written from the same staged B₀ values
-      write_symmetric<FM, FN, true>(E.outh, E.ldc, lds, ti, tj, wm, wn, lc, lg, tid, acc, sc,
-                                    S.mirrorOut != 0);
+      write_symmetric<FM, FN, true, kGram>(E.outh, E.ldc, lds, ti, tj, wm, wn, lc, lg, tid, acc, sc,
+                                           S.mirrorOut != 0);
     } else {
-      write_symmetric<FM, FN, false>(E.outh, E.ldc, lds, ti, tj, wm, wn, lc, lg, tid, acc, sc,
-                                     S.mirrorOut != 0);
+      write_symmetric<FM, FN, false, kGram>(E.outh, E.ldc, lds, ti, tj, wm, wn, lc, lg, tid, acc, sc,
+                                            S.mirrorOut != 0);
     }
     if constexpr (EPI == EPI_SYRK) {
       if (E.writeIdentity) {  // zero steps: Q₀ = I (rare; element by element)
@@ -1173,8 +1228,8 @@ __global__ __launch_bounds__(512) void gemm256_kernel(const GemmLaunch L) {
           static_for<0, FN>([&](auto fj) {
             static_for<0, 4>([&](auto rc) {
               constexpr int r = decltype(rc)::value;
-              const int i = gi0 + fi * 16 + 4 * lg + r;
-              const int j = gj0 + fj * 16 + lc;
+              const int i = gi0 + fi * 16 + lc;
+              const int j = gj0 + fj * 16 + 4 * lg + r;
               if (i <= j)
                 store_mirror<T>(E.outhb, E.ldc, i, j, (T)((i == j && i < E.mReal) ? E.sOutB : 0.f));
             });
@@ -1183,6 +1238,9 @@ __global__ __launch_bounds__(512) void gemm256_kernel(const GemmLaunch L) {
       }
     }
   } else {
+    // Every wave is done with the ring (and the tail loads have landed)
+    // before it is reused for staging.
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     if constexpr (EPI == EPI_UPDATE) {
       if (pref) {
         update_prefetched<FM, FN>(E, lds, ti, tj, wm, wn, lc, lg, tid, acc, wpf);
@@ -1197,8 +1255,9 @@ template <int EPI>
 hipError_t launch_epi(int op, int tile, const GemmLaunch& L, int blocks, hipStream_t st) {
   if (op == OP_F16 && tile == 256) {
     // the main loop runs whole groups of four k-tiles, phases of eight
+    // (K = 0 only for the A² launch: with c = 0, B = b·A needs no product)
     for (int k = 0; k < L.nseg; ++k)
-      if (L.seg[k].K <= 0 || L.seg[k].K % 256 != 0) return hipErrorInvalidValue;
+      if (L.seg[k].K < (EPI == EPI_SQ ? 0 : 1) || L.seg[k].K % 256 != 0) return hipErrorInvalidValue;
     if constexpr (EPI == EPI_UPDATE || EPI == EPI_OUT) {
       // one bucket per launch, so every segment shares the operand layout
       if (L.seg[0].transA)
@@ -1222,19 +1281,10 @@ hipError_t launch_epi(int op, int tile, const GemmLaunch& L, int blocks, hipStre
   return hipGetLastError();
 }
 
-hipError_t launch_gemm(int op, int tile, const GemmLaunch& L, int blocks, hipStream_t st) {
-  if (blocks <= 0) return hipSuccess;
-  const int epi = L.seg[0].epi;
-  for (int k = 1; k < L.nseg; ++k)
-    if (L.seg[k].epi != epi) return hipErrorInvalidValue;  // one epilogue per launch
-  switch (epi) {
-    case EPI_SYRK: return launch_epi<EPI_SYRK>(op, tile, L, blocks, st);
-    case EPI_SQ: return launch_epi<EPI_SQ>(op, tile, L, blocks, st);
-    case EPI_AXPY: return launch_epi<EPI_AXPY>(op, tile, L, blocks, st);
-    case EPI_UPDATE: return launch_epi<EPI_UPDATE>(op, tile, L, blocks, st);
-    case EPI_OUT: return launch_epi<EPI_OUT>(op, tile, L, blocks, st);
-    default: return hipErrorInvalidValue;
-  }
-}
+extern template hipError_t launch_epi<EPI_SYRK>(int, int, const GemmLaunch&, int, hipStream_t);
+extern template hipError_t launch_epi<EPI_SQ>(int, int, const GemmLaunch&, int, hipStream_t);
+extern template hipError_t launch_epi<EPI_AXPY>(int, int, const GemmLaunch&, int, hipStream_t);
+extern template hipError_t launch_epi<EPI_UPDATE>(int, int, const GemmLaunch&, int, hipStream_t);
+extern template hipError_t launch_epi<EPI_OUT>(int, int, const GemmLaunch&, int, hipStream_t);
 
 }  // namespace muon

@@ -383,3 +383,21 @@ def test_seeded_random_shapes(mns, dtype, seed):
         worst = max(worst, e)
         assert e <= tol, (tuple(x.shape), e)
     say("worst", worst)
+
+
+@pytest.mark.parametrize("steps", [1, 5, 12])
+def test_bf16_cubic_on_the_256_tile_path(mns, steps):
+    """Cubic coefficients (c = 0) on bf16 groups that run on 256-tiles: the
+    A² launch has nothing to multiply (B = b·A) and runs as a scaled copy of
+    A with no contraction; checked against the oracle's cubic iteration."""
+    shapes = [(600, 1500), (2300, 4700), (300, 2000)]
+    plan = mns.describe_plan(shapes, for_step=False, coeffs=mns.CUBIC, steps=steps)
+    assert all(g["tile"] == 256 and g["op"] == "f16" for g in plan["groups"])
+    xs = [W.gaussian(s, 620 + i, dtype=torch.bfloat16) for i, s in enumerate(shapes)]
+    say("bf16 cubic steps", steps, shapes)
+    outs = mns.muon_ns_batched([x.cuda() for x in xs], steps=steps, coeffs=mns.CUBIC)
+    torch.cuda.synchronize()
+    for x, o in zip(xs, outs):
+        e = rel(o.float(), oracle_ns(x.float(), steps=steps, coeffs=oracle.CUBIC))
+        say("cubic", steps, tuple(x.shape), "rel err", e)
+        assert e <= TOL_BF16
