@@ -44,19 +44,50 @@ def traffic_for(kind, workload):
     """HBM bytes per launch of the dominant kernel, from the committed
     FETCH_SIZE / WRITE_SIZE counter summary, if it was taken on the current
     kernel source (else None)."""
-    import hashlib
     path = os.path.join(ROOT, "profiles", f"{kind}_{workload}.traffic.json")
-    src = os.path.join(ROOT, "muon_newton_schulz_06_amd", "csrc", "gemm.hip")
     try:
         with open(path) as f:
             rec = json.load(f)
-        with open(src, "rb") as f:
-            sha = hashlib.sha256(f.read()).hexdigest()
+        sha = kernel_source_sha()
     except OSError:
         return None
     if rec.get("source_sha256") != sha:
         return None
     return rec.get("bytes_per_launch")
+
+
+def kernel_source_sha():
+    """sha256 over the 256-tile GEMM kernel sources (the template header and
+    its translation units), in name order."""
+    import hashlib
+    csrc = os.path.join(ROOT, "muon_newton_schulz_06_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(f for f in os.listdir(csrc) if f.startswith("gemm")):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def source_ids():
+    """git HEAD when the tree is a checkout (else None), and a sha256 over
+    every library source, the header and this script, which identifies the
+    measured code either way."""
+    import hashlib
+    import subprocess
+    try:
+        head = subprocess.run(["git", "-C", ROOT, "rev-parse", "HEAD"], capture_output=True,
+                              text=True, timeout=10).stdout.strip() or None
+    except Exception:
+        head = None
+    h = hashlib.sha256()
+    files = [os.path.join("include", f) for f in sorted(os.listdir(os.path.join(ROOT, "include")))]
+    csrc = os.path.join("muon_newton_schulz_06_amd", "csrc")
+    files += [os.path.join(csrc, f) for f in sorted(os.listdir(os.path.join(ROOT, csrc)))]
+    files += ["bench.py"]
+    for rel in files:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(rel.encode() + b"\0" + f.read())
+    return head, h.hexdigest()
 
 
 def workload_shapes(name):
@@ -76,11 +107,44 @@ def gram_flops(shapes, steps=5):
     return tot
 
 
-def cpu_baseline(budget_s=15.0):
+def parity_probe(mns, W, torch):
+    """GPU side of the parity figure of the main workload: one muon_step over
+    the matrices of layer 0 (the shapes, seeds and kernels of the benchmark;
+    each matrix's result does not depend on the batch it is in) with fp32
+    weights at zero and zero momentum, so W' = −lr·sc·O exposes the
+    orthogonalised update O itself.  Run outside the timed region."""
+    import numpy as np
+    layer = W.qwen_model_shapes(1)
+    # drawn on the CPU, as the oracle's inputs are (the device generator draws
+    # other values), then copied
+    inp = W.muon_inputs(layer, 5001, device="cpu", param_dtype=torch.float32)
+    inp.params = [torch.zeros_like(p, device="cuda") for p in inp.params]
+    inp.grads = [g.cuda() for g in inp.grads]
+    inp.momenta = [m.cuda() for m in inp.momenta]
+    mns.muon_step(inp.params, inp.grads, inp.momenta, beta=0.95, lr=0.02, steps=5)
+    torch.cuda.synchronize()
+    lr32 = float(np.float32(0.02))
+    out = []
+    for (r, c), p in zip(layer, inp.params):
+        sc = (max(1.0, r / c)) ** 0.5
+        out.append(-p.double().cpu().numpy() / (lr32 * sc))
+    del inp
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(probe=None, samples=None, budget_s=15.0):
     """The oracle as it stands, on a bounded sample of the workload: the
     matrices of layer 0 in the order k, q, down, v, o, gate, up, one full
     muon_step each (momentum, fp64 standard Newton–Schulz, update), until
-    about `budget_s` seconds of CPU work have been spent."""
+    about `budget_s` seconds of CPU work have been spent.
+
+    The same oracle runs also give the parity figures of the line: the
+    relative Frobenius error of the GPU's update O (probe, layer 0 in layer
+    order) against the oracle's for every matrix timed, and of each smaller
+    workload's sampled GPU outputs against the oracle's orthogonalisation of
+    the same inputs (samples: name → list of (input, GPU output, steps,
+    coefficients, tolerance)).  Returns (baseline, parity)."""
     import numpy as np
     import torch
 
@@ -91,24 +155,41 @@ def cpu_baseline(budget_s=15.0):
         threads = max([d.get("num_threads", 0) for d in threadpool_info()] or [os.cpu_count()])
     except Exception:
         threads = os.cpu_count()
+    c32 = tuple(float(np.float32(v)) for v in oracle.QUINTIC)  # what the library receives
     layer = W.qwen_model_shapes(1)            # q, k, v, o, gate, up, down
     order = [1, 0, 6, 2, 3, 4, 5]
     shapes = [layer[i] for i in order]
     inp = W.muon_inputs(layer, 5001, device="cpu")
     t0 = time.perf_counter()
-    done = []
+    done, errs = [], []
     for i in order:
         r, c = layer[i]
-        oracle.muon_step(inp.params[i].float().numpy(), inp.grads[i].numpy(),
-                         inp.momenta[i].numpy(), np.float32(0.95), 0.02, oracle.QUINTIC, 5, 1e-7)
+        _, _, O = oracle.muon_step(inp.params[i].float().numpy(), inp.grads[i].numpy(),
+                                   inp.momenta[i].numpy(), np.float32(0.95), 0.02, c32, 5, 1e-7)
         done.append((r, c))
+        if probe is not None:
+            errs.append(float(np.linalg.norm(probe[i] - O) / np.linalg.norm(O)))
         if time.perf_counter() - t0 > budget_s:
             break
     dt = time.perf_counter() - t0
     fl = gram_flops(done)
-    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+    base = {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"muon_step on {len(done)} of the {len(shapes)} matrices of layer 0 {done} "
                       f"(fp64 numpy, standard NS), {dt:.2f} s; algorithmic Gram flops / time"}
+    parity = {}
+    if probe is not None:
+        parity["qwen_full"] = {
+            "max_rel_err": max(errs), "tol": 2e-2, "matrices": done,
+            "how": "update O of one muon_step from zero momentum, recovered from fp32 weights "
+                   "at zero, against the oracle's O (relative Frobenius error), layer-0 matrices"}
+    for name, items in (samples or {}).items():
+        e = []
+        for x, out, steps, coeffs, tol in items:
+            ref = oracle.muon_orthogonalize(x, tuple(float(np.float32(v)) for v in coeffs), steps, 1e-7)
+            e.append(float(np.linalg.norm(out - ref) / np.linalg.norm(ref)))
+        parity[name] = {"max_rel_err": max(e), "tol": items[0][4], "matrices": len(items),
+                        "how": "muon_ns_batched outputs of sampled matrices against the oracle"}
+    return base, parity
 
 
 def other_configs(mns, W, torch):
@@ -144,7 +225,11 @@ def other_configs(mns, W, torch):
             fn()
         return timed(g.replay, reps)
 
-    out = []
+    def host(t):
+        return t.double().cpu().numpy()
+
+    out, samples = [], {}
+    Q = mns.QUINTIC
     x = W.ns_single(device="cuda")
     xo = [torch.empty_like(x)]
     wsx = torch.empty(mns.ns_workspace_size([tuple(x.shape)], dtype=torch.float32),
@@ -152,11 +237,13 @@ def other_configs(mns, W, torch):
     f1 = lambda: mns.muon_ns_batched([x], outs=xo, steps=5, workspace=wsx)  # noqa: E731
     out.append(entry("single 256x1024 fp32", timed(f1, 50), [(256, 1024)], MFMA_PEAK_F32,
                      "muon_ns_batched, fp32 MFMA, latency-bound", graph_ms(f1, 50)))
+    samples["single 256x1024 fp32"] = [(host(x), host(xo[0]), 5, Q, 1e-4)]
     xs = W.ns_uniform_batch(device="cuda")
     outs = [torch.empty_like(t) for t in xs]
     out.append(entry("uniform 32x(1024x4096) bf16",
                      timed(lambda: mns.muon_ns_batched(xs, outs=outs, steps=5), 10),
                      [tuple(t.shape) for t in xs], MFMA_PEAK_F16, "muon_ns_batched"))
+    samples["uniform 32x(1024x4096) bf16"] = [(host(xs[i]), host(outs[i]), 5, Q, 2e-2) for i in (0, 31)]
     del xs, outs
     ms_ = W.ns_small_mix(device="cuda")
     outs = [torch.empty_like(t) for t in ms_]
@@ -165,6 +252,8 @@ def other_configs(mns, W, torch):
     f3 = lambda: mns.muon_ns_batched(ms_, outs=outs, steps=5, workspace=wsm)  # noqa: E731
     out.append(entry("small mix 176 bf16", timed(f3, 20), [tuple(t.shape) for t in ms_],
                      MFMA_PEAK_F16, "muon_ns_batched", graph_ms(f3, 20)))
+    samples["small mix 176 bf16"] = [(host(ms_[i]), host(outs[i]), 5, Q, 2e-2)
+                                     for i in range(0, len(ms_), 11)]
     del ms_, outs
     shapes = W.qwen_model_shapes(1)
     inp = W.muon_inputs(shapes, 4001, device="cuda")
@@ -173,7 +262,7 @@ def other_configs(mns, W, torch):
                      shapes, MFMA_PEAK_F16, "muon_step"))
     del inp
     torch.cuda.empty_cache()
-    return out
+    return out, samples
 
 
 def selected_step(mns, torch, inp, shapes, stream, fraction, warmup=1, steps=3):
@@ -237,6 +326,9 @@ def main():
     ap.add_argument("--no-selected", action="store_true",
                     help="skip the row/column-selected step timing")
     ap.add_argument("--selected-fraction", type=float, default=0.25)
+    ap.add_argument("--overlap", action="store_true",
+                    help="muon_step's overlap option: HBM-bound passes of a later chunk under the "
+                         "products of an earlier one")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB read + 1 GiB write kernel (counter calibration)")
     args = ap.parse_args()
@@ -273,7 +365,7 @@ def main():
 
     def step():
         mns.muon_step(inp.params, inp.grads, inp.momenta, beta=0.95, lr=0.02, steps=5,
-                      workspace=ws, stream=stream)
+                      workspace=ws, stream=stream, overlap=args.overlap)
 
     for i in range(args.warmup):
         step()
@@ -326,16 +418,21 @@ def main():
     if not args.no_selected:
         print("[bench] timing the selected-row step", file=sys.stderr, flush=True)
         selected = selected_step(mns, torch, inp, shapes, stream, args.selected_fraction)
-    others = None
+    others, samples = None, None
+    del inp, ws
+    torch.cuda.empty_cache()
+    probe = None
+    if not args.no_cpu_baseline and args.workload == "qwen_full":
+        probe = parity_probe(mns, W, torch)
     if not args.no_other_configs:
-        del inp, ws
-        torch.cuda.empty_cache()
         print("[bench] timing the smaller workloads", file=sys.stderr, flush=True)
-        others = other_configs(mns, W, torch)
-    cpu = None
+        others, samples = other_configs(mns, W, torch)
+    cpu, parity = None, None
     if not args.no_cpu_baseline:
-        print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
-        cpu = cpu_baseline()
+        print("[bench] timing the CPU oracle sample (and the parity figures)", file=sys.stderr,
+              flush=True)
+        cpu, parity = cpu_baseline(probe, samples)
+    git_head, src_sha = source_ids()
     line = {
         "metric": METRIC, "value": tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
@@ -349,7 +446,8 @@ def main():
         "frac_mfma_peak": tflops / MFMA_PEAK_F16,
         "matrices_per_s": len(shapes) / (ms / 1e3),
         "elementwise_gbs": {k: breakdown[k]["gbs"] for k in ("momentum", "cast") if k in breakdown},
-        "roofline": roofline, "breakdown": breakdown, "cpu_baseline": cpu,
+        "roofline": roofline, "breakdown": breakdown, "cpu_baseline": cpu, "parity": parity,
+        "git_head": git_head, "source_sha256": src_sha,
         "selected_step": selected, "other_configs": others,
     }
     print(json.dumps(line), flush=True)

@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define MUON_NS_ABI_VERSION 4
+#define MUON_NS_ABI_VERSION 5
 
 typedef enum muon_status {
   MUON_OK = 0,
@@ -160,19 +160,49 @@ muon_status_t muon_step(void* const* params, const float* const* grads, float* c
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /* Options of muon_step_ex.  The pages define the plain step only (momentum
- * as above, no weight decay); these are the usual Muon-optimiser variants,
- * provided for use as a drop-in optimiser (DMuon summary §3: the module
- * replaces the optimiser without changing the framework):
+ * as above, no weight decay); the first three are the usual Muon-optimiser
+ * variants, provided for use as a drop-in optimiser (DMuon summary §3: the
+ * module replaces the optimiser without changing the framework); the last
+ * two choose how the work is scheduled and never change a result beyond
+ * what the grouping of matrices changes (see below).  A zero-initialised
+ * struct with grad_dtype = MUON_DTYPE_F32 is the plain step.
  *   nesterov = 1:  the matrix orthogonalised is u = g + beta·M' (M' the
  *                  updated momentum) instead of M'; the stored state is M'.
  *   weight_decay:  decoupled, W ← round((1 − lr·weight_decay)·W − lr·sc·O);
  *                  0 leaves the plain update unchanged.  Finite, ≥ 0.
  *   grad_dtype:    MUON_DTYPE_F32 or MUON_DTYPE_BF16 gradients (momentum
- *                  stays fp32; bf16 values are widened exactly). */
+ *                  stays fp32; bf16 values are widened exactly).
+ *   overlap = 1:   a call over at least 2^30 elements runs as two chunks of
+ *                  the matrix list (in order, 1/4 and 3/4 of the work) whose
+ *                  momentum / norm / cast passes run on a stream the library
+ *                  owns (one per device, default priority), each chunk's
+ *                  products waiting for its passes on `stream`, so the
+ *                  passes of the second chunk overlap the products of the
+ *                  first.  The call still orders all its work before later
+ *                  work on `stream`, and is capturable into a graph once
+ *                  the library's stream exists (while `stream` is being
+ *                  captured the library does not create it and runs on
+ *                  `stream` alone).  0 (and opts NULL): every launch on
+ *                  `stream`.  Measured on the 196-matrix Qwen2.5-7B-shaped
+ *                  step the overlap gains at most 0.4%: the products slow
+ *                  down by nearly as much as the passes they hide.
+ *   max_workspace_bytes > 0: a budget.  The matrices are split, in order,
+ *                  into consecutive chunks whose workspace fits the budget;
+ *                  the chunks run one after another on `stream`, reusing
+ *                  one region, so workspace_bytes ≥ the largest chunk's
+ *                  need suffices (≤ the budget).  A matrix that alone
+ *                  needs more returns MUON_ERR_WORKSPACE.  0: no budget.
+ * A matrix's result depends only on the configuration of its Gram group
+ * (tile, operand type, fp32 state: see muon_ns_batched), so chunking leaves
+ * it bit for bit unchanged unless the split changes that configuration (a
+ * group of one m mixing nearly square and wide matrices, or a tile table
+ * keyed by batch size). */
 typedef struct muon_step_opts {
   int32_t nesterov;          /* 0 or 1 */
   float weight_decay;
   muon_dtype_t grad_dtype;
+  int32_t overlap;           /* 0 or 1 */
+  uint64_t max_workspace_bytes;
 } muon_step_opts_t;
 
 /* muon_step with options; opts = NULL gives exactly muon_step.  grads[i]
@@ -222,7 +252,8 @@ muon_status_t muon_step_selected(void* const* params, const float* const* grads,
 muon_status_t muon_step_selected_workspace_size(const int64_t* rows, const int64_t* cols,
                                                 int32_t count, double fraction, size_t* bytes);
 
-/* Workspace bytes muon_step (and muon_step_ex) needs for these shapes.  Host only. */
+/* Workspace bytes muon_step (and muon_step_ex without a budget) needs for
+ * these shapes, with or without opts->overlap.  Host only. */
 muon_status_t muon_step_workspace_size(const int64_t* rows, const int64_t* cols, int32_t count,
                                        size_t* bytes);
 

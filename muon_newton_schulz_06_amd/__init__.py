@@ -32,7 +32,7 @@ CUBIC = (1.5, -0.5, 0.0)
 
 MUON_DTYPE_F32 = 0
 MUON_DTYPE_BF16 = 1
-ABI_VERSION = 4
+ABI_VERSION = 5
 NOALLOC_SCRATCH_BYTES = 64 << 20  # MUON_NOALLOC_SCRATCH_BYTES
 
 PROFILE_KINDS = {"momentum": 0, "norm": 1, "cast": 2, "syrk": 3, "gram128": 4, "final": 5,
@@ -68,7 +68,8 @@ class MuonTileEntry(ctypes.Structure):
 
 class MuonStepOpts(ctypes.Structure):
     _fields_ = [("nesterov", ctypes.c_int32), ("weight_decay", ctypes.c_float),
-                ("grad_dtype", ctypes.c_int32)]
+                ("grad_dtype", ctypes.c_int32), ("overlap", ctypes.c_int32),
+                ("max_workspace_bytes", ctypes.c_uint64)]
 
 
 _lib = None
@@ -334,11 +335,14 @@ def muon_ns_batched_noalloc(xs, outs, steps: int = 5, coeffs=QUINTIC, eps: float
 
 def muon_step(params, grads, momenta, beta: float = 0.95, lr: float = 0.02, steps: int = 5,
               coeffs=QUINTIC, eps: float = 1e-7, workspace=None, stream=None,
-              nesterov: bool = False, weight_decay: float = 0.0):
+              nesterov: bool = False, weight_decay: float = 0.0, overlap: bool = False,
+              max_workspace_bytes: int = 0):
     """One in-place Muon step over lists of weights (bf16 or fp32), gradients
     (fp32 or bf16, one dtype per call) and fp32 momenta (all contiguous, same
-    device).  nesterov / weight_decay select the muon_step_ex variants; with
-    their defaults and fp32 gradients the plain muon_step entry point runs."""
+    device).  nesterov / weight_decay / overlap / max_workspace_bytes select
+    the muon_step_ex options (see muon_step_opts_t); with their defaults and
+    fp32 gradients the plain muon_step entry point runs.  With a budget the
+    cached workspace is at most max_workspace_bytes."""
     L = load()
     params, grads, momenta = list(params), list(grads), list(momenta)
     n = len(params)
@@ -372,8 +376,12 @@ def muon_step(params, grads, momenta, beta: float = 0.95, lr: float = 0.02, step
     cols = (ctypes.c_int64 * n)(*[int(p.shape[1]) for p in params])
     need = ctypes.c_size_t(0)
     _check(L.muon_step_workspace_size(rows, cols, n, ctypes.byref(need)))
-    ws, ws_bytes = _workspace(int(need.value), dev, workspace, stream)
-    plain = (not nesterov) and float(weight_decay) == 0.0 and gdt == torch.float32
+    nbytes = int(need.value)
+    if max_workspace_bytes:
+        nbytes = min(nbytes, int(max_workspace_bytes))
+    ws, ws_bytes = _workspace(nbytes, dev, workspace, stream)
+    plain = ((not nesterov) and float(weight_decay) == 0.0 and gdt == torch.float32 and not overlap
+             and not max_workspace_bytes)
     with torch.cuda.device(dev):
         wsp = ctypes.c_void_p(ws.data_ptr() if ws is not None else 0)
         if plain:
@@ -381,7 +389,8 @@ def muon_step(params, grads, momenta, beta: float = 0.95, lr: float = 0.02, step
                                int(steps), _coeffs(coeffs), float(eps), wsp, ws_bytes,
                                _stream_handle(stream, dev)))
         else:
-            opts = MuonStepOpts(int(bool(nesterov)), float(weight_decay), _dtype_code(gdt))
+            opts = MuonStepOpts(int(bool(nesterov)), float(weight_decay), _dtype_code(gdt),
+                                int(bool(overlap)), int(max_workspace_bytes))
             _check(L.muon_step_ex(P, G, M, rows, cols, n, _dtype_code(pdt), float(beta),
                                   float(lr), int(steps), _coeffs(coeffs), float(eps),
                                   ctypes.byref(opts), wsp, ws_bytes, _stream_handle(stream, dev)))

@@ -183,8 +183,9 @@ T* at(void* ws, size_t off) {
   return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
 }
 
-muon_status_t enqueue(const Plan& P, const std::vector<CallerMat>& cm, int srcDtype, int dstDtype,
-                      float beta, float eps, const StepVariant& V, void* ws, hipStream_t st) {
+// Steps 1–3 (HBM-bound passes): momentum / sum of squares, α, cast.
+muon_status_t enqueue_passes(const Plan& P, const std::vector<CallerMat>& cm, int srcDtype,
+                             float beta, float eps, const StepVariant& V, void* ws, hipStream_t st) {
   Launcher Lr{st};
   const int count = (int)P.mats.size();
   std::vector<int> live;
@@ -311,6 +312,18 @@ muon_status_t enqueue(const Plan& P, const std::vector<CallerMat>& cm, int srcDt
     if (s != MUON_OK) return s;
   }
   }
+  return MUON_OK;
+}
+
+// Steps 4–6 (MFMA products): SYRK, Gram recursion, final product + update.
+muon_status_t enqueue_products(const Plan& P, const std::vector<CallerMat>& cm, int dstDtype,
+                               const StepVariant& V, void* ws, hipStream_t st) {
+  Launcher Lr{st};
+  const int count = (int)P.mats.size();
+  bool any = false;
+  for (int i = 0; i < count; ++i) any |= !P.mats[i].empty;
+  if (!any) return MUON_OK;
+  const ScalePlan& sc = P.scales;
 
   // Kernel configurations (tile, operand type) present, each launched
   // separately.
@@ -601,6 +614,222 @@ muon_status_t enqueue(const Plan& P, const std::vector<CallerMat>& cm, int srcDt
 }
 
 
+muon_status_t enqueue(const Plan& P, const std::vector<CallerMat>& cm, int srcDtype, int dstDtype,
+                      float beta, float eps, const StepVariant& V, void* ws, hipStream_t st) {
+  muon_status_t s = enqueue_passes(P, cm, srcDtype, beta, eps, V, ws, st);
+  if (s != MUON_OK) return s;
+  return enqueue_products(P, cm, dstDtype, V, ws, st);
+}
+
+// ----------------------------------------------------------------------------
+// Chunked steps.
+//
+// A step may run as consecutive chunks of the call's matrix list (in call
+// order), each with a plan of its own:
+//  * overlapped (on request, for calls of at least kOverlapMinElems
+//    elements): every chunk has its own workspace region; the chunks'
+//    HBM-bound passes run back to back on a side stream, and each chunk's
+//    products wait for its passes on the caller's stream, so the passes of
+//    the later chunk run while the products of the earlier one do (measured
+//    on the 196-matrix Qwen2.5-7B-shaped step: at most 0.4% faster than one
+//    stream — the products slow down by nearly as much as the passes they
+//    hide, the card being at its power limit — so it is not the default);
+//  * under a workspace budget: the chunks share one region and run one
+//    after another on the caller's stream.
+// A matrix's arithmetic depends only on the configuration of its Gram group
+// (tile, operand type, fp32 state), so chunking leaves each result bit for
+// bit unchanged whenever those configurations do not change with the split
+// (they can when a group mixes nearly square and wide matrices of one m, or
+// under a tile table keyed by batch size).
+
+constexpr int kMaxChunks = 2;
+constexpr int64_t kOverlapMinElems = int64_t(1) << 30;
+// Share of the algorithmic work in each overlapped chunk: the first chunk's
+// passes cannot be hidden, so it is the small one (2 chunks of 1/4 and 3/4
+// measured best among 2, 3 and 4 chunks).
+constexpr double kChunkShare[kMaxChunks] = {0.25, 0.75};
+
+struct ChunkPlan {
+  std::vector<int> idx;  // matrices of the call in this chunk
+  Plan plan;
+  size_t off = 0;        // offset of this chunk's workspace region
+};
+
+struct StepLayout {
+  std::vector<ChunkPlan> chunks;
+  size_t totalBytes = 0;
+  bool overlap = false;
+};
+
+double mat_work(int64_t r, int64_t c) {
+  const double m = (double)std::min(r, c), n = (double)std::max(r, c);
+  return 3.0 * m * m * n + 17.0 * m * m * m;
+}
+
+std::string plan_chunk(const int64_t* rows, const int64_t* cols, const std::vector<int>& idx, int steps,
+                       const float* coeffs, Plan* P) {
+  std::vector<int64_t> r, c;
+  for (int i : idx) {
+    r.push_back(rows[i]);
+    c.push_back(cols[i]);
+  }
+  return build_plan(r.data(), c.data(), (int)idx.size(), OP_F16, steps, coeffs[0], coeffs[1],
+                    coeffs[2], true, P);
+}
+
+// overlap: overlapped chunks when the call is large enough; otherwise one
+// plan (or the budget's chunks).  budget = 0: no workspace budget.
+std::string step_layout(const int64_t* rows, const int64_t* cols, int count, int steps,
+                        const float* coeffs, bool overlap, uint64_t budget, StepLayout* out) {
+  StepLayout& Lo = *out;
+  Lo = StepLayout();
+  int64_t elems = 0;
+  double work = 0;
+  for (int i = 0; i < count; ++i) {
+    elems += rows[i] * cols[i];
+    work += mat_work(rows[i], cols[i]);
+  }
+  std::vector<std::vector<int>> parts;
+  if (budget > 0) {
+    std::vector<int> cur;
+    for (int i = 0; i < count; ++i) {
+      std::vector<int> trial = cur;
+      trial.push_back(i);
+      Plan P;
+      std::string e = plan_chunk(rows, cols, trial, steps, coeffs, &P);
+      if (!e.empty()) return e;
+      if (P.totalBytes <= budget) {
+        cur.swap(trial);
+        continue;
+      }
+      if (cur.empty())
+        return "matrix " + std::to_string(i) + " alone needs " + std::to_string(P.totalBytes) +
+               " bytes of workspace, above the budget of " + std::to_string(budget);
+      parts.push_back(cur);
+      cur.assign(1, i);
+      std::string e2 = plan_chunk(rows, cols, cur, steps, coeffs, &P);
+      if (!e2.empty()) return e2;
+      if (P.totalBytes > budget)
+        return "matrix " + std::to_string(i) + " alone needs " + std::to_string(P.totalBytes) +
+               " bytes of workspace, above the budget of " + std::to_string(budget);
+    }
+    if (!cur.empty()) parts.push_back(cur);
+  } else if (overlap && elems >= kOverlapMinElems && count >= kMaxChunks && work > 0) {
+    double acc = 0, edge = 0;
+    int k = 0;
+    parts.assign(1, {});
+    for (int i = 0; i < count; ++i) {
+      if (k + 1 < kMaxChunks && acc >= (edge + kChunkShare[k]) * work && !parts[k].empty()) {
+        edge += kChunkShare[k];
+        ++k;
+        parts.push_back({});
+      }
+      parts[k].push_back(i);
+      acc += mat_work(rows[i], cols[i]);
+    }
+    Lo.overlap = parts.size() > 1;
+  } else {
+    parts.assign(1, {});
+    for (int i = 0; i < count; ++i) parts[0].push_back(i);
+  }
+  size_t off = 0, most = 0;
+  for (auto& idx : parts) {
+    ChunkPlan C;
+    C.idx = idx;
+    std::string e = plan_chunk(rows, cols, idx, steps, coeffs, &C.plan);
+    if (!e.empty()) return e;
+    if (budget > 0) {
+      C.off = 0;  // chunks share one region, one after another
+      most = std::max(most, C.plan.totalBytes);
+    } else {
+      C.off = off;
+      off += (C.plan.totalBytes + 255) / 256 * 256;
+    }
+    Lo.chunks.push_back(std::move(C));
+  }
+  Lo.totalBytes = budget > 0 ? most : off;
+  return "";
+}
+
+// Side stream and events of the overlapped step, one set per device; the
+// mutex also keeps each call's event records and waits together.
+struct SideRes {
+  hipStream_t side = nullptr;
+  hipEvent_t ev[kMaxChunks + 1] = {};
+  bool ready = false;
+};
+constexpr int kMaxSideDevices = 64;
+std::mutex g_side_mu;
+SideRes g_side[kMaxSideDevices];
+
+// g_side_mu held.  False: no side stream (the call then runs on its stream alone).
+bool side_resources(hipStream_t st, SideRes** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxSideDevices) return false;
+  SideRes& R = g_side[dev];
+  if (!R.ready) {
+    // never create the stream while the caller's stream is being captured
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(st, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return false;
+    if (hipStreamCreateWithFlags(&R.side, hipStreamNonBlocking) != hipSuccess) {
+      R.side = nullptr;
+      return false;
+    }
+    for (hipEvent_t& e : R.ev) {
+      if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) {
+        for (hipEvent_t& f : R.ev)
+          if (f) hipEventDestroy(f), f = nullptr;
+        hipStreamDestroy(R.side);
+        R.side = nullptr;
+        return false;
+      }
+    }
+    R.ready = true;
+  }
+  *out = &R;
+  return true;
+}
+
+std::vector<CallerMat> subset(const std::vector<CallerMat>& cm, const std::vector<int>& idx) {
+  std::vector<CallerMat> v;
+  for (int i : idx) v.push_back(cm[i]);
+  return v;
+}
+
+muon_status_t enqueue_step(const StepLayout& Lo, const std::vector<CallerMat>& cm, int dstDtype,
+                           float beta, float eps, const StepVariant& V, void* ws, hipStream_t st) {
+  if (Lo.overlap) {
+    std::lock_guard<std::mutex> lk(g_side_mu);
+    SideRes* R = nullptr;
+    if (side_resources(st, &R)) {
+      auto hip = [](hipError_t e, const char* what) {
+        return e == hipSuccess ? MUON_OK : fail(MUON_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+      };
+      muon_status_t s = hip(hipEventRecord(R->ev[0], st), "hipEventRecord");
+      if (s == MUON_OK) s = hip(hipStreamWaitEvent(R->side, R->ev[0], 0), "hipStreamWaitEvent");
+      for (size_t c = 0; s == MUON_OK && c < Lo.chunks.size(); ++c) {
+        const ChunkPlan& C = Lo.chunks[c];
+        s = enqueue_passes(C.plan, subset(cm, C.idx), MUON_DTYPE_F32, beta, eps, V,
+                           static_cast<char*>(ws) + C.off, R->side);
+        if (s == MUON_OK) s = hip(hipEventRecord(R->ev[c + 1], R->side), "hipEventRecord");
+      }
+      for (size_t c = 0; s == MUON_OK && c < Lo.chunks.size(); ++c) {
+        const ChunkPlan& C = Lo.chunks[c];
+        s = hip(hipStreamWaitEvent(st, R->ev[c + 1], 0), "hipStreamWaitEvent");
+        if (s == MUON_OK)
+          s = enqueue_products(C.plan, subset(cm, C.idx), dstDtype, V, static_cast<char*>(ws) + C.off, st);
+      }
+      return s;
+    }
+  }
+  for (const ChunkPlan& C : Lo.chunks) {
+    muon_status_t s = enqueue(C.plan, subset(cm, C.idx), MUON_DTYPE_F32, dstDtype, beta, eps, V,
+                              static_cast<char*>(ws) + C.off, st);
+    if (s != MUON_OK) return s;
+  }
+  return MUON_OK;
+}
+
 // ----------------------------------------------------------------------------
 // Row/column-selected step (Dion3 review, §3 "Method & Key Results" and §1
 // "Key Terms & Definitions", Error Feedback): per matrix the k = ⌈ρ·m⌉
@@ -824,10 +1053,13 @@ muon_status_t muon_step_workspace_size(const int64_t* rows, const int64_t* cols,
     muon_status_t s = check_shape(i, rows[i], cols[i]);
     if (s != MUON_OK) return s;
   }
-  Plan P;
-  std::string e = build_plan(rows, cols, count, OP_F16, 5, 1.f, 0.f, 0.f, true, &P);
+  // enough for the default (one plan) and for opts->overlap (a region per chunk)
+  const float unit[3] = {1.f, 0.f, 0.f};
+  StepLayout Ld, Ls;
+  std::string e = step_layout(rows, cols, count, 5, unit, false, 0, &Ld);
+  if (e.empty()) e = step_layout(rows, cols, count, 5, unit, true, 0, &Ls);
   if (!e.empty()) return fail(MUON_ERR_INVALID_ARG, e);
-  *bytes = P.totalBytes;
+  *bytes = std::max(Ld.totalBytes, Ls.totalBytes);
   return MUON_OK;
 }
 
@@ -931,6 +1163,8 @@ muon_status_t muon_step_ex(void* const* params, const void* const* grads, float*
   if (count < 0) return fail(MUON_ERR_INVALID_ARG, "count < 0");
   StepVariant V;
   float wd = 0.f;
+  bool overlap = false;
+  uint64_t budget = 0;
   if (opts) {
     if (opts->nesterov != 0 && opts->nesterov != 1)
       return fail(MUON_ERR_INVALID_ARG, "opts->nesterov must be 0 or 1");
@@ -938,9 +1172,13 @@ muon_status_t muon_step_ex(void* const* params, const void* const* grads, float*
       return fail(MUON_ERR_INVALID_ARG, "opts->weight_decay must be finite and >= 0");
     if (opts->grad_dtype != MUON_DTYPE_F32 && opts->grad_dtype != MUON_DTYPE_BF16)
       return fail(MUON_ERR_INVALID_ARG, "unknown opts->grad_dtype");
+    if (opts->overlap != 0 && opts->overlap != 1)
+      return fail(MUON_ERR_INVALID_ARG, "opts->overlap must be 0 or 1");
     V.nesterov = opts->nesterov;
     V.gradDtype = opts->grad_dtype;
     wd = opts->weight_decay;
+    overlap = opts->overlap != 0;
+    budget = opts->max_workspace_bytes;
   }
   if (count == 0) return MUON_OK;
   if (!params || !grads || !momentum || !rows || !cols)
@@ -972,17 +1210,17 @@ muon_status_t muon_step_ex(void* const* params, const void* const* grads, float*
   if (overlaps(ranges, &oa, &ob))
     return fail(MUON_ERR_ALIAS, "tensors of matrices " + std::to_string(oa) + " and " +
                                     std::to_string(ob) + " overlap");
-  Plan P;
-  std::string e = build_plan(rows, cols, count, OP_F16, steps, coeffs[0], coeffs[1], coeffs[2], true, &P);
-  if (!e.empty()) return fail(MUON_ERR_INVALID_ARG, e);
+  StepLayout Lo;
+  std::string e = step_layout(rows, cols, count, steps, coeffs, overlap, budget, &Lo);
+  if (!e.empty()) return fail(budget > 0 ? MUON_ERR_WORKSPACE : MUON_ERR_INVALID_ARG, e);
   if (!workspace) return fail(MUON_ERR_WORKSPACE, "workspace is NULL");
   if ((uintptr_t)workspace & 255) return fail(MUON_ERR_WORKSPACE, "workspace not 256-byte aligned");
-  if (workspace_bytes < P.totalBytes)
-    return fail(MUON_ERR_WORKSPACE, "workspace too small: need " + std::to_string(P.totalBytes) +
+  if (workspace_bytes < Lo.totalBytes)
+    return fail(MUON_ERR_WORKSPACE, "workspace too small: need " + std::to_string(Lo.totalBytes) +
                                         " bytes, got " + std::to_string(workspace_bytes));
   {
     int who = 0;
-    if (workspace_overlaps(ranges, (uintptr_t)workspace, (uintptr_t)workspace + P.totalBytes, &who))
+    if (workspace_overlaps(ranges, (uintptr_t)workspace, (uintptr_t)workspace + Lo.totalBytes, &who))
       return fail(MUON_ERR_ALIAS, "workspace overlaps a tensor of matrix " + std::to_string(who));
   }
   std::vector<CallerMat> cm(count);
@@ -996,7 +1234,7 @@ muon_status_t muon_step_ex(void* const* params, const void* const* grads, float*
   }
   muon_status_t s = check_device();
   if (s != MUON_OK) return s;
-  return enqueue(P, cm, MUON_DTYPE_F32, param_dtype, beta, eps, V, workspace, (hipStream_t)stream);
+  return enqueue_step(Lo, cm, param_dtype, beta, eps, V, workspace, (hipStream_t)stream);
 }
 
 muon_status_t muon_step(void* const* params, const float* const* grads, float* const* momentum,

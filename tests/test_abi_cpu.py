@@ -40,7 +40,7 @@ def test_exports_every_declared_symbol():
     assert "muon_ns_batched" in names and "muon_step" in names
     for n in names:
         assert hasattr(L, n), n
-    assert mns.abi_version() == 4
+    assert mns.abi_version() == 5
 
 
 def test_library_binds_hip_runtime_only_by_soname():
@@ -187,11 +187,12 @@ def test_step_rejects_bad_arguments():
                                 None, 0, None) == 0
 
 
-def _step_ex(opts, n=2, rows=(4, 8), cols=(8, 4), g=None, gbytes=None, **kw):
+def _step_ex(opts, n=2, rows=(4, 8), cols=(8, 4), g=None, gbytes=None, stride=0x10000, **kw):
     vp = ctypes.c_void_p
-    P = (vp * n)(*[0x1000000 + i * 0x10000 for i in range(n)])
-    G = (vp * n)(*(g or [0x2000000 + i * 0x10000 for i in range(n)]))
-    M = (vp * n)(*[0x3000000 + i * 0x10000 for i in range(n)])
+    base = 0x1000000 if stride == 0x10000 else 0x100000000
+    P = (vp * n)(*[base + i * stride for i in range(n)])
+    G = (vp * n)(*(g or [2 * base + i * stride for i in range(n)]))
+    M = (vp * n)(*[3 * base + i * stride for i in range(n)])
     R = (ctypes.c_int64 * n)(*rows[:n])
     C = (ctypes.c_int64 * n)(*cols[:n])
     o = ctypes.byref(opts) if opts is not None else None
@@ -219,6 +220,38 @@ def test_step_ex_rejects_bad_options():
                                    ctypes.byref(O(5, 0.0, 0)), None, 0, None) == 1
     assert mns.load().muon_step_ex(None, None, None, None, None, 0, 1, 0.9, 0.1, 5, C3, 1e-7,
                                    None, None, 0, None) == 0
+
+
+def test_step_ex_scheduling_options():
+    """overlap must be 0 or 1; a workspace budget that one matrix alone
+    exceeds is a workspace error; a budget that fits needs only the largest
+    chunk's workspace (with no device the call then stops at the device
+    check, after every host check has passed)."""
+    O = mns.MuonStepOpts
+    assert _step_ex(O(0, 0.0, 0, 2, 0)) == 1 and "overlap" in _err()
+    shapes = [(256, 1024), (512, 2048), (256, 1024)]
+    rows, cols = zip(*shapes)
+    one = mns.step_workspace_size(shapes[:1])
+    both = mns.step_workspace_size(shapes[:2])
+    far = dict(n=3, rows=rows, cols=cols, stride=0x1000000, ws=0x1000000000)
+    assert _step_ex(O(0, 0.0, 0, 0, one // 2), **far) == 4 and "budget" in _err()
+    # budget = what (512, 2048) alone needs: three chunks, the largest is that one
+    big = mns.step_workspace_size(shapes[1:2])
+    st = _step_ex(O(0, 0.0, 0, 0, big), **far)
+    if not torch.cuda.is_available():
+        assert st == 6, _err()
+    assert big < both
+
+
+def test_step_workspace_query_covers_both_schedules():
+    """The query covers the single-plan layout and the overlapped layout of a
+    large call (two chunks with a region each)."""
+    import workloads as W
+    shapes = W.qwen_model_shapes(28)
+    q = mns.step_workspace_size(shapes)
+    single = mns.describe_plan(shapes, for_step=True)["workspace_bytes"]
+    assert q >= single
+    assert q <= single * 1.001 + 3 * 256
 
 
 def test_step_ex_null_options_is_the_plain_step():
