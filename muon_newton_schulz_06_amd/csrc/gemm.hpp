@@ -426,12 +426,17 @@ constexpr int kRowB = 64;                 // bytes per 32-element fp16 k-row
 constexpr int kStageA = 256 * kRowB;      // 16 KiB
 constexpr int kStage = 2 * kStageA;       // A + B tiles, 32 KiB
 
-// Chunk swizzle for 64-byte rows.  The LDS serves 64 banks × 4 B per clock,
-// 16 lanes of a ds_read_b128 at a time: the 16 consecutive rows read by those
-// lanes must land on 16 distinct 16-byte bank groups, i.e. (r & 3, swizzle)
-// must be distinct over any 16 consecutive rows (measured: ~1.7× the LDS
-// read rate of a swizzle that only separates 8 rows).
-__device__ __forceinline__ int swz4(int r) { return (r ^ (r >> 2)) & 3; }
+// Chunk swizzle for 64-byte rows: the physical 16-byte chunk of logical
+// chunk c of row r is c ^ swz4(r).  A fragment read (lane l: row r0 + l%16,
+// chunk l/16) takes 4 LDS cycles per ds_read_b128 without bank conflicts only
+// for some swizzles, which were found by measurement on gfx950 (hardware
+// counters SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE over all 256 swizzles
+// that XOR two parities of the row's low four bits into the chunk index):
+// 96 of them are conflict-free, 144 take 8 cycles (among them (r ^ r>>2) & 3,
+// which separates any 16 consecutive rows across the 64 banks and would be
+// conflict-free if the LDS served 16 consecutive lanes per cycle), 16 take
+// 16.  The chosen one flips chunk bit 1 on rows with bit 2 set.
+__device__ __forceinline__ int swz4(int r) { return (r >> 1) & 2; }
 
 typedef __attribute__((address_space(3))) char* lds_ptr_t;
 
@@ -469,14 +474,22 @@ __device__ __forceinline__ void mfma16_acc(floatx4& acc, const half8& a, const h
 // k-tiles left of its diagonal block from the transposed position: rows k of
 // the stored matrix, 256 values each.  Such a panel sits in the same 16 KiB
 // of the ring slot as 32 k-rows of 512 bytes; 16-byte chunk c of row k is
-// stored at c ^ 4·(k & 3), so the four k-rows read together by one 16-lane
-// group of a transposed read cover the 64 banks once.
+// stored at c ^ tswz(k).  A transposed fragment read touches k-rows
+// 8·g + 0..3 (or + 4..7) for the four 16-lane groups g, so the swizzle must
+// separate both the rows inside a group (k bits 0, 1) and the groups (k bits
+// 3, 4).  Measured on gfx950 (shader-clock timing of the kernel's transposed
+// reads for all 65536 XOR maps from k bits 0, 1, 3, 4 to the chunk's low
+// four bits): 4·(k & 3) alone runs 1.41× the fastest, this one 1.08×.
+__device__ __forceinline__ int tswz(int k) {
+  return (4 * (k & 3)) ^ (2 * ((k >> 3) & 1)) ^ ((k >> 4) & 1);
+}
+
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) short4_t* lds_s4_t;
 
 __device__ __forceinline__ int tpan_off(int k, int i) {
-  return k * 512 + (((i >> 3) ^ (4 * (k & 3))) << 4) + (i & 7) * 2;
+  return k * 512 + (((i >> 3) ^ tswz(k)) << 4) + (i & 7) * 2;
 }
 
 // ds_read_b64_tr_b16: within each group of 16 lanes, lane j supplies the
@@ -883,7 +896,7 @@ __global__ __launch_bounds__(512) void gemm256_kernel(const GemmLaunch L) {
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
     const int r = wave * 4 + 2 * p + (lane >> 5);
-    offT[p] = r * ldT + (((lane & 31) ^ (4 * (r & 3))) << 3);
+    offT[p] = r * ldT + (((lane & 31) ^ tswz(r)) << 3);
   }
   auto tr_off = [offT](int p, int ld) __attribute__((always_inline)) {
     (void)ld;
