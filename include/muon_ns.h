@@ -37,6 +37,10 @@
  *     message is available from muon_last_error() (per thread).
  *   - NaN / Inf in the inputs propagate to the outputs; nothing is repaired.
  *   - No C++ exception crosses this boundary.
+ *   - Debugging: with MUON_DEBUG_SYNC=1 in the environment, every launch is
+ *     followed by a synchronisation of its stream and an error check, so a
+ *     failing kernel is named in muon_last_error() (not while the stream is
+ *     being captured into a graph).  The default is fully asynchronous.
  */
 #ifndef MUON_NS_H
 #define MUON_NS_H

@@ -25,6 +25,7 @@
 #include <algorithm>
 #include <atomic>
 #include <cmath>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <string>
@@ -72,10 +73,31 @@ hipEvent_t take_event() {  // g_prof_mu held
   return e;
 }
 
+// Debugging aid: with MUON_DEBUG_SYNC=1 in the environment every launch is
+// followed by a synchronisation of its stream and an error check, so a
+// failing kernel is named by muon_last_error().  Skipped while the stream is
+// being captured into a graph (a synchronisation is not allowed there).
+bool debug_sync() {
+  const char* e = std::getenv("MUON_DEBUG_SYNC");
+  return e && e[0] == '1';
+}
+
 struct Launcher {
   hipStream_t st;
   template <typename F>
   muon_status_t run(int kind, double work, const char* what, F&& f) {
+    muon_status_t s = run_(kind, work, what, f);
+    if (s != MUON_OK || !debug_sync()) return s;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(st, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return s;
+    hipError_t e = hipStreamSynchronize(st);
+    if (e == hipSuccess) e = hipGetLastError();
+    if (e != hipSuccess)
+      return fail(MUON_ERR_HIP, std::string(what) + " (debug synchronisation): " + hipGetErrorString(e));
+    return s;
+  }
+  template <typename F>
+  muon_status_t run_(int kind, double work, const char* what, F&& f) {
     hipEvent_t e0 = nullptr, e1 = nullptr;
     const bool prof = g_prof_on.load() && !g_no_events;
     if (prof) {

@@ -264,8 +264,9 @@ std::string Plan::json() const {
       << ",\"state32\":" << (gp.state32 ? "true" : "false")
       << ",\"count\":" << gp.count << ",\"buckets\":[";
     for (size_t k = 0; k < gp.buckets.size(); ++k) o << (k ? "," : "") << gp.buckets[k];
-    o << "],\"offAh\":" << gp.offAh << ",\"offQh\":[" << gp.offQh[0] << "," << gp.offQh[1]
-      << "]}";
+    o << "],\"offAh\":" << gp.offAh << ",\"offBh\":" << gp.offBh << ",\"offPAh\":" << gp.offPAh
+      << ",\"offQh\":[" << gp.offQh[0] << "," << gp.offQh[1] << "],\"strideh\":" << gp.strideh
+      << "}";
   }
   o << "],\"buckets\":[";
   for (size_t bi = 0; bi < buckets.size(); ++bi) {
