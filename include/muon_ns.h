@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define MUON_NS_ABI_VERSION 5
+#define MUON_NS_ABI_VERSION 6
 
 typedef enum muon_status {
   MUON_OK = 0,
@@ -270,22 +270,37 @@ muon_status_t muon_describe_plan(const int64_t* rows, const int64_t* cols, int32
                                  int32_t for_step, muon_dtype_t dtype, int32_t steps,
                                  const float coeffs[3], char* buf, size_t buf_len);
 
-/* Tile table: the tile edge the planner uses for a Gram group, keyed by the
- * group's size m, operand type (0: fp16 operands, 1: fp32 operands) and
- * batch-size class floor(log2(number of matrices in the group)).  DMuon
- * summary §2.4 tunes kernel configurations per shape at start-up and keeps
- * them in a cache; `python -m muon_newton_schulz_06_amd.autotune` measures
- * such a table and installs it with this call.
- *   tile: 128 or 256 for fp16 groups, 64 or 128 for fp32 groups;
- *   m ≥ 1, 0 ≤ count_class ≤ 31, at most 4096 entries.
- * The table replaces the previous one process-wide (n = 0 clears it); groups
- * without an entry use the built-in choice.  Groups that carry fp32 A-chain
- * state always use 128.  An invalid entry leaves the table unchanged. */
+/* Tuning table: the launch configuration the planner uses for a Gram group
+ * (one m and operand type), keyed by the group's size m, its largest n, its
+ * operand type (0: fp16 operands, 1: fp32 operands) and batch-size class
+ * floor(log2(number of matrices in the group)).  DMuon summary §2.4 tunes
+ * kernel configurations per shape at start-up and keeps them in a cache;
+ * `python -m muon_newton_schulz_06_amd.autotune` measures such a table and
+ * installs it with this call.  Per entry:
+ *   m ≥ 1; n ≥ 0 (0 matches any n; an entry with the group's own n takes
+ *   precedence); 0 ≤ count_class ≤ 31;
+ *   tile:       128 or 256 for fp16 groups, 64 or 128 for fp32 groups, or 0
+ *               for the built-in choice;
+ *   xcd_window: logical tiles each XCD runs in a row (8, 16, 32 or 64), or 0
+ *               for the built-in 32;
+ *   band:       tile rows per band of the tile order (1, 2, 4 or 8), or 0
+ *               for the built-in 4.
+ * At most 4096 entries.  The table replaces the previous one process-wide
+ * (n = 0 clears it); groups without an entry use the built-in choices.
+ * Groups that carry fp32 A-chain state always use 128-tiles (the tile order
+ * still applies).  An invalid entry leaves the table unchanged.  The tile
+ * changes the summation order of the products, so results under a table
+ * keyed by batch size may differ in the last bits from one batch to another;
+ * the tile order changes nothing but the order in which tiles run. */
 typedef struct muon_tile_entry {
   int64_t m;
+  int64_t n;
   int32_t op;
   int32_t count_class;
   int32_t tile;
+  int32_t xcd_window;
+  int32_t band;
+  int32_t reserved; /* 0 */
 } muon_tile_entry_t;
 
 muon_status_t muon_set_tile_table(const muon_tile_entry_t* entries, int32_t n);

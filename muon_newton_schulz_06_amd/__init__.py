@@ -32,7 +32,7 @@ CUBIC = (1.5, -0.5, 0.0)
 
 MUON_DTYPE_F32 = 0
 MUON_DTYPE_BF16 = 1
-ABI_VERSION = 5
+ABI_VERSION = 6
 NOALLOC_SCRATCH_BYTES = 64 << 20  # MUON_NOALLOC_SCRATCH_BYTES
 
 PROFILE_KINDS = {"momentum": 0, "norm": 1, "cast": 2, "syrk": 3, "gram128": 4, "final": 5,
@@ -62,8 +62,10 @@ class MuonNsDesc(ctypes.Structure):
 
 
 class MuonTileEntry(ctypes.Structure):
-    _fields_ = [("m", ctypes.c_int64), ("op", ctypes.c_int32), ("count_class", ctypes.c_int32),
-                ("tile", ctypes.c_int32)]
+    _fields_ = [("m", ctypes.c_int64), ("n", ctypes.c_int64), ("op", ctypes.c_int32),
+                ("count_class", ctypes.c_int32), ("tile", ctypes.c_int32),
+                ("xcd_window", ctypes.c_int32), ("band", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 class MuonStepOpts(ctypes.Structure):
@@ -440,17 +442,22 @@ def muon_step_selected(params, grads, momenta, fraction: float, beta: float = 0.
 
 
 def set_tile_table(entries):
-    """Install the planner's tile table: an iterable of dicts with keys m, op
-    ("f16" or "f32"), count_class (floor(log2(matrices in the group))) and
-    tile.  An empty iterable clears it."""
+    """Install the planner's tuning table: an iterable of dicts with keys m,
+    op ("f16" or "f32"), count_class (floor(log2(matrices in the group))) and
+    optionally n (the group's largest n; 0 or absent: any), tile,
+    xcd_window and band (0 or absent: built-in).  An empty iterable clears
+    it."""
     entries = list(entries)
     arr = (MuonTileEntry * max(len(entries), 1))()
     for i, e in enumerate(entries):
         op = e["op"]
         arr[i].m = int(e["m"])
+        arr[i].n = int(e.get("n", 0))
         arr[i].op = {"f16": 0, "f32": 1}[op] if isinstance(op, str) else int(op)
         arr[i].count_class = int(e["count_class"])
-        arr[i].tile = int(e["tile"])
+        arr[i].tile = int(e.get("tile", 0))
+        arr[i].xcd_window = int(e.get("xcd_window", 0))
+        arr[i].band = int(e.get("band", 0))
     _check(load().muon_set_tile_table(arr, len(entries)))
 
 

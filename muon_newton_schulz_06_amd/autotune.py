@@ -1,15 +1,16 @@
-"""Tile autotuning with a cached configuration table.
+"""Launch-configuration autotuning with a cached table.
 
 DMuon's technical summary (gist.science, Korean), §2.4, tunes kernel
 configurations per matrix shape when training starts and keeps the winners
-in a cache.  Here the configuration with a measurable effect is the tile
-edge of a Gram group (fp16 groups: 128 or 256; fp32 groups: 64 or 128),
-keyed by the group's size m, operand type and batch-size class
+in a cache.  Here a Gram group's configuration is its tile edge (fp16
+groups: 128 or 256; fp32 groups: 64 or 128) and the order in which its tiles
+run (logical tiles per XCD run: 16, 32, 64; tile rows per band: 2, 4, 8),
+keyed by the group's size m, largest n, operand type and batch-size class
 floor(log2(matrices in the group)) — exactly what `muon_set_tile_table`
-takes.  For every group of a workload each candidate is installed, the whole
-call is timed with HIP events (median of `reps` after a warm-up), and the
-fastest candidate is kept; the other groups keep their current choice while
-one group is being tuned.
+takes.  For every group of a workload the knobs are searched one after the
+other (tile, then XCD run, then band), each candidate installed and the
+whole call timed with HIP events (median of `reps` after a warm-up); the
+other groups keep their current choice while one group is being tuned.
 
     python -m muon_newton_schulz_06_amd.autotune --out tiles.json   # Qwen2.5-7B set
     python -m muon_newton_schulz_06_amd.autotune --apply tiles.json
@@ -22,6 +23,8 @@ import math
 import sys
 
 CANDIDATES = {"f16": (128, 256), "f32": (64, 128)}
+XCD_WINDOWS = (16, 32, 64)
+BANDS = (2, 4, 8)
 
 
 def count_class(count: int) -> int:
@@ -29,12 +32,12 @@ def count_class(count: int) -> int:
 
 
 def groups_of(shapes, for_step=True, dtype=None):
-    """(m, op, count, state32) of every Gram group the planner forms."""
+    """(m, n_max, op, count, state32) of every Gram group the planner forms."""
     import torch
 
     from . import describe_plan
     p = describe_plan(shapes, for_step=for_step, dtype=dtype or torch.bfloat16)
-    return [(g["m"], g["op"], g["count"], g["state32"]) for g in p["groups"]]
+    return [(g["m"], g["n_max"], g["op"], g["count"], g["state32"]) for g in p["groups"]]
 
 
 def save(entries, path, meta=None):
@@ -52,18 +55,20 @@ def apply(path):
     set_tile_table(load_table(path))
 
 
-def tune(shapes, reps: int = 5, seed: int = 17, device="cuda", log=sys.stderr):
-    """Tune the tile of every group of a `muon_step` over `shapes` (bf16
-    weights, fp32 gradients); returns the table entries (also installed)."""
+def tune(shapes, reps: int = 5, seed: int = 17, device="cuda", log=sys.stderr, run=None):
+    """Tune every group of a `muon_step` over `shapes` (bf16 weights, fp32
+    gradients), or of the call `run` if given; returns the table entries
+    (also installed)."""
     import torch
 
     from . import muon_step, set_tile_table
-    from .schedule import _inputs
 
-    ps, gs, ms = _inputs(shapes, seed, device)
+    if run is None:
+        from .schedule import _inputs
+        ps, gs, ms = _inputs(shapes, seed, device)
 
-    def run():
-        muon_step(ps, gs, ms)
+        def run():
+            muon_step(ps, gs, ms)
 
     def timed():
         run()
@@ -79,25 +84,31 @@ def tune(shapes, reps: int = 5, seed: int = 17, device="cuda", log=sys.stderr):
             t.append(e0.elapsed_time(e1))
         return sorted(t)[len(t) // 2]
 
+    def entries_of(chosen):
+        return [dict(m=k[0], n=k[1], op=k[2], count_class=k[3], **v) for k, v in chosen.items()]
+
     chosen = {}
     set_tile_table([])
-    for m, op, count, state32 in groups_of(shapes):
-        if state32:
-            continue  # fixed to 128 by the precision policy
-        key = (m, op, count_class(count))
-        best = None
-        for tile in CANDIDATES[op]:
-            trial = dict(chosen)
-            trial[key] = tile
-            set_tile_table([{"m": k[0], "op": k[1], "count_class": k[2], "tile": v}
-                            for k, v in trial.items()])
-            ms_ = timed()
-            print(f"[autotune] m={m} {op} x{count}: tile {tile} -> {ms_:.3f} ms", file=log,
-                  flush=True)
-            if best is None or ms_ < best[1]:
-                best = (tile, ms_)
-        chosen[key] = best[0]
-    entries = [{"m": k[0], "op": k[1], "count_class": k[2], "tile": v} for k, v in chosen.items()]
+    for m, n, op, count, state32 in groups_of(shapes):
+        key = (m, n, op, count_class(count))
+        conf = {"tile": 0, "xcd_window": 0, "band": 0}
+        knobs = [("xcd_window", XCD_WINDOWS), ("band", BANDS)]
+        if not state32:  # fp32-state groups are fixed to 128-tiles by the precision policy
+            knobs.insert(0, ("tile", CANDIDATES[op]))
+        for name, values in knobs:
+            best = None
+            for v in values:
+                trial = dict(chosen)
+                trial[key] = dict(conf, **{name: v})
+                set_tile_table(entries_of(trial))
+                t = timed()
+                print(f"[autotune] m={m} n={n} {op} x{count}: {name} {v} -> {t:.3f} ms", file=log,
+                      flush=True)
+                if best is None or t < best[1]:
+                    best = (v, t)
+            conf[name] = best[0]
+        chosen[key] = conf
+    entries = entries_of(chosen)
     set_tile_table(entries)
     return entries
 
@@ -113,13 +124,13 @@ def main(argv=None):
     shapes = QWEN_LAYER * args.layers
     if args.apply:
         apply(args.apply)
-        print(json.dumps([{"m": m, "op": op, "count": c}
-                          for m, op, c, _ in groups_of(shapes)]))
+        print(json.dumps([{"m": m, "n": n, "op": op, "count": c}
+                          for m, n, op, c, _ in groups_of(shapes)]))
         return
     import torch
     entries = tune(shapes, reps=args.reps)
     meta = {"device": torch.cuda.get_device_name(0), "workload": f"{args.layers} Qwen2.5-7B layers",
-            "what": "fastest tile per (m, op, count class), whole muon_step timed"}
+            "what": "fastest tile, XCD run and band per (m, n, op, count class), whole muon_step timed"}
     if args.out:
         save(entries, args.out, meta)
     print(json.dumps({"meta": meta, "entries": entries}))

@@ -347,17 +347,25 @@ muon_status_t enqueue_products(const Plan& P, const std::vector<CallerMat>& cm, 
   if (!any) return MUON_OK;
   const ScalePlan& sc = P.scales;
 
-  // Kernel configurations (tile, operand type) present, each launched
-  // separately.
-  std::vector<std::pair<int, int>> cfgs;
+  // Kernel configurations (tile, operand type, tile order) present, each
+  // launched separately.
+  struct Cfg {
+    int tile, op, xcdShift, band;
+    bool operator==(const Cfg& o) const {
+      return tile == o.tile && op == o.op && xcdShift == o.xcdShift && band == o.band;
+    }
+    bool has(const GroupPlan& g) const { return *this == Cfg{g.tile, g.op, g.xcdShift, g.band}; }
+  };
+  std::vector<Cfg> cfgs;
   for (const GroupPlan& g : P.groups) {
-    const auto cf = std::make_pair(g.tile, g.op);
+    const Cfg cf{g.tile, g.op, g.xcdShift, g.band};
     if (std::find(cfgs.begin(), cfgs.end(), cf) == cfgs.end()) cfgs.push_back(cf);
   }
 
   // Helper: launch a list of segments (≤ kMaxSegs per launch).
-  auto launch_segs = [&](int tile, int op, std::vector<GemmSeg>& segs, std::vector<double>& works,
+  auto launch_segs = [&](const Cfg& cf, std::vector<GemmSeg>& segs, std::vector<double>& works,
                          int kind, const char* what) -> muon_status_t {
+    const int tile = cf.tile, op = cf.op;
     for (const GemmSeg& S : segs)
       if (tile == 256 && (S.in32 || S.out32))
         return fail(MUON_ERR_UNSUPPORTED, "internal: fp32 state on a 256-tile launch");
@@ -376,6 +384,8 @@ muon_status_t enqueue_products(const Plan& P, const std::vector<CallerMat>& cm, 
       }
       L.segStart[ns] = blocks;
       L.nseg = (int)ns;
+      L.xcdShift = cf.xcdShift;
+      L.band = cf.band;
       int k = kind;
       if (kind == 4 && tile == 256) k = (L.seg[0].epi == EPI_AXPY) ? 6 : 7;
       muon_status_t s = Lr.run(k, work, what, [&] { return launch_gemm(op, tile, L, blocks, st); });
@@ -419,11 +429,12 @@ muon_status_t enqueue_products(const Plan& P, const std::vector<CallerMat>& cm, 
   auto symflops = [](const GroupPlan& g) { return (double)g.count * g.m * g.m * (double)(g.m + 1); };
 
   // 4. SYRK per stored shape
-  for (const auto& [tile, op] : cfgs) {
+  for (const Cfg& cf : cfgs) {
+    const int tile = cf.tile;
     std::vector<GemmSeg> segs;
     std::vector<double> works;
     for (const GroupPlan& g : P.groups) {
-      if (g.tile != tile || g.op != op) continue;
+      if (!cf.has(g)) continue;
       for (int bi : g.buckets) {
         const BucketPlan& bp = P.buckets[bi];
         GemmSeg S = sym_seg(g, tile);
@@ -447,7 +458,7 @@ muon_status_t enqueue_products(const Plan& P, const std::vector<CallerMat>& cm, 
         works.push_back((double)bp.mats.size() * bp.m * (double)(bp.m + 1) * bp.n);
       }
     }
-    muon_status_t s = launch_segs(tile, op, segs, works, 3, "SYRK kernel");
+    muon_status_t s = launch_segs(cf, segs, works, 3, "SYRK kernel");
     if (s != MUON_OK) return s;
   }
 
@@ -457,12 +468,13 @@ muon_status_t enqueue_products(const Plan& P, const std::vector<CallerMat>& cm, 
   int qcur = 0;  // Qh buffer holding the current Q
   for (int k = 0; k < P.steps; ++k) {
     const bool hasQ = k >= 1, hasA = k <= P.steps - 2;
-    for (const auto& [tile, op] : cfgs) {
+    for (const Cfg& cf : cfgs) {
+    const int tile = cf.tile;
       // (i) A² → B (and Q₁ at k = 0)
       std::vector<GemmSeg> segs;
       std::vector<double> works;
       for (const GroupPlan& g : P.groups) {
-        if (g.tile != tile || g.op != op) continue;
+        if (!cf.has(g)) continue;
         GemmSeg S = sym_seg(g, tile);
         S.A = S.B = S.inh = at<char>(ws, g.offAh);
         S.in32 = f32(g, g.offA32);
@@ -487,13 +499,13 @@ muon_status_t enqueue_products(const Plan& P, const std::vector<CallerMat>& cm, 
         segs.push_back(S);
         works.push_back(symflops(g));
       }
-      muon_status_t s = launch_segs(tile, op, segs, works, 4, "Gram A^2 kernel");
+      muon_status_t s = launch_segs(cf, segs, works, 4, "Gram A^2 kernel");
       if (s != MUON_OK) return s;
       // (ii) Q ← a·Q + B·Q and P·A = a·A + B·A
       segs.clear();
       works.clear();
       for (const GroupPlan& g : P.groups) {
-        if (g.tile != tile || g.op != op) continue;
+        if (!cf.has(g)) continue;
         if (hasQ) {
           GemmSeg S = sym_seg(g, tile);
           S.A = at<char>(ws, g.offBh);
@@ -533,14 +545,14 @@ muon_status_t enqueue_products(const Plan& P, const std::vector<CallerMat>& cm, 
           works.push_back(symflops(g));
         }
       }
-      s = launch_segs(tile, op, segs, works, 4, "Gram Q/PA kernel");
+      s = launch_segs(cf, segs, works, 4, "Gram Q/PA kernel");
       if (s != MUON_OK) return s;
       // (iii) A ← a·PA + B·PA
       if (hasA) {
         segs.clear();
         works.clear();
         for (const GroupPlan& g : P.groups) {
-          if (g.tile != tile || g.op != op) continue;
+          if (!cf.has(g)) continue;
           GemmSeg S = sym_seg(g, tile);
           S.A = at<char>(ws, g.offBh);
           S.B = S.inh = at<char>(ws, g.offPAh);
@@ -560,7 +572,7 @@ muon_status_t enqueue_products(const Plan& P, const std::vector<CallerMat>& cm, 
           segs.push_back(S);
           works.push_back(symflops(g));
         }
-        s = launch_segs(tile, op, segs, works, 4, "Gram A-update kernel");
+        s = launch_segs(cf, segs, works, 4, "Gram A-update kernel");
         if (s != MUON_OK) return s;
       }
     }
@@ -577,6 +589,8 @@ muon_status_t enqueue_products(const Plan& P, const std::vector<CallerMat>& cm, 
       std::memset(&L, 0, sizeof(L));
       L.userDtype = dstDtype;
       L.decay = P.forStep ? V.decay : 1.f;
+      L.xcdShift = g.xcdShift;
+      L.band = g.band;
       GemmSeg& S = L.seg[0];
       const char* qh = at<char>(ws, g.offQh[qcur] + g.strideh * (bp.gramStart + c0));
       // X₀ᵀ as rows (128-tile kernel), or X₀ read through transposed panels
@@ -1347,14 +1361,22 @@ muon_status_t muon_set_tile_table(const muon_tile_entry_t* entries, int32_t n) {
   g_err.clear();
   if (n < 0 || n > 4096) return fail(MUON_ERR_INVALID_ARG, "n outside [0, 4096]");
   if (n > 0 && !entries) return fail(MUON_ERR_INVALID_ARG, "entries is NULL");
-  std::vector<std::pair<TileKey, int>> v;
+  std::vector<std::pair<TileKey, TileConf>> v;
   for (int i = 0; i < n; ++i) {
     const muon_tile_entry_t& e = entries[i];
-    const bool okTile = e.op == OP_F16 ? (e.tile == 128 || e.tile == 256)
-                                       : (e.op == OP_F32 && (e.tile == 64 || e.tile == 128));
-    if (e.m < 1 || e.count_class < 0 || e.count_class > 31 || !okTile)
+    const bool okTile = e.op == OP_F16 ? (e.tile == 0 || e.tile == 128 || e.tile == 256)
+                                       : (e.op == OP_F32 && (e.tile == 0 || e.tile == 64 || e.tile == 128));
+    int xs = 0;
+    if (e.xcd_window != 0) {
+      for (int k = 3; k <= 6; ++k)
+        if (e.xcd_window == (1 << k)) xs = k;
+    }
+    const bool okWin = e.xcd_window == 0 || xs != 0;
+    const bool okBand = e.band == 0 || e.band == 1 || e.band == 2 || e.band == 4 || e.band == 8;
+    if (e.m < 1 || e.n < 0 || e.count_class < 0 || e.count_class > 31 || !okTile || !okWin || !okBand ||
+        e.reserved != 0)
       return fail(MUON_ERR_INVALID_ARG, "tile entry " + std::to_string(i) + " is invalid");
-    v.push_back({TileKey{e.m, e.op, e.count_class}, e.tile});
+    v.push_back({TileKey{e.m, e.n, e.op, e.count_class}, TileConf{e.tile, xs, e.band}});
   }
   set_tile_table(v);
   return MUON_OK;

@@ -90,6 +90,8 @@ struct GemmLaunch {
   int32_t nseg;
   int32_t userDtype;          // muon_dtype_t of the caller matrices
   float decay;                // EPI_UPDATE: factor applied to W before the update
+  int32_t xcdShift;           // log2 of the logical tiles per XCD run (0: the default, 5)
+  int32_t band;               // tile rows per band of the tile order (0: the default, 4)
   int32_t segStart[kMaxSegs + 1];  // prefix of workgroups per segment
   GemmSeg seg[kMaxSegs];
   void* user[kMaxUser];        // caller weights (EPI_UPDATE) or outputs (EPI_OUT)

@@ -64,35 +64,39 @@ template <> struct OpInfo<_Float16> { static constexpr int BK = 64; };
 template <> struct OpInfo<float> { static constexpr int BK = 32; };
 
 // Workgroups are dispatched round-robin over the 8 XCDs, each with its own
-// L2.  Logical tiles are handed out in windows of 8 × 32: inside a window
-// XCD x runs a contiguous run of 32 logical tiles (which share operand row
+// L2.  Logical tiles are handed out in windows of 8 × C: inside a window
+// XCD x runs a contiguous run of C logical tiles (which share operand row
 // panels in its L2), and all XCDs work inside the same window (which keeps
 // the working set of the shared last-level cache small).  The tail of the
-// grid that does not fill a window keeps the identity mapping.
-__device__ __forceinline__ int xcd_window_remap(int b, int G) {
-  constexpr int X = 8, C = 32, W = X * C;
+// grid that does not fill a window keeps the identity mapping.  C = 2^cShift
+// (32 unless the launch's tuning entry says otherwise).
+__device__ __forceinline__ int xcd_window_remap(int b, int G, int cShift) {
+  constexpr int X = 8;
+  const int C = 1 << cShift, W = X * C;
   const int full = G / W;
   if (b >= full * W) return b;
   const int x = b % X, i = b / X;
-  return (i / C) * W + x * C + (i % C);
+  return (i >> cShift) * W + x * C + (i & (C - 1));
 }
 
-// Tile order inside one matrix: bands of kBand tile rows, column by column
-// inside a band, so consecutive tiles reuse the band's row panels of A and a
-// short run of B panels.  sym: upper triangle only (ti ≤ tj).
+// Tile order inside one matrix: bands of `band` tile rows (4 unless the
+// launch's tuning entry says otherwise), column by column inside a band, so
+// consecutive tiles reuse the band's row panels of A and a short run of B
+// panels.  sym: upper triangle only (ti ≤ tj).
 constexpr int kBand = 4;
+constexpr int kXcdShift = 5;
 
-__device__ __forceinline__ void decode_tile(int t, int tilesM, int tilesN, bool sym, int& ti,
-                                            int& tj) {
+__device__ __forceinline__ void decode_tile(int t, int tilesM, int tilesN, bool sym, int band,
+                                            int& ti, int& tj) {
   int r0 = 0;
   for (;;) {
-    const int h = min(kBand, tilesM - r0);
+    const int h = min(band, tilesM - r0);
     const int cnt = sym ? h * (h + 1) / 2 + h * (tilesN - r0 - h) : h * tilesN;
     if (t < cnt || r0 + h >= tilesM) break;
     t -= cnt;
     r0 += h;
   }
-  const int h = min(kBand, tilesM - r0);
+  const int h = min(band, tilesM - r0);
   if (sym) {
     int col = r0;
     for (;;) {
@@ -217,7 +221,7 @@ struct TilePos {
 };
 
 __device__ __forceinline__ TilePos locate(const GemmLaunch& L) {
-  const int lid = xcd_window_remap(blockIdx.x, gridDim.x);
+  const int lid = xcd_window_remap(blockIdx.x, gridDim.x, L.xcdShift > 0 ? L.xcdShift : kXcdShift);
   TilePos p;
   p.seg = 0;
   while (p.seg + 1 < L.nseg && lid >= L.segStart[p.seg + 1]) ++p.seg;
@@ -225,7 +229,7 @@ __device__ __forceinline__ TilePos locate(const GemmLaunch& L) {
   int t = lid - L.segStart[p.seg];
   p.mat = t / S.tilesPerMat;
   t -= p.mat * S.tilesPerMat;
-  decode_tile(t, S.tilesM, S.tilesN, S.sym != 0, p.ti, p.tj);
+  decode_tile(t, S.tilesM, S.tilesN, S.sym != 0, L.band > 0 ? L.band : kBand, p.ti, p.tj);
   return p;
 }
 

@@ -33,18 +33,15 @@ float pow2_scale(double bound) {
 }
 
 std::mutex g_table_mu;
-std::map<TileKey, int> g_table;
+std::map<TileKey, TileConf> g_table;
 
 int choose_tile(int op, int64_t m, int count) {
-  if (const int t = tile_from_table(m, op, count)) return t;
   if (op == OP_F32) {
     // fp32 products are latency-bound for small groups: 64-tiles give four
     // times the workgroups when 128-tiles would not fill the 256 CUs twice.
     const int64_t t = (m + 127) / 128;
     return double(count) * double(t * (t + 1) / 2) < 512.0 ? 64 : 128;
   }
-  int ov = tile_override();
-  if (ov) return ov;
   // The 256-tile kernel (direct-to-LDS ring, staged epilogues) is several
   // times faster per tile than the register-staged 128-tile kernel, which
   // outweighs the padding of m up to a multiple of 256 and a partly filled
@@ -66,16 +63,17 @@ int count_class(int count) {
   return c;
 }
 
-void set_tile_table(const std::vector<std::pair<TileKey, int>>& entries) {
+void set_tile_table(const std::vector<std::pair<TileKey, TileConf>>& entries) {
   std::lock_guard<std::mutex> lk(g_table_mu);
   g_table.clear();
   for (const auto& e : entries) g_table[e.first] = e.second;
 }
 
-int tile_from_table(int64_t m, int op, int count) {
+TileConf conf_from_table(int64_t m, int64_t n, int op, int count) {
   std::lock_guard<std::mutex> lk(g_table_mu);
-  auto it = g_table.find(TileKey{m, op, count_class(count)});
-  return it == g_table.end() ? 0 : it->second;
+  auto it = g_table.find(TileKey{m, n, op, count_class(count)});
+  if (it == g_table.end()) it = g_table.find(TileKey{m, 0, op, count_class(count)});
+  return it == g_table.end() ? TileConf{} : it->second;
 }
 
 int tile_override() {
@@ -191,9 +189,16 @@ std::string build_plan(const int64_t* rows, const int64_t* cols, int count, int 
     // 128-tile kernel carries that state.  Wide matrices (n > 2m) are well
     // conditioned and run state-free.
     bool nearSquare = false;
-    for (int bi : gp.buckets) nearSquare |= P.buckets[bi].n <= 2 * P.buckets[bi].m;
+    for (int bi : gp.buckets) {
+      nearSquare |= P.buckets[bi].n <= 2 * P.buckets[bi].m;
+      gp.nMax = std::max(gp.nMax, P.buckets[bi].n);
+    }
     gp.state32 = (gp.op == OP_F16) && gp.m <= kState32MaxM && nearSquare;
-    gp.tile = gp.state32 ? 128 : choose_tile(gp.op, gp.m, gp.count);
+    const TileConf tc = conf_from_table(gp.m, gp.nMax, gp.op, gp.count);
+    const int ov = gp.op == OP_F16 ? tile_override() : 0;
+    gp.tile = gp.state32 ? 128 : tc.tile ? tc.tile : ov ? ov : choose_tile(gp.op, gp.m, gp.count);
+    gp.xcdShift = tc.xcdShift;
+    gp.band = tc.band;
     gp.Mp = round_up(gp.m, gp.tile);
   }
   for (BucketPlan& bp : P.buckets) {
@@ -259,7 +264,9 @@ std::string Plan::json() const {
     << ",\"partials\":" << totalPartials << ",\"sX\":" << scales.sX << ",\"groups\":[";
   for (size_t g = 0; g < groups.size(); ++g) {
     const GroupPlan& gp = groups[g];
-    o << (g ? "," : "") << "{\"m\":" << gp.m << ",\"Mp\":" << gp.Mp << ",\"tile\":" << gp.tile
+    o << (g ? "," : "") << "{\"m\":" << gp.m << ",\"n_max\":" << gp.nMax << ",\"Mp\":" << gp.Mp
+      << ",\"tile\":" << gp.tile << ",\"xcd_window\":" << (1 << (gp.xcdShift ? gp.xcdShift : 5))
+      << ",\"band\":" << (gp.band ? gp.band : 4)
       << ",\"op\":\"" << (gp.op == OP_F32 ? "f32" : "f16") << "\""
       << ",\"state32\":" << (gp.state32 ? "true" : "false")
       << ",\"count\":" << gp.count << ",\"buckets\":[";

@@ -44,8 +44,11 @@ struct BucketPlan {
 // Matrices of one Gram size m: they share every Gram-space launch.
 struct GroupPlan {
   int64_t m = 0, Mp = 0;
+  int64_t nMax = 0;         // largest n among the group's matrices (tuning key)
   int op = 0;               // OpType of the group's MFMA operands
   int tile = 128;
+  int xcdShift = 0;         // launch tile order: log2 tiles per XCD run (0: default)
+  int band = 0;             // launch tile order: tile rows per band (0: default)
   int count = 0;
   std::vector<int> buckets;
   // Gram-space iterates, operand type, scaled, full (mirrored) matrices.
@@ -84,16 +87,25 @@ struct Plan {
 // Environment override of the tile (MUON_TILE=128|256), 0 when unset.
 int tile_override();
 
-// Tile table installed through the C ABI: (m, op, count class) → tile.
+// Tuning table installed through the C ABI: (m, n, op, count class) →
+// (tile, XCD run length, band).  n = 0 in a key matches any n; an entry for
+// the group's own n (its largest matrix's) takes precedence.
 struct TileKey {
-  int64_t m;
+  int64_t m, n;
   int op, countClass;
   bool operator<(const TileKey& o) const {
-    return m != o.m ? m < o.m : (op != o.op ? op < o.op : countClass < o.countClass);
+    if (m != o.m) return m < o.m;
+    if (n != o.n) return n < o.n;
+    return op != o.op ? op < o.op : countClass < o.countClass;
   }
 };
-void set_tile_table(const std::vector<std::pair<TileKey, int>>& entries);
-int tile_from_table(int64_t m, int op, int count);  // 0 when absent
+struct TileConf {
+  int tile = 0;      // 0: the built-in choice
+  int xcdShift = 0;  // 0: the built-in 5 (32 tiles per XCD run)
+  int band = 0;      // 0: the built-in 4
+};
+void set_tile_table(const std::vector<std::pair<TileKey, TileConf>>& entries);
+TileConf conf_from_table(int64_t m, int64_t n, int op, int count);  // zeros when absent
 int count_class(int count);
 
 // Largest Gram size m that keeps fp32 state for the A-chain on the

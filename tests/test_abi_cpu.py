@@ -40,7 +40,7 @@ def test_exports_every_declared_symbol():
     assert "muon_ns_batched" in names and "muon_step" in names
     for n in names:
         assert hasattr(L, n), n
-    assert mns.abi_version() == 5
+    assert mns.abi_version() == 6
 
 
 def test_library_binds_hip_runtime_only_by_soname():

@@ -20,19 +20,81 @@ def test_profile_and_validate_small_shapes():
     assert len(meas) == 2 and all(m > 0 for m in meas)
 
 
-def test_autotune_small_workload_installs_a_table():
+def _oracle_check(mns, xs, outs, tol):
+    import numpy as np
+
+    import oracle
+    q32 = tuple(float(np.float32(v)) for v in oracle.QUINTIC)
+    worst = 0.0
+    for x, o in zip(xs, outs):
+        ref = oracle.muon_orthogonalize(x.double().cpu().numpy(), q32, 5, 1e-7)
+        e = float(np.linalg.norm(o.double().cpu().numpy() - ref) / np.linalg.norm(ref))
+        worst = max(worst, e)
+        assert e <= tol, (tuple(x.shape), e)
+    return worst
+
+
+def test_autotune_small_workload_installs_a_table_and_keeps_parity():
+    """The tuner searches tile, XCD run and band for every group of a small
+    muon_step, installs the winners (the plan shows them), and muon_ns_batched
+    under the installed table still meets the bound against the oracle."""
     if not torch.cuda.is_available():
         pytest.fail("GPU tests need a HIP device")
     import muon_newton_schulz_06_amd as mns
+    import workloads as W
     from muon_newton_schulz_06_amd import autotune
-    shapes = [(512, 2048)] * 4 + [(100, 100)] * 2
+    shapes = [(512, 2048)] * 4 + [(100, 100)] * 2 + [(300, 1400)] * 3
     try:
         entries = autotune.tune(shapes, reps=1)
-        keys = {(e["m"], e["op"]) for e in entries}
-        assert keys == {(512, "f16"), (100, "f32")}
+        keys = {(e["m"], e["n"], e["op"]) for e in entries}
+        assert keys == {(512, 2048, "f16"), (100, 100, "f32"), (300, 1400, "f16")}
         p = mns.describe_plan(shapes)
         for e in entries:
             g = next(g for g in p["groups"] if g["m"] == e["m"] and g["op"] == e["op"])
-            assert g["tile"] == e["tile"]
+            assert g["tile"] == e["tile"] and g["xcd_window"] == e["xcd_window"] and g["band"] == e["band"]
+        xs = [W.gaussian(s, 8600 + i, dtype=torch.bfloat16, device="cuda") for i, s in enumerate(shapes)]
+        outs = mns.muon_ns_batched(xs, steps=5)
+        torch.cuda.synchronize()
+        _oracle_check(mns, xs, outs, 2e-2)
+    finally:
+        mns.set_tile_table([])
+
+
+@pytest.mark.parametrize("conf", [
+    {"tile": 128, "xcd_window": 16, "band": 2},
+    {"tile": 256, "xcd_window": 64, "band": 8},
+    {"tile": 256, "xcd_window": 8, "band": 1},
+])
+def test_parity_under_installed_configurations(conf):
+    """Every value the table accepts, installed for every group of a mixed
+    batch (a 256- or 128-tile fp16 group, an fp32 group, a state-carrying
+    group), gives outputs within the bound of the oracle; the tile order
+    alone changes no bit."""
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a HIP device")
+    import muon_newton_schulz_06_amd as mns
+    import workloads as W
+    shapes = [(600, 1500), (1500, 600), (700, 2000), (200, 300), (1200, 1300)]
+    xs = [W.gaussian(s, 8700 + i, dtype=torch.bfloat16, device="cuda") for i, s in enumerate(shapes)]
+    base = mns.muon_ns_batched(xs, steps=5)
+    torch.cuda.synchronize()
+    plan = mns.describe_plan(shapes, for_step=False)
+    entries = []
+    for g in plan["groups"]:
+        e = {"m": g["m"], "op": g["op"], "count_class": 0 if g["count"] == 1 else 1,
+             "xcd_window": conf["xcd_window"], "band": conf["band"]}
+        if g["op"] == "f16":
+            e["tile"] = conf["tile"]
+        entries.append(e)
+    try:
+        mns.set_tile_table(entries)
+        p = mns.describe_plan(shapes, for_step=False)
+        assert all(g["xcd_window"] == conf["xcd_window"] and g["band"] == conf["band"] for g in p["groups"])
+        outs = mns.muon_ns_batched(xs, steps=5)
+        torch.cuda.synchronize()
+        _oracle_check(mns, xs, outs, 2e-2)
+        if conf["tile"] == 256:
+            for a, b in zip(outs, base):
+                assert torch.equal(a, b)
     finally:
         mns.set_tile_table([])

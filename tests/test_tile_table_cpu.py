@@ -69,3 +69,41 @@ def test_count_class_and_table_files(tmp_path):
     assert json.loads(path.read_text())["meta"]["device"] == "x"
     autotune.apply(str(path))
     assert _tiles([(3584, 18944)] * 140)[(3584, "f16", 140)] == 256
+
+
+def _groups(shapes, for_step=True):
+    return {g["m"]: g for g in mns.describe_plan(shapes, for_step=for_step)["groups"]}
+
+
+def test_entries_keyed_by_n_take_precedence_over_any_n():
+    mns.set_tile_table([{"m": 512, "n": 3584, "op": "f16", "count_class": 2, "tile": 128, "band": 2},
+                        {"m": 512, "n": 0, "op": "f16", "count_class": 2, "tile": 256, "xcd_window": 16}])
+    g = _groups([(512, 3584)] * 4)[512]
+    assert g["n_max"] == 3584 and g["tile"] == 128 and g["band"] == 2 and g["xcd_window"] == 32
+    g = _groups([(512, 2048)] * 4)[512]
+    assert g["n_max"] == 2048 and g["tile"] == 256 and g["xcd_window"] == 16 and g["band"] == 4
+    # a group's n is its largest matrix's
+    g = _groups([(512, 2048)] * 2 + [(3584, 512)] * 2)[512]
+    assert g["n_max"] == 3584 and g["tile"] == 128
+
+
+def test_tile_order_only_entries_keep_the_built_in_tile():
+    mns.set_tile_table([{"m": 3584, "op": "f16", "count_class": 1, "xcd_window": 64, "band": 8}])
+    g = _groups([(3584, 3584)] * 2)[3584]
+    assert g["tile"] == 256 and g["xcd_window"] == 64 and g["band"] == 8
+    # state-carrying groups keep 128-tiles but take the tile order
+    mns.set_tile_table([{"m": 1500, "op": "f16", "count_class": 0, "tile": 256, "band": 1}])
+    g = _groups([(1500, 1600)])[1500]
+    assert g["state32"] and g["tile"] == 128 and g["band"] == 1
+
+
+def test_invalid_tile_order_entries_are_refused():
+    import ctypes
+    mns.set_tile_table([{"m": 512, "op": "f16", "count_class": 2, "tile": 128}])
+    for bad in ({"xcd_window": 12}, {"xcd_window": 128}, {"band": 3}, {"band": 16}, {"n": -1}):
+        with pytest.raises(mns.MuonError):
+            mns.set_tile_table([dict({"m": 512, "op": "f16", "count_class": 2}, **bad)])
+    arr = (mns.MuonTileEntry * 1)()
+    arr[0].m, arr[0].op, arr[0].count_class, arr[0].reserved = 512, 0, 2, 1
+    assert mns.load().muon_set_tile_table(arr, 1) == 1
+    assert _tiles([(512, 3584)] * 4)[(512, "f16", 4)] == 128
