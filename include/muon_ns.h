@@ -23,6 +23,19 @@
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default
  *     stream), asynchronously: results are valid once the stream reaches
  *     the enqueued work.  No entry point synchronises the host with the GPU.
+ *   - Concurrent lanes: a call whose Gram-space products have fewer than
+ *     1536 tiles of all its groups (six rounds of the 256 compute units)
+ *     and that holds at least two matrices splits its matrices into two
+ *     sets of about equal work (three when under 256 tiles in at least three
+ *     groups), each running its whole product chain on its own stream.  The extra streams are the library's (default priority,
+ *     created on the first such call on a device, never while `stream` is
+ *     being captured); they wait for an event recorded on `stream` and
+ *     `stream` waits for each of them at the end, so the call is still one
+ *     ordered piece of work on `stream` and can be captured into a graph
+ *     once they exist (before that, a captured call runs on `stream`
+ *     alone).  A matrix's arithmetic does not depend on the split, so the
+ *     results are the same bit for bit.  MUON_LANES=1..4 in the environment
+ *     fixes the number of lanes.
  *   - `workspace` is caller-allocated device memory of at least the size
  *     the matching *_workspace_size query returns, 256-byte aligned, that
  *     overlaps no tensor of the call (MUON_ERR_ALIAS otherwise).  Its
@@ -316,7 +329,8 @@ muon_status_t muon_set_tile_table(const muon_tile_entry_t* entries, int32_t n);
  *        8 selected step: B = M + g and row scores, 9 its top-k,
  *        10 its gather, 11 its scatter of the update.
  * work is algorithmic flops for kinds 3–7 and algorithmic HBM bytes for the
- * others. */
+ * others.  The launches of concurrent lanes overlap in time, so their
+ * kernel times add up to more than the call's duration. */
 muon_status_t muon_profile_enable(int32_t on);
 muon_status_t muon_profile_read(int32_t kind, double* total_ms, int64_t* launches, double* work);
 

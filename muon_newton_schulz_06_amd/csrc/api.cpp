@@ -338,14 +338,59 @@ muon_status_t enqueue_passes(const Plan& P, const std::vector<CallerMat>& cm, in
 }
 
 // Steps 4–6 (MFMA products): SYRK, Gram recursion, final product + update.
-muon_status_t enqueue_products(const Plan& P, const std::vector<CallerMat>& cm, int dstDtype,
-                               const StepVariant& V, void* ws, hipStream_t st) {
+// Relative cost of one matrix's step (SYRK, final product and the Gram
+// products of five steps, in units of m²n and m³ multiply-adds).
+double mat_work(int64_t r, int64_t c) {
+  const double m = (double)std::min(r, c), n = (double)std::max(r, c);
+  return 3.0 * m * m * n + 17.0 * m * m * m;
+}
+
+// The matrices one stream processes: pieces [b0, b1) of the plan's buckets
+// (bucket-local positions).  A lane runs the whole product chain of its
+// matrices; lanes share nothing but the plan's scales.
+struct Piece {
+  int bucket, b0, b1;
+};
+using Lane = std::vector<Piece>;
+
+muon_status_t enqueue_lane(const Plan& P, const Lane& lane, const std::vector<CallerMat>& cm,
+                           int dstDtype, const StepVariant& V, void* ws, hipStream_t st) {
   Launcher Lr{st};
-  const int count = (int)P.mats.size();
-  bool any = false;
-  for (int i = 0; i < count; ++i) any |= !P.mats[i].empty;
-  if (!any) return MUON_OK;
   const ScalePlan& sc = P.scales;
+  // the lane's matrices of each group, as merged ranges of group positions
+  std::vector<std::vector<std::pair<int, int>>> granges(P.groups.size());
+  for (const Piece& pc : lane) {
+    const BucketPlan& bp = P.buckets[pc.bucket];
+    if (pc.b1 > pc.b0) granges[bp.group].push_back({bp.gramStart + pc.b0, bp.gramStart + pc.b1});
+  }
+  for (auto& r : granges) {
+    std::sort(r.begin(), r.end());
+    std::vector<std::pair<int, int>> merged;
+    for (const auto& x : r) {
+      if (!merged.empty() && merged.back().second == x.first) merged.back().second = x.second;
+      else merged.push_back(x);
+    }
+    r.swap(merged);
+  }
+  // A Gram-space segment built at the group's base, emitted once per range
+  // of the lane (every operand and result of these products is a group array).
+  auto emit = [&](size_t gi, const GemmSeg& S0, std::vector<GemmSeg>& segs, std::vector<double>& works) {
+    const GroupPlan& g = P.groups[gi];
+    for (const auto& r : granges[gi]) {
+      GemmSeg S = S0;
+      const size_t oh = g.strideh * (size_t)r.first, o32 = g.stride32 * (size_t)r.first;
+      S.A = static_cast<const char*>(S.A) + oh;
+      S.B = static_cast<const char*>(S.B) + oh;
+      if (S.inh) S.inh = static_cast<const char*>(S.inh) + oh;
+      S.outh = static_cast<char*>(S.outh) + oh;
+      if (S.outhb) S.outhb = static_cast<char*>(S.outhb) + oh;
+      if (S.in32) S.in32 += o32 / sizeof(float);
+      if (S.out32) S.out32 += o32 / sizeof(float);
+      S.count = r.second - r.first;
+      segs.push_back(S);
+      works.push_back((double)S.count * g.m * g.m * (double)(g.m + 1));
+    }
+  };
 
   // Kernel configurations (tile, operand type, tile order) present, each
   // launched separately.
@@ -357,7 +402,9 @@ muon_status_t enqueue_products(const Plan& P, const std::vector<CallerMat>& cm, 
     bool has(const GroupPlan& g) const { return *this == Cfg{g.tile, g.op, g.xcdShift, g.band}; }
   };
   std::vector<Cfg> cfgs;
-  for (const GroupPlan& g : P.groups) {
+  for (size_t gi = 0; gi < P.groups.size(); ++gi) {
+    const GroupPlan& g = P.groups[gi];
+    if (granges[gi].empty()) continue;
     const Cfg cf{g.tile, g.op, g.xcdShift, g.band};
     if (std::find(cfgs.begin(), cfgs.end(), cf) == cfgs.end()) cfgs.push_back(cf);
   }
@@ -426,20 +473,21 @@ muon_status_t enqueue_products(const Plan& P, const std::vector<CallerMat>& cm, 
   auto f32 = [&](const GroupPlan& g, size_t off) -> float* {
     return g.state32 ? at<float>(ws, off) : nullptr;
   };
-  auto symflops = [](const GroupPlan& g) { return (double)g.count * g.m * g.m * (double)(g.m + 1); };
 
   // 4. SYRK per stored shape
   for (const Cfg& cf : cfgs) {
     const int tile = cf.tile;
     std::vector<GemmSeg> segs;
     std::vector<double> works;
-    for (const GroupPlan& g : P.groups) {
-      if (!cf.has(g)) continue;
-      for (int bi : g.buckets) {
-        const BucketPlan& bp = P.buckets[bi];
+    for (const Piece& pc : lane) {
+      const BucketPlan& bp = P.buckets[pc.bucket];
+      const GroupPlan& g = P.groups[bp.group];
+      if (!cf.has(g) || pc.b1 <= pc.b0) continue;
+      const int pos = bp.gramStart + pc.b0;  // group position of the piece's first matrix
+      {
         GemmSeg S = sym_seg(g, tile);
-        S.count = (int)bp.mats.size();
-        S.A = S.B = at<char>(ws, bp.offXh);
+        S.count = pc.b1 - pc.b0;
+        S.A = S.B = at<char>(ws, bp.offXh + bp.strideX * pc.b0);
         S.strideA = S.strideB = bp.Mp * bp.Np;
         S.lda = S.ldb = (int32_t)bp.Np;
         S.K = (int32_t)bp.Np;
@@ -447,15 +495,15 @@ muon_status_t enqueue_products(const Plan& P, const std::vector<CallerMat>& cm, 
         upper(S, tile, false);
         S.u = 1.0f / (sc.sX * sc.sX);
         S.sOut = sc.sA[0];
-        S.outh = at<char>(ws, g.offAh + g.strideh * bp.gramStart);
-        if (g.state32) S.out32 = at<float>(ws, g.offA32 + g.stride32 * bp.gramStart);
+        S.outh = at<char>(ws, g.offAh + g.strideh * pos);
+        if (g.state32) S.out32 = at<float>(ws, g.offA32 + g.stride32 * pos);
         if (P.steps == 0) {
           S.writeIdentity = 1;
-          S.outhb = at<char>(ws, g.offQh[0] + g.strideh * bp.gramStart);
+          S.outhb = at<char>(ws, g.offQh[0] + g.strideh * pos);
           S.sOutB = sc.sQ[0];
         }
         segs.push_back(S);
-        works.push_back((double)bp.mats.size() * bp.m * (double)(bp.m + 1) * bp.n);
+        works.push_back((double)S.count * bp.m * (double)(bp.m + 1) * bp.n);
       }
     }
     muon_status_t s = launch_segs(cf, segs, works, 3, "SYRK kernel");
@@ -473,8 +521,9 @@ muon_status_t enqueue_products(const Plan& P, const std::vector<CallerMat>& cm, 
       // (i) A² → B (and Q₁ at k = 0)
       std::vector<GemmSeg> segs;
       std::vector<double> works;
-      for (const GroupPlan& g : P.groups) {
-        if (!cf.has(g)) continue;
+      for (size_t gi = 0; gi < P.groups.size(); ++gi) {
+        const GroupPlan& g = P.groups[gi];
+        if (!cf.has(g) || granges[gi].empty()) continue;
         GemmSeg S = sym_seg(g, tile);
         S.A = S.B = S.inh = at<char>(ws, g.offAh);
         S.in32 = f32(g, g.offA32);
@@ -496,16 +545,16 @@ muon_status_t enqueue_products(const Plan& P, const std::vector<CallerMat>& cm, 
           S.outhb = at<char>(ws, g.offQh[0]);
           S.sOutB = sc.sQ[1];
         }
-        segs.push_back(S);
-        works.push_back(symflops(g));
+        emit(gi, S, segs, works);
       }
       muon_status_t s = launch_segs(cf, segs, works, 4, "Gram A^2 kernel");
       if (s != MUON_OK) return s;
       // (ii) Q ← a·Q + B·Q and P·A = a·A + B·A
       segs.clear();
       works.clear();
-      for (const GroupPlan& g : P.groups) {
-        if (!cf.has(g)) continue;
+      for (size_t gi = 0; gi < P.groups.size(); ++gi) {
+        const GroupPlan& g = P.groups[gi];
+        if (!cf.has(g) || granges[gi].empty()) continue;
         if (hasQ) {
           GemmSeg S = sym_seg(g, tile);
           S.A = at<char>(ws, g.offBh);
@@ -521,8 +570,7 @@ muon_status_t enqueue_products(const Plan& P, const std::vector<CallerMat>& cm, 
           S.ymu = a * S.sIn;
           S.outh = at<char>(ws, g.offQh[qcur ^ 1]);
           S.sOut = sc.sQ[k + 1];
-          segs.push_back(S);
-          works.push_back(symflops(g));
+          emit(gi, S, segs, works);
         }
         if (hasA) {
           GemmSeg S = sym_seg(g, tile);
@@ -541,8 +589,7 @@ muon_status_t enqueue_products(const Plan& P, const std::vector<CallerMat>& cm, 
           S.ymu = a * S.sIn;
           S.outh = at<char>(ws, g.offPAh);
           S.sOut = sc.sPA[k];
-          segs.push_back(S);
-          works.push_back(symflops(g));
+          emit(gi, S, segs, works);
         }
       }
       s = launch_segs(cf, segs, works, 4, "Gram Q/PA kernel");
@@ -551,8 +598,9 @@ muon_status_t enqueue_products(const Plan& P, const std::vector<CallerMat>& cm, 
       if (hasA) {
         segs.clear();
         works.clear();
-        for (const GroupPlan& g : P.groups) {
-          if (!cf.has(g)) continue;
+        for (size_t gi = 0; gi < P.groups.size(); ++gi) {
+          const GroupPlan& g = P.groups[gi];
+          if (!cf.has(g) || granges[gi].empty()) continue;
           GemmSeg S = sym_seg(g, tile);
           S.A = at<char>(ws, g.offBh);
           S.B = S.inh = at<char>(ws, g.offPAh);
@@ -569,8 +617,7 @@ muon_status_t enqueue_products(const Plan& P, const std::vector<CallerMat>& cm, 
           S.ymu = a * S.sIn;
           S.outh = at<char>(ws, g.offAh);
           S.sOut = sc.sA[k + 1];
-          segs.push_back(S);
-          works.push_back(symflops(g));
+          emit(gi, S, segs, works);
         }
         s = launch_segs(cf, segs, works, 4, "Gram A-update kernel");
         if (s != MUON_OK) return s;
@@ -580,11 +627,12 @@ muon_status_t enqueue_products(const Plan& P, const std::vector<CallerMat>& cm, 
   }
 
   // 6. final product with the fused output / update
-  for (const BucketPlan& bp : P.buckets) {
+  for (const Piece& pc : lane) {
+    const BucketPlan& bp = P.buckets[pc.bucket];
     const GroupPlan& g = P.groups[bp.group];
     const int tile = g.tile;
-    for (size_t c0 = 0; c0 < bp.mats.size(); c0 += kMaxUser) {
-      const size_t cn = std::min(bp.mats.size() - c0, (size_t)kMaxUser);
+    for (size_t c0 = (size_t)pc.b0; c0 < (size_t)pc.b1; c0 += kMaxUser) {
+      const size_t cn = std::min((size_t)pc.b1 - c0, (size_t)kMaxUser);
       GemmLaunch L;
       std::memset(&L, 0, sizeof(L));
       L.userDtype = dstDtype;
@@ -650,6 +698,192 @@ muon_status_t enqueue_products(const Plan& P, const std::vector<CallerMat>& cm, 
 }
 
 
+// ----------------------------------------------------------------------------
+// Concurrent lanes.  A launch whose tiles do not fill the GPU a whole number
+// of times leaves compute units idle in its last round, and a chain of
+// dependent launches that fill less than one round idles between products.
+// Splitting the plan's matrices over several streams ("lanes"), each running
+// the whole product chain of its matrices, lets one lane's tiles fill the
+// gaps another leaves.  A matrix's arithmetic does not depend on its lane, so
+// the results are the same bit for bit.
+
+constexpr int kMaxLanes = 4;
+constexpr int kMaxLaneDevices = 64;
+// Gram-space tiles per product (all groups of the call) below which the
+// products run in two lanes, and below which three (when the call has at
+// least three groups).  Measured on MI355X (whole calls, one lane against
+// several): two lanes are faster up to 4.2 rounds of the 256 compute units
+// (1062 tiles: two Qwen2.5-7B-shaped layers, 3%; one layer 10%, 32 and 64 ×
+// 1024×4096 13% and 6%) and slower from 8.3 rounds on (2124 tiles: four
+// layers, 2%; the 28-layer set 6%); three lanes are best for the small mix
+// (240 tiles in four groups: 16% against 7% with two) and no better than two
+// for one group.
+constexpr double kLaneTwoBelow = 1536;
+constexpr double kLaneThreeBelow = 256;
+
+int lane_count(const Plan& P) {
+  if (const char* e = std::getenv("MUON_LANES")) {
+    const int v = std::atoi(e);
+    if (v >= 1 && v <= kMaxLanes) return v;
+  }
+  double tiles = 0;
+  int mats = 0, groups = 0;
+  for (const GroupPlan& g : P.groups) {
+    if (g.count == 0) continue;
+    const double t = (double)(g.Mp / g.tile);
+    tiles += g.count * t * (t + 1) / 2;
+    mats += g.count;
+    ++groups;
+  }
+  if (mats < 2 || tiles >= kLaneTwoBelow) return 1;
+  return (tiles < kLaneThreeBelow && groups >= 3) ? 3 : 2;
+}
+
+Lane whole_lane(const Plan& P) {
+  Lane l;
+  for (size_t b = 0; b < P.buckets.size(); ++b)
+    l.push_back(Piece{(int)b, 0, (int)P.buckets[b].mats.size()});
+  return l;
+}
+
+// Lanes of about equal work: a group whose work exceeds a lane's share is cut
+// into ranges of consecutive group positions of about equal work; groups and
+// ranges then go to the least loaded lane, largest first.
+std::vector<Lane> plan_lanes(const Plan& P, int L) {
+  if (L <= 1) return {whole_lane(P)};
+  struct Item {
+    int group, s, e;
+    double work;
+  };
+  // work of every group position (positions follow the buckets' gramStart)
+  std::vector<std::vector<double>> pw(P.groups.size());
+  double total = 0;
+  for (size_t gi = 0; gi < P.groups.size(); ++gi) pw[gi].assign(P.groups[gi].count, 0.0);
+  for (const BucketPlan& bp : P.buckets)
+    for (size_t k = 0; k < bp.mats.size(); ++k) {
+      const double w = mat_work(bp.m, bp.n);
+      pw[bp.group][bp.gramStart + k] = w;
+      total += w;
+    }
+  if (total <= 0) return {whole_lane(P)};
+  const double share = total / L;
+  std::vector<Item> items;
+  for (size_t gi = 0; gi < P.groups.size(); ++gi) {
+    const std::vector<double>& w = pw[gi];
+    double gw = 0;
+    for (double x : w) gw += x;
+    if (w.empty() || gw <= 0) continue;
+    const int pieces = std::max(1, std::min((int)w.size(), (int)std::ceil(gw / share - 1e-9)));
+    double acc = 0;
+    int s = 0, cut = 1;
+    for (int k = 0; k < (int)w.size(); ++k) {
+      acc += w[k];
+      const bool last = k + 1 == (int)w.size();
+      if (last || (cut < pieces && acc >= gw * cut / pieces)) {
+        double iw = 0;
+        for (int j = s; j <= k; ++j) iw += w[j];
+        items.push_back(Item{(int)gi, s, k + 1, iw});
+        s = k + 1;
+        ++cut;
+      }
+    }
+  }
+  std::stable_sort(items.begin(), items.end(), [](const Item& a, const Item& b) { return a.work > b.work; });
+  std::vector<double> load(L, 0.0);
+  std::vector<std::vector<Item>> assigned(L);
+  for (const Item& it : items) {
+    const int l = (int)(std::min_element(load.begin(), load.end()) - load.begin());
+    load[l] += it.work;
+    assigned[l].push_back(it);
+  }
+  std::vector<Lane> lanes;
+  for (int l = 0; l < L; ++l) {
+    Lane lane;
+    for (const Item& it : assigned[l]) {
+      for (int bi : P.groups[it.group].buckets) {
+        const BucketPlan& bp = P.buckets[bi];
+        const int lo = std::max(it.s, bp.gramStart);
+        const int hi = std::min(it.e, bp.gramStart + (int)bp.mats.size());
+        if (hi > lo) lane.push_back(Piece{bi, lo - bp.gramStart, hi - bp.gramStart});
+      }
+    }
+    if (!lane.empty()) lanes.push_back(std::move(lane));
+  }
+  if (lanes.empty()) lanes.push_back(whole_lane(P));
+  return lanes;
+}
+
+// Streams and events of the lanes, one set per device, created on the first
+// call that needs them (never while the caller's stream is being captured);
+// the mutex also keeps each call's event records and waits together.
+struct LaneRes {
+  hipStream_t side[kMaxLanes - 1] = {};
+  hipEvent_t ev[kMaxLanes] = {};
+  bool ready = false;
+};
+std::mutex g_lane_mu;
+LaneRes g_lane[kMaxLaneDevices];
+
+bool lane_resources(hipStream_t st, LaneRes** out) {  // g_lane_mu held
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxLaneDevices) return false;
+  LaneRes& R = g_lane[dev];
+  if (!R.ready) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(st, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return false;
+    bool ok = true;
+    for (hipStream_t& s : R.side)
+      if (ok && hipStreamCreateWithFlags(&s, hipStreamNonBlocking) != hipSuccess) s = nullptr, ok = false;
+    for (hipEvent_t& e : R.ev)
+      if (ok && hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) e = nullptr, ok = false;
+    if (!ok) {
+      for (hipStream_t& s : R.side)
+        if (s) hipStreamDestroy(s), s = nullptr;
+      for (hipEvent_t& e : R.ev)
+        if (e) hipEventDestroy(e), e = nullptr;
+      return false;
+    }
+    R.ready = true;
+  }
+  *out = &R;
+  return true;
+}
+
+muon_status_t enqueue_products(const Plan& P, const std::vector<CallerMat>& cm, int dstDtype,
+                               const StepVariant& V, void* ws, hipStream_t st) {
+  bool any = false;
+  for (const MatPlan& m : P.mats) any |= !m.empty;
+  if (!any) return MUON_OK;
+  // callers that must not make the library create streams or events (the
+  // entry point that allocates nothing) run on their stream alone
+  const std::vector<Lane> lanes = plan_lanes(P, g_no_events ? 1 : lane_count(P));
+  if (lanes.size() > 1) {
+    std::lock_guard<std::mutex> lk(g_lane_mu);
+    LaneRes* R = nullptr;
+    if (lane_resources(st, &R)) {
+      auto hip = [](hipError_t e, const char* what) {
+        return e == hipSuccess ? MUON_OK : fail(MUON_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+      };
+      muon_status_t s = hip(hipEventRecord(R->ev[0], st), "hipEventRecord");
+      for (size_t i = 1; s == MUON_OK && i < lanes.size(); ++i)
+        s = hip(hipStreamWaitEvent(R->side[i - 1], R->ev[0], 0), "hipStreamWaitEvent");
+      if (s != MUON_OK) return s;
+      for (size_t i = 0; s == MUON_OK && i < lanes.size(); ++i)
+        s = enqueue_lane(P, lanes[i], cm, dstDtype, V, ws, i ? R->side[i - 1] : st);
+      // every lane is joined back, after a failure too, so that later work
+      // on the caller's stream stays ordered after what was enqueued
+      for (size_t i = 1; i < lanes.size(); ++i) {
+        muon_status_t j = hip(hipEventRecord(R->ev[i], R->side[i - 1]), "hipEventRecord");
+        if (j == MUON_OK) j = hip(hipStreamWaitEvent(st, R->ev[i], 0), "hipStreamWaitEvent");
+        if (s == MUON_OK) s = j;
+      }
+      return s;
+    }
+  }
+  return enqueue_lane(P, whole_lane(P), cm, dstDtype, V, ws, st);
+}
+
+
 muon_status_t enqueue(const Plan& P, const std::vector<CallerMat>& cm, int srcDtype, int dstDtype,
                       float beta, float eps, const StepVariant& V, void* ws, hipStream_t st) {
   muon_status_t s = enqueue_passes(P, cm, srcDtype, beta, eps, V, ws, st);
@@ -696,11 +930,6 @@ struct StepLayout {
   size_t totalBytes = 0;
   bool overlap = false;
 };
-
-double mat_work(int64_t r, int64_t c) {
-  const double m = (double)std::min(r, c), n = (double)std::max(r, c);
-  return 3.0 * m * m * n + 17.0 * m * m * m;
-}
 
 std::string plan_chunk(const int64_t* rows, const int64_t* cols, const std::vector<int>& idx, int steps,
                        const float* coeffs, Plan* P) {
@@ -1120,6 +1349,22 @@ muon_status_t muon_describe_plan(const int64_t* rows, const int64_t* cols, int32
                              for_step != 0, &P);
   if (!e.empty()) return fail(MUON_ERR_INVALID_ARG, e);
   std::string j = P.json();
+  // the concurrent lanes the products would run in: [bucket, b0, b1] pieces
+  {
+    std::string l = ",\"lanes\":[";
+    const std::vector<Lane> lanes = plan_lanes(P, lane_count(P));
+    for (size_t i = 0; i < lanes.size(); ++i) {
+      l += i ? ",[" : "[";
+      for (size_t k = 0; k < lanes[i].size(); ++k) {
+        const Piece& pc = lanes[i][k];
+        l += (k ? ",[" : "[") + std::to_string(pc.bucket) + "," + std::to_string(pc.b0) + "," +
+             std::to_string(pc.b1) + "]";
+      }
+      l += "]";
+    }
+    l += "]";
+    if (!j.empty() && j.back() == '}') j.insert(j.size() - 1, l);
+  }
   const size_t n = std::min(j.size(), buf_len - 1);
   std::memcpy(buf, j.data(), n);
   buf[n] = '\0';

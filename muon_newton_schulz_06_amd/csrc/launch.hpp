@@ -26,8 +26,9 @@ hipError_t launch_sel_gather(const SelLaunch& L, int64_t blocks, hipStream_t st)
 hipError_t launch_sel_scatter(const SelLaunch& L, int64_t blocks, hipStream_t st);
 
 // Library state shared across translation units (implemented in api.cpp):
-// the calling thread's last-error message, and whether launches made by this
-// thread record profiling events.
+// the calling thread's last-error message, and whether calls made by this
+// thread may use events and streams the library creates (profiling events,
+// concurrent lanes); off for the entry point that allocates nothing.
 void set_last_error(const std::string& msg);
 void set_no_events(bool on);
 
