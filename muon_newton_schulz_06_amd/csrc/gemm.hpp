@@ -149,39 +149,13 @@ struct EpiArgs {
   float u, sOut, sOutB, sIn, p0, p1, p2, lrsc, decay;
 };
 
-// Epilogue for one accumulator element (i, j) (register-staged kernel).  EPI
+// Epilogue for one accumulator element (i, j) of a dense result (register-
+// staged kernel; symmetric results go through sym_value / mirror_rows).  EPI
 // is a compile-time constant so each instantiation carries only its own code.
 template <typename T, int EPI>
 __device__ __forceinline__ void epilogue(const EpiArgs<T>& E, int i, int j, float acc) {
-  const int ldc = E.ldc;
-  if constexpr (EPI == EPI_SYRK) {
-    if (i > j) return;
-    const float g = E.u * acc;
-    if (E.out32) E.out32[(int64_t)i * ldc + j] = g;
-    store_mirror<T>(E.outh, ldc, i, j, to_op<T>(E.sOut * g));
-    if (E.writeIdentity) {
-      const float q = (i == j && i < E.mReal) ? E.sOutB : 0.f;
-      store_mirror<T>(E.outhb, ldc, i, j, to_op<T>(q));
-    }
-  } else if constexpr (EPI == EPI_SQ) {
-    if (i > j) return;
-    const int64_t e = (int64_t)i * ldc + j;
-    const float a = E.in32 ? E.in32[e] : E.sIn * (float)E.inh[e];
-    const float bb = E.p1 * a + E.p2 * (E.u * acc);
-    const T bh = to_op<T>(E.sOut * bb);
-    store_mirror<T>(E.outh, ldc, i, j, bh);
-    if (E.outhb) {  // Q₁ = a·I + B₀ from the stored B₀ (as the 256-tile kernel does)
-      const float q = (E.sOutB / E.sOut) * (float)bh + ((i == j && i < E.mReal) ? E.sOutB * E.p0 : 0.f);
-      store_mirror<T>(E.outhb, ldc, i, j, to_op<T>(q));
-    }
-  } else if constexpr (EPI == EPI_AXPY) {
-    if (i > j) return;
-    const int64_t e = (int64_t)i * ldc + j;
-    const float prev = E.in32 ? E.in32[e] : E.sIn * (float)E.inh[e];
-    const float y = E.p0 * prev + E.u * acc;
-    if (E.out32) E.out32[e] = y;
-    store_mirror<T>(E.outh, ldc, i, j, to_op<T>(E.sOut * y));
-  } else if constexpr (EPI == EPI_UPDATE) {
+  static_assert(EPI == EPI_UPDATE || EPI == EPI_OUT, "dense epilogues only");
+  if constexpr (EPI == EPI_UPDATE) {
     if (i >= E.mReal || j >= E.nReal) return;
     const int64_t e = (int64_t)i * E.userLd + j;
     const float o = E.u * acc;
@@ -198,6 +172,99 @@ __device__ __forceinline__ void epilogue(const EpiArgs<T>& E, int i, int j, floa
     const float v = E.u * acc;
     if (E.userDtype == 1) ((uint16_t*)E.user)[e] = f32_to_bf16_rne(v);
     else ((float*)E.user)[e] = v;
+  }
+}
+
+// Symmetric results of the register-staged kernel: the element (i, j), i ≤ j,
+// is stored at (i, j) only (and its fp32 copy, and the second copy's value at
+// (i, j)); the returned stored value is staged so that the transposed
+// position is written afterwards from LDS with coalesced rows (mirror_rows).
+template <typename T, int EPI>
+__device__ __forceinline__ T sym_value(const EpiArgs<T>& E, int i, int j, float acc) {
+  const int ldc = E.ldc;
+  const int64_t e = (int64_t)i * ldc + j;
+  if constexpr (EPI == EPI_SYRK) {
+    const float g = E.u * acc;
+    if (E.out32) E.out32[e] = g;
+    const T v = to_op<T>(E.sOut * g);
+    E.outh[e] = v;
+    if (E.writeIdentity) E.outhb[e] = to_op<T>((i == j && i < E.mReal) ? E.sOutB : 0.f);
+    return v;
+  } else if constexpr (EPI == EPI_SQ) {
+    const float a = E.in32 ? E.in32[e] : E.sIn * (float)E.inh[e];
+    const float bb = E.p1 * a + E.p2 * (E.u * acc);
+    const T bh = to_op<T>(E.sOut * bb);
+    E.outh[e] = bh;
+    if (E.outhb) {  // Q₁ = a·I + B₀ from the stored B₀ (as the 256-tile kernel does)
+      const float q = (E.sOutB / E.sOut) * (float)bh + ((i == j && i < E.mReal) ? E.sOutB * E.p0 : 0.f);
+      E.outhb[e] = to_op<T>(q);
+    }
+    return bh;
+  } else {
+    static_assert(EPI == EPI_AXPY, "symmetric epilogues only");
+    const float prev = E.in32 ? E.in32[e] : E.sIn * (float)E.inh[e];
+    const float y = E.p0 * prev + E.u * acc;
+    if (E.out32) E.out32[e] = y;
+    const T v = to_op<T>(E.sOut * y);
+    E.outh[e] = v;
+    return v;
+  }
+}
+
+// Staged symmetric tile: element (il, jl) at il·BN + (jl ^ (il/4)): the
+// column reads of mirror_rows (32 or 16 lanes at rows il = 4a + e, one
+// column) then fall in distinct banks, as do the staging writes (one row, 32
+// consecutive columns), and the tile needs no padding.
+template <int BN>
+__device__ __forceinline__ int sym_stage_idx(int il, int jl) {
+  return il * BN + (jl ^ ((il >> 2) & (BN - 1)));
+}
+
+// The transposed copy of a staged symmetric tile (ti, tj): block (tj, ti) of
+// the result, row by row (each thread writes 4 consecutive elements of a
+// row; the staged tile is read down its columns).  On a
+// diagonal tile only the strictly lower elements are written, from the
+// upper ones.  The second copy (first-step Q₁, or the zero-step identity)
+// has no identity term off the diagonal, so its transposed values follow
+// from the staged ones as at (i, j).
+template <typename T, int EPI, int BM, int BN, int NT>
+__device__ __forceinline__ void mirror_rows(const EpiArgs<T>& E, const T* st, int ti, int tj, int tid) {
+  static_assert(BM == BN, "square tiles");
+  constexpr int TPR = BM / 4;        // threads per row of the transposed block
+  constexpr int RPP = NT / TPR;      // rows per pass
+  const bool diag = ti == tj;
+  const int il0 = (tid % TPR) * 4;
+  const float qs = EPI == EPI_SQ ? E.sOutB / E.sOut : 0.f;
+#pragma unroll 1
+  for (int jl = tid / TPR; jl < BN; jl += RPP) {
+    const int64_t row = (int64_t)(tj * BN + jl) * E.ldc + ti * BM + il0;
+    T v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = st[sym_stage_idx<BN>(il0 + e, jl)];
+    if (!diag || il0 + 3 < jl) {
+      if constexpr (sizeof(T) == 4) {
+        *(float4*)(E.outh + row) = make_float4(v[0], v[1], v[2], v[3]);
+      } else {
+        typedef T t4 __attribute__((ext_vector_type(4)));
+        t4 h = {v[0], v[1], v[2], v[3]};
+        *(t4*)(E.outh + row) = h;
+      }
+      if (EPI == EPI_SQ && E.outhb) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) E.outhb[row + e] = to_op<T>(qs * (float)v[e] + 0.f);
+      } else if (EPI == EPI_SYRK && E.writeIdentity) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) E.outhb[row + e] = to_op<T>(0.f);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (il0 + e >= jl) continue;
+        E.outh[row + e] = v[e];
+        if (EPI == EPI_SQ && E.outhb) E.outhb[row + e] = to_op<T>(qs * (float)v[e] + 0.f);
+        else if (EPI == EPI_SYRK && E.writeIdentity) E.outhb[row + e] = to_op<T>(0.f);
+      }
+    }
   }
 }
 
@@ -411,7 +478,26 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const GemmLaunch L) 
   // row 8·(r/4) + 4·(l/32) + r%4, column l%32 of the block.
   const EpiArgs<T> E = make_epi<T, EPI>(L, S, mat);
   const int gi0 = ti * BM + wm * WTM, gj0 = tj * BN + wn * WTN;
-  epilogue_all<T, EPI, FM, FN>(E, gi0, gj0, lh, lr, acc);
+  if constexpr (EPI == EPI_SYRK || EPI == EPI_SQ || EPI == EPI_AXPY) {
+    // Symmetric results: the tile's elements i ≤ j are stored directly and
+    // staged in LDS (the ring is free: the loop ended with a barrier); the
+    // transposed block is then written row by row from the staged tile, so
+    // that copy is exactly the transpose of what was stored.
+    static_assert(BM * BN * sizeof(T) <= sizeof(smem), "staged tile must fit");
+    T* st = (T*)smem;
+    static_for<0, FM * FN * 16>([&](auto ic) {
+      constexpr int idx = decltype(ic)::value;
+      constexpr int fi = idx / (FN * 16), fj = (idx / 16) % FN, r = idx % 16;
+      const int il = wm * WTM + fi * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+      const int jl = wn * WTN + fj * 32 + lr;
+      if (ti < tj || il <= jl)
+        st[sym_stage_idx<BN>(il, jl)] = sym_value<T, EPI>(E, ti * BM + il, tj * BN + jl, acc[fi][fj][r]);
+    });
+    __syncthreads();
+    mirror_rows<T, EPI, BM, BN, NT>(E, st, ti, tj, tid);
+  } else {
+    epilogue_all<T, EPI, FM, FN>(E, gi0, gj0, lh, lr, acc);
+  }
 }
 
 // ---------------------------------------------------------------------------
