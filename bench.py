@@ -255,6 +255,8 @@ def other_configs(mns, W, torch):
     samples["small mix 176 bf16"] = [(host(ms_[i]), host(outs[i]), 5, Q, 2e-2)
                                      for i in range(0, len(ms_), 11)]
     del ms_, outs
+    iso = sorted(isolated_calls(mns, W, torch, "small_mix", warm=1, calls=5)["ms_per_call"])
+    out[-1]["ms_isolated_call"] = iso[len(iso) // 2]
     shapes = W.qwen_model_shapes(1)
     inp = W.muon_inputs(shapes, 4001, device="cuda")
     out.append(entry("one Qwen2.5-7B layer muon_step",
@@ -263,6 +265,27 @@ def other_configs(mns, W, torch):
     del inp
     torch.cuda.empty_cache()
     return out, samples
+
+
+def isolated_calls(mns, W, torch, which, warm=3, calls=3):
+    """Wall time of single muon_ns_batched calls of a smaller workload, each
+    started on an idle GPU (synchronisation and a 2 ms pause before it): the
+    latency of one call, host submission included."""
+    xs = W.ns_small_mix(device="cuda") if which == "small_mix" else W.ns_uniform_batch(device="cuda")
+    outs = [torch.empty_like(t) for t in xs]
+    ws = torch.empty(mns.ns_workspace_size([tuple(t.shape) for t in xs]), dtype=torch.uint8,
+                     device="cuda")
+    for _ in range(warm):
+        mns.muon_ns_batched(xs, outs=outs, steps=5, workspace=ws)
+    torch.cuda.synchronize()
+    ms = []
+    for _ in range(calls):
+        time.sleep(0.002)
+        t0 = time.perf_counter()
+        mns.muon_ns_batched(xs, outs=outs, steps=5, workspace=ws)
+        torch.cuda.synchronize()
+        ms.append((time.perf_counter() - t0) * 1e3)
+    return {"isolated": which, "matrices": len(xs), "ms_per_call": ms}
 
 
 def selected_step(mns, torch, inp, shapes, stream, fraction, warmup=1, steps=3):
@@ -331,6 +354,9 @@ def main():
                          "products of an earlier one")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB read + 1 GiB write kernel (counter calibration)")
+    ap.add_argument("--isolated", choices=["small_mix", "uniform"],
+                    help="run only isolated calls of a smaller workload (each after a "
+                         "synchronisation and a 2 ms pause; kernel-trace runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the step shards by matrix across GPUs "
@@ -356,6 +382,9 @@ def main():
     mns.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.isolated:
+        print(json.dumps(isolated_calls(mns, W, torch, args.isolated)), flush=True)
+        return
     shapes = workload_shapes(args.workload)
     seed0 = 5001
     print(f"[bench] generating {len(shapes)} matrices on {dev}", file=sys.stderr, flush=True)

@@ -168,22 +168,6 @@ def _stream_handle(stream, device):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def _ld(t: torch.Tensor) -> int:
-    """Row stride in elements of a 2-D tensor whose rows are contiguous.
-    Strides of size-1 dimensions carry no information and are ignored."""
-    if t.dim() != 2:
-        raise ValueError("matrices must be 2-D")
-    rows, cols = t.shape
-    if t.numel() == 0:
-        return max(cols, 1)
-    if cols > 1 and t.stride(1) != 1:
-        raise ValueError("matrix rows must be contiguous (stride(1) == 1)")
-    ld = t.stride(0) if rows > 1 else cols
-    if ld < cols:
-        raise ValueError("row stride smaller than the row length")
-    return ld
-
-
 _ws_cache: dict = {}
 _ws_lock = threading.Lock()
 
@@ -221,14 +205,50 @@ def release_workspace():
         _ws_cache.clear()
 
 
+def _mat_fields(t: torch.Tensor):
+    """(address or 0, rows, cols, row stride in elements) of a 2-D matrix
+    whose rows are contiguous; strides of size-1 dimensions carry no
+    information and are ignored, an empty matrix gets max(cols, 1).  Few
+    tensor accesses: for calls of many small matrices the binding's cost is
+    mostly this."""
+    if t.dim() != 2:
+        raise ValueError("matrices must be 2-D")
+    rows, cols = t.shape
+    if rows == 0 or cols == 0:
+        return 0, rows, cols, max(cols, 1)
+    s0, s1 = t.stride()
+    if cols > 1 and s1 != 1:
+        raise ValueError("matrix rows must be contiguous (stride(1) == 1)")
+    ld = s0 if rows > 1 else cols
+    if ld < cols:
+        raise ValueError("row stride smaller than the row length")
+    return t.data_ptr(), rows, cols, ld
+
+
+def _same_device_dtype(xs, outs):
+    """The one CUDA/HIP device and dtype of every x and out (ValueError /
+    TypeError otherwise), with matching shapes."""
+    dev, dt = xs[0].device, xs[0].dtype
+    if dev.type != "cuda" or {t.device for t in xs} != {dev} or {t.device for t in outs} != {dev}:
+        raise ValueError("all tensors must be on one CUDA/HIP device")
+    if {t.dtype for t in xs} != {dt} or {t.dtype for t in outs} != {dt}:
+        raise TypeError("all tensors must share one dtype")
+    if any(x.shape != o.shape for x, o in zip(xs, outs)):
+        raise ValueError("out shape differs from x shape")
+    return dev, dt
+
+
 def _ns_descs(xs, outs):
-    arr = (MuonNsDesc * max(len(xs), 1))()
-    for i, (x, o) in enumerate(zip(xs, outs)):
-        arr[i].x = x.data_ptr() if x.numel() else None
-        arr[i].out = o.data_ptr() if o.numel() else None
-        arr[i].rows, arr[i].cols = int(x.shape[0]), int(x.shape[1])
-        arr[i].ld_x, arr[i].ld_out = _ld(x), _ld(o)
-    return arr
+    """muon_ns_desc_t array (six 8-byte fields per matrix), filled in one
+    ctypes construction from a flat list."""
+    flat = []
+    for x, o in zip(xs, outs):
+        px, r, c, lx = _mat_fields(x)
+        po, _, _, lo = _mat_fields(o)
+        flat += (px, po, r, c, lx, lo)
+    n = max(len(xs), 1)
+    buf = (ctypes.c_int64 * (6 * n))(*flat)
+    return (MuonNsDesc * n).from_buffer(buf)
 
 
 def ns_workspace_size(shapes, dtype=torch.bfloat16) -> int:
@@ -286,15 +306,7 @@ def muon_ns_batched(xs, outs=None, steps: int = 5, coeffs=QUINTIC, eps: float = 
         raise ValueError("xs and outs differ in length")
     if not xs:
         return outs
-    dev = xs[0].device
-    dt = xs[0].dtype
-    for x, o in zip(xs, outs):
-        if x.device != dev or o.device != dev or dev.type != "cuda":
-            raise ValueError("all tensors must be on one CUDA/HIP device")
-        if x.dtype != dt or o.dtype != dt:
-            raise TypeError("all tensors must share one dtype")
-        if tuple(x.shape) != tuple(o.shape):
-            raise ValueError("out shape differs from x shape")
+    dev, dt = _same_device_dtype(xs, outs)
     code = _dtype_code(dt)
     arr = _ns_descs(xs, outs)
     need = ctypes.c_size_t(0)
@@ -319,15 +331,7 @@ def muon_ns_batched_noalloc(xs, outs, steps: int = 5, coeffs=QUINTIC, eps: float
         raise ValueError("xs and outs differ in length")
     if not xs:
         return outs
-    dev = xs[0].device
-    dt = xs[0].dtype
-    for x, o in zip(xs, outs):
-        if x.device != dev or o.device != dev or dev.type != "cuda":
-            raise ValueError("all tensors must be on one CUDA/HIP device")
-        if x.dtype != dt or o.dtype != dt:
-            raise TypeError("all tensors must share one dtype")
-        if tuple(x.shape) != tuple(o.shape):
-            raise ValueError("out shape differs from x shape")
+    dev, dt = _same_device_dtype(xs, outs)
     arr = _ns_descs(xs, outs)
     with torch.cuda.device(dev):
         _check(L.muon_ns_batched_noalloc(arr, len(xs), int(steps), _coeffs(coeffs), _dtype_code(dt),

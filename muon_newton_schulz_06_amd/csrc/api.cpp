@@ -27,6 +27,7 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <functional>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -82,10 +83,21 @@ bool debug_sync() {
   return e && e[0] == '1';
 }
 
+// A launch recorded for later submission (see enqueue_lanes).
+using Thunk = std::function<muon_status_t()>;
+
 struct Launcher {
   hipStream_t st;
+  // When set, launches are recorded here (with their stream) instead of
+  // being made; the launch functors hold copies of their arguments.
+  std::vector<Thunk>* defer = nullptr;
   template <typename F>
   muon_status_t run(int kind, double work, const char* what, F&& f) {
+    if (defer) {
+      const hipStream_t s0 = st;
+      defer->push_back([s0, kind, work, what, f]() { return Launcher{s0}.run(kind, work, what, f); });
+      return MUON_OK;
+    }
     muon_status_t s = run_(kind, work, what, f);
     if (s != MUON_OK || !debug_sync()) return s;
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
@@ -206,13 +218,22 @@ T* at(void* ws, size_t off) {
 }
 
 // Steps 1–3 (HBM-bound passes): momentum / sum of squares, α, cast.
+// The HBM-bound passes (momentum / sum of squares, norm finish, cast) over
+// every matrix of the plan, or over the matrices `only` lists.
 muon_status_t enqueue_passes(const Plan& P, const std::vector<CallerMat>& cm, int srcDtype,
-                             float beta, float eps, const StepVariant& V, void* ws, hipStream_t st) {
-  Launcher Lr{st};
+                             float beta, float eps, const StepVariant& V, void* ws, hipStream_t st,
+                             const std::vector<int>* only = nullptr,
+                             std::vector<Thunk>* defer = nullptr) {
+  Launcher Lr{st, defer};
   const int count = (int)P.mats.size();
   std::vector<int> live;
-  for (int i = 0; i < count; ++i)
-    if (!P.mats[i].empty) live.push_back(i);
+  if (only) {
+    for (int i : *only)
+      if (!P.mats[i].empty) live.push_back(i);
+  } else {
+    for (int i = 0; i < count; ++i)
+      if (!P.mats[i].empty) live.push_back(i);
+  }
   if (live.empty()) return MUON_OK;
   float* partials = at<float>(ws, P.offPartials);
   float* alpha = at<float>(ws, P.offAlpha);
@@ -256,7 +277,7 @@ muon_status_t enqueue_passes(const Plan& P, const std::vector<CallerMat>& cm, in
       blocks += mp.partialCnt;
     }
     L.n = (int)cn;
-    muon_status_t s = Lr.run(0, bytes, "momentum/norm kernel", [&] { return launch_ew(L, blocks, st); });
+    muon_status_t s = Lr.run(0, bytes, "momentum/norm kernel", [=] { return launch_ew(L, blocks, st); });
     if (s != MUON_OK) return s;
   }
   // 2. alpha
@@ -276,7 +297,7 @@ muon_status_t enqueue_passes(const Plan& P, const std::vector<CallerMat>& cm, in
       bytes += 4.0 * P.mats[i].partialCnt;
     }
     L.n = (int)cn;
-    muon_status_t s = Lr.run(1, bytes, "norm finish kernel", [&] { return launch_norm(L, st); });
+    muon_status_t s = Lr.run(1, bytes, "norm finish kernel", [=] { return launch_norm(L, st); });
     if (s != MUON_OK) return s;
   }
   // 3. cast into both operand layouts (one launch sequence per operand type)
@@ -330,7 +351,7 @@ muon_status_t enqueue_passes(const Plan& P, const std::vector<CallerMat>& cm, in
       if (L.nesterov) bytes += (V.gradDtype == MUON_DTYPE_BF16 ? 2.0 : 4.0) * mp.numel;
     }
     L.n = (int)cn;
-    muon_status_t s = Lr.run(2, bytes, "cast kernel", [&] { return launch_cast(L, blocks, st); });
+    muon_status_t s = Lr.run(2, bytes, "cast kernel", [=] { return launch_cast(L, blocks, st); });
     if (s != MUON_OK) return s;
   }
   }
@@ -354,8 +375,9 @@ struct Piece {
 using Lane = std::vector<Piece>;
 
 muon_status_t enqueue_lane(const Plan& P, const Lane& lane, const std::vector<CallerMat>& cm,
-                           int dstDtype, const StepVariant& V, void* ws, hipStream_t st) {
-  Launcher Lr{st};
+                           int dstDtype, const StepVariant& V, void* ws, hipStream_t st,
+                           std::vector<Thunk>* defer = nullptr) {
+  Launcher Lr{st, defer};
   const ScalePlan& sc = P.scales;
   // the lane's matrices of each group, as merged ranges of group positions
   std::vector<std::vector<std::pair<int, int>>> granges(P.groups.size());
@@ -435,7 +457,7 @@ muon_status_t enqueue_lane(const Plan& P, const Lane& lane, const std::vector<Ca
       L.band = cf.band;
       int k = kind;
       if (kind == 4 && tile == 256) k = (L.seg[0].epi == EPI_AXPY) ? 6 : 7;
-      muon_status_t s = Lr.run(k, work, what, [&] { return launch_gemm(op, tile, L, blocks, st); });
+      muon_status_t s = Lr.run(k, work, what, [=] { return launch_gemm(op, tile, L, blocks, st); });
       if (s != MUON_OK) return s;
     }
     return MUON_OK;
@@ -689,8 +711,9 @@ muon_status_t enqueue_lane(const Plan& P, const Lane& lane, const std::vector<Ca
       const int blocks = S.tilesPerMat * S.count;
       L.segStart[1] = blocks;
       const double work = 2.0 * (double)cn * bp.m * (double)bp.m * bp.n;
+      const int op = g.op;
       muon_status_t s = Lr.run(5, work, "final product kernel",
-                               [&] { return launch_gemm(g.op, tile, L, blocks, st); });
+                               [=] { return launch_gemm(op, tile, L, blocks, st); });
       if (s != MUON_OK) return s;
     }
   }
@@ -849,8 +872,16 @@ bool lane_resources(hipStream_t st, LaneRes** out) {  // g_lane_mu held
   return true;
 }
 
-muon_status_t enqueue_products(const Plan& P, const std::vector<CallerMat>& cm, int dstDtype,
-                               const StepVariant& V, void* ws, hipStream_t st) {
+// The products (and, with passes, the HBM-bound passes before them) of a
+// plan.  With several lanes every lane's launches are recorded first and
+// then submitted round-robin, one launch per lane at a time, so that every
+// lane has work on the GPU from the start (submitting one lane's whole chain
+// before the next would start the later lanes only after the host has made
+// the earlier lanes' launches); each lane runs its own passes, so its
+// products wait for its matrices only.
+muon_status_t enqueue_lanes(const Plan& P, const std::vector<CallerMat>& cm, int srcDtype,
+                            int dstDtype, float beta, float eps, const StepVariant& V, void* ws,
+                            hipStream_t st, bool passes) {
   bool any = false;
   for (const MatPlan& m : P.mats) any |= !m.empty;
   if (!any) return MUON_OK;
@@ -864,12 +895,29 @@ muon_status_t enqueue_products(const Plan& P, const std::vector<CallerMat>& cm, 
       auto hip = [](hipError_t e, const char* what) {
         return e == hipSuccess ? MUON_OK : fail(MUON_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
       };
-      muon_status_t s = hip(hipEventRecord(R->ev[0], st), "hipEventRecord");
+      // record every lane's launches (nothing is enqueued yet)
+      std::vector<std::vector<Thunk>> q(lanes.size());
+      muon_status_t s = MUON_OK;
+      for (size_t i = 0; s == MUON_OK && i < lanes.size(); ++i) {
+        const hipStream_t ls = i ? R->side[i - 1] : st;
+        if (passes) {
+          std::vector<int> mats;
+          for (const Piece& pc : lanes[i])
+            for (int k = pc.b0; k < pc.b1; ++k) mats.push_back(P.buckets[pc.bucket].mats[k]);
+          s = enqueue_passes(P, cm, srcDtype, beta, eps, V, ws, ls, &mats, &q[i]);
+        }
+        if (s == MUON_OK) s = enqueue_lane(P, lanes[i], cm, dstDtype, V, ws, ls, &q[i]);
+      }
+      if (s != MUON_OK) return s;
+      s = hip(hipEventRecord(R->ev[0], st), "hipEventRecord");
       for (size_t i = 1; s == MUON_OK && i < lanes.size(); ++i)
         s = hip(hipStreamWaitEvent(R->side[i - 1], R->ev[0], 0), "hipStreamWaitEvent");
       if (s != MUON_OK) return s;
-      for (size_t i = 0; s == MUON_OK && i < lanes.size(); ++i)
-        s = enqueue_lane(P, lanes[i], cm, dstDtype, V, ws, i ? R->side[i - 1] : st);
+      size_t most = 0;
+      for (const auto& v : q) most = std::max(most, v.size());
+      for (size_t k = 0; s == MUON_OK && k < most; ++k)
+        for (size_t i = 0; s == MUON_OK && i < lanes.size(); ++i)
+          if (k < q[i].size()) s = q[i][k]();
       // every lane is joined back, after a failure too, so that later work
       // on the caller's stream stays ordered after what was enqueued
       for (size_t i = 1; i < lanes.size(); ++i) {
@@ -880,15 +928,21 @@ muon_status_t enqueue_products(const Plan& P, const std::vector<CallerMat>& cm, 
       return s;
     }
   }
+  if (passes) {
+    muon_status_t s = enqueue_passes(P, cm, srcDtype, beta, eps, V, ws, st);
+    if (s != MUON_OK) return s;
+  }
   return enqueue_lane(P, whole_lane(P), cm, dstDtype, V, ws, st);
 }
 
+muon_status_t enqueue_products(const Plan& P, const std::vector<CallerMat>& cm, int dstDtype,
+                               const StepVariant& V, void* ws, hipStream_t st) {
+  return enqueue_lanes(P, cm, MUON_DTYPE_F32, dstDtype, 0.f, 0.f, V, ws, st, false);
+}
 
 muon_status_t enqueue(const Plan& P, const std::vector<CallerMat>& cm, int srcDtype, int dstDtype,
                       float beta, float eps, const StepVariant& V, void* ws, hipStream_t st) {
-  muon_status_t s = enqueue_passes(P, cm, srcDtype, beta, eps, V, ws, st);
-  if (s != MUON_OK) return s;
-  return enqueue_products(P, cm, dstDtype, V, ws, st);
+  return enqueue_lanes(P, cm, srcDtype, dstDtype, beta, eps, V, ws, st, true);
 }
 
 // ----------------------------------------------------------------------------
