@@ -944,7 +944,25 @@ __global__ __launch_bounds__(512) void gemm256_kernel(const GemmLaunch L) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave / WN, wn = wave - wm * WN;
+  // A diagonal tile of a Gram-space product needs only its 16×16 blocks on or
+  // above the diagonal: the epilogue writes the upper elements and takes the
+  // lower ones from the transposed upper half.  Each wave skips the MFMAs of
+  // the quarters of its 128×64 region (two block rows) that lie wholly below
+  // the diagonal: wave (wm, wn) runs 2, 4, 4, 4 quarters in row half 0
+  // (wn = 0..3) and 0, 0, 2, 4 in row half 1.  The waves of a workgroup are
+  // dealt to the CU's four SIMDs in turn (waves w and w + 4 share one), so on
+  // diagonal tiles row half 0 takes the column strips in reverse order: each
+  // SIMD then has 4 or 6 of its 8 quarters to run, not up to 8.  (The SYRK,
+  // whose contraction is up to 5× longer, ran 3% slower with the per-quarter
+  // branches than the diagonal tiles saved, so it computes its tiles in full.)
+  const bool diagT = kGram && ti == tj;
+  const int wm = wave / WN;
+  const int wn = (diagT && wm == 0) ? WN - 1 - wave : wave - wm * WN;
+  int runMask = 0xf;  // bit q: quarter q (block rows 2q, 2q + 1) has work
+  if (diagT)
+    for (int q = 0; q < 4; ++q)
+      if (wm * 8 + 2 * q > wn * 4 + 3) runMask &= ~(1 << q);
+  runMask = __builtin_amdgcn_readfirstlane(runMask);
   const int lc = lane & 15, lg = lane >> 4;
 
   const T* Ag = (const T*)S.A + mat * S.strideA + (int64_t)ti * BM * S.lda;
@@ -1102,8 +1120,11 @@ __global__ __launch_bounds__(512) void gemm256_kernel(const GemmLaunch L) {
   };
   // Symmetric products swap the operand roles (B fragments first), which
   // transposes the accumulator layout (see stage_rows).
-  auto mma = [&acc](const half8 (&fa)[2], const half8 (&fb)[FN], auto qc) __attribute__((always_inline)) {
+  auto mma = [&acc, runMask](const half8 (&fa)[2], const half8 (&fb)[FN], auto qc) __attribute__((always_inline)) {
     constexpr int q = decltype(qc)::value;
+    if constexpr (kGram) {
+      if (!(runMask & (1 << q))) return;
+    }
 #pragma unroll
     for (int f = 0; f < 2; ++f)
 #pragma unroll
