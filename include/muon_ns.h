@@ -27,9 +27,11 @@
  *     1536 tiles of all its groups (six rounds of the 256 compute units)
  *     and that holds at least two matrices splits its matrices into two
  *     sets of about equal work (three when under 256 tiles in at least three
- *     groups), each running its whole product chain on its own stream.  The extra streams are the library's (default priority,
- *     created on the first such call on a device, never while `stream` is
- *     being captured); they wait for an event recorded on `stream` and
+ *     groups), each running its own passes and whole product chain on its
+ *     own stream; the launches are made round-robin across the lanes.  The
+ *     extra streams are the library's (default priority, created on the
+ *     first such call on a device, never while `stream` is being
+ *     captured); they wait for an event recorded on `stream` and
  *     `stream` waits for each of them at the end, so the call is still one
  *     ordered piece of work on `stream` and can be captured into a graph
  *     once they exist (before that, a captured call runs on `stream`
