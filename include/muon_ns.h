@@ -138,8 +138,9 @@ muon_status_t muon_ns_batched(const muon_ns_desc_t* desc, int32_t count, int32_t
  * no workspace argument: the workspace is a fixed array of
  * MUON_NOALLOC_SCRATCH_BYTES in the library's own device memory, one per
  * device.  Neither this call nor anything it calls allocates device memory
- * (no hipMalloc / hipFree, no allocating library routine), and it records no
- * profiling events.
+ * (no hipMalloc / hipFree, no allocating library routine), it records no
+ * profiling events, and it runs on `stream` alone (no concurrent lanes, so
+ * it creates no stream or event either).
  *   - A request whose workspace (muon_ns_workspace_size) exceeds
  *     MUON_NOALLOC_SCRATCH_BYTES returns MUON_ERR_WORKSPACE before any HIP
  *     call; nothing is enqueued.
