@@ -751,9 +751,9 @@ constexpr int kDenseIters = 16;
 
 // bf16 weights of the update, fetched into registers ahead of use: the first
 // half-tile while the last k-tiles are multiplied, the second half before the
-// first is staged.  Every thread issues exactly kDenseIters loads per half
-// (addresses clamped into the matrix, so the count is uniform and every
-// access is in bounds); values outside the matrix are never used.
+// first is staged.  Every thread issues exactly kDenseIters loads per half;
+// only tiles that lie wholly inside the matrix prefetch (weight_prefetch_ok),
+// so every address is in bounds without clamping.
 struct WeightPrefetch {
   uint2 v[2][kDenseIters];
 };
@@ -769,13 +769,11 @@ __device__ __forceinline__ bool weight_prefetch_ok(const EpiArgs<_Float16>& E, i
 template <int kHalf>
 __device__ __forceinline__ void weight_prefetch(const EpiArgs<_Float16>& E, int ti, int tj, int tid,
                                                 WeightPrefetch& W) {
-  const uint16_t* w = (const uint16_t*)E.user;
-  const int64_t j = min((int64_t)tj * 256 + (tid & 63) * 4, (int64_t)E.nReal - 4);
+  const uint16_t* w = (const uint16_t*)E.user + ((int64_t)ti * 256 + kHalf * 128 + (tid >> 6)) * E.userLd +
+                      (int64_t)tj * 256 + (tid & 63) * 4;
+  const int64_t step8 = 8 * E.userLd;  // 8 rows
 #pragma unroll
-  for (int it = 0; it < kDenseIters; ++it) {
-    const int64_t i = min((int64_t)ti * 256 + kHalf * 128 + it * 8 + (tid >> 6), (int64_t)E.mReal - 1);
-    W.v[kHalf][it] = *(const uint2*)(w + i * E.userLd + j);
-  }
+  for (int it = 0; it < kDenseIters; ++it) W.v[kHalf][it] = *(const uint2*)(w + it * step8);
 }
 
 // acc of the waves of row half `half` → LDS as fp32 rows (u applied).
