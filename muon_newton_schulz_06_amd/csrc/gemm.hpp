@@ -504,9 +504,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const GemmLaunch L) 
 // 256×256 fp16 kernel with direct global→LDS loads.
 //
 // 8 waves (2 × 4, each a 128×64 block of 16×16×32 MFMAs), k-tile 32, and a
-// 4-stage LDS ring (4 × 32 KiB): the loads of k-tile kt+3 are in flight
-// while k-tile kt is multiplied, so about three k-tiles of latency are
-// covered without registers for staging.  Each 16-byte load lands straight
+// 4-stage LDS ring (4 × 32 KiB): a slot is refilled as soon as every wave
+// has read it, so the loads of k-tiles kt+1 .. kt+3 are in flight while
+// k-tile kt is multiplied, without registers for staging.  Each 16-byte load lands straight
 // in LDS (global_load_lds_dwordx4: a wave writes 1 KiB contiguously); the
 // bank swizzle is applied on the global side by choosing which chunk each
 // lane fetches.  One barrier per k-tile.  Each ring slot is its own LDS
@@ -608,8 +608,8 @@ __device__ __forceinline__ int stage_off(int row, int col) {
 // Gram-space products fetch the previous iterate's block into this staged
 // format during their last k-tiles (see issue_y): rows 0..191 into ring
 // slots 0..2 as those are released, rows 192..255 one slot beyond the ring
-// (they are fetched while slot 3 still holds the last k-tile).  kY selects
-// that placement for every staged access of the tile.
+// (fetched while slot 3 still holds the last k-tile).  kY selects that
+// placement for every staged access of the tile.
 template <bool kY>
 __device__ __forceinline__ int soff(int row, int col) {
   return stage_off(row, col) + ((kY && row >= 192) ? kStage : 0);
@@ -1052,9 +1052,10 @@ __global__ __launch_bounds__(512) void gemm256_kernel(const GemmLaunch L) {
   // ti ≤ tj.  It is fetched into LDS during the last four k-tiles, in the
   // staged format of the output tile (row r at r·512, 16-byte chunk c at
   // c ^ (r & 31); see soff), a quarter of 64 rows (32 KiB, four loads per
-  // wave, like a k-tile) at a time: rows 192..255 beyond the ring when
-  // k-tile KT − 1 is issued, rows 0..63, 64..127, 128..191 into ring slots
-  // 0, 1, 2 as k-tiles KT − 4, KT − 3, KT − 2 release them.  Wave w fetches
+  // wave, like a k-tile) at a time: rows 0..63 and 192..255 (the latter
+  // beyond the ring) once k-tile KT − 4 has released slot 0, then rows
+  // 64..127 and 128..191 into slots 1 and 2 as k-tiles KT − 3 and KT − 2
+  // release them.  Wave w fetches
   // rows 8w .. 8w + 7 of a quarter, two 512-byte rows per instruction; a
   // lane fetches the logical chunk that lands at its physical position.
   [[maybe_unused]] int offY[4];
@@ -1136,8 +1137,8 @@ __global__ __launch_bounds__(512) void gemm256_kernel(const GemmLaunch L) {
   constexpr auto kQ2 = std::integral_constant<int, 2>{};
   constexpr auto kQ3 = std::integral_constant<int, 3>{};
 
-  // Weight update: the first half of the tile's bf16 weights is loaded after
-  // the loads of k-tile KT − 1 are issued (in k-tile KT − 3) and lands while
+  // Weight update: the first half of the tile's bf16 weights is loaded in
+  // k-tile KT − 3 (after every k-tile's loads are issued) and lands while
   // the last k-tiles are multiplied.
   [[maybe_unused]] WeightPrefetch wpf;
   [[maybe_unused]] EpiArgs<T> Ew;
@@ -1147,14 +1148,15 @@ __global__ __launch_bounds__(512) void gemm256_kernel(const GemmLaunch L) {
     pref = KT >= 4 && weight_prefetch_ok(Ew, ti, tj);
   }
 
-  // One k-tile k (ring slot cur; nxt holds k + 1; fill held k − 1; pc its
-  // parity, selecting the B registers):
+  // One k-tile k (ring slot cur = k mod 4; nxt holds k + 1; pc its parity,
+  // selecting the B registers):
   //   quarters 0-2: read the next A quarter of k while the MFMAs of the
-  //   current one run;
+  //   current one run — the last reads of slot cur;
   //   wait until k-tile k + 1 has landed for every wave (each k-tile is four
-  //   loads per wave; younger loads stay in flight) — the barrier also means
-  //   every wave is done with slot fill;  refill fill with k + 3 (and the
-  //   tail loads);
+  //   loads per wave; k + 2 and k + 3 stay in flight) and until the wave's
+  //   own LDS reads have completed — after the barrier no wave reads slot
+  //   cur again, so it is refilled at once with k + 4 (or the tail loads):
+  //   three k-tiles are in flight while one is multiplied;
   //   quarter 3: read B and A quarter 0 of k + 1 (same phase) while its
   //   MFMAs run.
   // The barrier is a bare s_barrier: a __syncthreads() would also wait for
@@ -1185,34 +1187,40 @@ __global__ __launch_bounds__(512) void gemm256_kernel(const GemmLaunch L) {
     mma(fay, bset(pc), kQ3);
   };
   // Steps with k + 1 in the same phase and at least four k-tiles after k.
-  auto plain = [&](const char* cur, const char* nxt, char* fill, int k, auto pc, auto tac, auto tbc) __attribute__((always_inline)) {
+  auto plain = [&](char* cur, const char* nxt, int k, auto pc, auto tac, auto tbc) __attribute__((always_inline)) {
     first_half(cur, pc, tac);
-    asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
-    issue(fill, k + 3);
+    asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    issue(cur, k + 4);
     second_half(nxt, pc, tac, tbc);
   };
   // Any step: phase ends and the last k-tiles (tail loads, shorter waits).
-  auto step = [&](const char* cur, const char* nxt, char* fill, int k, int k1, auto pc, auto tac,
+  // Loads younger than k-tile k + 1 when step k waits for it: k + 2 and
+  // k + 3 while they exist; for the Gram products the Y quarters 0 and 3
+  // (issued in step KT − 4) and 1 (step KT − 3); for the weight update the
+  // prefetched half-tile (step KT − 3).
+  auto step = [&](char* cur, const char* nxt, int k, int k1, auto pc, auto tac,
                   auto tbc) __attribute__((always_inline)) {
     first_half(cur, pc, tac);
     const int r = KT - 1 - k;  // k-tiles after this one
-    if (kGram && (r == 1 || r == 2)) {
-      // k-tile k + 1 has landed once at most the younger loads (k-tile
-      // KT − 1 or the first Y quarter, and one more Y quarter) are pending
-      asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
-    } else if (r >= 2) {
+    if (r >= 3) {
+      asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    } else if (kGram && r >= 1) {
+      asm volatile("s_waitcnt vmcnt(12) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    } else if (r == 2) {
       asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
     } else if (r == 1) {
       if (pref) asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
       else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-    } else if (kGram) {
-      // every wave is done with slot KT − 2 before Y refills it
-      asm volatile("s_barrier" ::: "memory");
     }
-    if (r >= 3) issue(fill, k + 3);
+    if (r >= 4) issue(cur, k + 4);
     if constexpr (kGram) {
-      if (r == 3) issue_y(3);
-      else if (r <= 2) issue_y(2 - r);
+      // k-tiles KT − 4 .. KT − 2 sit in slots 0..2 (KT is a multiple of 8)
+      if (r == 3) {
+        issue_y(0);
+        issue_y(3);
+      } else if (r == 2 || r == 1) {
+        issue_y(3 - r);
+      }
     }
     if constexpr (EPI == EPI_UPDATE) {
       if (pref && r == 2) weight_prefetch<0>(Ew, ti, tj, tid, wpf);
@@ -1233,16 +1241,16 @@ __global__ __launch_bounds__(512) void gemm256_kernel(const GemmLaunch L) {
     if (k0 < k1) head(st0, kEven, tac, tbc);
     int kt = k0;
     for (; kt + 4 < k1 && kt + 8 <= KT; kt += 4) {
-      plain(st0, st1, st3, kt, kEven, tac, tbc);
-      plain(st1, st2, st0, kt + 1, kOdd, tac, tbc);
-      plain(st2, st3, st1, kt + 2, kEven, tac, tbc);
-      plain(st3, st0, st2, kt + 3, kOdd, tac, tbc);
+      plain(st0, st1, kt, kEven, tac, tbc);
+      plain(st1, st2, kt + 1, kOdd, tac, tbc);
+      plain(st2, st3, kt + 2, kEven, tac, tbc);
+      plain(st3, st0, kt + 3, kOdd, tac, tbc);
     }
     for (; kt < k1; kt += 4) {
-      step(st0, st1, st3, kt, k1, kEven, tac, tbc);
-      step(st1, st2, st0, kt + 1, k1, kOdd, tac, tbc);
-      step(st2, st3, st1, kt + 2, k1, kEven, tac, tbc);
-      step(st3, st0, st2, kt + 3, k1, kOdd, tac, tbc);
+      step(st0, st1, kt, k1, kEven, tac, tbc);
+      step(st1, st2, kt + 1, k1, kOdd, tac, tbc);
+      step(st2, st3, kt + 2, k1, kEven, tac, tbc);
+      step(st3, st0, kt + 3, k1, kOdd, tac, tbc);
     }
   };
 
@@ -1253,7 +1261,8 @@ __global__ __launch_bounds__(512) void gemm256_kernel(const GemmLaunch L) {
       issue(st0, 0);
       issue(st1, 1);
       issue(st2, 2);
-      asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+      issue(st3, 3);
+      asm volatile("s_waitcnt vmcnt(12)\n\ts_barrier" ::: "memory");
       phase(0, dA, std::true_type{}, std::true_type{});
       phase(dA, dB, std::false_type{}, std::true_type{});
       phase(dB, KT, std::false_type{}, std::false_type{});
@@ -1264,29 +1273,29 @@ __global__ __launch_bounds__(512) void gemm256_kernel(const GemmLaunch L) {
       issue_y(3);
     }
   } else {
+    // One layout for every k-tile: KT ≥ 8 (a multiple of 8), so the loop of
+    // whole groups runs at least once (written so, which keeps the
+    // accumulators in place).
     issue(st0, 0);
-    if (KT > 1) issue(st1, 1);
-    if (KT > 2) issue(st2, 2);
-    if (KT > 2) asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
-    else if (KT > 1) asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-    // One layout for every k-tile: KT ≥ 8, so the loop of whole groups runs
-    // at least once (written so, which keeps the accumulators in place).
+    issue(st1, 1);
+    issue(st2, 2);
+    issue(st3, 3);
+    asm volatile("s_waitcnt vmcnt(12)\n\ts_barrier" ::: "memory");
     constexpr auto ta = std::bool_constant<TR == 1>{};
     constexpr auto tb = std::bool_constant<TR == 2>{};
     head(st0, kEven, ta, tb);
     int kt = 0;
     do {
-      plain(st0, st1, st3, kt, kEven, ta, tb);
-      plain(st1, st2, st0, kt + 1, kOdd, ta, tb);
-      plain(st2, st3, st1, kt + 2, kEven, ta, tb);
-      plain(st3, st0, st2, kt + 3, kOdd, ta, tb);
+      plain(st0, st1, kt, kEven, ta, tb);
+      plain(st1, st2, kt + 1, kOdd, ta, tb);
+      plain(st2, st3, kt + 2, kEven, ta, tb);
+      plain(st3, st0, kt + 3, kOdd, ta, tb);
       kt += 4;
     } while (kt + 4 < KT);
-    step(st0, st1, st3, kt, KT, kEven, ta, tb);
-    step(st1, st2, st0, kt + 1, KT, kOdd, ta, tb);
-    step(st2, st3, st1, kt + 2, KT, kEven, ta, tb);
-    step(st3, st0, st2, kt + 3, KT, kOdd, ta, tb);
+    step(st0, st1, kt, KT, kEven, ta, tb);
+    step(st1, st2, kt + 1, KT, kOdd, ta, tb);
+    step(st2, st3, kt + 2, KT, kEven, ta, tb);
+    step(st3, st0, kt + 3, KT, kOdd, ta, tb);
   }
 
   // Wait states between the last MFMA writing an accumulator and the first
