@@ -352,6 +352,9 @@ def main():
     ap.add_argument("--overlap", action="store_true",
                     help="muon_step's overlap option: HBM-bound passes of a later chunk under the "
                          "products of an earlier one")
+    ap.add_argument("--no-carried-exponents", action="store_true",
+                    help="run the step without scale_exp (every operand cast in its own pass "
+                         "after the norm), as a caller without optimiser state would")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB read + 1 GiB write kernel (counter calibration)")
     ap.add_argument("--isolated", choices=["small_mix", "uniform"],
@@ -391,10 +394,15 @@ def main():
     inp = W.muon_inputs(shapes, seed0, device=dev)
     ws = torch.empty(mns.step_workspace_size(shapes), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
+    # the optimiser state a training loop carries besides the momenta: one
+    # operand exponent per matrix, recorded by each step for the next (the
+    # first warm-up step casts every operand in its own pass)
+    carried = not args.no_carried_exponents
+    sx = mns.scale_exp_buffer(len(shapes), dev) if carried else None
 
     def step():
         mns.muon_step(inp.params, inp.grads, inp.momenta, beta=0.95, lr=0.02, steps=5,
-                      workspace=ws, stream=stream, overlap=args.overlap)
+                      workspace=ws, stream=stream, overlap=args.overlap, scale_exp=sx)
 
     for i in range(args.warmup):
         step()
@@ -471,6 +479,7 @@ def main():
                    "op": "muon_step", "ns_steps": 5, "coeffs": "quintic (3.4445, -4.775, 2.0315)",
                    "param_dtype": "bf16", "grad_dtype": "f32", "momentum_dtype": "f32",
                    "mfma_operands": "f16 (power-of-two scaled)", "accumulate": "f32",
+                   "operand_exponents": "carried across steps (scale_exp)" if carried else "none",
                    "algorithmic_tflop_per_step": F / 1e12, "parallelism": "single GPU"},
         "frac_mfma_peak": tflops / MFMA_PEAK_F16,
         "matrices_per_s": len(shapes) / (ms / 1e3),

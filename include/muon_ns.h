@@ -67,7 +67,7 @@
 extern "C" {
 #endif
 
-#define MUON_NS_ABI_VERSION 6
+#define MUON_NS_ABI_VERSION 7
 
 typedef enum muon_status {
   MUON_OK = 0,
@@ -179,13 +179,18 @@ muon_status_t muon_step(void* const* params, const float* const* grads, float* c
                         const float coeffs[3], float eps,
                         void* workspace, size_t workspace_bytes, void* stream);
 
+/* An entry of muon_step_opts_t.scale_exp that carries no exponent. */
+#define MUON_SCALE_EXP_UNKNOWN INT32_MIN
+
 /* Options of muon_step_ex.  The pages define the plain step only (momentum
  * as above, no weight decay); the first three are the usual Muon-optimiser
  * variants, provided for use as a drop-in optimiser (DMuon summary §3: the
- * module replaces the optimiser without changing the framework); the last
- * two choose how the work is scheduled and never change a result beyond
- * what the grouping of matrices changes (see below).  A zero-initialised
- * struct with grad_dtype = MUON_DTYPE_F32 is the plain step.
+ * module replaces the optimiser without changing the framework); overlap and
+ * max_workspace_bytes choose how the work is scheduled and never change a
+ * result beyond what the grouping of matrices changes (see below);
+ * scale_exp lets the momentum pass write the half-precision operand itself.
+ * A zero-initialised struct with grad_dtype = MUON_DTYPE_F32 is the plain
+ * step.
  *   nesterov = 1:  the matrix orthogonalised is u = g + beta·M' (M' the
  *                  updated momentum) instead of M'; the stored state is M'.
  *   weight_decay:  decoupled, W ← round((1 − lr·weight_decay)·W − lr·sc·O);
@@ -223,8 +228,35 @@ typedef struct muon_step_opts {
   muon_dtype_t grad_dtype;
   int32_t overlap;           /* 0 or 1 */
   uint64_t max_workspace_bytes;
+  int32_t* scale_exp;        /* NULL or count int32 on the device (see below) */
 } muon_step_opts_t;
 
+/*   scale_exp:     NULL, or device memory of the call's device holding one
+ *                  int32 per matrix (count entries, 4-byte aligned, not
+ *                  overlapping any tensor of the call or the workspace),
+ *                  read and rewritten by the call: the optimiser state of a
+ *                  per-matrix power-of-two operand exponent.  Initialise it
+ *                  to MUON_SCALE_EXP_UNKNOWN (any value outside [-100, 100]
+ *                  means unknown).  With it, matrices on the fp16 256-tile
+ *                  path have their momentum pass write the MFMA operand X₀'
+ *                  = u·2^e (u the matrix orthogonalised) directly, instead of
+ *                  a second pass re-reading the fp32 momentum after the norm;
+ *                  the products then use X₀ = ρ·X₀' with ρ = sX/((‖u‖+eps)·2^e)
+ *                  applied in fp32 in the SYRK (ρ²) and final-product (ρ)
+ *                  epilogues.  X₀' is kept when ‖u‖·2^e ∈ [2^9, 2^14] (no
+ *                  fp16 overflow, entries as far from fp16's subnormal range
+ *                  as the normalised operand's); otherwise, and when e is
+ *                  unknown, the matrix is cast from the momentum as without
+ *                  scale_exp.  Each entry is then rewritten to the exponent
+ *                  that puts ‖u‖·2^e in [2^12, 2^13) (MUON_SCALE_EXP_UNKNOWN
+ *                  when ‖u‖ is 0 or not finite), for the next step.  Results
+ *                  agree with the call without scale_exp to the rounding of
+ *                  the fp16 operand (the same precision, another scale), not
+ *                  bit for bit; ‖u‖ is also summed in another order (per
+ *                  64×64 tile), so even a matrix that falls back to the cast
+ *                  may differ in the last bits.  Matrices on other paths
+ *                  (fp32 groups, 128-tile groups) ignore their entry and
+ *                  leave it unchanged. */
 /* muon_step with options; opts = NULL gives exactly muon_step.  grads[i]
  * has opts->grad_dtype; every other argument, the workspace size and the
  * error behaviour are those of muon_step (an invalid option returns

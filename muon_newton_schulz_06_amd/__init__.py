@@ -25,6 +25,7 @@ __all__ = [
     "ns_workspace_size", "step_workspace_size", "describe_plan", "profile_enable",
     "profile_read", "abi_version", "PROFILE_KINDS", "set_tile_table", "muon_step_selected",
     "step_selected_workspace_size", "muon_ns_batched_noalloc", "NOALLOC_SCRATCH_BYTES",
+    "SCALE_EXP_UNKNOWN", "scale_exp_buffer",
 ]
 
 QUINTIC = (3.4445, -4.7750, 2.0315)
@@ -32,7 +33,7 @@ CUBIC = (1.5, -0.5, 0.0)
 
 MUON_DTYPE_F32 = 0
 MUON_DTYPE_BF16 = 1
-ABI_VERSION = 6
+ABI_VERSION = 7
 NOALLOC_SCRATCH_BYTES = 64 << 20  # MUON_NOALLOC_SCRATCH_BYTES
 
 PROFILE_KINDS = {"momentum": 0, "norm": 1, "cast": 2, "syrk": 3, "gram128": 4, "final": 5,
@@ -71,7 +72,17 @@ class MuonTileEntry(ctypes.Structure):
 class MuonStepOpts(ctypes.Structure):
     _fields_ = [("nesterov", ctypes.c_int32), ("weight_decay", ctypes.c_float),
                 ("grad_dtype", ctypes.c_int32), ("overlap", ctypes.c_int32),
-                ("max_workspace_bytes", ctypes.c_uint64)]
+                ("max_workspace_bytes", ctypes.c_uint64), ("scale_exp", ctypes.c_void_p)]
+
+
+# muon_step_opts_t.scale_exp entry that carries no exponent (INT32_MIN)
+SCALE_EXP_UNKNOWN = -2**31
+
+
+def scale_exp_buffer(n: int, device) -> torch.Tensor:
+    """A fresh carried-exponent buffer for muon_step(scale_exp=...): n int32
+    entries on `device`, all unknown."""
+    return torch.full((n,), SCALE_EXP_UNKNOWN, dtype=torch.int32, device=device)
 
 
 _lib = None
@@ -342,13 +353,15 @@ def muon_ns_batched_noalloc(xs, outs, steps: int = 5, coeffs=QUINTIC, eps: float
 def muon_step(params, grads, momenta, beta: float = 0.95, lr: float = 0.02, steps: int = 5,
               coeffs=QUINTIC, eps: float = 1e-7, workspace=None, stream=None,
               nesterov: bool = False, weight_decay: float = 0.0, overlap: bool = False,
-              max_workspace_bytes: int = 0):
+              max_workspace_bytes: int = 0, scale_exp=None):
     """One in-place Muon step over lists of weights (bf16 or fp32), gradients
     (fp32 or bf16, one dtype per call) and fp32 momenta (all contiguous, same
-    device).  nesterov / weight_decay / overlap / max_workspace_bytes select
-    the muon_step_ex options (see muon_step_opts_t); with their defaults and
-    fp32 gradients the plain muon_step entry point runs.  With a budget the
-    cached workspace is at most max_workspace_bytes."""
+    device).  nesterov / weight_decay / overlap / max_workspace_bytes /
+    scale_exp select the muon_step_ex options (see muon_step_opts_t); with
+    their defaults and fp32 gradients the plain muon_step entry point runs.
+    With a budget the cached workspace is at most max_workspace_bytes.
+    scale_exp: None or a contiguous int32 tensor of len(params) entries on the
+    params' device (see scale_exp_buffer), read and rewritten by the call."""
     L = load()
     params, grads, momenta = list(params), list(grads), list(momenta)
     n = len(params)
@@ -380,6 +393,11 @@ def muon_step(params, grads, momenta, beta: float = 0.95, lr: float = 0.02, step
     M = (vp * n)(*[m.data_ptr() for m in momenta])
     rows = (ctypes.c_int64 * n)(*[int(p.shape[0]) for p in params])
     cols = (ctypes.c_int64 * n)(*[int(p.shape[1]) for p in params])
+    if scale_exp is not None:
+        if (scale_exp.dtype != torch.int32 or scale_exp.device != dev or not scale_exp.is_contiguous()
+                or scale_exp.numel() != n):
+            raise ValueError("scale_exp must be a contiguous int32 tensor of len(params) entries "
+                             "on the params' device")
     need = ctypes.c_size_t(0)
     _check(L.muon_step_workspace_size(rows, cols, n, ctypes.byref(need)))
     nbytes = int(need.value)
@@ -387,7 +405,7 @@ def muon_step(params, grads, momenta, beta: float = 0.95, lr: float = 0.02, step
         nbytes = min(nbytes, int(max_workspace_bytes))
     ws, ws_bytes = _workspace(nbytes, dev, workspace, stream)
     plain = ((not nesterov) and float(weight_decay) == 0.0 and gdt == torch.float32 and not overlap
-             and not max_workspace_bytes)
+             and not max_workspace_bytes and scale_exp is None)
     with torch.cuda.device(dev):
         wsp = ctypes.c_void_p(ws.data_ptr() if ws is not None else 0)
         if plain:
@@ -396,7 +414,8 @@ def muon_step(params, grads, momenta, beta: float = 0.95, lr: float = 0.02, step
                                _stream_handle(stream, dev)))
         else:
             opts = MuonStepOpts(int(bool(nesterov)), float(weight_decay), _dtype_code(gdt),
-                                int(bool(overlap)), int(max_workspace_bytes))
+                                int(bool(overlap)), int(max_workspace_bytes),
+                                scale_exp.data_ptr() if scale_exp is not None else None)
             _check(L.muon_step_ex(P, G, M, rows, cols, n, _dtype_code(pdt), float(beta),
                                   float(lr), int(steps), _coeffs(coeffs), float(eps),
                                   ctypes.byref(opts), wsp, ws_bytes, _stream_handle(stream, dev)))

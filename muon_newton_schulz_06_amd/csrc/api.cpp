@@ -200,7 +200,14 @@ struct CallerMat {
   int64_t ldDst;
   const void* grad;  // step only
   float lrsc;
+  int32_t* hint = nullptr;  // step only: carried operand exponent (null: none)
 };
+
+// A bucket whose momentum pass writes the fp16 operand itself: fusable and
+// every matrix of the call carries an exponent (a call passes all or none).
+bool fused_bucket(const Plan& P, const BucketPlan& bp, const std::vector<CallerMat>& cm) {
+  return P.forStep && bp.fusable && !bp.mats.empty() && cm[bp.mats[0]].hint != nullptr;
+}
 
 // Step options resolved on the host (defaults: the plain step).
 struct StepVariant {
@@ -216,6 +223,10 @@ template <typename T>
 T* at(void* ws, size_t off) {
   return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
 }
+
+// Workgroups of the fallback cast of fused operands (it walks the tiles of
+// the matrices that failed their check with a grid stride).
+constexpr int64_t kCastFallbackBlocks = 1024;
 
 // Steps 1–3 (HBM-bound passes): momentum / sum of squares, α, cast.
 // The HBM-bound passes (momentum / sum of squares, norm finish, cast) over
@@ -237,10 +248,55 @@ muon_status_t enqueue_passes(const Plan& P, const std::vector<CallerMat>& cm, in
   if (live.empty()) return MUON_OK;
   float* partials = at<float>(ws, P.offPartials);
   float* alpha = at<float>(ws, P.offAlpha);
+  float* rho = at<float>(ws, P.offRho);
+  int32_t* okf = at<int32_t>(ws, P.offOk);
   const ScalePlan& sc = P.scales;
+  // matrices whose momentum pass also writes the operand (carried exponents)
+  std::vector<char> fused(count, 0);
+  std::vector<int> flat, fz;
+  for (int i : live) {
+    fused[i] = !V.presummed && fused_bucket(P, P.buckets[P.mats[i].bucket], cm);
+    (fused[i] ? fz : flat).push_back(i);
+  }
 
-  // 1. momentum / sum of squares
-  for (size_t c0 = 0; c0 < (V.presummed ? 0 : live.size()); c0 += kMaxUser) {
+  // 1a. momentum fused with the cast (64×64 tiles of the padded stored matrix)
+  for (size_t c0 = 0; c0 < fz.size(); c0 += kMaxUser) {
+    MomCastLaunch L;
+    std::memset(&L, 0, sizeof(L));
+    L.gradDtype = V.gradDtype;
+    L.nesterov = V.nesterov;
+    L.beta = beta;
+    L.partials = partials;
+    int64_t blocks = 0;
+    double bytes = 0;
+    const size_t cn = std::min(fz.size() - c0, (size_t)kMaxUser);
+    for (size_t k = 0; k < cn; ++k) {
+      const int i = fz[c0 + k];
+      const MatPlan& mp = P.mats[i];
+      const BucketPlan& bp = P.buckets[mp.bucket];
+      MomCastMat& C = L.mat[k];
+      C.grad = cm[i].grad;
+      C.mom = (float*)cm[i].src;
+      C.xh = at<char>(ws, bp.offXh + bp.strideX * mp.posBucket);
+      C.hint = cm[i].hint;
+      C.rows = mp.rows;
+      C.cols = mp.cols;
+      C.tall = mp.tall ? 1 : 0;
+      C.rp = (int32_t)(mp.tall ? bp.Np : bp.Mp);
+      C.cp = (int32_t)(mp.tall ? bp.Mp : bp.Np);
+      C.tilesC = C.cp / (mp.tall ? kFuseTallC : kFuseWideC);
+      C.blockStart = blocks;
+      C.partialOff = mp.partialOff;
+      blocks += mp.tileCnt;
+      bytes += (V.gradDtype == MUON_DTYPE_BF16 ? 10.0 : 12.0) * mp.numel + 2.0 * (double)bp.Mp * (double)bp.Np;
+    }
+    L.n = (int)cn;
+    muon_status_t s = Lr.run(0, bytes, "momentum + cast kernel", [=] { return launch_momcast(L, blocks, st); });
+    if (s != MUON_OK) return s;
+  }
+
+  // 1b. momentum / sum of squares
+  for (size_t c0 = 0; c0 < (V.presummed ? 0 : flat.size()); c0 += kMaxUser) {
     EwLaunch L;
     std::memset(&L, 0, sizeof(L));
     L.mode = P.forStep ? 0 : 1;
@@ -251,9 +307,9 @@ muon_status_t enqueue_passes(const Plan& P, const std::vector<CallerMat>& cm, in
     L.vec = 1;
     int64_t blocks = 0;
     double bytes = 0;
-    const size_t cn = std::min(live.size() - c0, (size_t)kMaxUser);
+    const size_t cn = std::min(flat.size() - c0, (size_t)kMaxUser);
     for (size_t k = 0; k < cn; ++k) {
-      const int i = live[c0 + k];
+      const int i = flat[c0 + k];
       const MatPlan& mp = P.mats[i];
       EwMat& e = L.mat[k];
       e.rows = mp.rows;
@@ -287,28 +343,39 @@ muon_status_t enqueue_passes(const Plan& P, const std::vector<CallerMat>& cm, in
     L.eps = eps;
     L.partials = partials;
     L.alpha = alpha;
+    L.sX = sc.sX;
+    L.rho = rho;
+    L.ok = okf;
     const size_t cn = std::min(live.size() - c0, (size_t)kMaxUser);
     double bytes = 0;
     for (size_t k = 0; k < cn; ++k) {
       const int i = live[c0 + k];
+      const int64_t cnt = V.presummed ? 1 : fused[i] ? P.mats[i].tileCnt : P.mats[i].partialCnt;
       L.off[k] = P.mats[i].partialOff;
-      L.cnt[k] = V.presummed ? 1 : P.mats[i].partialCnt;
+      L.cnt[k] = cnt;
       L.alphaIdx[k] = i;
-      bytes += 4.0 * P.mats[i].partialCnt;
+      L.hint[k] = fused[i] ? cm[i].hint : nullptr;
+      L.rhoIdx[k] = P.mats[i].rhoPos;
+      bytes += 4.0 * cnt;
     }
     L.n = (int)cn;
     muon_status_t s = Lr.run(1, bytes, "norm finish kernel", [=] { return launch_norm(L, st); });
     if (s != MUON_OK) return s;
   }
   // 3. cast into both operand layouts (one launch sequence per operand type)
+  // Fused matrices go through the strided fallback launch (a small grid that
+  // casts only the matrices whose fused operand failed its check).
+  for (int strided = 0; strided < 2; ++strided)
   for (int op : {(int)OP_F16, (int)OP_F32}) {
   std::vector<int> castMats;
-  for (int i : live)
+  for (int i : (strided ? fz : flat))
     if (P.buckets[P.mats[i].bucket].op == op) castMats.push_back(i);
   const size_t esz = op == OP_F32 ? 4 : 2;
   for (size_t c0 = 0; c0 < castMats.size(); c0 += kMaxUser) {
     CastLaunch L;
     std::memset(&L, 0, sizeof(L));
+    L.strided = strided;
+    L.ok = okf;
     L.srcDtype = P.forStep ? MUON_DTYPE_F32 : srcDtype;
     L.outOp = op;
     L.sX = sc.sX;
@@ -343,14 +410,19 @@ muon_status_t enqueue_passes(const Plan& P, const std::vector<CallerMat>& cm, in
         C.cp = (int32_t)bp.Mp;
       }
       C.alphaIdx = i;
+      C.okIdx = strided ? i : -1;
       C.tilesC = C.cp / kCastTile;
       C.blockStart = blocks;
       blocks += (int64_t)(C.rp / kCastTile) * C.tilesC;
-      bytes += (P.forStep ? 4.0 : (srcDtype == MUON_DTYPE_BF16 ? 2.0 : 4.0)) * mp.numel +
-               (bp.xT ? 2.0 : 1.0) * esz * (double)bp.Mp * (double)bp.Np;
-      if (L.nesterov) bytes += (V.gradDtype == MUON_DTYPE_BF16 ? 2.0 : 4.0) * mp.numel;
+      // the fallback moves nothing unless a check fails
+      if (!strided) {
+        bytes += (P.forStep ? 4.0 : (srcDtype == MUON_DTYPE_BF16 ? 2.0 : 4.0)) * mp.numel +
+                 (bp.xT ? 2.0 : 1.0) * esz * (double)bp.Mp * (double)bp.Np;
+        if (L.nesterov) bytes += (V.gradDtype == MUON_DTYPE_BF16 ? 2.0 : 4.0) * mp.numel;
+      }
     }
     L.n = (int)cn;
+    if (strided) blocks = std::min<int64_t>(blocks, kCastFallbackBlocks);
     muon_status_t s = Lr.run(2, bytes, "cast kernel", [=] { return launch_cast(L, blocks, st); });
     if (s != MUON_OK) return s;
   }
@@ -516,6 +588,7 @@ muon_status_t enqueue_lane(const Plan& P, const Lane& lane, const std::vector<Ca
         S.epi = EPI_SYRK;
         upper(S, tile, false);
         S.u = 1.0f / (sc.sX * sc.sX);
+        if (fused_bucket(P, bp, cm)) S.rho = at<float>(ws, P.offRho) + bp.rhoStart + pc.b0;
         S.sOut = sc.sA[0];
         S.outh = at<char>(ws, g.offAh + g.strideh * pos);
         if (g.state32) S.out32 = at<float>(ws, g.offA32 + g.stride32 * pos);
@@ -699,6 +772,7 @@ muon_status_t enqueue_lane(const Plan& P, const Lane& lane, const std::vector<Ca
       S.sym = 0;
       S.epi = P.forStep ? EPI_UPDATE : EPI_OUT;
       S.u = 1.0f / (sc.sQ[P.steps] * sc.sX);
+      if (fused_bucket(P, bp, cm)) S.rho = at<float>(ws, P.offRho) + bp.rhoStart + c0;
       S.userBase = 0;
       for (size_t k = 0; k < cn; ++k) {
         const int i = bp.mats[c0 + k];
@@ -1500,6 +1574,7 @@ muon_status_t muon_step_ex(void* const* params, const void* const* grads, float*
   float wd = 0.f;
   bool overlap = false;
   uint64_t budget = 0;
+  int32_t* scaleExp = nullptr;
   if (opts) {
     if (opts->nesterov != 0 && opts->nesterov != 1)
       return fail(MUON_ERR_INVALID_ARG, "opts->nesterov must be 0 or 1");
@@ -1514,6 +1589,7 @@ muon_status_t muon_step_ex(void* const* params, const void* const* grads, float*
     wd = opts->weight_decay;
     overlap = opts->overlap != 0;
     budget = opts->max_workspace_bytes;
+    scaleExp = opts->scale_exp;
   }
   if (count == 0) return MUON_OK;
   if (!params || !grads || !momentum || !rows || !cols)
@@ -1545,6 +1621,13 @@ muon_status_t muon_step_ex(void* const* params, const void* const* grads, float*
   if (overlaps(ranges, &oa, &ob))
     return fail(MUON_ERR_ALIAS, "tensors of matrices " + std::to_string(oa) + " and " +
                                     std::to_string(ob) + " overlap");
+  if (scaleExp) {
+    if ((uintptr_t)scaleExp & 3) return fail(MUON_ERR_INVALID_ARG, "opts->scale_exp not 4-byte aligned");
+    const uintptr_t lo = (uintptr_t)scaleExp, hi = lo + (uintptr_t)count * 4;
+    int who = 0;
+    if (workspace_overlaps(ranges, lo, hi, &who))
+      return fail(MUON_ERR_ALIAS, "opts->scale_exp overlaps a tensor of matrix " + std::to_string(who));
+  }
   StepLayout Lo;
   std::string e = step_layout(rows, cols, count, steps, coeffs, overlap, budget, &Lo);
   if (!e.empty()) return fail(budget > 0 ? MUON_ERR_WORKSPACE : MUON_ERR_INVALID_ARG, e);
@@ -1557,9 +1640,13 @@ muon_status_t muon_step_ex(void* const* params, const void* const* grads, float*
     int who = 0;
     if (workspace_overlaps(ranges, (uintptr_t)workspace, (uintptr_t)workspace + Lo.totalBytes, &who))
       return fail(MUON_ERR_ALIAS, "workspace overlaps a tensor of matrix " + std::to_string(who));
+    const uintptr_t lo = (uintptr_t)scaleExp, hi = lo + (uintptr_t)count * 4;
+    if (scaleExp && lo < (uintptr_t)workspace + Lo.totalBytes && (uintptr_t)workspace < hi)
+      return fail(MUON_ERR_ALIAS, "opts->scale_exp overlaps the workspace");
   }
   std::vector<CallerMat> cm(count);
   for (int i = 0; i < count; ++i) {
+    cm[i].hint = scaleExp ? scaleExp + i : nullptr;
     cm[i].src = momentum[i];
     cm[i].ldSrc = cols[i];
     cm[i].dst = params[i];

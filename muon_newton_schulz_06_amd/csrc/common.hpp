@@ -84,6 +84,10 @@ struct GemmSeg {
   //   EPI_SQ:   ylam = p2·u, ymu = p1·sIn (with p2 = 0 the launch has K = 0)
   float ylam, ymu;
   int32_t pad_;
+  // Fused operands (muon_step with carried exponents): per matrix of the
+  // segment, X₀ = rho[mat]·(the stored operand); the SYRK scales by rho²,
+  // the final product by rho.  Null: 1.
+  const float* rho;
 };
 
 struct GemmLaunch {
@@ -124,6 +128,13 @@ struct EwLaunch {
   EwMat mat[kMaxUser];
 };
 
+// Carried operand exponents (muon_step with scale_exp): a matrix whose
+// momentum pass wrote its fp16 operand as u·2^e keeps that operand when
+// ‖u‖·2^e lies in [2^kFuseLo, 2^kFuseHi]; the exponent written back for the
+// next step puts ‖u‖·2^e in [2^12, 2^13).  Entries outside
+// [-kFuseExpMax, kFuseExpMax] mean "unknown".
+constexpr int kFuseLo = 9, kFuseHi = 14, kFuseTarget = 13, kFuseExpMax = 100;
+
 struct NormLaunch {
   int32_t n;
   float eps;
@@ -132,6 +143,13 @@ struct NormLaunch {
   int64_t off[kMaxUser];
   int64_t cnt[kMaxUser];
   int32_t alphaIdx[kMaxUser];
+  // fused operands (null hint: the matrix was not fused)
+  float sX;                   // operand scale of the exact cast
+  int32_t pad_;
+  float* rho;                 // per matrix (rhoIdx): factor from the fused operand to X₀
+  int32_t* ok;                // per matrix (alphaIdx): 1 when the fused operand stands
+  int32_t* hint[kMaxUser];    // carried exponent, read and rewritten
+  int32_t rhoIdx[kMaxUser];
 };
 
 // Cast (scaled) + transpose into the two operand layouts.
@@ -147,6 +165,8 @@ struct CastMat {
   int32_t alphaIdx;
   int32_t tilesC;      // cp / kCastTile
   int64_t blockStart;
+  int32_t okIdx;       // ≥ 0: skip the matrix when ok[okIdx] (its fused operand stands)
+  int32_t pad_;
 };
 
 struct CastLaunch {
@@ -159,7 +179,44 @@ struct CastLaunch {
   float beta;
   int32_t pad_;
   const float* alpha;  // per-matrix 1 / (‖x‖_F + eps)
+  const int32_t* ok;   // per-matrix flags written by the norm finish (fused operands)
+  // 1: a small grid walks the tiles of every matrix whose fused operand
+  // failed its check (okIdx ≥ 0 and !ok), skipping the others whole; the
+  // matrices' blockStart is then the running sum of their tile counts
+  int32_t strided;
+  int32_t pad2_;
   CastMat mat[kMaxUser];
+};
+
+// Momentum fused with the operand cast: one tile of the stored matrix per
+// workgroup, M ← β·M + g, the tile's Σu², and, when the matrix's carried
+// exponent e is known, the fp16 operand u·2^e with its zero padding (stored
+// layout for wide matrices, transposed for tall ones).  Wide matrices take
+// 16×256 tiles (a wave reads 1 KiB of a row), tall ones 64×64 (the cast's
+// tile: 128-byte rows of the transposed operand; 64×128 tiles, with twice
+// the LDS per workgroup, measured 10% slower on the Qwen-shaped set).
+constexpr int kFuseWideR = 16, kFuseWideC = 256, kFuseTallR = 64, kFuseTallC = 64;
+
+struct MomCastMat {
+  const void* grad;     // stored rows × cols, contiguous
+  float* mom;           // momentum, read + written
+  void* xh;             // fp16 operand X₀: rp × cp (wide) or cp × rp (tall), padded
+  const int32_t* hint;  // carried exponent
+  int64_t rows, cols;
+  int32_t rp, cp;       // padded stored extents (multiples of 256)
+  int32_t tilesC;       // cp / tile width
+  int32_t tall;         // 1: X₀ is the transpose of the stored matrix
+  int64_t blockStart;
+  int64_t partialOff;   // one partial per tile
+};
+
+struct MomCastLaunch {
+  int32_t n;
+  int32_t gradDtype;    // muon_dtype_t
+  int32_t nesterov;     // 1: u = g + β·M' (else u = M')
+  float beta;
+  float* partials;
+  MomCastMat mat[kMaxUser];
 };
 
 

@@ -11,7 +11,13 @@
 //    fixed order (deterministic, no float atomics);
 //  * scaled cast: X₀ = α·sX·M rounded to the MFMA operand type, written in
 //    both the stored and the transposed layout (with zero padding to the
-//    tile), so every later product reads k-contiguous rows.
+//    tile), so every later product reads k-contiguous rows;
+//  * momentum fused with the cast, for callers that carry a power-of-two
+//    operand exponent e per matrix from the previous step: the momentum pass
+//    writes the fp16 operand as u·2^e directly (no second pass over the
+//    fp32 momentum), the norm finish checks that ‖u‖·2^e keeps it in range
+//    and hands the products the exact factor ρ = α·sX·2^(−e) (X₀ = ρ·u·2^e),
+//    and the cast runs only for matrices that fail the check.
 // Reductions use 64-lane wavefront shuffles, then one LDS slot per wave.
 #include <hip/hip_runtime.h>
 
@@ -167,6 +173,8 @@ __global__ __launch_bounds__(kEwThreads) void ew_kernel(const EwLaunch L) {
   }
 }
 
+__device__ __forceinline__ bool exp_known(int e) { return e >= -kFuseExpMax && e <= kFuseExpMax; }
+
 __global__ __launch_bounds__(256) void norm_kernel(const NormLaunch L) {
   const int i = blockIdx.x;
   const int tid = threadIdx.x;
@@ -179,7 +187,29 @@ __global__ __launch_bounds__(256) void norm_kernel(const NormLaunch L) {
   __syncthreads();
   if (tid == 0) {
     const double t = part[0] + part[1] + part[2] + part[3];
-    L.alpha[L.alphaIdx[i]] = (float)(1.0 / (sqrt(t) + (double)L.eps));
+    const double nrm = sqrt(t);
+    const float alpha = (float)(1.0 / (nrm + (double)L.eps));
+    L.alpha[L.alphaIdx[i]] = alpha;
+    int32_t* h = L.hint[i];
+    if (h) {
+      // The fused operand u·2^e stands when ‖u‖·2^e ∈ [2^kFuseLo, 2^kFuseHi]:
+      // every entry is then below 2^15 (|u_ij| ≤ ‖u‖) and the bulk of them far
+      // above fp16's subnormal range.  (A NaN norm fails the comparison.)
+      const int e = *h;
+      const bool known = exp_known(e);
+      const double x = known ? ldexp(nrm, e) : 0.0;
+      const bool ok = known && x >= ldexp(1.0, kFuseLo) && x <= ldexp(1.0, kFuseHi);
+      L.ok[L.alphaIdx[i]] = ok ? 1 : 0;
+      L.rho[L.rhoIdx[i]] = ok ? (alpha * L.sX) * ldexpf(1.f, -e) : 1.f;
+      // next step's exponent: ‖u‖ = f·2^q (f ∈ [0.5, 1)) → e' = kFuseTarget − q
+      int en = INT32_MIN;
+      if (nrm > 0.0 && nrm < 1e300) {
+        int q;
+        (void)frexp(nrm, &q);
+        if (exp_known(kFuseTarget - q)) en = kFuseTarget - q;
+      }
+      *h = en;
+    }
   }
 }
 
@@ -306,13 +336,161 @@ __device__ void cast_tile(const CastLaunch& L, const CastMat& C, int64_t t) {
 }
 
 __global__ __launch_bounds__(256) void cast_kernel(const CastLaunch L) {
+  if (L.strided) {
+    // fallback for fused operands: almost always every matrix is skipped
+    for (int mi = 0; mi < L.n; ++mi) {
+      const CastMat& C = L.mat[mi];
+      if (L.ok[C.okIdx]) continue;
+      const int64_t tiles = (int64_t)(C.rp / kCastTile) * C.tilesC;
+      for (int64_t t = blockIdx.x; t < tiles; t += gridDim.x) {
+        if (L.outOp == OP_F16) cast_tile<_Float16>(L, C, t);
+        else cast_tile<float>(L, C, t);
+        __syncthreads();  // the next tile reuses the LDS tile
+      }
+    }
+    return;
+  }
   const int64_t b = blockIdx.x;
   int mi = 0;
   while (mi + 1 < L.n && b >= L.mat[mi + 1].blockStart) ++mi;
   const CastMat& C = L.mat[mi];
+  if (C.okIdx >= 0 && L.ok[C.okIdx]) return;  // the momentum pass wrote the operand
   const int64_t t = b - C.blockStart;
   if (L.outOp == OP_F16) cast_tile<_Float16>(L, C, t);
   else cast_tile<float>(L, C, t);
+}
+
+// Momentum fused with the cast: one TR×TC tile of the stored matrix per
+// workgroup (TC/4 threads per row, each 4 consecutive columns of rows ty,
+// ty + RPI, …).  Elements outside rows × cols are not touched in M, add
+// nothing to Σu² and are written as 0 in the operand (so the padding needs
+// no other pass).  The operand is written only when the carried exponent is
+// known; otherwise the cast writes it after the norm finish.  TALL: the
+// operand is the transpose, staged through an fp32 LDS tile (pitch TC + 1)
+// and written as 16-byte runs of 8 consecutive stored rows.
+template <int TR, int TC, bool TALL, int GD, bool NEST>
+__device__ void momcast_tile(const MomCastLaunch& L, const MomCastMat& C, int64_t t) {
+  constexpr int TPR = TC / 4, RPI = 256 / TPR, Q = TR / RPI;
+  __shared__ float tile[TALL ? TR : 1][TALL ? TC + 1 : 1];
+  __shared__ float part[4];
+  const int tr = (int)(t / C.tilesC), tc = (int)(t - (int64_t)tr * C.tilesC);
+  const int tid = threadIdx.x;
+  const int tx = tid % TPR, ty = tid / TPR;
+  const int cl = 4 * tx;
+  const int64_t r0 = (int64_t)tr * TR, c0 = (int64_t)tc * TC;
+  const int e = *C.hint;
+  const bool wr = exp_known(e);
+  const float s2 = wr ? ldexpf(1.f, e) : 0.f;
+  const bool full = (r0 + TR <= C.rows) && (c0 + TC <= C.cols);
+  const bool vec = full && (C.cols % 4 == 0) && (((uintptr_t)C.mom & 15) == 0) &&
+                   (((uintptr_t)C.grad & (GD == 1 ? 7 : 15)) == 0);
+  float v[Q][4];
+  float ss = 0.f;
+  if (vec) {
+    // every load of the tile is issued before the first store (g and M may
+    // not be proven disjoint by the compiler)
+    f32x4 mq[Q], gq[Q];
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      const int64_t ix = (r0 + ty + RPI * q) * C.cols + c0 + cl;
+      gq[q] = load4<GD>(C.grad, ix);
+      mq[q] = *(const f32x4*)(C.mom + ix);
+    }
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const float mv = fmaf(L.beta, mq[q][c], gq[q][c]);
+        mq[q][c] = mv;
+        const float u = NEST ? fmaf(L.beta, mv, gq[q][c]) : mv;
+        v[q][c] = u;
+        ss += u * u;
+      }
+      *(f32x4*)(C.mom + (r0 + ty + RPI * q) * C.cols + c0 + cl) = mq[q];
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      const int64_t r = r0 + ty + RPI * q;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int64_t cc = c0 + cl + c;
+        float u = 0.f;
+        if (r < C.rows && cc < C.cols) {
+          const int64_t ix = r * C.cols + cc;
+          const float gv = load_as_f32(C.grad, ix, GD);
+          const float mv = fmaf(L.beta, C.mom[ix], gv);
+          C.mom[ix] = mv;
+          u = NEST ? fmaf(L.beta, mv, gv) : mv;
+          ss += u * u;
+        }
+        v[q][c] = u;
+      }
+    }
+  }
+  ss = wave_sum(ss);
+  if ((tid & 63) == 0) part[tid >> 6] = ss;
+  if (wr) {
+    if constexpr (TALL) {
+#pragma unroll
+      for (int q = 0; q < Q; ++q)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) tile[ty + RPI * q][cl + c] = v[q][c] * s2;
+    } else {
+      _Float16* S = (_Float16*)C.xh;
+#pragma unroll
+      for (int q = 0; q < Q; ++q) {
+        half4_t h;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) h[c] = (_Float16)(v[q][c] * s2);
+        *(half4_t*)(S + (r0 + ty + RPI * q) * C.cp + c0 + cl) = h;
+      }
+    }
+  }
+  __syncthreads();
+  if (tid == 0) L.partials[C.partialOff + t] = part[0] + part[1] + part[2] + part[3];
+  if constexpr (TALL) {
+    if (!wr) return;
+    // TC output rows of TR values: TR/8 runs of 8 per row
+    constexpr int RUNS = TR / 8;
+    _Float16* Tt = (_Float16*)C.xh;
+#pragma unroll
+    for (int p = 0; p < TC * RUNS / 256; ++p) {
+      const int id = p * 256 + tid;
+      const int cl2 = id / RUNS, rl0 = (id % RUNS) * 8;
+      half8_t h;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) h[k] = (_Float16)tile[rl0 + k][cl2];
+      *(half8_t*)(Tt + (c0 + cl2) * C.rp + r0 + rl0) = h;
+    }
+  }
+}
+
+template <int GD, bool NEST>
+__device__ __forceinline__ void momcast_any(const MomCastLaunch& L, const MomCastMat& C, int64_t t) {
+  if (C.tall) momcast_tile<kFuseTallR, kFuseTallC, true, GD, NEST>(L, C, t);
+  else momcast_tile<kFuseWideR, kFuseWideC, false, GD, NEST>(L, C, t);
+}
+
+__global__ __launch_bounds__(256) void momcast_kernel(const MomCastLaunch L) {
+  const int64_t b = blockIdx.x;
+  int mi = 0;
+  while (mi + 1 < L.n && b >= L.mat[mi + 1].blockStart) ++mi;
+  const MomCastMat& C = L.mat[mi];
+  const int64_t t = b - C.blockStart;
+  if (L.gradDtype == 1) {
+    if (L.nesterov) momcast_any<1, true>(L, C, t);
+    else momcast_any<1, false>(L, C, t);
+  } else {
+    if (L.nesterov) momcast_any<0, true>(L, C, t);
+    else momcast_any<0, false>(L, C, t);
+  }
+}
+
+hipError_t launch_momcast(const MomCastLaunch& L, int64_t blocks, hipStream_t st) {
+  if (blocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(momcast_kernel, dim3((unsigned)blocks), dim3(256), 0, st, L);
+  return hipGetLastError();
 }
 
 hipError_t launch_ew(const EwLaunch& L, int64_t blocks, hipStream_t st) {

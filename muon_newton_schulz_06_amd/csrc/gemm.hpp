@@ -329,6 +329,10 @@ __device__ __forceinline__ EpiArgs<T> make_epi(const GemmLaunch& L, const GemmSe
     E.user = L.user[k];
     E.userLd = L.userLd[k];
     E.lrsc = L.lrsc[k];
+    if (S.rho) E.lrsc *= S.rho[mat];  // O = Q·X₀ = ρ·Q·(stored operand)
+  }
+  if constexpr (EPI == EPI_SYRK) {
+    if (S.rho) E.u *= S.rho[mat] * S.rho[mat];  // G = ρ²·(stored operand)(stored operand)ᵀ
   }
   return E;
 }

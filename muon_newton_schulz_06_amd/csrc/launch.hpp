@@ -18,6 +18,9 @@ hipError_t launch_norm(const NormLaunch& L, hipStream_t st);
 // Scaled cast into the two operand layouts (and zero padding).
 hipError_t launch_cast(const CastLaunch& L, int64_t blocks, hipStream_t st);
 
+// Momentum fused with the operand cast (elementwise.hip).
+hipError_t launch_momcast(const MomCastLaunch& L, int64_t blocks, hipStream_t st);
+
 // Selected-row step: B = M + g with row scores; top-k per matrix; gather of
 // the selected block; scatter of the update and the buffer decay.
 hipError_t launch_sel_accum(const SelLaunch& L, int64_t blocks, hipStream_t st);

@@ -212,13 +212,26 @@ std::string build_plan(const int64_t* rows, const int64_t* cols, int count, int 
     }
   }
 
-  // partial sums of squares: one per elementwise workgroup
+  int rpos = 0;
+  for (BucketPlan& bp : P.buckets) {
+    bp.fusable = forStep && bp.op == OP_F16 && P.groups[bp.group].tile == 256;
+    bp.rhoStart = rpos;
+    for (int k = 0; k < (int)bp.mats.size(); ++k) P.mats[bp.mats[k]].rhoPos = rpos + k;
+    rpos += (int)bp.mats.size();
+  }
+
+  // partial sums of squares: one per elementwise workgroup (flat pass) or
+  // per 64×64 tile (fused pass)
   int64_t np = 0;
   for (MatPlan& mp : P.mats) {
     if (mp.empty) continue;
     mp.partialOff = np;
     mp.partialCnt = (mp.numel + kEwElems - 1) / kEwElems;
-    np += mp.partialCnt;
+    const BucketPlan& bp = P.buckets[mp.bucket];
+    if (bp.fusable)
+      mp.tileCnt = mp.tall ? (bp.Np / kFuseTallR) * (bp.Mp / kFuseTallC)
+                           : (bp.Mp / kFuseWideR) * (bp.Np / kFuseWideC);
+    np += std::max(mp.partialCnt, mp.tileCnt);
   }
   P.totalPartials = np;
 
@@ -226,6 +239,10 @@ std::string build_plan(const int64_t* rows, const int64_t* cols, int count, int 
   P.offPartials = off;
   off = align_up(off + size_t(np) * 4);
   P.offAlpha = off;
+  off = align_up(off + size_t(count) * 4);
+  P.offRho = off;
+  off = align_up(off + size_t(count) * 4);
+  P.offOk = off;
   off = align_up(off + size_t(count) * 4);
   for (GroupPlan& gp : P.groups) {
     gp.strideh = size_t(gp.Mp) * size_t(gp.Mp) * esz_of(gp.op);

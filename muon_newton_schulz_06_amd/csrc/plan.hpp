@@ -21,7 +21,11 @@ struct MatPlan {
   int group = -1;              // index into Plan::groups
   int posGroup = -1;
   int64_t numel = 0;
-  int64_t partialOff = 0, partialCnt = 0;
+  // partial sums of squares: partialCnt for the flat momentum / norm pass,
+  // tileCnt (64×64 tiles of the padded stored matrix) for the fused
+  // momentum + cast pass (fusable buckets only); max of both reserved
+  int64_t partialOff = 0, partialCnt = 0, tileCnt = 0;
+  int rhoPos = -1;             // position in bucket order (operand factor ρ)
 };
 
 // Matrices of one stored shape: they share the SYRK, cast and final launches.
@@ -39,6 +43,10 @@ struct BucketPlan {
   // The 128-tile kernel reads X₀ᵀ for the final product; the 256-tile kernel
   // reads X₀ through transposed panels, so its buckets keep X₀ alone.
   bool xT = true;
+  // Step plans: fp16 operand on the 256-tile path (X₀ alone), so the
+  // momentum pass can write the operand itself (carried exponents).
+  bool fusable = false;
+  int rhoStart = 0;         // bucket-order position of mats[0]
 };
 
 // Matrices of one Gram size m: they share every Gram-space launch.
@@ -78,6 +86,8 @@ struct Plan {
   std::vector<GroupPlan> groups;
   size_t offPartials = 0;
   size_t offAlpha = 0;
+  size_t offRho = 0;       // float per matrix, bucket order (fused operand factor ρ)
+  size_t offOk = 0;        // int32 per matrix, call order (fused operand stands)
   int64_t totalPartials = 0;
   size_t totalBytes = 0;
   ScalePlan scales;

@@ -22,7 +22,7 @@ import math
 
 import torch
 
-from . import QUINTIC, muon_step, muon_step_selected
+from . import QUINTIC, SCALE_EXP_UNKNOWN, muon_step, muon_step_selected
 
 
 class Muon(torch.optim.Optimizer):
@@ -43,11 +43,19 @@ class Muon(torch.optim.Optimizer):
                        orthogonalised and applied, the buffer keeps β·B there
                        and B elsewhere (not combinable with nesterov or
                        weight_decay; bf16 gradients are widened to fp32)
+    carry_exponents (optimiser-wide, default True): keep each matrix's
+                       power-of-two operand exponent between steps (state
+                       "operand_exp", an int32 scalar) and pass them as
+                       muon_step_ex's scale_exp, so the momentum pass writes
+                       the half-precision operand itself (no separate cast
+                       pass over the fp32 momentum after the first step)
     """
 
     def __init__(self, params, lr: float = 0.02, momentum: float = 0.95, nesterov: bool = False,
                  weight_decay: float = 0.0, ns_steps: int = 5, ns_coefficients=QUINTIC,
-                 eps: float = 1e-7, selected_fraction=None):
+                 eps: float = 1e-7, selected_fraction=None, carry_exponents: bool = True):
+        self._carry = bool(carry_exponents)
+        self._exp_bufs: dict = {}
         defaults = dict(lr=lr, momentum=momentum, nesterov=nesterov, weight_decay=weight_decay,
                         ns_steps=ns_steps, ns_coefficients=tuple(ns_coefficients), eps=eps,
                         selected_fraction=selected_fraction)
@@ -106,19 +114,52 @@ class Muon(torch.optim.Optimizer):
                                        coeffs=group["ns_coefficients"], eps=group["eps"],
                                        stream=stream)
                     continue
+                sx = self._exponents(ps, dev) if self._carry and dev.type == "cuda" else None
                 muon_step(ps, gs, ms, beta=group["momentum"], lr=group["lr"],
                           steps=group["ns_steps"], coeffs=group["ns_coefficients"],
                           eps=group["eps"], nesterov=group["nesterov"],
                           weight_decay=group["weight_decay"],
-                          stream=stream)
+                          stream=stream, scale_exp=sx)
         return loss
 
+    def _exponents(self, ps, dev):
+        """The carried exponents of one batched call as one int32 tensor whose
+        entries the parameters' states hold as views (so the library's
+        rewrite is the state).  Rebuilt from the states when the call's
+        parameters change or a state was loaded."""
+        key = tuple(id(p) for p in ps)
+        buf = self._exp_bufs.get(key)
+        if buf is not None:
+            ok = True
+            for k, p in enumerate(ps):
+                e = self.state[p].get("operand_exp")
+                if e is None or e.data_ptr() != buf[k].data_ptr():
+                    ok = False
+                    break
+            if ok:
+                return buf
+        held = [self.state[p].get("operand_exp") for p in ps]
+        if all(e is not None for e in held):
+            buf = torch.stack([e.to(device=dev, dtype=torch.int32).reshape(()) for e in held])
+        else:
+            buf = torch.full((len(ps),), SCALE_EXP_UNKNOWN, dtype=torch.int32, device=dev)
+            for k, e in enumerate(held):
+                if e is not None:
+                    buf[k] = e.to(device=dev, dtype=torch.int32).reshape(())
+        for k, p in enumerate(ps):
+            self.state[p]["operand_exp"] = buf[k]
+        self._exp_bufs[key] = buf
+        return buf
+
     def load_state_dict(self, state_dict):
-        """torch's loader casts floating-point state to the parameter dtype;
-        the momentum is fp32 state whatever the parameter dtype, so the saved
-        fp32 buffers are put back after the base class has loaded."""
+        """torch's loader casts state to the parameter dtype; the momentum is
+        fp32 state and the carried operand exponent int32 whatever the
+        parameter dtype, so the saved tensors are put back after the base
+        class has loaded."""
         saved = {pid: s["momentum_buffer"] for pid, s in state_dict["state"].items()
                  if isinstance(s, dict) and "momentum_buffer" in s}
+        exps = {pid: s["operand_exp"] for pid, s in state_dict["state"].items()
+                if isinstance(s, dict) and "operand_exp" in s}
         super().load_state_dict(state_dict)
         ids = itertools.chain.from_iterable(g["params"] for g in state_dict["param_groups"])
         params = itertools.chain.from_iterable(g["params"] for g in self.param_groups)
@@ -126,6 +167,9 @@ class Muon(torch.optim.Optimizer):
             if pid in saved:
                 self.state[p]["momentum_buffer"] = saved[pid].to(
                     device=p.device, dtype=torch.float32).contiguous()
+            if pid in exps:
+                self.state[p]["operand_exp"] = torch.as_tensor(exps[pid]).to(
+                    device=p.device, dtype=torch.int32).reshape(())
 
 
 def _check_hyper(h):

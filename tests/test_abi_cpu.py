@@ -40,7 +40,7 @@ def test_exports_every_declared_symbol():
     assert "muon_ns_batched" in names and "muon_step" in names
     for n in names:
         assert hasattr(L, n), n
-    assert mns.abi_version() == 6
+    assert mns.abi_version() == 7
 
 
 def test_library_binds_hip_runtime_only_by_soname():
@@ -243,6 +243,23 @@ def test_step_ex_scheduling_options():
     assert big < both
 
 
+def test_step_ex_scale_exp_checks():
+    """opts->scale_exp must be 4-byte aligned and overlap neither a tensor of
+    the call nor the workspace; a valid pointer passes every host check."""
+    O = mns.MuonStepOpts
+
+    def o(p):
+        return O(0, 0.0, 0, 0, 0, p)
+
+    assert _step_ex(o(0x5000001)) == 1 and "scale_exp" in _err()
+    assert _step_ex(o(0x3000000 + 8)) == 3 and "scale_exp" in _err()  # inside momentum[0]
+    assert _step_ex(o(0x100000000 + 64)) == 3 and "workspace" in _err()
+    st = _step_ex(o(0x5000000))
+    if not torch.cuda.is_available():
+        assert st == 6, _err()
+    assert mns.SCALE_EXP_UNKNOWN == -2**31
+
+
 def test_step_workspace_query_covers_both_schedules():
     """The query covers the single-plan layout and the overlapped layout of a
     large call (two chunks with a region each)."""
@@ -433,6 +450,7 @@ def test_selected_workspace_grows_with_the_fraction():
     # the fp32 selected blocks alone: k × n floats per matrix, k = ⌈ρ·m⌉
     blocks = sum(4 * math.ceil(0.25 * min(r, c)) * max(r, c) for r, c in shapes)
     assert sizes[1] >= blocks
-    assert mns.step_selected_workspace_size([(0, 5), (7, 0)], 0.5) <= 512   # no blocks, no scores
+    # no blocks, no scores: only the per-matrix scalars (α, ρ, flags), 256-byte aligned
+    assert mns.step_selected_workspace_size([(0, 5), (7, 0)], 0.5) <= 1024
     with pytest.raises(mns.MuonError):
         mns.step_selected_workspace_size(shapes, 0.0)

@@ -47,25 +47,35 @@ def _grads(ps, seed, step):
             for j, p in enumerate(ps)]
 
 
-def test_optimizer_equals_direct_library_call(mns):
+@pytest.mark.parametrize("carry", [True, False])
+def test_optimizer_equals_direct_library_call(mns, carry):
+    """Bitwise equal to muon_step on the same tensors, with the carried
+    operand exponents (the default) against muon_step with one scale_exp
+    buffer per call, and without them against the plain call."""
     ps = _model(71)
     ref_w = [p.detach().clone() for p in ps]
     ref_m = [torch.zeros(p.shape, dtype=torch.float32, device="cuda") for p in ps]
-    opt = mns.Muon(ps, lr=0.03, momentum=0.9, nesterov=True, weight_decay=0.05)
+    opt = mns.Muon(ps, lr=0.03, momentum=0.9, nesterov=True, weight_decay=0.05,
+                   carry_exponents=carry)
+    groups = {dt: [j for j, p in enumerate(ps) if p.dtype == dt] for dt in (torch.bfloat16, torch.float32)}
+    sx = {dt: mns.scale_exp_buffer(len(idx), "cuda") if carry else None for dt, idx in groups.items()}
     for step in range(3):
         gs = _grads(ps, 500, step)
         for p, g in zip(ps, gs):
             p.grad = g
         opt.step()
-        for dt in (torch.bfloat16, torch.float32):
-            idx = [j for j, p in enumerate(ps) if p.dtype == dt]
+        for dt, idx in groups.items():
             mns.muon_step([ref_w[j] for j in idx], [gs[j] for j in idx], [ref_m[j] for j in idx],
-                          beta=0.9, lr=0.03, nesterov=True, weight_decay=0.05)
+                          beta=0.9, lr=0.03, nesterov=True, weight_decay=0.05, scale_exp=sx[dt])
         torch.cuda.synchronize()
         for j, p in enumerate(ps):
             assert torch.equal(p.detach(), ref_w[j]), ("weights", step, j)
             assert torch.equal(opt.state[p]["momentum_buffer"], ref_m[j]), ("momentum", step, j)
-    say("optimizer == muon_step over 3 steps")
+        if carry:
+            for dt, idx in groups.items():
+                got = [int(opt.state[ps[j]]["operand_exp"]) for j in idx]
+                assert got == sx[dt].cpu().tolist(), ("exponents", step, dt)
+    say("optimizer == muon_step over 3 steps, carried exponents", carry)
 
 
 def test_optimizer_follows_the_oracle(mns):

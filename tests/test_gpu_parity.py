@@ -229,8 +229,11 @@ def test_run_to_run_bitwise_determinism(mns):
 
 # ------------------------------------------------------------------ muon_step
 def _check_step(mns, shapes, seed0, check_idx, nsteps=2, nesterov=False, weight_decay=0.0,
-                grad_dtype=torch.float32):
+                grad_dtype=torch.float32, fused=False):
     inp = W.muon_inputs(shapes, seed0, device="cuda")
+    # carried operand exponents: the first step casts and records them, the
+    # later ones have the momentum pass write the fp16 operand
+    sx = mns.scale_exp_buffer(len(shapes), "cuda") if fused else None
     host_W = [p.float().cpu().double().numpy() for p in inp.params]
     host_M = [m.cpu().numpy() for m in inp.momenta]
     lr32, wd32 = float(np.float32(0.02)), float(np.float32(weight_decay))
@@ -240,9 +243,9 @@ def _check_step(mns, shapes, seed0, check_idx, nsteps=2, nesterov=False, weight_
         grads = [g.to(grad_dtype) for g in grads]
         host_g = [g.float().cpu().numpy() for g in grads]
         say("muon_step", step, "over", len(shapes), "matrices", "nesterov", nesterov,
-            "weight_decay", weight_decay, "grads", grad_dtype)
+            "weight_decay", weight_decay, "grads", grad_dtype, "carried exponents", fused)
         mns.muon_step(inp.params, grads, inp.momenta, beta=0.95, lr=0.02, steps=5,
-                      nesterov=nesterov, weight_decay=weight_decay)
+                      nesterov=nesterov, weight_decay=weight_decay, scale_exp=sx)
         torch.cuda.synchronize()
         for j in range(len(shapes)):
             Mn = oracle.momentum_update(host_M[j], host_g[j], np.float32(0.95))
@@ -299,6 +302,26 @@ def test_muon_step_variants(mns, nesterov, weight_decay, grad_dtype):
         shapes.append((2304, 2304))  # the 256-tile kernels (weights prefetched in the update)
     _check_step(mns, shapes, 950, range(len(shapes)), nsteps=2, nesterov=nesterov,
                 weight_decay=weight_decay, grad_dtype=grad_dtype)
+
+
+@pytest.mark.parametrize("nesterov,weight_decay,grad_dtype", [
+    (False, 0.0, torch.float32),
+    (True, 0.1, torch.bfloat16),
+])
+def test_muon_step_carried_exponents(mns, nesterov, weight_decay, grad_dtype):
+    """muon_step with scale_exp over three steps (the first casts and records
+    the exponents, the later two take the operand the momentum pass wrote):
+    wide, tall and ragged shapes on the fp16 256-tile path next to an fp32
+    group and a 128-tile group, element by element against the oracle."""
+    shapes = [(300, 1200), (1100, 256), (96, 200), (384, 384), (600, 1500), (2304, 512),
+              (513, 2100), (1536, 1536), (1, 64)]
+    _check_step(mns, shapes, 970, range(len(shapes)), nsteps=3, nesterov=nesterov,
+                weight_decay=weight_decay, grad_dtype=grad_dtype, fused=True)
+
+
+def test_muon_step_qwen_layer_carried_exponents(mns):
+    shapes = W.qwen_layer_shapes()
+    _check_step(mns, shapes, 4003, check_idx=[1, 0], nsteps=2, fused=True)
 
 
 def test_muon_step_fp32_params_expose_the_update(mns):
