@@ -259,9 +259,14 @@ def other_configs(mns, W, torch):
     out[-1]["ms_isolated_call"] = iso[len(iso) // 2]
     shapes = W.qwen_model_shapes(1)
     inp = W.muon_inputs(shapes, 4001, device="cuda")
-    out.append(entry("one Qwen2.5-7B layer muon_step",
-                     timed(lambda: mns.muon_step(inp.params, inp.grads, inp.momenta, steps=5), 10),
-                     shapes, MFMA_PEAK_F16, "muon_step"))
+    plain = timed(lambda: mns.muon_step(inp.params, inp.grads, inp.momenta, steps=5), 10)
+    # as a training loop runs it: operand exponents carried from step to step
+    # (the untimed first call of `timed` records them)
+    sx = mns.scale_exp_buffer(len(shapes), "cuda")
+    carried = timed(lambda: mns.muon_step(inp.params, inp.grads, inp.momenta, steps=5, scale_exp=sx), 10)
+    out.append(entry("one Qwen2.5-7B layer muon_step", carried, shapes, MFMA_PEAK_F16,
+                     "muon_step, operand exponents carried across steps (scale_exp)"))
+    out[-1]["ms_without_carried_exponents"] = plain
     del inp
     torch.cuda.empty_cache()
     return out, samples
