@@ -300,9 +300,17 @@ std::string Plan::json() const {
       << (bp.op == OP_F32 ? "f32" : "f16") << "\",\"x_transposed_copy\":" << (bp.xT ? "true" : "false")
       << ",\"group\":"
       << bp.group << ",\"Mp\":" << bp.Mp << ",\"Np\":" << bp.Np << ",\"gram_start\":"
-      << bp.gramStart << ",\"mats\":[";
+      << bp.gramStart << ",\"fusable\":" << (bp.fusable ? "true" : "false")
+      << ",\"rho_start\":" << bp.rhoStart << ",\"mats\":[";
     for (size_t k = 0; k < bp.mats.size(); ++k) o << (k ? "," : "") << bp.mats[k];
     o << "]}";
+  }
+  o << "],\"mats\":[";
+  for (size_t i = 0; i < mats.size(); ++i) {
+    const MatPlan& mp = mats[i];
+    o << (i ? "," : "") << "{\"empty\":" << (mp.empty ? "true" : "false") << ",\"bucket\":" << mp.bucket
+      << ",\"partial_off\":" << mp.partialOff << ",\"partial_cnt\":" << mp.partialCnt
+      << ",\"tile_cnt\":" << mp.tileCnt << ",\"rho_pos\":" << mp.rhoPos << "}";
   }
   o << "],\"scales\":{\"sA\":[";
   for (size_t k = 0; k < scales.sA.size(); ++k) o << (k ? "," : "") << scales.sA[k];
