@@ -116,3 +116,34 @@ def test_overlapped_step_graph_replays_match_eager(mns):
         say("replay", step)
         assert_same(gp, eager[step][0], "weights")
         assert_same(gm, eager[step][1], "momentum")
+
+
+def test_schedules_with_carried_exponents_bitwise(mns):
+    """With carried operand exponents too, a matrix's result depends only on
+    its own exponent and its Gram group's configuration: the budgeted
+    chunks (every matrix its own chunk) and the overlapped schedule equal one
+    plan bit for bit over three steps (the first casts, the later two take the
+    fused operand), exponents included."""
+    shapes = W.qwen_layer_shapes()
+    budget = max(mns.step_workspace_size([s]) for s in shapes)
+    base = W.muon_inputs(shapes, 6401, device="cuda")
+    runs = {name: (clone(base), mns.scale_exp_buffer(len(shapes), "cuda"))
+            for name in ("one plan", "budget", "overlap")}
+    for step in range(3):
+        g = base.grads if step == 0 else W.fresh_grads(shapes, 6401, step, device="cuda")
+        for name, ((p, _, m), sx) in runs.items():
+            say(name, "step", step)
+            kw = {}
+            if name == "budget":
+                kw = dict(workspace=torch.empty(budget, dtype=torch.uint8, device="cuda"),
+                          max_workspace_bytes=budget)
+            elif name == "overlap":
+                kw = dict(overlap=True)
+            mns.muon_step(p, [x.clone() for x in g], m, scale_exp=sx, **kw)
+        torch.cuda.synchronize()
+        (p0, _, m0), x0 = runs["one plan"]
+        for name in ("budget", "overlap"):
+            (p, _, m), sx = runs[name]
+            assert_same(p, p0, name + " weights")
+            assert_same(m, m0, name + " momentum")
+            assert torch.equal(sx, x0), (name, "exponents", step)

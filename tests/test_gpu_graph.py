@@ -91,3 +91,45 @@ def test_selected_step_graph_replays_match_eager(mns):
         for j in range(len(shapes)):
             assert torch.equal(gp[j], eager[step][0][j]), ("weights", step, j)
             assert torch.equal(gm[j], eager[step][1][j]), ("buffer", step, j)
+
+
+def test_muon_step_with_carried_exponents_graph_replays_match_eager(mns):
+    """With scale_exp the call reads and rewrites the exponent array on the
+    device only, so the captured step carries the exponents from replay to
+    replay: three replays (the first casts, the later two take the fused
+    operand) equal three eager steps bit for bit, exponents included."""
+    shapes = [(256, 1024), (1024, 256), (128, 128), (512, 3584), (3584, 512), (300, 700)]
+    base = W.muon_inputs(shapes, 124, device="cuda")
+    ws = torch.empty(mns.step_workspace_size(shapes), dtype=torch.uint8, device="cuda")
+
+    def clone(inp):
+        return ([p.clone() for p in inp.params], [g.clone() for g in inp.grads],
+                [m.clone() for m in inp.momenta])
+
+    ep, eg, em = clone(base)
+    ex = mns.scale_exp_buffer(len(shapes), "cuda")
+    eager = []
+    for _ in range(3):
+        mns.muon_step(ep, eg, em, workspace=ws, scale_exp=ex)
+        eager.append(([p.clone() for p in ep], [m.clone() for m in em], ex.clone()))
+    torch.cuda.synchronize()
+
+    gp, gg, gm = clone(base)
+    gx = mns.scale_exp_buffer(len(shapes), "cuda")
+    ws2 = torch.empty_like(ws)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        mns.muon_step(gp, gg, gm, workspace=ws2, scale_exp=gx)
+    assert all(torch.equal(p, q) for p, q in zip(gp, base.params))
+    assert int(gx[0]) == mns.SCALE_EXP_UNKNOWN
+    for step in range(3):
+        graph.replay()
+        torch.cuda.synchronize()
+        junk = torch.randn(1 << 20, device="cuda").sum()
+        torch.cuda.synchronize()
+        assert torch.isfinite(junk)
+        assert torch.equal(gx, eager[step][2]), ("exponents", step)
+        for j in range(len(shapes)):
+            assert torch.equal(gp[j], eager[step][0][j]), ("weights", step, j)
+            assert torch.equal(gm[j], eager[step][1][j]), ("momentum", step, j)
