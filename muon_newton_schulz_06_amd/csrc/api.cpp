@@ -217,6 +217,9 @@ struct StepVariant {
   // 1: each matrix's Σx² is already in its first partial (the selected
   // step's top-k writes it), so the sum-of-squares pass is skipped
   int presummed = 0;
+  // passes enqueue_passes runs: bit 0 momentum / sum of squares, bit 1 norm
+  // finish, bit 2 cast
+  int stages = 7;
 };
 
 template <typename T>
@@ -259,8 +262,8 @@ muon_status_t enqueue_passes(const Plan& P, const std::vector<CallerMat>& cm, in
     (fused[i] ? fz : flat).push_back(i);
   }
 
-  // 1a. momentum fused with the cast (64×64 tiles of the padded stored matrix)
-  for (size_t c0 = 0; c0 < fz.size(); c0 += kMaxUser) {
+  // 1a. momentum fused with the cast (tiles of the padded stored matrix)
+  for (size_t c0 = 0; c0 < ((V.stages & 1) ? fz.size() : 0); c0 += kMaxUser) {
     MomCastLaunch L;
     std::memset(&L, 0, sizeof(L));
     L.gradDtype = V.gradDtype;
@@ -296,7 +299,7 @@ muon_status_t enqueue_passes(const Plan& P, const std::vector<CallerMat>& cm, in
   }
 
   // 1b. momentum / sum of squares
-  for (size_t c0 = 0; c0 < (V.presummed ? 0 : flat.size()); c0 += kMaxUser) {
+  for (size_t c0 = 0; c0 < ((V.presummed || !(V.stages & 1)) ? 0 : flat.size()); c0 += kMaxUser) {
     EwLaunch L;
     std::memset(&L, 0, sizeof(L));
     L.mode = P.forStep ? 0 : 1;
@@ -337,7 +340,7 @@ muon_status_t enqueue_passes(const Plan& P, const std::vector<CallerMat>& cm, in
     if (s != MUON_OK) return s;
   }
   // 2. alpha
-  for (size_t c0 = 0; c0 < live.size(); c0 += kMaxUser) {
+  for (size_t c0 = 0; c0 < ((V.stages & 2) ? live.size() : 0); c0 += kMaxUser) {
     NormLaunch L;
     std::memset(&L, 0, sizeof(L));
     L.eps = eps;
@@ -365,7 +368,7 @@ muon_status_t enqueue_passes(const Plan& P, const std::vector<CallerMat>& cm, in
   // 3. cast into both operand layouts (one launch sequence per operand type)
   // Fused matrices go through the strided fallback launch (a small grid that
   // casts only the matrices whose fused operand failed its check).
-  for (int strided = 0; strided < 2; ++strided)
+  for (int strided = 0; strided < ((V.stages & 4) ? 2 : 0); ++strided)
   for (int op : {(int)OP_F16, (int)OP_F32}) {
   std::vector<int> castMats;
   for (int i : (strided ? fz : flat))
@@ -1298,14 +1301,14 @@ muon_status_t enqueue_selected(const SelLayout& Lo, void* const* params, const f
         ((uintptr_t)params[i] & (4 * psz - 1)))
       vec = 0;
 
-  auto fill = [&](SelLaunch& L, size_t c0, size_t cn) {
+  auto fill_from = [&](SelLaunch& L, const std::vector<int>& lst, size_t c0, size_t cn) {
     std::memset(&L, 0, sizeof(L));
     L.n = (int)cn;
     L.paramDtype = paramDtype;
     L.beta = beta;
     L.vec = vec;
     for (size_t q = 0; q < cn; ++q) {
-      const int i = live[c0 + q];
+      const int i = lst[c0 + q];
       const SelMatLayout& s = Lo.mats[i];
       SelMat& M = L.mat[q];
       M.g = grads[i];
@@ -1325,6 +1328,7 @@ muon_status_t enqueue_selected(const SelLayout& Lo, void* const* params, const f
       M.lrsc = (float)(lr * std::sqrt(std::max(1.0, (double)rows[i] / (double)cols[i])));
     }
   };
+  auto fill = [&](SelLaunch& L, size_t c0, size_t cn) { fill_from(L, live, c0, cn); };
   // 1. B = M + g and the row scores
   for (size_t c0 = 0; c0 < live.size(); c0 += kMaxUser) {
     SelLaunch L;
@@ -1343,7 +1347,7 @@ muon_status_t enqueue_selected(const SelLayout& Lo, void* const* params, const f
                              [&] { return launch_sel_accum(L, blocks, st); });
     if (s != MUON_OK) return s;
   }
-  // 2. top-k per matrix, 3. gather
+  // 2. top-k per matrix
   for (size_t c0 = 0; c0 < live.size(); c0 += kMaxUser) {
     SelLaunch L;
     const size_t cn = std::min(live.size() - c0, (size_t)kMaxUser);
@@ -1353,18 +1357,10 @@ muon_status_t enqueue_selected(const SelLayout& Lo, void* const* params, const f
       bytes += 4.0 * L.mat[q].nChunks * (double)L.mat[q].m + 4.0 * L.mat[q].k + 4.0 * L.mat[q].m;
     muon_status_t s = Lr.run(9, bytes, "selected top-k kernel", [&] { return launch_sel_topk(L, st); });
     if (s != MUON_OK) return s;
-    int64_t blocks = 0;
-    bytes = 0;
-    for (size_t q = 0; q < cn; ++q) {
-      SelMat& M = L.mat[q];
-      M.blockStart = blocks;
-      blocks += ((M.tall ? M.rows : (int64_t)M.k) + 3) / 4;
-      bytes += 12.0 * (double)(M.tall ? M.rows : M.k) * (double)(M.tall ? M.k : M.cols);
-    }
-    s = Lr.run(10, bytes, "selected gather kernel", [&] { return launch_sel_gather(L, blocks, st); });
-    if (s != MUON_OK) return s;
   }
-  // 4. orthogonalise every block in place
+  // 3. the blocks' norms (the top-k wrote ‖B_S‖²_F), then the gather: blocks
+  // on the fp16 256-tile path have the gather write their operand directly
+  // (no fp32 copy, no cast pass); the others are copied and cast.
   std::vector<CallerMat> cm(count);
   for (int i = 0; i < count; ++i) {
     const SelMatLayout& s = Lo.mats[i];
@@ -1377,7 +1373,72 @@ muon_status_t enqueue_selected(const SelLayout& Lo, void* const* params, const f
   }
   StepVariant V;
   V.presummed = 1;  // ‖B_S‖²_F = Σ of the selected scores, written by the top-k
-  muon_status_t s = enqueue(Lo.ns, cm, MUON_DTYPE_F32, MUON_DTYPE_F32, 0.f, eps, V, ws, st);
+  V.stages = 2;     // norm finish only
+  muon_status_t s = enqueue_passes(Lo.ns, cm, MUON_DTYPE_F32, 0.f, eps, V, ws, st);
+  if (s != MUON_OK) return s;
+  std::vector<int> direct, copied;
+  for (int i : live) {
+    const BucketPlan& bp = Lo.ns.buckets[Lo.ns.mats[i].bucket];
+    (bp.op == OP_F16 && !bp.xT ? direct : copied).push_back(i);
+  }
+  for (size_t c0 = 0; c0 < copied.size(); c0 += kMaxUser) {
+    SelLaunch L;
+    const size_t cn = std::min(copied.size() - c0, (size_t)kMaxUser);
+    fill_from(L, copied, c0, cn);
+    int64_t blocks = 0;
+    double bytes = 0;
+    for (size_t q = 0; q < cn; ++q) {
+      SelMat& M = L.mat[q];
+      M.blockStart = blocks;
+      blocks += ((M.tall ? M.rows : (int64_t)M.k) + 3) / 4;
+      bytes += 12.0 * (double)(M.tall ? M.rows : M.k) * (double)(M.tall ? M.k : M.cols);
+    }
+    s = Lr.run(10, bytes, "selected gather kernel", [&] { return launch_sel_gather(L, blocks, st); });
+    if (s != MUON_OK) return s;
+  }
+  int gvec = 1;
+  for (int i : direct)
+    if ((cols[i] & 3) || ((uintptr_t)momentum[i] & 15)) gvec = 0;
+  for (size_t c0 = 0; c0 < direct.size(); c0 += kMaxUser) {
+    SelCastLaunch L;
+    std::memset(&L, 0, sizeof(L));
+    const size_t cn = std::min(direct.size() - c0, (size_t)kMaxUser);
+    L.n = (int)cn;
+    L.beta = beta;
+    L.sX = Lo.ns.scales.sX;
+    L.vec = gvec;
+    L.alpha = at<float>(ws, Lo.ns.offAlpha);
+    int64_t blocks = 0;
+    double bytes = 0;
+    for (size_t q = 0; q < cn; ++q) {
+      const int i = direct[c0 + q];
+      const SelMatLayout& sl = Lo.mats[i];
+      const MatPlan& mp = Lo.ns.mats[i];
+      const BucketPlan& bp = Lo.ns.buckets[mp.bucket];
+      SelCastMat& M = L.mat[q];
+      M.mom = momentum[i];
+      M.idx = at<int32_t>(ws, sl.offIdx);
+      M.x0 = at<_Float16>(ws, bp.offXh + bp.strideX * mp.posBucket);
+      M.rows = rows[i];
+      M.cols = cols[i];
+      M.k = (int32_t)sl.k;
+      M.tall = sl.tall;
+      M.Mp = (int32_t)bp.Mp;
+      M.Np = (int32_t)bp.Np;
+      M.alphaIdx = i;
+      M.blockStart = blocks;
+      blocks += sl.tall ? (int64_t)(bp.Mp / 64) * (bp.Np / 64) : (int64_t)(bp.Mp + 3) / 4;
+      bytes += 12.0 * (double)sl.k * (double)(sl.tall ? rows[i] : cols[i]) + 2.0 * (double)bp.Mp * (double)bp.Np;
+    }
+    s = Lr.run(10, bytes, "selected gather + cast kernel",
+               [&] { return launch_sel_gather_cast(L, blocks, st); });
+    if (s != MUON_OK) return s;
+  }
+  // 4. cast the copied blocks, orthogonalise every block in place
+  V.stages = 4;
+  s = enqueue_passes(Lo.ns, cm, MUON_DTYPE_F32, 0.f, eps, V, ws, st, &copied);
+  if (s != MUON_OK) return s;
+  s = enqueue_products(Lo.ns, cm, MUON_DTYPE_F32, V, ws, st);
   if (s != MUON_OK) return s;
   // 5. scatter the update (the gather has already decayed the buffer on S)
   for (size_t c0 = 0; c0 < live.size(); c0 += kMaxUser) {

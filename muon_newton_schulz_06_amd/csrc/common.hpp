@@ -252,4 +252,29 @@ struct SelLaunch {
   SelMat mat[kMaxUser];
 };
 
+// Gather of the selected block fused with its operand cast (blocks whose
+// Gram group runs fp16 on the 256-tile path): the operand X₀ = α·sX·B_S (the
+// k selected rows of the oriented view) is written directly, padded to
+// Mp × Np with zeros, and the buffer keeps β·B_S on S.  No fp32 copy of the
+// block is made (the block's fp32 buffer then only receives the product).
+struct SelCastMat {
+  float* mom;           // B = M + g (rows × cols), decayed on S
+  const int32_t* idx;   // the k selected indices along the short side, ascending
+  _Float16* x0;         // operand: Mp × Np, row stride Np
+  int64_t rows, cols;
+  int32_t k, tall;
+  int32_t Mp, Np;       // padded operand extents (multiples of 256)
+  int32_t alphaIdx;     // α of the block (norm finish)
+  int32_t pad_;
+  int64_t blockStart;   // wide: Mp / 4 workgroups (a wave per operand row); tall: (Mp/64)·(Np/64) tiles
+};
+struct SelCastLaunch {
+  int32_t n;
+  float beta;
+  float sX;
+  int32_t vec;          // 1: cols % 4 == 0 and 16-byte aligned rows (wide blocks)
+  const float* alpha;
+  SelCastMat mat[kMaxUser];
+};
+
 }  // namespace muon

@@ -26,6 +26,7 @@ hipError_t launch_momcast(const MomCastLaunch& L, int64_t blocks, hipStream_t st
 hipError_t launch_sel_accum(const SelLaunch& L, int64_t blocks, hipStream_t st);
 hipError_t launch_sel_topk(const SelLaunch& L, hipStream_t st);
 hipError_t launch_sel_gather(const SelLaunch& L, int64_t blocks, hipStream_t st);
+hipError_t launch_sel_gather_cast(const SelCastLaunch& L, int64_t blocks, hipStream_t st);
 hipError_t launch_sel_scatter(const SelLaunch& L, int64_t blocks, hipStream_t st);
 
 // Library state shared across translation units (implemented in api.cpp):

@@ -388,6 +388,94 @@ __global__ __launch_bounds__(kSelThreads) void sel_gather_kernel(const SelLaunch
 }
 
 // ---------------------------------------------------------------------------
+// Gather fused with the operand cast (blocks on the fp16 256-tile path).  The
+// operand values are those the cast would write from the fp32 block: the
+// same fp32 product v·(α·sX), rounded to fp16.
+//  * wide: a wave per operand row i: row idx[i] of B for i < k (the buffer
+//    decayed as it is read), zeros for the padding rows and columns;
+//  * tall: the operand is the block's transpose; a 64×64 tile of (stored
+//    rows, selections) is gathered — a wave reads 64 selected columns of one
+//    row — staged in LDS (pitch 65) and written as 16-byte runs of 8
+//    operand columns.
+typedef _Float16 half4s __attribute__((ext_vector_type(4)));
+typedef _Float16 half8s __attribute__((ext_vector_type(8)));
+
+__global__ __launch_bounds__(kSelThreads) void sel_gather_cast_kernel(const SelCastLaunch L) {
+  const int64_t b = blockIdx.x;
+  int mi = 0;
+  while (mi + 1 < L.n && b >= L.mat[mi + 1].blockStart) ++mi;
+  const SelCastMat& S = L.mat[mi];
+  const int64_t t = b - S.blockStart;
+  const float scale = L.alpha[S.alphaIdx] * L.sX;
+  const int tid = threadIdx.x, lane = tid & 63;
+  if (!S.tall) {
+    const int64_t i = t * (kSelThreads / 64) + (tid >> 6);
+    if (i >= S.Mp) return;
+    _Float16* dst = S.x0 + i * S.Np;
+    if (i >= S.k) {
+      for (int64_t c = (int64_t)lane * 8; c < S.Np; c += 512) *(half8s*)(dst + c) = half8s{};
+      return;
+    }
+    float* src = S.mom + (int64_t)S.idx[i] * S.cols;
+    if (L.vec) {
+      for (int64_t c0 = (int64_t)lane * 4; c0 < S.Np; c0 += 4 * 256) {
+        f32x4 v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int64_t c = c0 + q * 256;
+          v[q] = c < S.cols ? *(const f32x4*)(src + c) : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int64_t c = c0 + q * 256;
+          if (c >= S.Np) continue;
+          half4s h;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) h[e] = (_Float16)(v[q][e] * scale);
+          *(half4s*)(dst + c) = h;
+          if (c < S.cols) *(f32x4*)(src + c) = L.beta * v[q];
+        }
+      }
+    } else {
+      for (int64_t c = lane; c < S.Np; c += 64) {
+        const float v = c < S.cols ? src[c] : 0.f;
+        dst[c] = (_Float16)(v * scale);
+        if (c < S.cols) src[c] = L.beta * v;
+      }
+    }
+    return;
+  }
+  __shared__ float tile[64][65];  // [selection][stored row]
+  const int tilesN = S.Np / 64;
+  const int64_t s0 = (t / tilesN) * 64, r0 = (t % tilesN) * 64;
+  const int w = tid >> 6;
+  const int64_t s = s0 + lane;
+  const bool sel = s < S.k;
+  const int64_t col = sel ? S.idx[s] : 0;
+#pragma unroll 4
+  for (int q = 0; q < 16; ++q) {
+    const int64_t r = r0 + w + 4 * q;
+    float v = 0.f;
+    if (sel && r < S.rows) {
+      float* p = S.mom + r * S.cols + col;
+      v = *p;
+      *p = L.beta * v;
+    }
+    tile[lane][w + 4 * q] = v * scale;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int id = p * 256 + tid;
+    const int sl = id >> 3, rl0 = (id & 7) * 8;
+    half8s h;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) h[e] = (_Float16)tile[sl][rl0 + e];
+    *(half8s*)(S.x0 + (s0 + sl) * S.Np + r0 + rl0) = h;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Scatter: W_S ← round(W_S − lrsc·O_S), one wave per row of the block.
 //  * wide: block row i → stored row idx[i], a contiguous row update;
 //  * tall: block row r → stored row r at the selected columns.  The row is
@@ -530,6 +618,12 @@ hipError_t launch_sel_topk(const SelLaunch& L, hipStream_t st) {
 hipError_t launch_sel_gather(const SelLaunch& L, int64_t blocks, hipStream_t st) {
   if (blocks <= 0) return hipSuccess;
   hipLaunchKernelGGL(sel_gather_kernel, dim3((unsigned)blocks), dim3(kSelThreads), 0, st, L);
+  return hipGetLastError();
+}
+
+hipError_t launch_sel_gather_cast(const SelCastLaunch& L, int64_t blocks, hipStream_t st) {
+  if (blocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(sel_gather_cast_kernel, dim3((unsigned)blocks), dim3(kSelThreads), 0, st, L);
   return hipGetLastError();
 }
 
