@@ -67,6 +67,50 @@ def test_qwen_full_set_sampled(mns):
         assert frac <= expect
 
 
+def test_qwen_full_set_carried_exponents_sampled(mns):
+    """The benchmark's timed configuration: steps over the 196 matrices with
+    operand exponents carried from step to step (the first step records them,
+    the second has the momentum pass write the fp16 operands).  After the
+    second step (fresh gradients) one matrix of every shape is checked: the
+    momentum to fp32 rounding of the oracle's, every exponent of a fusable
+    matrix known, and every updated bf16 weight as in the one-step test."""
+    shapes = W.qwen_model_shapes(28)
+    say("generating the 196-matrix set")
+    inp = W.muon_inputs(shapes, 5001, device="cuda")
+    sx = mns.scale_exp_buffer(len(shapes), "cuda")
+    sample = [(3, 0), (17, 1), (26, 2), (8, 3), (22, 4), (1, 5), (14, 6)]  # (layer, shape index)
+    idx = [7 * layer + j for layer, j in sample]
+    say("first muon_step over 196 matrices (records the exponents)")
+    mns.muon_step(inp.params, inp.grads, inp.momenta, beta=0.95, lr=0.02, steps=5, scale_exp=sx)
+    torch.cuda.synchronize()
+    assert all(-100 <= e <= 100 for e in sx.cpu().tolist()), "an exponent was not recorded"
+    g2 = W.fresh_grads(shapes, 5001, 1, device="cuda")
+    host_W = {i: inp.params[i].float().cpu().double().numpy() for i in idx}
+    host_M = {i: inp.momenta[i].cpu().numpy() for i in idx}
+    host_g = {i: g2[i].cpu().numpy() for i in idx}
+    say("second muon_step over 196 matrices (fused operands)")
+    mns.muon_step(inp.params, g2, inp.momenta, beta=0.95, lr=0.02, steps=5, scale_exp=sx)
+    torch.cuda.synchronize()
+    c32 = tuple(float(np.float32(v)) for v in oracle.QUINTIC)
+    lr32 = float(np.float32(0.02))
+    got_W = {i: inp.params[i].float().cpu().double().numpy() for i in idx}
+    got_M = {i: inp.momenta[i].cpu().numpy() for i in idx}
+    del inp, g2
+    torch.cuda.empty_cache()
+    for i in idx:
+        r, c = shapes[i]
+        Mn = oracle.momentum_update(host_M[i], host_g[i], np.float32(0.95))
+        ulp = np.spacing(np.abs(Mn).astype(np.float32))
+        assert np.all(np.abs(got_M[i].astype(np.float64) - Mn) <= ulp), ("momentum", i)
+        O = oracle.muon_orthogonalize(got_M[i].astype(np.float64), c32, 5, 1e-7)
+        lrsc = lr32 * oracle.lr_shape_scale(r, c)
+        ok, frac, expect = weights_consistent(host_W[i], got_W[i], O, lrsc)
+        say("matrix", i, shapes[i], "weights consistent", ok, "fraction != oracle rounding", frac,
+            "bound", expect)
+        assert ok
+        assert frac <= expect
+
+
 def test_maximum_gram_size_block_diagonal(mns):
     """m = 32768 (the largest Gram size accepted), n = 131072, bf16: 128
     diagonal blocks of 256×1024 N(0,1) values, zeros elsewhere.  Frobenius
