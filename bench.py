@@ -107,12 +107,15 @@ def gram_flops(shapes, steps=5):
     return tot
 
 
-def parity_probe(mns, W, torch):
+def parity_probe(mns, W, torch, carried=True):
     """GPU side of the parity figure of the main workload: one muon_step over
     the matrices of layer 0 (the shapes, seeds and kernels of the benchmark;
     each matrix's result does not depend on the batch it is in) with fp32
     weights at zero and zero momentum, so W' = −lr·sc·O exposes the
-    orthogonalised update O itself.  Run outside the timed region."""
+    orthogonalised update O itself.  With carried operand exponents (the
+    benchmark's timed configuration) an identical step first records them,
+    weights and momenta are reset, and the measured step has the momentum
+    pass write the fp16 operands.  Run outside the timed region."""
     import numpy as np
     layer = W.qwen_model_shapes(1)
     # drawn on the CPU, as the oracle's inputs are (the device generator draws
@@ -121,7 +124,12 @@ def parity_probe(mns, W, torch):
     inp.params = [torch.zeros_like(p, device="cuda") for p in inp.params]
     inp.grads = [g.cuda() for g in inp.grads]
     inp.momenta = [m.cuda() for m in inp.momenta]
-    mns.muon_step(inp.params, inp.grads, inp.momenta, beta=0.95, lr=0.02, steps=5)
+    sx = mns.scale_exp_buffer(len(layer), "cuda") if carried else None
+    if carried:
+        mns.muon_step(inp.params, inp.grads, inp.momenta, beta=0.95, lr=0.02, steps=5, scale_exp=sx)
+        for t in inp.params + inp.momenta:
+            t.zero_()
+    mns.muon_step(inp.params, inp.grads, inp.momenta, beta=0.95, lr=0.02, steps=5, scale_exp=sx)
     torch.cuda.synchronize()
     lr32 = float(np.float32(0.02))
     out = []
@@ -133,7 +141,7 @@ def parity_probe(mns, W, torch):
     return out
 
 
-def cpu_baseline(probe=None, samples=None, budget_s=15.0):
+def cpu_baseline(probe=None, samples=None, budget_s=15.0, carried=True):
     """The oracle as it stands, on a bounded sample of the workload: the
     matrices of layer 0 in the order k, q, down, v, o, gate, up, one full
     muon_step each (momentum, fp64 standard Newton–Schulz, update), until
@@ -181,7 +189,9 @@ def cpu_baseline(probe=None, samples=None, budget_s=15.0):
         parity["qwen_full"] = {
             "max_rel_err": max(errs), "tol": 2e-2, "matrices": done,
             "how": "update O of one muon_step from zero momentum, recovered from fp32 weights "
-                   "at zero, against the oracle's O (relative Frobenius error), layer-0 matrices"}
+                   "at zero, against the oracle's O (relative Frobenius error), layer-0 matrices"
+                   + ("; the step runs as timed (operand exponents carried from an identical earlier step)"
+                      if carried else "")}
     for name, items in (samples or {}).items():
         e = []
         for x, out, steps, coeffs, tol in items:
@@ -465,7 +475,7 @@ def main():
     torch.cuda.empty_cache()
     probe = None
     if not args.no_cpu_baseline and args.workload == "qwen_full":
-        probe = parity_probe(mns, W, torch)
+        probe = parity_probe(mns, W, torch, carried)
     if not args.no_other_configs:
         print("[bench] timing the smaller workloads", file=sys.stderr, flush=True)
         others, samples = other_configs(mns, W, torch)
@@ -473,7 +483,7 @@ def main():
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle sample (and the parity figures)", file=sys.stderr,
               flush=True)
-        cpu, parity = cpu_baseline(probe, samples)
+        cpu, parity = cpu_baseline(probe, samples, carried=carried)
     git_head, src_sha = source_ids()
     line = {
         "metric": METRIC, "value": tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
