@@ -8,7 +8,10 @@ quintic steps; a wide, a tall, a square fp32-path and a small group
 step the momentum must agree to fp32 rounding (it is the same sum, formed
 with one fused multiply-add on the GPU and rounded once from fp64 by the
 oracle) and the weights' accumulated change must agree with the oracle's
-within the 2e-2 relative tolerance of the orthogonalised update.
+within the 2e-2 relative tolerance of the orthogonalised update.  The run
+is repeated with operand exponents carried from step to step (scale_exp):
+the momentum's norm grows over the first steps, so each step's exponent
+comes from a different norm than its own.
 """
 import sys
 
@@ -31,7 +34,8 @@ def rel(a, b):
     return float(np.linalg.norm(a - b) / np.linalg.norm(b))
 
 
-def test_ten_steps_follow_the_oracle():
+@pytest.mark.parametrize("carried", [False, True])
+def test_ten_steps_follow_the_oracle(carried):
     if not torch.cuda.is_available():
         pytest.fail("GPU tests need a HIP device")
     import muon_newton_schulz_06_amd as mns
@@ -43,9 +47,10 @@ def test_ten_steps_follow_the_oracle():
     Wo = [w.copy() for w in W0]
     Mo = [m.numpy().copy() for m in inp.momenta]
     lr32 = float(np.float32(LR))
+    sx = mns.scale_exp_buffer(len(SHAPES), "cuda") if carried else None
     for step in range(STEPS):
         grads = inp.grads if step == 0 else W.fresh_grads(SHAPES, 7300, step)
-        mns.muon_step(Wg, [g.cuda() for g in grads], Mg, beta=float(BETA), lr=LR, steps=5)
+        mns.muon_step(Wg, [g.cuda() for g in grads], Mg, beta=float(BETA), lr=LR, steps=5, scale_exp=sx)
         torch.cuda.synchronize()
         worst_m, worst_w = 0.0, 0.0
         for j, (r, c) in enumerate(SHAPES):
@@ -57,6 +62,6 @@ def test_ten_steps_follow_the_oracle():
             worst_m, worst_w = max(worst_m, em), max(worst_w, ew)
             assert em <= 1e-5, ("momentum", step, (r, c), em)
             assert ew <= 2e-2, ("weights", step, (r, c), ew)
-        print(f"[case] step {step}: momentum rel err {worst_m:.2e}, accumulated update rel err {worst_w:.2e}",
-              flush=True)
+        print(f"[case] carried {carried} step {step}: momentum rel err {worst_m:.2e}, "
+              f"accumulated update rel err {worst_w:.2e}", flush=True)
         sys.stdout.flush()
