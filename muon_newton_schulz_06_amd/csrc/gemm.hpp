@@ -1036,6 +1036,21 @@ __global__ __launch_bounds__(512) void gemm256_kernel(const GemmLaunch L) {
     }
   };
 
+  // Load j (0, 1: the A tile, 2, 3: the B tile) of issue(st, kt), the
+  // layout chosen by a select on the uniform ta / tb (kt < dA, kt < dB), the
+  // address formed where the load is issued.
+  auto refill_one = [&gA, &gB, offT, baseAT, baseBT, ldTA, ldTB, dstA, dstT](uint32_t sbase, int k0, bool ta, bool tb, auto jc) __attribute__((always_inline)) {
+    constexpr int j = decltype(jc)::value;
+    constexpr int p = j & 1;
+    if constexpr (j < 2) {
+      const T* g = ta ? baseAT + (int64_t)k0 * ldTA + offT[p] : gA[p] + k0;
+      dma16(g, __builtin_amdgcn_readfirstlane(sbase + (ta ? dstT + p * 1024 : dstA + p * 16 * kRowB)));
+    } else {
+      const T* g = tb ? baseBT + (int64_t)k0 * ldTB + offT[p] : gB[p] + k0;
+      dma16(g, __builtin_amdgcn_readfirstlane(sbase + kStageA + (tb ? dstT + p * 1024 : dstA + p * 16 * kRowB)));
+    }
+  };
+
   floatx4 acc[FM][FN];
 #pragma unroll
   for (int fi = 0; fi < FM; ++fi)
@@ -1136,6 +1151,32 @@ __global__ __launch_bounds__(512) void gemm256_kernel(const GemmLaunch L) {
         else mfma16_acc(acc[2 * q + f][fj], fa[f], fb[fj]);
       }
   };
+  // Quarter q's MFMAs with the refill of slot st (k-tile kt) spread over
+  // them: one load after each of the first FN MFMAs, so the matrix pipe
+  // keeps issuing while the loads go out (both are asm volatile, so their
+  // order is the source order).  A skipped quarter issues the loads alone.
+  static_assert(FN == 4, "four refill loads per k-tile and wave");
+  auto mma_refill = [&](const half8 (&fa)[2], const half8 (&fb)[FN], auto qc, char* st, int kt) __attribute__((always_inline)) {
+    constexpr int q = decltype(qc)::value;
+    const uint32_t sbase = __builtin_amdgcn_readfirstlane(lds_addr(st));
+    const int k0 = kt * BK;
+    const bool ta = kt < dA, tb = kt < dB;
+    if constexpr (kGram) {
+      if (!(runMask & (1 << q))) {
+        issue(st, kt);
+        return;
+      }
+    }
+    static_for<0, 2>([&](auto fc) {
+      constexpr int f = decltype(fc)::value;
+      static_for<0, FN>([&](auto jc) {
+        constexpr int fj = decltype(jc)::value;
+        if constexpr (kSym) mfma16_acc(acc[2 * q + f][fj], fb[fj], fa[f]);
+        else mfma16_acc(acc[2 * q + f][fj], fa[f], fb[fj]);
+        if constexpr (f == 0) refill_one(sbase, k0, ta, tb, std::integral_constant<int, fj>{});
+      });
+    });
+  };
   constexpr auto kQ0 = std::integral_constant<int, 0>{};
   constexpr auto kQ1 = std::integral_constant<int, 1>{};
   constexpr auto kQ2 = std::integral_constant<int, 2>{};
@@ -1194,8 +1235,14 @@ __global__ __launch_bounds__(512) void gemm256_kernel(const GemmLaunch L) {
   auto plain = [&](char* cur, const char* nxt, int k, auto pc, auto tac, auto tbc) __attribute__((always_inline)) {
     first_half(cur, pc, tac);
     asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    issue(cur, k + 4);
-    second_half(nxt, pc, tac, tbc);
+    if constexpr (kGram) {
+      issue(cur, k + 4);
+      second_half(nxt, pc, tac, tbc);
+    } else {
+      head(nxt, std::bool_constant<!decltype(pc)::value>{}, tac, tbc);
+      __builtin_amdgcn_sched_barrier(0);
+      mma_refill(fay, bset(pc), kQ3, cur, k + 4);
+    }
   };
   // Any step: phase ends and the last k-tiles (tail loads, shorter waits).
   // Loads younger than k-tile k + 1 when step k waits for it: k + 2 and
