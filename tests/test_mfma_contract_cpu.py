@@ -9,8 +9,8 @@ copies of accumulators, no other value placed in an accumulator register):
 a copy there would read a half-written result.  The compiler may insert such
 copies under register pressure, so every gemm256_kernel instance is compiled
 to assembly with the library's own flags and checked:
-  * its MFMAs use exactly FM·FN·4 = 128 accumulator VGPRs (each accumulator
-    in one place for the whole k-loop);
+  * its MFMAs use exactly FM·FN·4 = 128 accumulator registers, VGPRs or
+    AGPRs (each accumulator in one place for the whole k-loop);
   * between its first and last MFMA no other instruction reads or writes one
     of them (VALU, VMEM address operands, LDS read destinations).
 """
@@ -28,16 +28,17 @@ sys.path.insert(0, ROOT)
 from muon_newton_schulz_06_amd import build  # noqa: E402
 
 SOURCES = ["gemm_syrk", "gemm_sq", "gemm_axpy", "gemm_final"]
-REG = re.compile(r"\bv\[(\d+):(\d+)\]|\bv(\d+)\b")
+REG = re.compile(r"\b([va])\[(\d+):(\d+)\]|\b([va])(\d+)\b")
 
 
 def vregs(text):
+    """Vector registers named in text, as (file, index): file 'v' or 'a'."""
     out = set()
     for m in REG.finditer(text):
         if m.group(1):
-            out |= set(range(int(m.group(1)), int(m.group(2)) + 1))
+            out |= {(m.group(1), i) for i in range(int(m.group(2)), int(m.group(3)) + 1)}
         else:
-            out.add(int(m.group(3)))
+            out.add((m.group(4), int(m.group(5))))
     return out
 
 
@@ -51,7 +52,7 @@ def assembly(src):
 
 
 def violations(asm):
-    """(kernel, MFMA count, accumulator VGPRs, offending lines) per gemm256_kernel."""
+    """(kernel, MFMA count, accumulator registers, offending lines) per gemm256_kernel."""
     out = []
     for kern in re.findall(r"^(_ZN4muon14gemm256_kernel\w+):", asm, re.M):
         body = asm.split(kern + ":", 1)[1].split("s_endpgm", 1)[0].splitlines()
@@ -109,3 +110,19 @@ def test_checker_flags_a_copied_accumulator():
     ((kern, n_mfma, n_acc, bad),) = violations(asm)
     assert n_mfma == 2 and n_acc == 8
     assert len(bad) == 3
+
+
+def test_checker_flags_a_copied_agpr_accumulator():
+    """The same for accumulators held in AGPRs: a read-out between MFMAs is
+    flagged, and v0 is not confused with a0."""
+    asm = "\n".join([
+        "_ZN4muon14gemm256_kernelILi1ELi0EEEvNS_10GemmLaunchE:",
+        "\tv_mfma_f32_16x16x32_f16 a[0:3], v[0:3], v[4:7], a[0:3]",
+        "\tv_add_f32_e32 v8, v0, v1",
+        "\tv_accvgpr_read_b32 v9, a2",
+        "\tv_mfma_f32_16x16x32_f16 a[4:7], v[0:3], v[4:7], a[4:7]",
+        "\ts_endpgm",
+    ])
+    ((kern, n_mfma, n_acc, bad),) = violations(asm)
+    assert n_mfma == 2 and n_acc == 8
+    assert bad == ["v_accvgpr_read_b32 v9, a2"]
