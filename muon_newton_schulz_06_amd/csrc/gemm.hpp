@@ -647,22 +647,6 @@ __device__ __forceinline__ void stage_rows(char* lds, int wm, int wn, int lc, in
   });
 }
 
-// Symmetric layout: acc → LDS as rows of Cᵀ (one 2-byte write per element).
-template <bool kY, int FM, int FN>
-__device__ __forceinline__ void stage_cols(char* lds, int wm, int wn, int lc, int lg,
-                                           const floatx4 (&acc)[FM][FN]) {
-  static_for<0, FM>([&](auto fi) {
-    static_for<0, FN>([&](auto fj) {
-      static_for<0, 4>([&](auto rc) {
-        constexpr int r = decltype(rc)::value;
-        const int il = wm * 128 + fi * 16 + lc;
-        const int jl = wn * 64 + fj * 16 + 4 * lg + r;
-        *(_Float16*)(lds + soff<kY>(jl, il)) = (_Float16)acc[fi][fj][r];
-      });
-    });
-  });
-}
-
 // Second copy written from the same staged values (EPI_SQ, first step):
 // dst2 = rs·v + dv on the diagonal of the matrix (global index < mReal).
 struct SecondCopy {
@@ -682,42 +666,62 @@ __device__ __forceinline__ u32x4 second_value(u32x4 v, const SecondCopy& sc, int
   return __builtin_bit_cast(u32x4, h);
 }
 
-// Staged tile → global tile (tr, tc) of dst (and of sc.dst2 when kTwo).  On a
-// diagonal tile only the upper elements (cl ≥ rl, kUpper) or the strictly
-// lower ones (cl < rl) belong to this copy.
-template <bool kUpper, bool kTwo, bool kY>
+// Staged tile → global tile (tr, tc) of dst (and of sc.dst2 when kTwo):
+// half-wave h of an instruction writes one 512-byte row.
+template <bool kTwo, bool kY>
 __device__ __forceinline__ void store_staged(_Float16* dst, int ldc, const char* lds, int tr,
-                                             int tc, bool diag, int tid, const SecondCopy& sc) {
+                                             int tc, int tid, const SecondCopy& sc) {
 #pragma unroll
   for (int it = 0; it < 16; ++it) {
     const int idx = it * 512 + tid;
     const int rl = idx >> 5, c = idx & 31;
     const u32x4 v = *(const u32x4*)(lds + soff<kY>(rl, c * 8));
     const int64_t off = ((int64_t)tr * 256 + rl) * ldc + (int64_t)tc * 256 + c * 8;
-    _Float16* p = dst + off;
-    u32x4 v2 = v;
-    if constexpr (kTwo) v2 = second_value(v, sc, tr * 256 + rl, tc * 256 + c * 8);
-    if (!diag) {
-      *(u32x4*)p = v;
-      if constexpr (kTwo) *(u32x4*)(sc.dst2 + off) = v2;
-      continue;
+    *(u32x4*)(dst + off) = v;
+    if constexpr (kTwo) *(u32x4*)(sc.dst2 + off) = second_value(v, sc, tr * 256 + rl, tc * 256 + c * 8);
+  }
+}
+
+// Staged tile → global tile (tr, tc) through transposed LDS reads: output
+// element (r, c) of the tile is staged element (c, r) — the mirrored tile of
+// an off-diagonal result — or, with kDiag, output element (r, c) is the
+// staged (r, c) where c ≥ r and the staged (c, r) below the diagonal: the
+// whole diagonal tile from its upper elements alone (the only ones computed),
+// exactly symmetric.  Instruction it covers output rows 16·it .. 16·it + 15;
+// 16-lane group g of wave w the 16-byte column chunk 4w + g, lane i row
+// 16·it + i.  Two ds_read_b64_tr_b16 give a lane its chunk's 8 values from
+// staged rows 8q .. 8q + 7 at column 16·it + i (lane j of the group points at
+// staged row k0 + j/4, columns 16·it + 4·(j%4) .. +3).  Which reads a wave
+// needs depends on it and w only, so every branch is uniform.
+template <bool kDiag, bool kTwo, bool kY>
+__device__ __forceinline__ void store_transposed(_Float16* dst, int ldc, const char* lds, int tr,
+                                                 int tc, int tid, const SecondCopy& sc) {
+  const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int i = lane & 15, q = 4 * w + (lane >> 4), j = i;
+  const int c0 = 8 * q;
+#pragma unroll 4
+  for (int it = 0; it < 16; ++it) {
+    const int r0 = 16 * it, r = r0 + i;
+    // the wave's columns 32w .. 32w + 31 against rows r0 .. r0 + 15
+    const bool anyUpper = !kDiag || 32 * w + 31 >= r0;
+    const bool anyLower = !kDiag || 32 * w < r0 + 15;
+    half8 t{}, d{};
+    if (anyLower) {
+      const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s4_t)(lds + soff<kY>(c0 + (j >> 2), r0 + 4 * (j & 3))));
+      const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s4_t)(lds + soff<kY>(c0 + 4 + (j >> 2), r0 + 4 * (j & 3))));
+      t = __builtin_bit_cast(half8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     }
-    const int c0 = c * 8;
-    const bool all = kUpper ? (c0 >= rl) : (c0 + 7 < rl);
-    const bool none = kUpper ? (c0 + 7 < rl) : (c0 >= rl);
-    if (all) {
-      *(u32x4*)p = v;
-      if constexpr (kTwo) *(u32x4*)(sc.dst2 + off) = v2;
-    } else if (!none) {
-      const half8 hv = __builtin_bit_cast(half8, v);
-      const half8 hv2 = __builtin_bit_cast(half8, v2);
+    if constexpr (kDiag) {
+      if (anyUpper) d = *(const half8*)(lds + soff<kY>(r, c0));
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (kUpper ? (c0 + e >= rl) : (c0 + e < rl)) {
-          p[e] = hv[e];
-          if constexpr (kTwo) sc.dst2[off + e] = hv2[e];
-        }
+      for (int e = 0; e < 8; ++e) t[e] = c0 + e >= r ? d[e] : t[e];
     }
+    const u32x4 v = __builtin_bit_cast(u32x4, t);
+    const int64_t off = ((int64_t)tr * 256 + r) * ldc + (int64_t)tc * 256 + c0;
+    *(u32x4*)(dst + off) = v;
+    if constexpr (kTwo) *(u32x4*)(sc.dst2 + off) = second_value(v, sc, tr * 256 + r, tc * 256 + c0);
   }
 }
 
@@ -730,18 +734,18 @@ __device__ __forceinline__ void write_symmetric(_Float16* dst, int ldc, char* ld
                                                 int wm, int wn, int lc, int lg, int tid,
                                                 const floatx4 (&acc)[FM][FN],
                                                 const SecondCopy& sc, bool mirror) {
-  const bool diag = ti == tj;
   if constexpr (!kY) stage_rows<kY, FM, FN>(lds, wm, wn, lc, lg, acc);
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  store_staged<true, kTwo, kY>(dst, ldc, lds, ti, tj, diag, tid, sc);
-  // Block-upper output: an off-diagonal tile alone; a diagonal tile still
-  // gets its lower half from the transposed staging (exactly symmetric).
-  if (!mirror && !diag) return;
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  stage_cols<kY, FM, FN>(lds, wm, wn, lc, lg, acc);
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  store_staged<false, kTwo, kY>(dst, ldc, lds, tj, ti, diag, tid, sc);
-  // The kernel ends here (LDS is not used again), so no closing barrier.
+  // From here LDS is only read (the kernel ends after the stores).  A
+  // diagonal tile is written whole, its lower half read transposed from the
+  // upper; block-upper output stores an off-diagonal tile alone, mirrored
+  // output its transpose as well.
+  if (ti == tj) {
+    store_transposed<true, kTwo, kY>(dst, ldc, lds, ti, tj, tid, sc);
+    return;
+  }
+  store_staged<kTwo, kY>(dst, ldc, lds, ti, tj, tid, sc);
+  if (mirror) store_transposed<false, kTwo, kY>(dst, ldc, lds, tj, ti, tid, sc);
 }
 
 // Caller-facing outputs (weight update or plain output): the tile is staged
