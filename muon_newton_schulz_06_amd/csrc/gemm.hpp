@@ -620,14 +620,11 @@ __device__ __forceinline__ int soff(int row, int col) {
 }
 
 // Accumulators of the 256-tile kernel: 16×16×32 MFMAs, block (fi, fj) of a
-// wave's 128×64 region (lc = l%16, lg = l/16 below).
-//  * dense products (A fragments as the MFMA's first operand): lane l,
-//    register r holds row 16·fi + 4·lg + r, column 16·fj + lc;
-//  * symmetric products (operand roles swapped, B fragments first): lane l,
-//    register r holds row 16·fi + lc, column 16·fj + 4·lg + r — four
-//    consecutive columns of one row, which is what lets the previous iterate
-//    enter as the accumulators' start and off-diagonal tiles leave with one
-//    8-byte store per block.
+// wave's 128×64 region (lc = l%16, lg = l/16 below), operand roles swapped
+// (B fragments as the MFMA's first operand): lane l, register r holds row
+// 16·fi + lc, column 16·fj + 4·lg + r — four consecutive columns of one row,
+// so every epilogue reads and writes a 16-bit tile with one 8-byte access
+// per block.
 
 // Symmetric layout: acc → LDS as rows of C (one 8-byte write per block).
 template <bool kY, int FM, int FN>
@@ -748,126 +745,65 @@ __device__ __forceinline__ void write_symmetric(_Float16* dst, int ldc, char* ld
   if (mirror) store_transposed<false, kTwo, kY>(dst, ldc, lds, tj, ti, tid, sc);
 }
 
-// Caller-facing outputs (weight update or plain output): the tile is staged
-// in LDS in two 128-row halves as fp32 (row pitch 1040 bytes: 16 bytes of
-// padding keep the two lane halves of a store on different banks and every
-// address an immediate offset), then every thread handles runs of 4
-// consecutive columns with 8- or 16-byte global accesses.  Thread t covers
-// columns 4·(t % 64) + 0..3 of rows 8·it + t / 64 (it = 0..15) of each half.
-constexpr int kDensePitch = 1040;
-constexpr int kDenseIters = 16;
-
-// bf16 weights of the update, fetched into registers ahead of use: the first
-// half-tile while the last k-tiles are multiplied, the second half before the
-// first is staged.  Every thread issues exactly kDenseIters loads per half;
-// only tiles that lie wholly inside the matrix prefetch (weight_prefetch_ok),
-// so every address is in bounds without clamping.
-struct WeightPrefetch {
-  uint2 v[2][kDenseIters];
-};
-
-// Prefetching is used for bf16 weights with 8-byte aligned rows and tiles
-// that lie entirely inside the matrix (the fast path below has no bounds
-// checks).
-__device__ __forceinline__ bool weight_prefetch_ok(const EpiArgs<_Float16>& E, int ti, int tj) {
-  return E.userDtype == 1 && (E.userLd % 4 == 0) && (((uintptr_t)E.user & 15) == 0) &&
+// Caller-facing outputs (weight update or plain output).  The accumulators
+// have the same layout as the symmetric products' (lane: one row, four
+// consecutive columns per 16×16 block).  A bf16 tile wholly inside the matrix
+// with 16-byte aligned rows (dense_fast_ok) is staged in LDS and written with
+// the symmetric results' 16-byte row stores; for the weight update the
+// tile's current weights are fetched into that staging during the last
+// k-tiles (as the Gram products fetch Y) and updated in place.  Any other
+// tile (fp32 caller tensors, edge tiles, unaligned rows) is written from the
+// registers, element by element where needed.
+__device__ __forceinline__ bool dense_fast_ok(const EpiArgs<_Float16>& E, int ti, int tj) {
+  return E.userDtype == 1 && (E.userLd % 8 == 0) && (((uintptr_t)E.user & 15) == 0) &&
          (int64_t)ti * 256 + 256 <= E.mReal && (int64_t)tj * 256 + 256 <= E.nReal;
 }
 
-template <int kHalf>
-__device__ __forceinline__ void weight_prefetch(const EpiArgs<_Float16>& E, int ti, int tj, int tid,
-                                                WeightPrefetch& W) {
-  const uint16_t* w = (const uint16_t*)E.user + ((int64_t)ti * 256 + kHalf * 128 + (tid >> 6)) * E.userLd +
-                      (int64_t)tj * 256 + (tid & 63) * 4;
-  const int64_t step8 = 8 * E.userLd;  // 8 rows
-#pragma unroll
-  for (int it = 0; it < kDenseIters; ++it) W.v[kHalf][it] = *(const uint2*)(w + it * step8);
-}
-
-// acc of the waves of row half `half` → LDS as fp32 rows (u applied).
-template <int FM, int FN>
-__device__ __forceinline__ void stage_dense_half(char* lds, int half, float u, int wm, int wn,
-                                                 int lc, int lg, const floatx4 (&acc)[FM][FN]) {
-  if (half) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  if (wm == half) {
-    static_for<0, FM>([&](auto fi) {
-      static_for<0, FN>([&](auto fj) {
-        static_for<0, 4>([&](auto rc) {
-          constexpr int r = decltype(rc)::value;
-          const int row = fi * 16 + 4 * lg + r;
-          const int jl = wn * 64 + fj * 16 + lc;
-          *(float*)(lds + row * kDensePitch + jl * 4) = u * acc[fi][fj][r];
-        });
-      });
-    });
-  }
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-// Weight update of a tile inside the matrix with prefetched bf16 weights.
-template <int FM, int FN>
-__device__ __forceinline__ void update_prefetched(const EpiArgs<_Float16>& E, char* lds, int ti,
-                                                  int tj, int wm, int wn, int lc, int lg, int tid,
-                                                  const floatx4 (&acc)[FM][FN],
-                                                  WeightPrefetch& W) {
-  weight_prefetch<1>(E, ti, tj, tid, W);
-  const int c = tid & 63;
-  uint16_t* const w0 = (uint16_t*)E.user + ((int64_t)ti * 256 + (tid >> 6)) * E.userLd +
-                       (int64_t)tj * 256 + c * 4;
-  static_for<0, 2>([&](auto hc) {
-    constexpr int half = decltype(hc)::value;
-    stage_dense_half<FM, FN>(lds, half, E.u, wm, wn, lc, lg, acc);
-#pragma unroll
-    for (int it = 0; it < kDenseIters; ++it) {
-      const int row = it * 8 + (tid >> 6);
-      const u32x4 raw = *(const u32x4*)(lds + row * kDensePitch + c * 16);
-      const uint2 wv = W.v[half][it];
-      const uint32_t in[2] = {wv.x, wv.y};
+// Staged fast path: row il, columns jl .. jl + 3 of the tile, in the staged
+// layout soff<kPre> (kPre: the weights were fetched there).
+template <int EPI, bool kPre, int FM, int FN>
+__device__ __forceinline__ void dense_stage(const EpiArgs<_Float16>& E, char* lds, int wm, int wn,
+                                            int lc, int lg, const floatx4 (&acc)[FM][FN]) {
+  static_for<0, FM>([&](auto fi) {
+    static_for<0, FN>([&](auto fj) {
+      char* p = lds + soff<kPre>(wm * 128 + fi * 16 + lc, wn * 64 + fj * 16 + 4 * lg);
       uint32_t o[2];
+      if constexpr (EPI == EPI_UPDATE) {
+        const uint2 wv = *(const uint2*)p;
+        const uint32_t in[2] = {wv.x, wv.y};
 #pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        const float a0 = fmaf(-E.lrsc, __uint_as_float(raw[2 * p]), bf16_to_f32((uint16_t)(in[p] & 0xffffu)) * E.decay);
-        const float a1 = fmaf(-E.lrsc, __uint_as_float(raw[2 * p + 1]), bf16_to_f32((uint16_t)(in[p] >> 16)) * E.decay);
-        o[p] = (uint32_t)f32_to_bf16_rne(a0) | ((uint32_t)f32_to_bf16_rne(a1) << 16);
+        for (int h = 0; h < 2; ++h) {
+          const float a0 = fmaf(-E.lrsc, E.u * acc[fi][fj][2 * h], bf16_to_f32((uint16_t)(in[h] & 0xffffu)) * E.decay);
+          const float a1 = fmaf(-E.lrsc, E.u * acc[fi][fj][2 * h + 1], bf16_to_f32((uint16_t)(in[h] >> 16)) * E.decay);
+          o[h] = (uint32_t)f32_to_bf16_rne(a0) | ((uint32_t)f32_to_bf16_rne(a1) << 16);
+        }
+      } else {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          o[h] = (uint32_t)f32_to_bf16_rne(E.u * acc[fi][fj][2 * h]) |
+                 ((uint32_t)f32_to_bf16_rne(E.u * acc[fi][fj][2 * h + 1]) << 16);
       }
-      *(uint2*)(w0 + (int64_t)(half * 128 + it * 8) * E.userLd) = make_uint2(o[0], o[1]);
-    }
+      *(uint2*)p = make_uint2(o[0], o[1]);
+    });
   });
 }
 
+// Register path: each lane writes its four consecutive columns of a row per
+// block, as one 8- or 16-byte access where the row allows, else by element.
 template <int EPI, int FM, int FN>
-__device__ __forceinline__ void dense_staged(const EpiArgs<_Float16>& E, char* lds, int ti, int tj,
-                                             int wm, int wn, int lc, int lg, int tid,
-                                             const floatx4 (&acc)[FM][FN]) {
-  const bool vec_ok = (E.userLd % 4 == 0) && (((uintptr_t)E.user & 15) == 0);
-  for (int half = 0; half < 2; ++half) {
-    if (half) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if (wm == half) {
-      static_for<0, FM>([&](auto fi) {
-        static_for<0, FN>([&](auto fj) {
-          static_for<0, 4>([&](auto rc) {
-            constexpr int r = decltype(rc)::value;
-            const int row = fi * 16 + 4 * lg + r;
-            const int jl = wn * 64 + fj * 16 + lc;
-            *(float*)(lds + row * kDensePitch + jl * 4) = E.u * acc[fi][fj][r];
-          });
-        });
-      });
-    }
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-#pragma unroll 1
-    for (int it = 0; it < kDenseIters; ++it) {
-      const int idx = it * 512 + tid;
-      const int row = idx >> 6, c = idx & 63;
-      const int64_t i = (int64_t)ti * 256 + half * 128 + row;
-      const int64_t j = (int64_t)tj * 256 + c * 4;
-      if (i >= E.mReal || j >= E.nReal) continue;
-      const u32x4 raw = *(const u32x4*)(lds + row * kDensePitch + c * 16);
+__device__ __forceinline__ void dense_direct(const EpiArgs<_Float16>& E, int ti, int tj, int wm,
+                                             int wn, int lc, int lg, const floatx4 (&acc)[FM][FN]) {
+  const bool vec = (E.userLd % 4 == 0) && (((uintptr_t)E.user & 15) == 0);
+  static_for<0, FM>([&](auto fi) {
+    const int64_t i = (int64_t)ti * 256 + wm * 128 + fi * 16 + lc;
+    static_for<0, FN>([&](auto fj) {
+      const int64_t j = (int64_t)tj * 256 + wn * 64 + fj * 16 + 4 * lg;
+      if (i >= E.mReal || j >= E.nReal) return;
       float v[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = __uint_as_float(raw[e]);
+      for (int e = 0; e < 4; ++e) v[e] = E.u * acc[fi][fj][e];
       const int64_t base = i * E.userLd + j;
-      const bool full = vec_ok && (j + 3 < E.nReal);
+      const bool full = vec && (j + 3 < E.nReal);
       if constexpr (EPI == EPI_UPDATE) {
         if (E.userDtype == 1) {
           uint16_t* w = (uint16_t*)E.user + base;
@@ -876,10 +812,10 @@ __device__ __forceinline__ void dense_staged(const EpiArgs<_Float16>& E, char* l
             const uint32_t in[2] = {wv.x, wv.y};
             uint32_t o[2];
 #pragma unroll
-            for (int p = 0; p < 2; ++p) {
-              const float a0 = fmaf(-E.lrsc, v[2 * p], bf16_to_f32((uint16_t)(in[p] & 0xffffu)) * E.decay);
-              const float a1 = fmaf(-E.lrsc, v[2 * p + 1], bf16_to_f32((uint16_t)(in[p] >> 16)) * E.decay);
-              o[p] = (uint32_t)f32_to_bf16_rne(a0) | ((uint32_t)f32_to_bf16_rne(a1) << 16);
+            for (int h = 0; h < 2; ++h) {
+              const float a0 = fmaf(-E.lrsc, v[2 * h], bf16_to_f32((uint16_t)(in[h] & 0xffffu)) * E.decay);
+              const float a1 = fmaf(-E.lrsc, v[2 * h + 1], bf16_to_f32((uint16_t)(in[h] >> 16)) * E.decay);
+              o[h] = (uint32_t)f32_to_bf16_rne(a0) | ((uint32_t)f32_to_bf16_rne(a1) << 16);
             }
             *(uint2*)w = make_uint2(o[0], o[1]);
           } else {
@@ -916,8 +852,8 @@ __device__ __forceinline__ void dense_staged(const EpiArgs<_Float16>& E, char* l
             for (int e = 0; e < 4 && j + e < E.nReal; ++e) o[e] = v[e];
         }
       }
-    }
-  }
+    });
+  });
 }
 
 // TR (dense products only): 0 both operands direct, 1 A read transposed,
@@ -932,11 +868,10 @@ __global__ __launch_bounds__(512) void gemm256_kernel(const GemmLaunch L) {
   // (their B operand) added in the epilogue.
   constexpr bool kGram = EPI == EPI_SQ || EPI == EPI_AXPY;
   // 4-slot ring for the main loop, plus one slot for the last quarter of
-  // the Y block (Gram products); reused by the staged epilogues (one
-  // 256×256 fp16 tile for symmetric results, two fp32 half-tiles for dense).
-  constexpr int kLds = kGram ? 5 * kStage : kSym ? 4 * kStage : 128 * kDensePitch;
+  // the Y block (Gram products) or of the weights (update); reused by the
+  // staged epilogues (one 256×256 16-bit tile).
+  constexpr int kLds = (kGram || EPI == EPI_UPDATE) ? 5 * kStage : 4 * kStage;
   __shared__ __attribute__((aligned(1024))) char lds[kLds];
-  static_assert(128 * kDensePitch >= 4 * kStage && kLds >= 4 * kStage, "ring must fit");
   static_assert(4 * kStage >= 256 * 512, "a staged symmetric tile must fit");
   char* const st0 = lds;
   char* const st1 = lds + kStage;
@@ -1140,8 +1075,8 @@ __global__ __launch_bounds__(512) void gemm256_kernel(const GemmLaunch L) {
       fb[fj] = decltype(tbc)::value ? frag_t(st + kStageA, row0) : frag_n(st + kStageA, row0);
     }
   };
-  // Symmetric products swap the operand roles (B fragments first), which
-  // transposes the accumulator layout (see stage_rows).
+  // The operand roles are swapped (B fragments first), which transposes the
+  // accumulator layout: a lane holds four consecutive columns of one row.
   auto mma = [&acc, runMask](const half8 (&fa)[2], const half8 (&fb)[FN], auto qc) __attribute__((always_inline)) {
     constexpr int q = decltype(qc)::value;
     if constexpr (kGram) {
@@ -1151,8 +1086,7 @@ __global__ __launch_bounds__(512) void gemm256_kernel(const GemmLaunch L) {
     for (int f = 0; f < 2; ++f)
 #pragma unroll
       for (int fj = 0; fj < FN; ++fj) {
-        if constexpr (kSym) mfma16_acc(acc[2 * q + f][fj], fb[fj], fa[f]);
-        else mfma16_acc(acc[2 * q + f][fj], fa[f], fb[fj]);
+        mfma16_acc(acc[2 * q + f][fj], fb[fj], fa[f]);
       }
   };
   // Quarter q's MFMAs with the refill of slot st (k-tile kt) spread over
@@ -1175,8 +1109,7 @@ __global__ __launch_bounds__(512) void gemm256_kernel(const GemmLaunch L) {
       constexpr int f = decltype(fc)::value;
       static_for<0, FN>([&](auto jc) {
         constexpr int fj = decltype(jc)::value;
-        if constexpr (kSym) mfma16_acc(acc[2 * q + f][fj], fb[fj], fa[f]);
-        else mfma16_acc(acc[2 * q + f][fj], fa[f], fb[fj]);
+        mfma16_acc(acc[2 * q + f][fj], fb[fj], fa[f]);
         if constexpr (f == 0) refill_one(sbase, k0, ta, tb, std::integral_constant<int, fj>{});
       });
     });
@@ -1186,16 +1119,29 @@ __global__ __launch_bounds__(512) void gemm256_kernel(const GemmLaunch L) {
   constexpr auto kQ2 = std::integral_constant<int, 2>{};
   constexpr auto kQ3 = std::integral_constant<int, 3>{};
 
-  // Weight update: the first half of the tile's bf16 weights is loaded in
-  // k-tile KT − 3 (after every k-tile's loads are issued) and lands while
-  // the last k-tiles are multiplied.
-  [[maybe_unused]] WeightPrefetch wpf;
-  [[maybe_unused]] EpiArgs<T> Ew;
+  // Weight update on the staged path: the tile's bf16 weights are fetched
+  // into the epilogue's staging during the last four k-tiles, a quarter of
+  // 64 rows at a time into the slots the Gram products' Y block uses (same
+  // placement, same wave/lane assignment, so the same vmcnt counts hold).
+  [[maybe_unused]] const uint16_t* wbase = nullptr;
+  [[maybe_unused]] int64_t wld = 0;
   bool pref = false;
   if constexpr (EPI == EPI_UPDATE) {
-    Ew = make_epi<T, EPI>(L, S, mat);
-    pref = KT >= 4 && weight_prefetch_ok(Ew, ti, tj);
+    const EpiArgs<T> Ew = make_epi<T, EPI>(L, S, mat);
+    pref = dense_fast_ok(Ew, ti, tj);
+    wbase = (const uint16_t*)Ew.user + (int64_t)ti * BM * Ew.userLd + (int64_t)tj * BN;
+    wld = Ew.userLd;
   }
+  auto issue_w = [&](int q) __attribute__((always_inline)) {
+    char* dst = q == 3 ? lds + 4 * kStage : lds + q * kStage;
+    const uint32_t sbase = __builtin_amdgcn_readfirstlane(lds_addr(dst));
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int r = wave * 8 + 2 * p + (lane >> 5);
+      const uint16_t* g = wbase + (int64_t)(64 * q + r) * wld + (((lane & 31) ^ (r & 31)) << 3);
+      dma16(g, __builtin_amdgcn_readfirstlane(sbase + (wave * 8 + 2 * p) * 512));
+    }
+  };
 
   // One k-tile k (ring slot cur = k mod 4; nxt holds k + 1; pc its parity,
   // selecting the B registers):
@@ -1251,8 +1197,8 @@ __global__ __launch_bounds__(512) void gemm256_kernel(const GemmLaunch L) {
   // Any step: phase ends and the last k-tiles (tail loads, shorter waits).
   // Loads younger than k-tile k + 1 when step k waits for it: k + 2 and
   // k + 3 while they exist; for the Gram products the Y quarters 0 and 3
-  // (issued in step KT − 4) and 1 (step KT − 3); for the weight update the
-  // prefetched half-tile (step KT − 3).
+  // (issued in step KT − 4) and 1 (step KT − 3); the weight update's
+  // quarters likewise.
   auto step = [&](char* cur, const char* nxt, int k, int k1, auto pc, auto tac,
                   auto tbc) __attribute__((always_inline)) {
     first_half(cur, pc, tac);
@@ -1261,11 +1207,12 @@ __global__ __launch_bounds__(512) void gemm256_kernel(const GemmLaunch L) {
       asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     } else if (kGram && r >= 1) {
       asm volatile("s_waitcnt vmcnt(12) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    } else if (pref && r >= 1) {
+      asm volatile("s_waitcnt vmcnt(12) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     } else if (r == 2) {
       asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
     } else if (r == 1) {
-      if (pref) asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
-      else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
     }
     if (r >= 4) issue(cur, k + 4);
     if constexpr (kGram) {
@@ -1278,7 +1225,14 @@ __global__ __launch_bounds__(512) void gemm256_kernel(const GemmLaunch L) {
       }
     }
     if constexpr (EPI == EPI_UPDATE) {
-      if (pref && r == 2) weight_prefetch<0>(Ew, ti, tj, tid, wpf);
+      if (pref) {
+        if (r == 3) {
+          issue_w(0);
+          issue_w(3);
+        } else if (r == 2 || r == 1) {
+          issue_w(3 - r);
+        }
+      }
     }
     if (k + 1 < k1) head(nxt, std::bool_constant<!decltype(pc)::value>{}, tac, tbc);
     __builtin_amdgcn_sched_barrier(0);
@@ -1423,17 +1377,17 @@ __global__ __launch_bounds__(512) void gemm256_kernel(const GemmLaunch L) {
         });
       }
     }
-  } else {
-    // Every wave is done with the ring (and the tail loads have landed)
-    // before it is reused for staging.
+  } else if (EPI == EPI_UPDATE ? pref : dense_fast_ok(E, ti, tj)) {
+    // Every wave is done with the ring, and the weights have landed, before
+    // the staging is written; the rows are stored once all of it is.
+    constexpr bool kPre = EPI == EPI_UPDATE;
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if constexpr (EPI == EPI_UPDATE) {
-      if (pref) {
-        update_prefetched<FM, FN>(E, lds, ti, tj, wm, wn, lc, lg, tid, acc, wpf);
-        return;
-      }
-    }
-    dense_staged<EPI, FM, FN>(E, lds, ti, tj, wm, wn, lc, lg, tid, acc);
+    dense_stage<EPI, kPre, FM, FN>(E, lds, wm, wn, lc, lg, acc);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    const SecondCopy none{nullptr, 0.f, 0.f, 0};
+    store_staged<false, kPre>((_Float16*)E.user, (int)E.userLd, lds, ti, tj, tid, none);
+  } else {
+    dense_direct<EPI, FM, FN>(E, ti, tj, wm, wn, lc, lg, acc);
   }
 }
 
