@@ -679,43 +679,57 @@ __device__ __forceinline__ void store_staged(_Float16* dst, int ldc, const char*
   }
 }
 
-// Staged tile → global tile (tr, tc) through transposed LDS reads: output
-// element (r, c) of the tile is staged element (c, r) — the mirrored tile of
-// an off-diagonal result — or, with kDiag, output element (r, c) is the
-// staged (r, c) where c ≥ r and the staged (c, r) below the diagonal: the
-// whole diagonal tile from its upper elements alone (the only ones computed),
-// exactly symmetric.  Instruction it covers output rows 16·it .. 16·it + 15;
-// 16-lane group g of wave w the 16-byte column chunk 4w + g, lane i row
-// 16·it + i.  Two ds_read_b64_tr_b16 give a lane its chunk's 8 values from
-// staged rows 8q .. 8q + 7 at column 16·it + i (lane j of the group points at
-// staged row k0 + j/4, columns 16·it + 4·(j%4) .. +3).  Which reads a wave
-// needs depends on it and w only, so every branch is uniform.
-template <bool kDiag, bool kTwo, bool kY>
-__device__ __forceinline__ void store_transposed(_Float16* dst, int ldc, const char* lds, int tr,
-                                                 int tc, int tid, const SecondCopy& sc) {
+// Transposed LDS reads (ds_read_b64_tr_b16) of the staged tile, 16 output
+// rows at a time: 16-lane group g of wave w handles the 16-byte column chunk
+// q = 4w + g, lane i row r0 + i.  Two reads give a lane its chunk's 8 values
+// from staged rows 8q .. 8q + 7 at column r0 + i (lane j of the group points
+// at staged row k0 + j/4, columns r0 + 4·(j%4) .. +3).
+template <bool kY>
+__device__ __forceinline__ half8 tr_chunk(const char* lds, int r0, int c0, int j) {
+  const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s4_t)(lds + soff<kY>(c0 + (j >> 2), r0 + 4 * (j & 3))));
+  const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s4_t)(lds + soff<kY>(c0 + 4 + (j >> 2), r0 + 4 * (j & 3))));
+  return __builtin_bit_cast(half8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Diagonal tile: only its upper elements (c ≥ r) were computed.  Each lower
+// element (r, c) of the staged tile is replaced by the staged (c, r), in
+// place, which makes the tile exactly symmetric.  The reads touch upper
+// positions only (a chunk's lower lanes discard what they read elsewhere),
+// and a chunk that straddles the diagonal is written back with its upper
+// values unchanged, so no read sees a value other than the one it needs.
+// Which reads a wave needs depends on it and w only (uniform branches).
+template <bool kY>
+__device__ __forceinline__ void diag_fill(char* lds, int tid) {
   const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int i = lane & 15, q = 4 * w + (lane >> 4), j = i;
-  const int c0 = 8 * q;
+  const int i = lane & 15, c0 = 8 * (4 * w + (lane >> 4));
 #pragma unroll 4
   for (int it = 0; it < 16; ++it) {
     const int r0 = 16 * it, r = r0 + i;
     // the wave's columns 32w .. 32w + 31 against rows r0 .. r0 + 15
-    const bool anyUpper = !kDiag || 32 * w + 31 >= r0;
-    const bool anyLower = !kDiag || 32 * w < r0 + 15;
-    half8 t{}, d{};
-    if (anyLower) {
-      const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_s4_t)(lds + soff<kY>(c0 + (j >> 2), r0 + 4 * (j & 3))));
-      const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_s4_t)(lds + soff<kY>(c0 + 4 + (j >> 2), r0 + 4 * (j & 3))));
-      t = __builtin_bit_cast(half8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-    }
-    if constexpr (kDiag) {
-      if (anyUpper) d = *(const half8*)(lds + soff<kY>(r, c0));
+    if (32 * w >= r0 + 15) continue;  // no lower element
+    half8 t = tr_chunk<kY>(lds, r0, c0, i);
+    if (32 * w + 31 >= r0) {  // some upper element: merge
+      const half8 d = *(const half8*)(lds + soff<kY>(r, c0));
 #pragma unroll
       for (int e = 0; e < 8; ++e) t[e] = c0 + e >= r ? d[e] : t[e];
     }
-    const u32x4 v = __builtin_bit_cast(u32x4, t);
+    if (c0 < r) *(half8*)(lds + soff<kY>(r, c0)) = t;
+  }
+}
+
+// Staged tile → global tile (tr, tc), transposed: output element (r, c) is
+// staged element (c, r) (the mirrored tile of an off-diagonal result).
+template <bool kTwo, bool kY>
+__device__ __forceinline__ void store_transposed(_Float16* dst, int ldc, const char* lds, int tr,
+                                                 int tc, int tid, const SecondCopy& sc) {
+  const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int i = lane & 15, c0 = 8 * (4 * w + (lane >> 4));
+#pragma unroll 4
+  for (int it = 0; it < 16; ++it) {
+    const int r = 16 * it + i;
+    const u32x4 v = __builtin_bit_cast(u32x4, tr_chunk<kY>(lds, 16 * it, c0, i));
     const int64_t off = ((int64_t)tr * 256 + r) * ldc + (int64_t)tc * 256 + c0;
     *(u32x4*)(dst + off) = v;
     if constexpr (kTwo) *(u32x4*)(sc.dst2 + off) = second_value(v, sc, tr * 256 + r, tc * 256 + c0);
@@ -733,16 +747,17 @@ __device__ __forceinline__ void write_symmetric(_Float16* dst, int ldc, char* ld
                                                 const SecondCopy& sc, bool mirror) {
   if constexpr (!kY) stage_rows<kY, FM, FN>(lds, wm, wn, lc, lg, acc);
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  // From here LDS is only read (the kernel ends after the stores).  A
-  // diagonal tile is written whole, its lower half read transposed from the
-  // upper; block-upper output stores an off-diagonal tile alone, mirrored
-  // output its transpose as well.
+  // A diagonal tile is completed in LDS from its upper elements and written
+  // whole; block-upper output stores an off-diagonal tile alone, mirrored
+  // output its transpose as well (the kernel ends after the stores).
   if (ti == tj) {
-    store_transposed<true, kTwo, kY>(dst, ldc, lds, ti, tj, tid, sc);
+    diag_fill<kY>(lds, tid);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    store_staged<kTwo, kY>(dst, ldc, lds, ti, tj, tid, sc);
     return;
   }
   store_staged<kTwo, kY>(dst, ldc, lds, ti, tj, tid, sc);
-  if (mirror) store_transposed<false, kTwo, kY>(dst, ldc, lds, tj, ti, tid, sc);
+  if (mirror) store_transposed<kTwo, kY>(dst, ldc, lds, tj, ti, tid, sc);
 }
 
 // Caller-facing outputs (weight update or plain output).  The accumulators
