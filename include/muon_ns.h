@@ -327,8 +327,9 @@ muon_status_t muon_describe_plan(const int64_t* rows, const int64_t* cols, int32
  * installs it with this call.  Per entry:
  *   m ≥ 1; n ≥ 0 (0 matches any n; an entry with the group's own n takes
  *   precedence); 0 ≤ count_class ≤ 31;
- *   tile:       128 or 256 for fp16 groups, 64 or 128 for fp32 groups, or 0
- *               for the built-in choice;
+ *   tile:       128 or 256 for fp16 groups, 32, 64 or 128 for fp32 groups
+ *               (32: the contraction split over four waves, the built-in
+ *               choice for m ≤ 256), or 0 for the built-in choice;
  *   xcd_window: logical tiles each XCD runs in a row (8, 16, 32 or 64), or 0
  *               for the built-in 32;
  *   band:       tile rows per band of the tile order (1, 2, 4 or 8), or 0

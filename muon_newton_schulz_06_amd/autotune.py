@@ -3,7 +3,7 @@
 DMuon's technical summary (gist.science, Korean), §2.4, tunes kernel
 configurations per matrix shape when training starts and keeps the winners
 in a cache.  Here a Gram group's configuration is its tile edge (fp16
-groups: 128 or 256; fp32 groups: 64 or 128) and the order in which its tiles
+groups: 128 or 256; fp32 groups: 32, 64 or 128) and the order in which its tiles
 run (logical tiles per XCD run: 16, 32, 64; tile rows per band: 2, 4, 8),
 keyed by the group's size m, largest n, operand type and batch-size class
 floor(log2(matrices in the group)) — exactly what `muon_set_tile_table`
@@ -22,7 +22,7 @@ import json
 import math
 import sys
 
-CANDIDATES = {"f16": (128, 256), "f32": (64, 128)}
+CANDIDATES = {"f16": (128, 256), "f32": (32, 64, 128)}
 XCD_WINDOWS = (16, 32, 64)
 BANDS = (2, 4, 8)
 

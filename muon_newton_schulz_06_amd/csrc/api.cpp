@@ -1812,7 +1812,7 @@ muon_status_t muon_set_tile_table(const muon_tile_entry_t* entries, int32_t n) {
   for (int i = 0; i < n; ++i) {
     const muon_tile_entry_t& e = entries[i];
     const bool okTile = e.op == OP_F16 ? (e.tile == 0 || e.tile == 128 || e.tile == 256)
-                                       : (e.op == OP_F32 && (e.tile == 0 || e.tile == 64 || e.tile == 128));
+                                       : (e.op == OP_F32 && (e.tile == 0 || e.tile == 32 || e.tile == 64 || e.tile == 128));
     int xs = 0;
     if (e.xcd_window != 0) {
       for (int k = 3; k <= 6; ++k)

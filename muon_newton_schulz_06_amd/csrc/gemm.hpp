@@ -179,11 +179,20 @@ __device__ __forceinline__ void epilogue(const EpiArgs<T>& E, int i, int j, floa
 // is stored at (i, j) only (and its fp32 copy, and the second copy's value at
 // (i, j)); the returned stored value is staged so that the transposed
 // position is written afterwards from LDS with coalesced rows (mirror_rows).
+// The previous iterate's (i, j) element that the A² and a·Y + B·Y epilogues
+// combine with the product (A for A², Y for a·Y + B·Y).
+template <typename T>
+__device__ __forceinline__ float sym_prev(const EpiArgs<T>& E, int i, int j) {
+  const int64_t e = (int64_t)i * E.ldc + j;
+  return E.in32 ? E.in32[e] : E.sIn * (float)E.inh[e];
+}
+
 template <typename T, int EPI>
-__device__ __forceinline__ T sym_value(const EpiArgs<T>& E, int i, int j, float acc) {
+__device__ __forceinline__ T sym_value_with(const EpiArgs<T>& E, int i, int j, float acc, float prev) {
   const int ldc = E.ldc;
   const int64_t e = (int64_t)i * ldc + j;
   if constexpr (EPI == EPI_SYRK) {
+    (void)prev;
     const float g = E.u * acc;
     if (E.out32) E.out32[e] = g;
     const T v = to_op<T>(E.sOut * g);
@@ -191,7 +200,7 @@ __device__ __forceinline__ T sym_value(const EpiArgs<T>& E, int i, int j, float 
     if (E.writeIdentity) E.outhb[e] = to_op<T>((i == j && i < E.mReal) ? E.sOutB : 0.f);
     return v;
   } else if constexpr (EPI == EPI_SQ) {
-    const float a = E.in32 ? E.in32[e] : E.sIn * (float)E.inh[e];
+    const float a = prev;
     const float bb = E.p1 * a + E.p2 * (E.u * acc);
     const T bh = to_op<T>(E.sOut * bb);
     E.outh[e] = bh;
@@ -202,13 +211,17 @@ __device__ __forceinline__ T sym_value(const EpiArgs<T>& E, int i, int j, float 
     return bh;
   } else {
     static_assert(EPI == EPI_AXPY, "symmetric epilogues only");
-    const float prev = E.in32 ? E.in32[e] : E.sIn * (float)E.inh[e];
     const float y = E.p0 * prev + E.u * acc;
     if (E.out32) E.out32[e] = y;
     const T v = to_op<T>(E.sOut * y);
     E.outh[e] = v;
     return v;
   }
+}
+
+template <typename T, int EPI>
+__device__ __forceinline__ T sym_value(const EpiArgs<T>& E, int i, int j, float acc) {
+  return sym_value_with<T, EPI>(E, i, j, acc, EPI == EPI_SYRK ? 0.f : sym_prev(E, i, j));
 }
 
 // Staged symmetric tile: element (il, jl) at il·BN + (jl ^ (il/4)): the
@@ -501,6 +514,117 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const GemmLaunch L) 
     mirror_rows<T, EPI, BM, BN, NT>(E, st, ti, tj, tid);
   } else {
     epilogue_all<T, EPI, FM, FN>(E, gi0, gj0, lh, lr, acc);
+  }
+}
+
+// fp32 products of small matrices (m ≤ 256): 32×32 tiles with each k-tile's
+// 32-wide contraction split over the workgroup's four waves, so a wave runs a
+// quarter of the MFMAs of a 32×32 block (the register-staged kernel's wave
+// runs all of them) and a single matrix's launch spreads over four times the
+// compute units of a 64-tile launch.  Wave w takes the 16-byte k-chunk
+// 4·(w/2) + 2·(lane/32) + w%2 of every 128-byte k-row: four 32×32×2 MFMAs
+// per k-tile, lanes 0-31 and 32-63 supplying the two k of each, so the four
+// waves cover k = 16·(w/2) + 8·(lane/32) + 4·(w%2) + 0..3 once.  The partial
+// sums are added in wave order (0, 1, 2, 3), so a result does not depend on
+// timing.  The epilogue inputs of the Gram products (A or Y at the block's
+// upper elements) are read before the main loop, hiding their latency.
+// Wave 0 then applies the register-staged kernel's epilogue to the block
+// (32×32 accumulator layout as there); all threads write the mirrored rows.
+template <int EPI>
+__global__ __launch_bounds__(256) void gemm32_kernel(const GemmLaunch L) {
+  using T = float;
+  constexpr int BM = 32, BN = 32, BK = 32, CH = 8, NT = 256;
+  constexpr bool kSym = EPI == EPI_SYRK || EPI == EPI_SQ || EPI == EPI_AXPY;
+  constexpr bool kPrev = EPI == EPI_SQ || EPI == EPI_AXPY;
+  __shared__ u32x4 smem[2][(BM + BN) * CH];  // double-buffered k-tile, 16 KiB
+  __shared__ floatx16 part[3][64];           // partial sums of waves 1..3
+
+  const TilePos tp = locate(L);
+  const GemmSeg& S = L.seg[tp.seg];
+  const int mat = tp.mat, ti = tp.ti, tj = tp.tj;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 31, lh = lane >> 5;
+
+  // Thread t stages 16-byte chunk t % 8 of row t / 8 of the A and B tiles.
+  const T* Ag = (const T*)S.A + mat * S.strideA + (int64_t)ti * BM * S.lda;
+  const T* Bg = (const T*)S.B + mat * S.strideB + (int64_t)tj * BN * S.ldb;
+  const int c = tid % CH, r = tid / CH;
+  const T* ap = Ag + (int64_t)r * S.lda + c * 4;
+  const T* bp = Bg + (int64_t)r * S.ldb + c * 4;
+  const int so = r * CH + (c ^ swz8(r));
+
+  const EpiArgs<T> E = make_epi<T, EPI>(L, S, mat);
+  float prev[16];
+  if constexpr (kPrev) {
+    if (wave == 0) {
+      static_for<0, 16>([&](auto rc) {
+        constexpr int rr = decltype(rc)::value;
+        const int il = 8 * (rr >> 2) + 4 * lh + (rr & 3);
+        prev[rr] = (ti < tj || il <= lr) ? sym_prev(E, ti * BM + il, tj * BN + lr) : 0.f;
+      });
+    }
+  }
+
+  floatx16 acc[1][1];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) acc[0][0][e] = 0.f;
+
+  const int KT = S.K / BK;
+  u32x4 ra = *(const u32x4*)ap, rb = *(const u32x4*)bp;
+  smem[0][so] = ra;
+  smem[0][BM * CH + so] = rb;
+  __syncthreads();
+  const int ch = 4 * (wave >> 1) + 2 * lh + (wave & 1);
+  const int ro = lr * CH + (ch ^ swz8(lr));
+  for (int kt = 0; kt < KT; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < KT) {
+      ra = *(const u32x4*)(ap + (kt + 1) * BK);
+      rb = *(const u32x4*)(bp + (kt + 1) * BK);
+    }
+    const u32x4 va = smem[buf][ro];
+    const u32x4 vb = smem[buf][BM * CH + ro];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(va[e]), __uint_as_float(vb[e]),
+                                                        acc[0][0], 0, 0, 0);
+    if (kt + 1 < KT) {
+      smem[buf ^ 1][so] = ra;
+      smem[buf ^ 1][BM * CH + so] = rb;
+    }
+    __syncthreads();
+  }
+  if (wave > 0) part[wave - 1][lane] = acc[0][0];
+  __syncthreads();
+  if (wave == 0) {
+#pragma unroll
+    for (int p = 0; p < 3; ++p) {
+      const floatx16 v = part[p][lane];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[0][0][e] += v[e];
+    }
+  }
+
+  // 32×32 accumulator layout: lane l, register r holds
+  // row 8·(r/4) + 4·(l/32) + r%4, column l%32 of the block.
+  if constexpr (kSym) {
+    // The ring is free (the loop ended with a barrier): the block is staged
+    // there for the mirrored rows, as in the register-staged kernel.
+    T* st = (T*)smem;
+    if (wave == 0) {
+      static_for<0, 16>([&](auto rc) {
+        constexpr int rr = decltype(rc)::value;
+        const int il = 8 * (rr >> 2) + 4 * lh + (rr & 3);
+        if (ti < tj || il <= lr)
+          st[sym_stage_idx<BN>(il, lr)] =
+              sym_value_with<T, EPI>(E, ti * BM + il, tj * BN + lr, acc[0][0][rr], kPrev ? prev[rr] : 0.f);
+      });
+    }
+    __syncthreads();
+    mirror_rows<T, EPI, BM, BN, NT>(E, st, ti, tj, tid);
+  } else {
+    if (wave == 0) epilogue_all<T, EPI, 1, 1>(E, ti * BM, tj * BN, lh, lr, acc);
   }
 }
 
@@ -1430,6 +1554,8 @@ hipError_t launch_epi(int op, int tile, const GemmLaunch& L, int blocks, hipStre
     hipLaunchKernelGGL((gemm_kernel<float, 128, 128, 2, 2, EPI>), dim3(blocks), dim3(256), 0, st, L);
   } else if (op == OP_F32 && tile == 64) {
     hipLaunchKernelGGL((gemm_kernel<float, 64, 64, 2, 2, EPI>), dim3(blocks), dim3(256), 0, st, L);
+  } else if (op == OP_F32 && tile == 32) {
+    hipLaunchKernelGGL((gemm32_kernel<EPI>), dim3(blocks), dim3(256), 0, st, L);
   } else {
     return hipErrorInvalidValue;
   }

@@ -37,8 +37,14 @@ std::map<TileKey, TileConf> g_table;
 
 int choose_tile(int op, int64_t m, int count) {
   if (op == OP_F32) {
+    // Small matrices: 32-tiles with the contraction split over four waves
+    // (a quarter of a 64-tile wave's MFMAs per wave, four times the
+    // workgroups).  Decided by m alone: the split changes the order of the
+    // fp32 sums, and a chunked call must pick the tiles one plan would.
+    if (m <= 256) return 32;
     // fp32 products are latency-bound for small groups: 64-tiles give four
-    // times the workgroups when 128-tiles would not fill the 256 CUs twice.
+    // times the workgroups when 128-tiles would not fill the 256 CUs twice
+    // (both kernels add each element's products in the same order).
     const int64_t t = (m + 127) / 128;
     return double(count) * double(t * (t + 1) / 2) < 512.0 ? 64 : 128;
   }
@@ -199,12 +205,12 @@ std::string build_plan(const int64_t* rows, const int64_t* cols, int count, int 
     gp.tile = gp.state32 ? 128 : tc.tile ? tc.tile : ov ? ov : choose_tile(gp.op, gp.m, gp.count);
     gp.xcdShift = tc.xcdShift;
     gp.band = tc.band;
-    gp.Mp = round_up(gp.m, gp.tile);
+    gp.Mp = round_up(gp.m, std::max(gp.tile, kCastTile));  // the cast pads in 64×64 tiles
   }
   for (BucketPlan& bp : P.buckets) {
     const GroupPlan& gp = P.groups[bp.group];
     bp.Mp = gp.Mp;
-    bp.Np = round_up(bp.n, gp.tile);
+    bp.Np = round_up(bp.n, std::max(gp.tile, kCastTile));
     for (int k = 0; k < (int)bp.mats.size(); ++k) {
       MatPlan& mp = P.mats[bp.mats[k]];
       mp.group = bp.group;

@@ -87,6 +87,31 @@ def test_budget_chunks_equal_one_plan_bitwise(mns):
     assert ei.value.status_name == "WORKSPACE"
 
 
+def test_budget_chunks_of_fp32_groups_equal_one_plan_bitwise(mns):
+    """Small nearly square matrices run fp32 products on tiles chosen by m
+    alone, so chunks of fewer matrices pick the tiles of the whole call and
+    the weights match one plan bit for bit."""
+    shapes = [(128, 128), (256, 300), (200, 200)] * 4 + [(700, 800)] * 2
+    plan = mns.describe_plan(shapes, for_step=True)
+    assert {g["m"]: g["op"] for g in plan["groups"]} == {128: "f32", 256: "f32", 200: "f32", 700: "f32"}
+    budget = max(mns.step_workspace_size([s]) for s in shapes)
+    assert budget < mns.step_workspace_size(shapes)
+    base = W.muon_inputs(shapes, 6301, device="cuda")
+    p1, g1, m1 = clone(base)
+    p2, g2, m2 = clone(base)
+    for step in range(2):
+        if step:
+            g1 = W.fresh_grads(shapes, 6301, step, device="cuda")
+            g2 = [g.clone() for g in g1]
+        say("fp32 groups, budget", budget, "step", step)
+        ws = torch.empty(budget, dtype=torch.uint8, device="cuda")
+        mns.muon_step(p1, g1, m1, workspace=ws, max_workspace_bytes=budget)
+        mns.muon_step(p2, g2, m2)
+        torch.cuda.synchronize()
+        assert_same(p1, p2, "weights")
+        assert_same(m1, m2, "momentum")
+
+
 def test_overlapped_step_graph_replays_match_eager(mns):
     """The overlapped schedule forks to the library's stream and joins back
     with events; captured into a graph (the stream exists after the first

@@ -86,6 +86,26 @@ def test_fp32_ragged_tall_wide(mns):
         assert e <= TOL_F32
 
 
+def test_fp32_split_contraction_tiles(mns):
+    """fp32 groups with m ≤ 256 run on 32-tiles whose contraction is split
+    over four waves: several tiles per matrix, ragged m padded to 64, long
+    SYRK contractions (n up to 4096), a tall input and a 40-matrix group (one
+    launch over many matrices), each matrix against the oracle."""
+    shapes = [(250, 3000), (96, 4096), (256, 256), (1000, 160), (33, 70)] + [(64, 200)] * 40
+    plan = mns.describe_plan(shapes, for_step=False, dtype=torch.float32)
+    assert all(g["tile"] == 32 for g in plan["groups"]), plan["groups"]
+    say("fp32 32-tile path", shapes[:5], "+ 40 x (64, 200)")
+    xs = [W.gaussian(s, 900 + i) for i, s in enumerate(shapes)]
+    outs = mns.muon_ns_batched([x.cuda() for x in xs], steps=5)
+    torch.cuda.synchronize()
+    for i, (x, o) in enumerate(zip(xs, outs)):
+        if i >= 5 and i % 13:
+            continue  # a sample of the group
+        e = rel(o, oracle_ns(x))
+        say(tuple(x.shape), e)
+        assert e <= TOL_F32
+
+
 # ------------------------------------------------------------------ bf16 path
 def test_bf16_ragged_mixed_batch(mns):
     shapes = [(300, 700), (700, 300), (129, 129), (1, 513), (513, 1), (64, 4096),

@@ -4,6 +4,7 @@ refused whole, and the state-carrying groups ignore the table."""
 import json
 
 import pytest
+import torch
 
 import muon_newton_schulz_06_amd as mns
 from muon_newton_schulz_06_amd import autotune
@@ -42,6 +43,7 @@ def test_invalid_tables_are_refused_and_leave_the_table_unchanged():
     mns.set_tile_table([{"m": 512, "op": "f16", "count_class": 2, "tile": 128}])
     bad = [
         [{"m": 512, "op": "f16", "count_class": 2, "tile": 64}],   # 64 is fp32 only
+        [{"m": 512, "op": "f16", "count_class": 2, "tile": 32}],   # 32 is fp32 only
         [{"m": 512, "op": "f32", "count_class": 2, "tile": 256}],  # 256 is fp16 only
         [{"m": 0, "op": "f16", "count_class": 2, "tile": 128}],
         [{"m": 512, "op": "f16", "count_class": 40, "tile": 128}],
@@ -107,3 +109,29 @@ def test_invalid_tile_order_entries_are_refused():
     arr[0].m, arr[0].op, arr[0].count_class, arr[0].reserved = 512, 0, 2, 1
     assert mns.load().muon_set_tile_table(arr, 1) == 1
     assert _tiles([(512, 3584)] * 4)[(512, "f16", 4)] == 128
+
+
+def test_fp32_small_groups_take_split_contraction_tiles():
+    """fp32 groups with m ≤ 256 use 32-tiles (contraction split over four
+    waves) whatever their matrix count — the split changes the fp32 summation
+    order, so a chunk of a call must pick what the whole call picks — and pad
+    to the cast's 64-element tiles; larger fp32 groups keep 64 or 128."""
+    for reps in (1, 3, 64):
+        shapes = [(256, 1024), (100, 130), (1024, 200), (512, 700)] * reps
+        p = mns.describe_plan(shapes, for_step=False, dtype=torch.float32)
+        g = {gr["m"]: gr for gr in p["groups"]}
+        assert g[256]["tile"] == 32 and g[100]["tile"] == 32 and g[200]["tile"] == 32
+        assert g[512]["tile"] in (64, 128)
+        for b in p["buckets"]:
+            t = p["groups"][b["group"]]["tile"]
+            assert b["Mp"] % max(t, 64) == 0 and b["Np"] % max(t, 64) == 0
+            assert 0 <= b["Mp"] - b["m"] < max(t, 64) and 0 <= b["Np"] - b["n"] < max(t, 64)
+    # a table may pick 32 for an fp32 group, and 64 for a small one
+    mns.set_tile_table([{"m": 512, "op": "f32", "count_class": 0, "tile": 32},
+                        {"m": 256, "op": "f32", "count_class": 0, "tile": 64}])
+    try:
+        p = mns.describe_plan([(512, 700), (256, 1024)], for_step=False, dtype=torch.float32)
+        t = {gr["m"]: gr["tile"] for gr in p["groups"]}
+        assert t == {512: 32, 256: 64}
+    finally:
+        mns.set_tile_table([])
