@@ -526,10 +526,12 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const GemmLaunch L) 
 // per k-tile, lanes 0-31 and 32-63 supplying the two k of each, so the four
 // waves cover k = 16·(w/2) + 8·(lane/32) + 4·(w%2) + 0..3 once.  The partial
 // sums are added in wave order (0, 1, 2, 3), so a result does not depend on
-// timing.  The epilogue inputs of the Gram products (A or Y at the block's
-// upper elements) are read before the main loop, hiding their latency.
-// Wave 0 then applies the register-staged kernel's epilogue to the block
-// (32×32 accumulator layout as there); all threads write the mirrored rows.
+// timing: wave w adds them for accumulator registers 4w .. 4w + 3 (rows
+// 8w + 4·(lane/32) + 0..3 of the block, 32×32 accumulator layout as in the
+// register-staged kernel) and applies that kernel's epilogue to those rows.
+// The epilogue inputs of the Gram products (A or Y at the block's upper
+// elements) are read before the main loop, hiding their latency; all
+// threads write the mirrored rows.
 template <int EPI>
 __global__ __launch_bounds__(256) void gemm32_kernel(const GemmLaunch L) {
   using T = float;
@@ -537,7 +539,7 @@ __global__ __launch_bounds__(256) void gemm32_kernel(const GemmLaunch L) {
   constexpr bool kSym = EPI == EPI_SYRK || EPI == EPI_SQ || EPI == EPI_AXPY;
   constexpr bool kPrev = EPI == EPI_SQ || EPI == EPI_AXPY;
   __shared__ u32x4 smem[2][(BM + BN) * CH];  // double-buffered k-tile, 16 KiB
-  __shared__ floatx16 part[3][64];           // partial sums of waves 1..3
+  __shared__ floatx16 part[4][64];           // partial sums of the four waves
 
   const TilePos tp = locate(L);
   const GemmSeg& S = L.seg[tp.seg];
@@ -555,15 +557,13 @@ __global__ __launch_bounds__(256) void gemm32_kernel(const GemmLaunch L) {
   const int so = r * CH + (c ^ swz8(r));
 
   const EpiArgs<T> E = make_epi<T, EPI>(L, S, mat);
-  float prev[16];
+  // this wave's output rows: il0 + q, q = 0..3 (registers 4w + q)
+  const int il0 = 8 * wave + 4 * lh;
+  float prev[4];
   if constexpr (kPrev) {
-    if (wave == 0) {
-      static_for<0, 16>([&](auto rc) {
-        constexpr int rr = decltype(rc)::value;
-        const int il = 8 * (rr >> 2) + 4 * lh + (rr & 3);
-        prev[rr] = (ti < tj || il <= lr) ? sym_prev(E, ti * BM + il, tj * BN + lr) : 0.f;
-      });
-    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      prev[q] = (ti < tj || il0 + q <= lr) ? sym_prev(E, ti * BM + il0 + q, tj * BN + lr) : 0.f;
   }
 
   floatx16 acc[1][1];
@@ -595,36 +595,36 @@ __global__ __launch_bounds__(256) void gemm32_kernel(const GemmLaunch L) {
     }
     __syncthreads();
   }
-  if (wave > 0) part[wave - 1][lane] = acc[0][0];
+  part[wave][lane] = acc[0][0];
   __syncthreads();
-  if (wave == 0) {
-#pragma unroll
-    for (int p = 0; p < 3; ++p) {
-      const floatx16 v = part[p][lane];
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[0][0][e] += v[e];
-    }
-  }
-
   // 32×32 accumulator layout: lane l, register r holds
   // row 8·(r/4) + 4·(l/32) + r%4, column l%32 of the block.
+  float v[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float* pp = (const float*)&part[0][lane] + 4 * wave + q;
+    float x = pp[0];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) x += pp[w * 64 * 16];
+    v[q] = x;
+  }
+
   if constexpr (kSym) {
     // The ring is free (the loop ended with a barrier): the block is staged
     // there for the mirrored rows, as in the register-staged kernel.
     T* st = (T*)smem;
-    if (wave == 0) {
-      static_for<0, 16>([&](auto rc) {
-        constexpr int rr = decltype(rc)::value;
-        const int il = 8 * (rr >> 2) + 4 * lh + (rr & 3);
-        if (ti < tj || il <= lr)
-          st[sym_stage_idx<BN>(il, lr)] =
-              sym_value_with<T, EPI>(E, ti * BM + il, tj * BN + lr, acc[0][0][rr], kPrev ? prev[rr] : 0.f);
-      });
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int il = il0 + q;
+      if (ti < tj || il <= lr)
+        st[sym_stage_idx<BN>(il, lr)] =
+            sym_value_with<T, EPI>(E, ti * BM + il, tj * BN + lr, v[q], kPrev ? prev[q] : 0.f);
     }
     __syncthreads();
     mirror_rows<T, EPI, BM, BN, NT>(E, st, ti, tj, tid);
   } else {
-    if (wave == 0) epilogue_all<T, EPI, 1, 1>(E, ti * BM, tj * BN, lh, lr, acc);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) epilogue<T, EPI>(E, ti * BM + il0 + q, tj * BN + lr, v[q]);
   }
 }
 
