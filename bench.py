@@ -56,15 +56,26 @@ def traffic_for(kind, workload):
     return rec.get("bytes_per_launch")
 
 
+def strip_comments(text: str) -> str:
+    """C++ source without // and /* */ comments and without blank lines or
+    trailing spaces (string literals in these sources hold no comment
+    markers), so that edits of comments alone leave the code's hash as it
+    was."""
+    import re
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = (re.sub(r"//.*$", "", ln).rstrip() for ln in text.splitlines())
+    return "\n".join(ln for ln in lines if ln)
+
+
 def kernel_source_sha():
-    """sha256 over the 256-tile GEMM kernel sources (the template header and
-    its translation units), in name order."""
+    """sha256 over the code (comments stripped) of the GEMM kernel sources
+    (the template header and its translation units), in name order."""
     import hashlib
     csrc = os.path.join(ROOT, "muon_newton_schulz_06_amd", "csrc")
     h = hashlib.sha256()
     for name in sorted(f for f in os.listdir(csrc) if f.startswith("gemm")):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+        with open(os.path.join(csrc, name), encoding="utf-8") as f:
+            h.update(name.encode() + b"\0" + strip_comments(f.read()).encode())
     return h.hexdigest()
 
 

@@ -15,7 +15,7 @@
 // only.  Diagonal tiles store the element of the upper half into both (i, j)
 // and (j, i), so every stored iterate is exactly symmetric.
 //
-// Two kernels share the tile mapping and the epilogues:
+// Three kernels share the tile mapping and the epilogues:
 //  * gemm256_kernel: 256×256 fp16 tiles, 8 waves, direct global→LDS loads
 //    into a 4-slot ring.  Gram-space iterates are stored block-upper (only
 //    the 256×256 blocks on or above the diagonal, except the last Q, which
@@ -23,9 +23,11 @@
 //    left of its diagonal block from the transposed position, and the final
 //    product reads X₀ᵀ as transposed panels of X₀ (X₀ is kept in one layout);
 //  * gemm_kernel: 128×128 (fp32: also 64×64) tiles, 4 waves, register-staged
-//    double buffering (fp32 groups and groups carrying fp32 state); full,
-//    mirrored operands and both layouts of X₀.
-// Both keep k-rows in LDS with a 16-byte-chunk XOR swizzle chosen for the
+//    double buffering (fp32 groups with m > 256 and groups carrying fp32
+//    state); full, mirrored operands and both layouts of X₀;
+//  * gemm32_kernel: fp32 groups with m ≤ 256, 32×32 tiles whose contraction
+//    is split over four waves, with gemm_kernel's operands and epilogues.
+// All keep k-rows in LDS with a 16-byte-chunk XOR swizzle chosen for the
 // 64-bank LDS (conflict-free ds_read_b128 fragment reads).
 //
 // This header holds the kernel templates; each gemm_*.hip translation unit
