@@ -807,9 +807,10 @@ __device__ __forceinline__ void store_staged(_Float16* dst, int ldc, const char*
 
 // Transposed LDS reads (ds_read_b64_tr_b16) of the staged tile, 16 output
 // rows at a time: 16-lane group g of wave w handles the 16-byte column chunk
-// q = 4w + g, lane i row r0 + i.  Two reads give a lane its chunk's 8 values
-// from staged rows 8q .. 8q + 7 at column r0 + i (lane j of the group points
-// at staged row k0 + j/4, columns r0 + 4·(j%4) .. +3).
+// q = 4w + g (c0 = 8q), lane i row r0 + i.  Two reads give a lane its
+// chunk's 8 values from staged rows c0 .. c0 + 7 at column r0 + i (lane j of
+// the group points at staged row c0 + j/4, then c0 + 4 + j/4, columns
+// r0 + 4·(j%4) .. +3).
 template <bool kY>
 __device__ __forceinline__ half8 tr_chunk(const char* lds, int r0, int c0, int j) {
   const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
