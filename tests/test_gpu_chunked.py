@@ -112,6 +112,28 @@ def test_budget_chunks_of_fp32_groups_equal_one_plan_bitwise(mns):
         assert_same(m1, m2, "momentum")
 
 
+def test_fp32_64_and_128_tiles_give_the_same_bits(mns):
+    """The built-in tile of an fp32 group with m > 256 depends on its matrix
+    count (64-tiles for small groups, 128 otherwise), which a chunked call
+    changes; both kernels add each element's products in the same order, so
+    the results must not depend on the choice."""
+    xs = [W.gaussian((512, 1024), 31, device="cuda"), W.gaussian((700, 900), 32, device="cuda")]
+    res = {}
+    try:
+        for tile in (64, 128):
+            mns.set_tile_table([{"m": 512, "op": "f32", "count_class": 0, "tile": tile},
+                                {"m": 700, "op": "f32", "count_class": 0, "tile": tile}])
+            p = mns.describe_plan([tuple(x.shape) for x in xs], for_step=False, dtype=torch.float32)
+            assert all(g["tile"] == tile for g in p["groups"]), p["groups"]
+            say("fp32 groups on", tile, "tiles")
+            res[tile] = [o.clone() for o in mns.muon_ns_batched(xs, steps=5)]
+            torch.cuda.synchronize()
+    finally:
+        mns.set_tile_table([])
+    for a, b in zip(res[64], res[128]):
+        assert torch.equal(a, b), tuple(a.shape)
+
+
 def test_overlapped_step_graph_replays_match_eager(mns):
     """The overlapped schedule forks to the library's stream and joins back
     with events; captured into a graph (the stream exists after the first
